@@ -1,0 +1,70 @@
+"""Packing metadata of a native-resolution text+image batch (oracle, fp64/int).
+
+TEST INFRASTRUCTURE: used only by tests, the smoke check and the CPU baseline.
+
+Source: Mage-Flow tech report, NR-MMDiT section. Images of any resolution and
+aspect ratio are encoded, flattened into variable-length latent token
+sequences and packed into one contiguous batch; prompt embeddings are packed
+the same way instead of being padded; attention is kept inside each sample
+through per-sample cumulative offsets. The editing paragraph of the same
+section orders a sample's sequence as the text condition first, then the
+latent tokens. The mageflow.net architecture page (section 2) encodes the
+2D spatial position of every latent token.
+
+Readings taken where the pages are silent:
+* a sample is [prompt tokens ; image tokens] (text first);
+* the image grid is flattened row-major (row outer, column inner);
+* positions are zero-based integers with no centring or rescaling;
+* prompt tokens carry position (0, 0).
+"""
+from __future__ import annotations
+
+import numpy as np
+
+
+def segment_lengths(grid_hw, text_len) -> np.ndarray:
+    """L_i = text_len_i + h_i * w_i for every sample (int64)."""
+    g = np.asarray(grid_hw, dtype=np.int64).reshape(-1, 2)
+    t = np.asarray(text_len, dtype=np.int64).reshape(-1)
+    if g.shape[0] != t.shape[0]:
+        raise ValueError("grid_hw and text_len disagree on the number of samples")
+    if (g < 1).any() or (t < 0).any():
+        raise ValueError("grid sides must be >= 1 and prompt lengths >= 0")
+    return t + g[:, 0] * g[:, 1]
+
+
+def cu_seqlens(grid_hw, text_len) -> np.ndarray:
+    """Per-sample cumulative offsets: cu[0] = 0, cu[i+1] = cu[i] + L_i (int32)."""
+    lengths = segment_lengths(grid_hw, text_len)
+    cu = np.zeros(lengths.shape[0] + 1, dtype=np.int64)
+    for i, length in enumerate(lengths):
+        cu[i + 1] = cu[i] + length
+    if cu[-1] >= 2**31:
+        raise ValueError("packed batch exceeds int32 token indices")
+    return cu.astype(np.int32)
+
+
+def token_positions(grid_hw, text_len):
+    """Per-token (row, col) position and sample id of the packed sequence.
+
+    Returns ``pos`` int32 [T, 2] and ``seg_id`` int32 [T]. Token u of sample i
+    (u counted from the start of the sample) is a prompt token at (0, 0) when
+    u < text_len_i; otherwise it is image token p = u - text_len_i, which sits
+    at row p // w_i and column p % w_i of the latent grid.
+    """
+    g = np.asarray(grid_hw, dtype=np.int64).reshape(-1, 2)
+    t = np.asarray(text_len, dtype=np.int64).reshape(-1)
+    lengths = segment_lengths(g, t)
+    total = int(lengths.sum())
+    pos = np.zeros((total, 2), dtype=np.int32)
+    seg = np.zeros(total, dtype=np.int32)
+    start = 0
+    for i in range(g.shape[0]):
+        h, w, n_text = int(g[i, 0]), int(g[i, 1]), int(t[i])
+        seg[start : start + n_text + h * w] = i
+        # prompt tokens stay at (0, 0)
+        p = np.arange(h * w, dtype=np.int64)
+        pos[start + n_text : start + n_text + h * w, 0] = p // w
+        pos[start + n_text : start + n_text + h * w, 1] = p % w
+        start += n_text + h * w
+    return pos, seg

@@ -1,0 +1,415 @@
+"""Pins of the fp64 oracle against what the pages and the mathematics fix.
+
+Each test checks the oracle against something other than itself: hand-worked
+examples (tests/golden), closed forms, invariants, special cases that reduce
+to a textbook result, brute force on tiny inputs, and finite differences.
+"""
+import itertools
+import json
+import math
+import os
+
+import numpy as np
+import pytest
+
+from oracle import attention, packing, rectified_flow, rope
+from text_image_diffusion_varlen_amd import workloads
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
+
+
+def _golden(name):
+    with open(os.path.join(GOLDEN, name)) as f:
+        return json.load(f)
+
+
+# ---------------------------------------------------------------- packing
+
+def test_packing_hand_example():
+    g = _golden("packing_small.json")
+    cu = packing.cu_seqlens(g["grid_hw"], g["text_len"])
+    pos, seg = packing.token_positions(g["grid_hw"], g["text_len"])
+    assert cu.tolist() == g["cu_seqlens"]
+    assert pos.tolist() == g["pos"]
+    assert seg.tolist() == g["seg_id"]
+
+
+def _positions_by_enumeration(grid_hw, text_len):
+    """Independent construction: emit the prompt, then walk the grid with nested loops."""
+    pos, seg = [], []
+    for i, ((h, w), t) in enumerate(zip(grid_hw, text_len)):
+        for _ in range(t):
+            pos.append((0, 0))
+            seg.append(i)
+        for r in range(h):
+            for c in range(w):
+                pos.append((r, c))
+                seg.append(i)
+    return pos, seg
+
+
+@pytest.mark.parametrize("seed", range(6))
+def test_packing_matches_enumeration(seed):
+    rng = np.random.default_rng(100 + seed)
+    n = int(rng.integers(1, 6))
+    grid = [(int(rng.integers(1, 9)), int(rng.integers(1, 9))) for _ in range(n)]
+    text = [int(rng.integers(0, 7)) for _ in range(n)]
+    pos, seg = packing.token_positions(grid, text)
+    pos_e, seg_e = _positions_by_enumeration(grid, text)
+    assert [tuple(p) for p in pos.tolist()] == pos_e
+    assert seg.tolist() == seg_e
+    cu = packing.cu_seqlens(grid, text)
+    # offsets are where the sample id changes
+    starts = [0] + [j for j in range(1, len(seg_e)) if seg_e[j] != seg_e[j - 1]] + [len(seg_e)]
+    assert cu.tolist() == starts
+
+
+@pytest.mark.parametrize("config", ["tiny", "1024sq", "mixed", "2048sq", "train65k"])
+def test_packing_invariants_on_configs(config):
+    grid, text = workloads.make_segments(config)
+    cu = packing.cu_seqlens(grid, text)
+    pos, seg = packing.token_positions(grid, text)
+    assert cu[0] == 0 and cu[-1] == pos.shape[0]
+    assert np.all(np.diff(cu) == text + grid[:, 0] * grid[:, 1])
+    for i in range(len(text)):
+        a, b = cu[i], cu[i + 1]
+        assert np.all(seg[a:b] == i)
+        p = pos[a + text[i] : b]
+        h, w = grid[i]
+        assert p[:, 0].max() < h and p[:, 1].max() < w and p.min() >= 0
+        # every grid cell exactly once
+        cells = p[:, 0].astype(np.int64) * w + p[:, 1]
+        assert np.array_equal(np.sort(cells), np.arange(h * w))
+        assert np.all(pos[a : a + text[i]] == 0)
+    if config == "train65k":
+        assert cu[-1] <= 65536
+
+
+def test_packing_rejects_bad_segments():
+    with pytest.raises(ValueError):
+        packing.cu_seqlens([[0, 4]], [3])
+    with pytest.raises(ValueError):
+        packing.cu_seqlens([[2, 4]], [-1])
+    with pytest.raises(ValueError):
+        packing.cu_seqlens([[2, 4], [1, 1]], [3])
+
+
+def test_workload_recipes():
+    g, t = workloads.make_segments("mixed")
+    assert g.tolist() == [[32, 128], [128, 32], [48, 84], [64, 64], [32, 32]]
+    assert np.all((t >= 77) & (t <= 256))
+    g, t = workloads.make_segments("train65k")
+    assert np.all(g % 2 == 0) and g.min() >= 32 and g.max() <= 128
+    w = workloads.make_workload("tiny")
+    assert w.q.shape == (288, 2, 64) and w.dtype == "f32"
+    # bf16 rounding of the generator is round-to-nearest-even
+    x = np.array([1.0, 1.0 + 2**-8, 1.0 + 3 * 2**-8, -2.0 - 2**-7 * 1.5], dtype=np.float32)
+    r = workloads.bf16_bits_to_f32(workloads.f32_to_bf16_bits(x))
+    assert r.tolist() == [1.0, 1.0, 1.0 + 2**-6, -2.0 - 2**-6]
+
+
+# ---------------------------------------------------------------- rope
+
+def test_rope_hand_examples():
+    for case in _golden("rope_small.json")["cases"]:
+        x = np.array(case["x"], dtype=np.float64).reshape(1, 1, -1)
+        got = rope.rope2d(x, np.array([case["pos"]]))[0, 0]
+        exp = []
+        for j, phi in enumerate(case["pair_angles"]):
+            x0, x1 = case["x"][2 * j], case["x"][2 * j + 1]
+            exp += [x0 * math.cos(phi) - x1 * math.sin(phi), x0 * math.sin(phi) + x1 * math.cos(phi)]
+        np.testing.assert_allclose(got, exp, rtol=0, atol=1e-15)
+
+
+def test_rope_frequency_ladder():
+    for d in (8, 64, 128):
+        f = rope.axis_frequencies(d // 2)
+        assert f.shape == (d // 4,)
+        assert f[0] == 1.0
+        ratio = f[1:] / f[:-1]
+        np.testing.assert_allclose(ratio, ratio[0], rtol=1e-13)
+        # one more rung of the ladder reaches exactly 1/theta
+        np.testing.assert_allclose(f[-1] * ratio[0], 1.0 / 10000.0, rtol=1e-12)
+
+
+def _rand(shape, seed):
+    return np.random.default_rng(seed).standard_normal(shape)
+
+
+@pytest.mark.parametrize("d", [8, 64, 128])
+def test_rope_is_complex_rotation(d):
+    """Each channel pair, read as a complex number x0 + i x1, is multiplied by exp(i phi)."""
+    x = _rand((5, 3, d), 1)
+    pos = np.array([[0, 0], [1, 7], [63, 2], [127, 127], [9, 0]])
+    got = rope.rope2d(x, pos)
+    z = x[..., 0::2] + 1j * x[..., 1::2]
+    half = d // 4
+    for t in range(5):
+        for p in range(d // 2):
+            axis, j = (0, p) if p < half else (1, p - half)
+            phi = pos[t, axis] * 10000.0 ** (-2.0 * j / (d // 2))
+            w = z[t, :, p] * np.exp(1j * phi)
+            np.testing.assert_allclose(got[t, :, 2 * p], w.real, atol=1e-12)
+            np.testing.assert_allclose(got[t, :, 2 * p + 1], w.imag, atol=1e-12)
+
+
+def test_rope_norm_identity_inverse_composition():
+    x = _rand((40, 2, 64), 2)
+    rng = np.random.default_rng(3)
+    p1 = rng.integers(0, 128, size=(40, 2))
+    p2 = rng.integers(0, 128, size=(40, 2))
+    r = rope.rope2d(x, p1)
+    np.testing.assert_allclose(np.linalg.norm(r, axis=-1), np.linalg.norm(x, axis=-1), rtol=1e-13)
+    np.testing.assert_array_equal(rope.rope2d(x, np.zeros_like(p1)), x)
+    np.testing.assert_allclose(rope.rope2d_inverse(r, p1), x, atol=1e-12)
+    np.testing.assert_allclose(rope.rope2d(r, p2), rope.rope2d(x, p1 + p2), atol=1e-11)
+
+
+def test_rope_relative_position_invariance():
+    """R(p) q . R(p') k depends only on p - p' (a shared integer shift changes nothing)."""
+    q = _rand((30, 2, 128), 4)
+    k = _rand((30, 2, 128), 5)
+    rng = np.random.default_rng(6)
+    pq = rng.integers(0, 100, size=(30, 2))
+    pk = rng.integers(0, 100, size=(30, 2))
+    base = np.einsum("thd,shd->tsh", rope.rope2d(q, pq), rope.rope2d(k, pk))
+    for shift in ([5, 0], [0, 11], [17, 23]):
+        s = np.array(shift)
+        moved = np.einsum("thd,shd->tsh", rope.rope2d(q, pq + s), rope.rope2d(k, pk + s))
+        np.testing.assert_allclose(moved, base, atol=1e-10)
+    # and it is not invariant to a shift of only one side (the rotation does something)
+    moved = np.einsum("thd,shd->tsh", rope.rope2d(q, pq + 3), rope.rope2d(k, pk))
+    assert np.abs(moved - base).max() > 1e-2
+
+
+def test_rope_reduces_to_1d_on_a_single_row():
+    """On a 1 x w grid the row half is untouched and the column half is ordinary 1D RoPE
+    over d/2 channels (pair j at angle col * theta^(-2j/(d/2)))."""
+    d = 64
+    x = _rand((12, 2, d), 7)
+    pos = np.stack([np.zeros(12, int), np.arange(12)], axis=1)
+    got = rope.rope2d(x, pos)
+    np.testing.assert_array_equal(got[..., : d // 2], x[..., : d // 2])
+    xb = x[..., d // 2 :]
+    z = xb[..., 0::2] + 1j * xb[..., 1::2]
+    m = d // 2
+    inv = 10000.0 ** (-np.arange(0, m, 2) / m)
+    w = z * np.exp(1j * np.arange(12)[:, None, None] * inv[None, None, :])
+    np.testing.assert_allclose(got[..., d // 2 :: 2], w.real, atol=1e-12)
+    np.testing.assert_allclose(got[..., d // 2 + 1 :: 2], w.imag, atol=1e-12)
+
+
+def test_rope3d_reduces_to_2d_at_frame_zero():
+    x = _rand((10, 2, 16), 8)
+    rng = np.random.default_rng(9)
+    p = rng.integers(0, 50, size=(10, 2))
+    p3 = np.concatenate([p, np.zeros((10, 1), int)], axis=1)
+    # row/col blocks of 8 channels and an empty frame block: identical to rope2d
+    np.testing.assert_allclose(rope.rope3d(x, p3, (8, 8, 0)), rope.rope2d(x, p), atol=1e-14)
+    # the frame block only turns when the frame index changes
+    y = rope.rope3d(x, p3, (4, 4, 8))
+    np.testing.assert_array_equal(y[..., 8:], x[..., 8:])
+    p3[:, 2] = 1
+    assert np.abs(rope.rope3d(x, p3, (4, 4, 8))[..., 8:] - x[..., 8:]).max() > 1e-3
+
+
+# ---------------------------------------------------------------- attention
+
+def _brute_attention(q, k, v, scale):
+    """Triple loop in pure Python floats: no BLAS, no vectorization."""
+    L, H, d = len(q), len(q[0]), len(q[0][0])
+    out = [[[0.0] * len(v[0][0]) for _ in range(H)] for _ in range(L)]
+    for h in range(H):
+        for i in range(L):
+            s = [sum(q[i][h][c] * k[j][h][c] for c in range(d)) * scale for j in range(len(k))]
+            m = max(s)
+            e = [math.exp(x - m) for x in s]
+            z = sum(e)
+            for c in range(len(v[0][0])):
+                out[i][h][c] = sum(e[j] * v[j][h][c] for j in range(len(k))) / z
+    return out
+
+
+def test_attention_hand_example():
+    g = _golden("attention_small.json")
+    q = np.array(g["q"])[:, None, :]
+    k = np.array(g["k"])[:, None, :]
+    v = np.array(g["v"])[:, None, :]
+    got = attention.sample_attention(q, k, v)[:, 0, :]
+    np.testing.assert_allclose(got, g["out"], atol=1e-12)
+
+
+@pytest.mark.parametrize("L,H,d", [(1, 1, 4), (7, 2, 8), (23, 2, 16)])
+def test_attention_matches_brute_force(L, H, d):
+    rng = np.random.default_rng(L * 31 + d)
+    q, k, v = (rng.standard_normal((L, H, d)) for _ in range(3))
+    got = attention.sample_attention(q, k, v, row_block=5)
+    exp = _brute_attention(q.tolist(), k.tolist(), v.tolist(), 1.0 / math.sqrt(d))
+    np.testing.assert_allclose(got, np.array(exp), atol=1e-12)
+
+
+def test_attention_special_cases():
+    rng = np.random.default_rng(11)
+    q, v = rng.standard_normal((9, 2, 8)), rng.standard_normal((9, 2, 8))
+    # zero keys: uniform weights -> mean of v
+    got = attention.sample_attention(q, np.zeros_like(q), v)
+    np.testing.assert_allclose(got, np.broadcast_to(v.mean(axis=0), v.shape), atol=1e-13)
+    # constant values: output is that constant
+    c = np.broadcast_to(rng.standard_normal((1, 2, 8)), v.shape)
+    got = attention.sample_attention(q, rng.standard_normal(q.shape), c)
+    np.testing.assert_allclose(got, c, atol=1e-13)
+    # a single token attends only to itself
+    got = attention.sample_attention(q[:1], q[:1] * 3, v[:1])
+    np.testing.assert_allclose(got, v[:1], atol=0)
+    # two keys: weight of key 0 is the logistic function of the score gap
+    k2 = rng.standard_normal((2, 1, 8))
+    v2 = np.array([[[1.0] * 8], [[0.0] * 8]])
+    q1 = rng.standard_normal((3, 1, 8))
+    got = attention.sample_attention(q1, k2, v2)[:, 0, 0]
+    gap = (q1[:, 0] @ (k2[0, 0] - k2[1, 0])) / math.sqrt(8)
+    np.testing.assert_allclose(got, 1.0 / (1.0 + np.exp(-gap)), atol=1e-14)
+
+
+def test_attention_sharp_limit_is_argmax():
+    rng = np.random.default_rng(12)
+    q, k, v = (rng.standard_normal((6, 1, 8)) for _ in range(3))
+    got = attention.sample_attention(q, k, v, scale=1e4)
+    best = np.argmax(q[:, 0] @ k[:, 0].T, axis=1)
+    np.testing.assert_allclose(got[:, 0], v[best, 0], atol=1e-9)
+
+
+def test_attention_permutation_rules():
+    rng = np.random.default_rng(13)
+    q, k, v = (rng.standard_normal((15, 2, 8)) for _ in range(3))
+    base = attention.sample_attention(q, k, v)
+    perm = rng.permutation(15)
+    np.testing.assert_allclose(attention.sample_attention(q, k[perm], v[perm]), base, atol=1e-13)
+    np.testing.assert_allclose(attention.sample_attention(q[perm], k, v), base[perm], atol=1e-13)
+
+
+def test_packed_equals_masked_dense():
+    grid, text = [[3, 4], [1, 1], [2, 5], [4, 1]], [2, 0, 5, 3]
+    cu = packing.cu_seqlens(grid, text)
+    _, seg = packing.token_positions(grid, text)
+    rng = np.random.default_rng(14)
+    T = int(cu[-1])
+    q, k, v = (rng.standard_normal((T, 2, 8)) for _ in range(3))
+    np.testing.assert_allclose(
+        attention.packed_attention(q, k, v, cu), attention.masked_attention(q, k, v, seg), atol=1e-13)
+    # a sample's output does not depend on the other samples' contents
+    k2 = k.copy()
+    k2[cu[1] :] = rng.standard_normal(k2[cu[1] :].shape)
+    a = attention.packed_attention(q, k, v, cu)
+    b = attention.packed_attention(q, k2, v, cu)
+    np.testing.assert_array_equal(a[: cu[1]], b[: cu[1]])
+
+
+def test_joint_attention_pipeline_small():
+    """Full path = explicit rotation + masked dense attention, on the hand-worked packing."""
+    g = _golden("packing_small.json")
+    rng = np.random.default_rng(15)
+    T = g["cu_seqlens"][-1]
+    q, k, v = (rng.standard_normal((T, 2, 8)) for _ in range(3))
+    got = attention.joint_attention(q, k, v, g["grid_hw"], g["text_len"])
+    pos = np.array(g["pos"])
+    exp = attention.masked_attention(rope.rope2d(q, pos), rope.rope2d(k, pos), v, np.array(g["seg_id"]))
+    np.testing.assert_allclose(got, exp, atol=1e-13)
+    rows = [0, 5, 9, 13]
+    np.testing.assert_allclose(
+        attention.joint_attention_rows(q, k, v, g["grid_hw"], g["text_len"], rows), got[rows], atol=1e-13)
+
+
+def test_joint_attention_image_only_shift_invariance():
+    """With no prompt tokens every position is an image position; a common shift of
+    all of them leaves the attention output unchanged (relative RoPE)."""
+    grid, text = [[3, 5]], [0]
+    rng = np.random.default_rng(16)
+    q, k, v = (rng.standard_normal((15, 2, 16)) for _ in range(3))
+    base = attention.joint_attention(q, k, v, grid, text)
+    pos, _ = packing.token_positions(grid, text)
+    cu = packing.cu_seqlens(grid, text)
+    moved = pos + np.array([7, 4])
+    got = attention.packed_attention(rope.rope2d(q, moved), rope.rope2d(k, moved), v, cu)
+    np.testing.assert_allclose(got, base, atol=1e-12)
+
+
+def test_lse_matches_brute_force():
+    rng = np.random.default_rng(17)
+    q, k = rng.standard_normal((5, 1, 4)), rng.standard_normal((7, 1, 4))
+    lse = attention.sample_attention_lse(q, k)
+    for i in range(5):
+        s = [float(q[i, 0] @ k[j, 0]) / 2.0 for j in range(7)]
+        assert abs(lse[i, 0] - math.log(sum(math.exp(x) for x in s))) < 1e-12
+
+
+def _numeric_grad(f, x, eps=1e-6):
+    g = np.zeros_like(x)
+    for idx in itertools.product(*map(range, x.shape)):
+        xp = x.copy()
+        xp[idx] += eps
+        xm = x.copy()
+        xm[idx] -= eps
+        g[idx] = (f(xp) - f(xm)) / (2 * eps)
+    return g
+
+
+def test_attention_backward_finite_differences():
+    grid, text = [[2, 2], [1, 3]], [1, 2]
+    T = 10
+    rng = np.random.default_rng(18)
+    q, k, v, w = (rng.standard_normal((T, 2, 4)) for _ in range(4))
+
+    def loss(qq, kk, vv):
+        return float(np.sum(attention.joint_attention(qq, kk, vv, grid, text) * w))
+
+    dq, dk, dv = attention.joint_attention_backward(q, k, v, w, grid, text)
+    np.testing.assert_allclose(dq, _numeric_grad(lambda x: loss(x, k, v), q), atol=1e-7)
+    np.testing.assert_allclose(dk, _numeric_grad(lambda x: loss(q, x, v), k), atol=1e-7)
+    np.testing.assert_allclose(dv, _numeric_grad(lambda x: loss(q, k, x), v), atol=1e-7)
+
+
+# ---------------------------------------------------------------- rectified flow
+
+def test_rf_hand_example():
+    g = _golden("rf_small.json")
+    np.testing.assert_array_equal(rectified_flow.interpolate(g["z0"], g["z1"], g["t"]), g["z_t"])
+    np.testing.assert_array_equal(rectified_flow.target_velocity(g["z0"], g["z1"]), g["velocity"])
+    assert rectified_flow.interpolate(g["z0"], g["z1"], 0.0).tolist() == g["z0"]
+    assert rectified_flow.interpolate(g["z0"], g["z1"], 1.0).tolist() == g["z1"]
+
+
+@pytest.mark.parametrize("steps", [1, 4, 20, 30])
+def test_rf_euler_follows_the_straight_path(steps):
+    rng = np.random.default_rng(19)
+    z0, z1 = rng.standard_normal((2, 3, 8)), rng.standard_normal((2, 3, 8))
+    grid = rectified_flow.uniform_grid(steps)
+    fields = [lambda z, t: z1 - z0, lambda z, t: (z1 - z) / (1.0 - t)]
+    for field in fields:
+        for solver in (rectified_flow.euler, rectified_flow.midpoint):
+            states = solver(z0, field, grid)
+            for t, z in zip(grid, states):
+                np.testing.assert_allclose(z, t * z1 + (1 - t) * z0, atol=1e-12)
+            np.testing.assert_allclose(states[-1], z1, atol=1e-12)
+
+
+def test_rf_euler_is_inexact_on_a_curved_field():
+    """A field that is not constant along the path (v = -z, exact flow z0 e^{-t}): one
+    Euler step lands at z0 (1 - dt) per step, not on the exponential -- the solver is
+    genuinely stepping, not returning a closed form."""
+    z0 = np.array([1.0])
+    st = rectified_flow.euler(z0, lambda z, t: -z, rectified_flow.uniform_grid(4))
+    np.testing.assert_allclose(st[-1], [0.75**4], atol=1e-15)
+    st = rectified_flow.midpoint(z0, lambda z, t: -z, rectified_flow.uniform_grid(4))
+    np.testing.assert_allclose(st[-1], [(1 - 0.25 + 0.25**2 / 2) ** 4], atol=1e-15)
+
+
+def test_rf_loss_and_cfg():
+    rng = np.random.default_rng(20)
+    z0, z1 = rng.standard_normal((4, 6)), rng.standard_normal((4, 6))
+    assert rectified_flow.loss(z1 - z0, z0, z1) == 0.0
+    np.testing.assert_allclose(rectified_flow.loss(np.zeros_like(z0), z0, z1),
+                               np.mean(np.sum((z1 - z0) ** 2, axis=1)), rtol=1e-14)
+    vu, vc = rng.standard_normal((2, 5))
+    np.testing.assert_allclose(rectified_flow.cfg_combine(vu, vc, 0.0), vu)
+    np.testing.assert_allclose(rectified_flow.cfg_combine(vu, vc, 1.0), vc, atol=1e-15)
+    np.testing.assert_allclose(rectified_flow.cfg_combine(vu, vc, 5.0), 5 * vc - 4 * vu, atol=1e-13)

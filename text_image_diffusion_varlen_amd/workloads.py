@@ -1,0 +1,180 @@
+"""Seeded synthetic workloads for packed joint text+image attention.
+
+This module only draws random numbers. It holds none of the attention, RoPE or
+packing arithmetic, so both the GPU path and the CPU oracle can consume its
+output without sharing any of the method's code.
+
+A workload is a list of segments. Segment i is one prompt of ``text_len[i]``
+tokens followed by one image whose latent grid is ``grid_hw[i] = (h, w)`` at
+16 px per latent token (the VAE downsamples 16x with 128 channels: Mage-Flow
+tech report, Mage-VAE section; the 2x2 latent patches of the mageflow.net
+architecture page, section 2, give the same 16 px). Q, K and V are
+``[tokens, heads, head_dim]`` row-major in the packed (concatenated) order.
+
+bf16 inputs are drawn as float32 N(0, 1) and rounded to bf16 with
+round-to-nearest-even. Both sides read exactly those bf16 values; the float32
+view returned here holds them exactly.
+
+Random draws come in a fixed order per seed: segment metadata first, then q,
+k, v, each as ``standard_normal((T, H, d), float32)``.
+"""
+from __future__ import annotations
+
+from dataclasses import dataclass, field
+
+import numpy as np
+
+__all__ = [
+    "Workload",
+    "CONFIGS",
+    "make_workload",
+    "make_segments",
+    "make_custom",
+    "f32_to_bf16_bits",
+    "bf16_bits_to_f32",
+]
+
+# Packing budget of the training-style block (tokens per packed block).
+TRAIN_TOKEN_BUDGET = 65536
+
+
+def f32_to_bf16_bits(x: np.ndarray) -> np.ndarray:
+    """Round float32 values to bf16 (round to nearest, ties to even).
+
+    Returns the 16-bit patterns as uint16. Inputs are finite here.
+    """
+    b = np.ascontiguousarray(x, dtype=np.float32).view(np.uint32)
+    lsb = (b >> np.uint32(16)) & np.uint32(1)
+    rounded = (b + np.uint32(0x7FFF) + lsb) >> np.uint32(16)
+    return rounded.astype(np.uint16)
+
+
+def bf16_bits_to_f32(bits: np.ndarray) -> np.ndarray:
+    """Widen bf16 bit patterns to float32 (exact)."""
+    return (np.asarray(bits, dtype=np.uint16).astype(np.uint32) << np.uint32(16)).view(np.float32)
+
+
+@dataclass
+class Workload:
+    """One packed batch: segment metadata plus Q/K/V of the joint sequence."""
+
+    name: str
+    grid_hw: np.ndarray  # int32 [n, 2], (h, w) latent grid of each image
+    text_len: np.ndarray  # int32 [n], prompt tokens of each segment
+    heads: int
+    head_dim: int
+    dtype: str  # "bf16" or "f32"
+    q: np.ndarray = field(repr=False)  # float32 [T, H, d], exactly representable in dtype
+    k: np.ndarray = field(repr=False)
+    v: np.ndarray = field(repr=False)
+    seed: int = 0
+
+    @property
+    def n_seg(self) -> int:
+        return int(self.grid_hw.shape[0])
+
+    @property
+    def tokens(self) -> int:
+        return int(self.q.shape[0])
+
+    def bits(self, name: str) -> np.ndarray:
+        """bf16 bit patterns (uint16) of q, k or v; only for bf16 workloads."""
+        if self.dtype != "bf16":
+            raise ValueError("bit patterns exist only for bf16 workloads")
+        return f32_to_bf16_bits(getattr(self, name))
+
+
+def _draw_train_segments(rng: np.random.Generator, budget: int):
+    """Training-style block: images of independent H, W in multiples of 32 px in
+    [512, 2048], prompt length uniform in [77, 256], appended until the next
+    sample would exceed the token budget (that sample is dropped)."""
+    grids, texts, used = [], [], 0
+    while True:
+        h = int(rng.integers(16, 65)) * 2  # 32 px multiples -> grid side = px / 16
+        w = int(rng.integers(16, 65)) * 2
+        t = int(rng.integers(77, 257))
+        if used + t + h * w > budget:
+            break
+        grids.append((h, w))
+        texts.append(t)
+        used += t + h * w
+    return grids, texts
+
+
+# name -> (segment recipe, heads, head_dim, dtype, value scale, default seed)
+CONFIGS = {
+    # One 256x256 image (16x16 grid) and a 32-token prompt, fp32, 2 heads x 64.
+    "tiny": dict(grids=[(16, 16)], texts=[32], heads=2, head_dim=64, dtype="f32", scale=1.0 / 8.0, seed=0),
+    # One 1024x1024 image (64x64 grid) and a 256-token prompt.
+    "1024sq": dict(grids=[(64, 64)], texts=[256], heads=24, head_dim=128, dtype="bf16", scale=1.0, seed=1),
+    # Five mixed-aspect images, prompt lengths drawn uniformly in [77, 256].
+    "mixed": dict(
+        grids=[(32, 128), (128, 32), (48, 84), (64, 64), (32, 32)],
+        texts="draw",
+        heads=24,
+        head_dim=128,
+        dtype="bf16",
+        scale=1.0,
+        seed=2,
+    ),
+    # One 2048x2048 image (128x128 grid) and a 256-token prompt.
+    "2048sq": dict(grids=[(128, 128)], texts=[256], heads=24, head_dim=128, dtype="bf16", scale=1.0, seed=3),
+    # Training-style packed block under a 65536-token budget.
+    "train65k": dict(grids="train", texts="train", heads=24, head_dim=128, dtype="bf16", scale=1.0, seed=4),
+}
+
+
+def make_segments(config: str, seed: int | None = None):
+    """Draw only the segment metadata of a config: (grid_hw int32 [n,2], text_len int32 [n])."""
+    c = CONFIGS[config]
+    seed = c["seed"] if seed is None else seed
+    rng = np.random.default_rng(seed)
+    grids, texts = _segments_from_rng(c, rng)
+    return np.asarray(grids, dtype=np.int32).reshape(-1, 2), np.asarray(texts, dtype=np.int32)
+
+
+def _segments_from_rng(c, rng):
+    if c["grids"] == "train":
+        return _draw_train_segments(rng, TRAIN_TOKEN_BUDGET)
+    grids = list(c["grids"])
+    if c["texts"] == "draw":
+        texts = [int(rng.integers(77, 257)) for _ in grids]
+    else:
+        texts = list(c["texts"])
+    return grids, texts
+
+
+def _draw_qkv(rng, n_tokens, heads, head_dim, dtype, scale):
+    out = []
+    for _ in range(3):
+        x = rng.standard_normal((n_tokens, heads, head_dim), dtype=np.float32)
+        if scale != 1.0:
+            x = (x * np.float32(scale)).astype(np.float32)
+        if dtype == "bf16":
+            x = bf16_bits_to_f32(f32_to_bf16_bits(x))
+        out.append(np.ascontiguousarray(x))
+    return out
+
+
+def make_workload(config: str, seed: int | None = None) -> Workload:
+    """Build the seeded workload of a named config."""
+    c = CONFIGS[config]
+    seed = c["seed"] if seed is None else seed
+    rng = np.random.default_rng(seed)
+    grids, texts = _segments_from_rng(c, rng)
+    grid_hw = np.asarray(grids, dtype=np.int32).reshape(-1, 2)
+    text_len = np.asarray(texts, dtype=np.int32)
+    # Buffer size only: every segment contributes its prompt and its image grid.
+    n_tokens = int(text_len.astype(np.int64).sum() + (grid_hw[:, 0].astype(np.int64) * grid_hw[:, 1]).sum())
+    q, k, v = _draw_qkv(rng, n_tokens, c["heads"], c["head_dim"], c["dtype"], c["scale"])
+    return Workload(config, grid_hw, text_len, c["heads"], c["head_dim"], c["dtype"], q, k, v, seed)
+
+
+def make_custom(grid_hw, text_len, heads, head_dim, dtype="bf16", seed=0, scale=1.0, name="custom") -> Workload:
+    """Workload from explicit segments (used for edge cases: empty prompts, 1-wide grids, ragged tails)."""
+    grid_hw = np.asarray(grid_hw, dtype=np.int32).reshape(-1, 2)
+    text_len = np.asarray(text_len, dtype=np.int32).reshape(-1)
+    rng = np.random.default_rng(seed)
+    n_tokens = int(text_len.astype(np.int64).sum() + (grid_hw[:, 0].astype(np.int64) * grid_hw[:, 1]).sum())
+    q, k, v = _draw_qkv(rng, n_tokens, heads, head_dim, dtype, scale)
+    return Workload(name, grid_hw, text_len, heads, head_dim, dtype, q, k, v, seed)
