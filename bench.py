@@ -1,0 +1,239 @@
+#!/usr/bin/env python3
+"""Benchmark of packed joint text+image attention with 2D RoPE on one MI355X.
+
+One step = one call of mf_attn_packed over the whole packed batch: metadata
+check and tile table, 2D-RoPE prologue, per-sample flash attention. Inputs are
+seeded synthetic tensors already resident in device memory; the library's own
+metadata builder produces cu_seqlens before the timed region.
+
+Prints one JSON line. `value` is packed joint-attention TFLOP/s, counting only
+in-sample work: 4 * sum_i L_i^2 * head_dim * heads per step.
+
+  python bench.py [--steps K] [--warmup W] [--config 1024sq|mixed|2048sq|train65k|tiny]
+"""
+from __future__ import annotations
+
+import argparse
+import ctypes
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+PEAK = {"bf16": 2.5e15, "f32": 157.3e12}  # dense MFMA bf16; fp32 vector ALU
+HBM_PEAK = 8.0e12
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "attn_fwd_bf16_1024sq_traffic.json")
+KERNEL_SOURCES = [
+    os.path.join(ROOT, "text_image_diffusion_varlen_amd", "csrc", "attn_fwd.hip"),
+    os.path.join(ROOT, "text_image_diffusion_varlen_amd", "csrc", "mf_common.h"),
+]
+DESCRIPTIONS = {
+    "tiny": "one 256x256 image (16x16 grid) + 32 prompt tokens, L=288, 2 heads x 64, fp32",
+    "1024sq": "one 1024x1024 image (64x64 grid) + 256 prompt tokens, L=4352, 24 heads x 128, bf16",
+    "mixed": "5 mixed-aspect images (32x128, 128x32, 48x84, 64x64, 32x32 grids) + prompts of 77-256 tokens, 24 heads x 128, bf16",
+    "2048sq": "one 2048x2048 image (128x128 grid) + 256 prompt tokens, L=16640, 24 heads x 128, bf16",
+    "train65k": "training-style packed block under a 65536-token budget, 24 heads x 128, bf16",
+}
+
+
+def kernel_sha() -> str:
+    h = hashlib.sha256()
+    for p in KERNEL_SOURCES:
+        with open(p, "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()
+
+
+def stored_traffic(config: str):
+    """Measured HBM bytes per launch of the attention kernel, if the counters were
+    taken on the current kernel source for this workload; else None."""
+    if config != "1024sq" or not os.path.exists(TRAFFIC_FILE):
+        return None
+    with open(TRAFFIC_FILE) as f:
+        rec = json.load(f)
+    if rec.get("source_sha256") != kernel_sha():
+        return None
+    return rec.get("traffic_bytes")
+
+
+class HipEvents:
+    """Raw hipEvent_t handles from the HIP runtime already loaded by torch."""
+
+    def __init__(self, n):
+        self.hip = ctypes.CDLL("libamdhip64.so.7")
+        self.hip.hipEventCreate.argtypes = [ctypes.POINTER(ctypes.c_void_p)]
+        self.hip.hipEventElapsedTime.argtypes = [ctypes.POINTER(ctypes.c_float), ctypes.c_void_p, ctypes.c_void_p]
+        self.hip.hipEventDestroy.argtypes = [ctypes.c_void_p]
+        self.ev = []
+        for _ in range(n):
+            e = ctypes.c_void_p()
+            if self.hip.hipEventCreate(ctypes.byref(e)) != 0:
+                raise RuntimeError("hipEventCreate failed")
+            self.ev.append(e.value)
+
+    def elapsed_ms(self, a, b) -> float:
+        ms = ctypes.c_float()
+        rc = self.hip.hipEventElapsedTime(ctypes.byref(ms), ctypes.c_void_p(self.ev[a]), ctypes.c_void_p(self.ev[b]))
+        if rc != 0:
+            raise RuntimeError(f"hipEventElapsedTime failed ({rc})")
+        return ms.value
+
+    def close(self):
+        for e in self.ev:
+            self.hip.hipEventDestroy(ctypes.c_void_p(e))
+
+
+def sample_lengths(w):
+    return (w.text_len.astype("int64") + w.grid_hw[:, 0].astype("int64") * w.grid_hw[:, 1]).tolist()
+
+
+def cpu_baseline(w, budget_s: float):
+    """The fp64 oracle (as it stands) on host cores, over as many whole heads of the
+    same workload as fit in the time budget (at least one)."""
+    import numpy as np
+    from oracle import attention
+
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([int(i.get("num_threads", 1)) for i in threadpool_info() if i.get("user_api") == "blas"] or [1])
+    except Exception:  # threadpoolctl missing: report the affinity set
+        threads = len(os.sched_getaffinity(0))
+    lengths = sample_lengths(w)
+    per_head = 4.0 * sum(L * L for L in lengths) * w.head_dim
+    t0 = time.perf_counter()
+    heads = 0
+    while heads < w.heads:
+        h = slice(heads, heads + 1)
+        attention.joint_attention(w.q[:, h], w.k[:, h], w.v[:, h], w.grid_hw, w.text_len)
+        heads += 1
+        if time.perf_counter() - t0 > budget_s:
+            break
+    dt = time.perf_counter() - t0
+    return {
+        "value": per_head * heads / dt / 1e12,
+        "unit": "TFLOP/s",
+        "cores": threads,
+        "kind": "oracle",
+        "sample": f"{heads} of {w.heads} heads of the same workload (all rows, fp64 numpy), {dt:.1f} s",
+    }
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--config", default="1024sq", choices=sorted(DESCRIPTIONS))
+    ap.add_argument("--seed", type=int, default=None)
+    ap.add_argument("--cpu-budget", type=float, default=15.0, help="seconds of oracle work for cpu_baseline")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    args = ap.parse_args()
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print("bench.py measures one GPU only: this build has no multi-GPU path "
+              "(samples would shard by segment across GPUs; see the design notes).", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    from text_image_diffusion_varlen_amd import binding, workloads
+
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(1)
+    torch.cuda.set_device(0)
+    w = workloads.make_workload(args.config, seed=args.seed)
+    dt = torch.bfloat16 if w.dtype == "bf16" else torch.float32
+    q, k, v = (torch.from_numpy(x).to(dt).cuda() for x in (w.q, w.k, w.v))
+    grid = torch.from_numpy(w.grid_hw).cuda()
+    text = torch.from_numpy(w.text_len).cuda()
+    cu, _, _ = binding.build_metadata(grid, text, w.tokens)
+    out = torch.empty_like(q)
+    torch.cuda.synchronize()
+    if binding.get_device_error() != binding.MF_OK:
+        raise RuntimeError(binding.last_error())
+
+    lengths = sample_lengths(w)
+    flops = 4.0 * sum(L * L for L in lengths) * w.head_dim * w.heads
+    elem = 2 if w.dtype == "bf16" else 4
+    qkvo_bytes = 4.0 * w.tokens * w.heads * w.head_dim * elem
+
+    for _ in range(args.warmup):
+        binding.attn_packed(q, k, v, cu, grid, text, out=out)
+    torch.cuda.synchronize()
+
+    # Timed region: K whole steps, torch events on the stream the library launches on.
+    start, stop = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    start.record()
+    for _ in range(args.steps):
+        binding.attn_packed(q, k, v, cu, grid, text, out=out)
+    stop.record()
+    torch.cuda.synchronize()
+    ms = start.elapsed_time(stop) / args.steps
+    if binding.get_device_error() != binding.MF_OK:
+        raise RuntimeError(binding.last_error())
+
+    # Per-kernel durations: the same calls with HIP events between the three kernels.
+    ev = HipEvents(4 * args.steps)
+    for s in range(args.steps):
+        binding.attn_packed_profiled(q, k, v, cu, grid, text, ev.ev[4 * s : 4 * s + 4], out=out)
+    torch.cuda.synchronize()
+    stage = {"meta": 0.0, "rope_pack": 0.0, "attn": 0.0}
+    for s in range(args.steps):
+        b = 4 * s
+        stage["meta"] += ev.elapsed_ms(b, b + 1) / args.steps
+        stage["rope_pack"] += ev.elapsed_ms(b + 1, b + 2) / args.steps
+        stage["attn"] += ev.elapsed_ms(b + 2, b + 3) / args.steps
+    ev.close()
+
+    attn_s = stage["attn"] / 1e3
+    achieved = flops / attn_s
+    rope_bytes = 6.0 * w.tokens * w.heads * w.head_dim * elem
+    result = {
+        "metric": "packed joint-attn TFLOP/s (bf16, 2D RoPE) + % of MFMA peak; tokens/s",
+        "value": round(flops / (ms / 1e3) / 1e12, 2),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": w.dtype,
+        "data": "synthetic",
+        "config": {
+            "workload": f"{args.config}: {DESCRIPTIONS[args.config]}",
+            "tokens": w.tokens,
+            "samples": w.n_seg,
+            "heads": w.heads,
+            "head_dim": w.head_dim,
+            "seed": w.seed,
+            "flop_per_step": flops,
+        },
+        "pct_mfma_peak": round(100.0 * flops / (ms / 1e3) / PEAK[w.dtype], 2),
+        "tokens_per_s": round(w.tokens / (ms / 1e3), 1),
+        "stages_ms": {k2: round(v2, 4) for k2, v2 in stage.items()},
+        "rope_pack_gbps": round(rope_bytes / (stage["rope_pack"] / 1e3) / 1e9, 1),
+        "roofline": {
+            "kernel": f"attn_fwd_{w.dtype}_kernel<{w.head_dim}>",
+            "bound": "mfma" if w.dtype == "bf16" else "alu",
+            "achieved": round(achieved / 1e12, 2),
+            "peak": PEAK[w.dtype] / 1e12,
+            "unit": "TFLOP/s",
+            "frac": round(achieved / PEAK[w.dtype], 4),
+            "traffic": stored_traffic(args.config),
+            "algorithmic_bytes": qkvo_bytes,
+        },
+    }
+    if not args.no_cpu_baseline:
+        result["cpu_baseline"] = cpu_baseline(w, args.cpu_budget)
+    print(json.dumps(result), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,159 @@
+/*
+ * mf_attn.h -- packed joint text+image attention with 2D RoPE (gfx950 / MI355X).
+ *
+ * C ABI of libmfattn.so. Every pointer argument named "device" is HIP device
+ * memory owned by the caller; the library never frees caller memory. All
+ * work is enqueued on the caller's stream and returns without waiting, except
+ * where a function says it synchronizes. Functions return an mf_status; on a
+ * negative status nothing was enqueued and mf_last_error() holds a message.
+ *
+ * Operation (sources, by page and section):
+ *  - Mage-Flow tech report, NR-MMDiT section: text and image tokens of one
+ *    sample are concatenated and processed by joint self-attention; samples
+ *    of different resolutions and prompt lengths are packed back to back with
+ *    no padding, and per-sample cumulative offsets keep attention inside each
+ *    sample without an explicit block-diagonal mask. The editing paragraph of
+ *    that section puts the text condition before the latent tokens.
+ *  - mageflow.net architecture page, section 2: joint bidirectional attention
+ *    and 2D rotary position embeddings; section 8: text tokens are updated by
+ *    image tokens too (no causal mask).
+ *  - Mage-Flow tech report, Mage-VAE section: 16x spatial reduction, so an
+ *    image of H x W pixels has an (H/16) x (W/16) latent grid.
+ *
+ * Conventions fixed by this library where the pages are silent:
+ *  - sample i = [text_len[i] prompt tokens ; h_i * w_i image tokens], the grid
+ *    flattened row-major; L_i = text_len[i] + h_i * w_i;
+ *    cu_seqlens[0] = 0, cu_seqlens[i+1] = cu_seqlens[i] + L_i; T = cu_seqlens[n];
+ *  - prompt tokens sit at position (0, 0); image token p at (p / w, p % w);
+ *  - 2D RoPE: channels [0, d/2) turn with the row, [d/2, d) with the column;
+ *    adjacent pairs (2j, 2j+1) inside each half, frequency theta^(-2j/(d/2));
+ *    pair (x0, x1) -> (x0 cos - x1 sin, x0 sin + x1 cos); queries and keys
+ *    only; theta = 10000 in mf_attn_packed;
+ *  - softmax scale 1/sqrt(d); equal head counts for q, k, v.
+ *
+ * Tensor layout: q, k, v and out are contiguous [T][heads][head_dim] with
+ * elements of the given dtype (MF_BF16: bfloat16 bit patterns; MF_F32:
+ * float). Metadata arrays are contiguous int32 in device memory.
+ * Supported: head_dim in {64, 128}; 1 <= heads <= 256; 1 <= n_seg <= 4096;
+ * 1 <= h, w <= 512; 0 <= text_len; T < 2^31 (and every buffer < 2^31 elements
+ * per head).
+ */
+#ifndef MF_ATTN_H
+#define MF_ATTN_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  MF_OK = 0,
+  MF_ERR_INVALID_ARG = -1, /* bad scalar, null or overlapping pointer */
+  MF_ERR_METADATA = -2,    /* cu_seqlens / grid / prompt lengths inconsistent (device-detected) */
+  MF_ERR_UNSUPPORTED = -3, /* head_dim, dtype or size outside the supported set */
+  MF_ERR_HIP = -4,         /* a HIP runtime call failed */
+  MF_ERR_OOM = -5          /* workspace allocation failed */
+} mf_status;
+
+typedef enum { MF_BF16 = 0, MF_F32 = 1 } mf_dtype;
+
+#define MF_MAX_SEGMENTS 4096
+#define MF_MAX_GRID_SIDE 512
+#define MF_ROPE_THETA 10000.0f
+
+/* Library version as major*10000 + minor*100 + patch. */
+int mf_version(void);
+
+/* Message of the last failing call on this host thread ("" if none). */
+const char* mf_last_error(void);
+
+/*
+ * Packed joint attention with 2D RoPE: out = per-sample softmax(R(q) R(k)^T /
+ * sqrt(d)) v, where R is the 2D rotation at each token's (row, col).
+ *   q, k, v   device [total_tokens][heads][head_dim], dtype
+ *   cu_seqlens device int32 [n_seg + 1], must equal the prefix sums of L_i
+ *   grid_hw   device int32 [n_seg][2] = (h, w) latent grid of each image
+ *   text_len  device int32 [n_seg]
+ *   out       device [total_tokens][heads][head_dim], dtype; must not overlap
+ *             q, k, v or the metadata
+ * The library checks the metadata on the device (L_i >= 1, sides in range,
+ * cu_seqlens consistent, cu_seqlens[n_seg] == total_tokens). On a mismatch no
+ * output is written and mf_get_device_error() reports MF_ERR_METADATA.
+ * Uses a library-owned workspace per device (grown on demand, never shrunk,
+ * freed at process exit); calls on one device are serialized by the caller's
+ * stream order only, so concurrent calls on different streams of one device
+ * must use mf_attn_packed_ws with separate workspaces.
+ */
+int mf_attn_packed(const void* q, const void* k, const void* v, const int32_t* cu_seqlens,
+                   const int32_t* grid_hw, const int32_t* text_len, void* out, int32_t n_seg,
+                   int64_t total_tokens, int32_t heads, int32_t head_dim, int32_t dtype,
+                   hipStream_t stream);
+
+/*
+ * mf_attn_packed that also records four caller-created hipEvent_t on `stream`
+ * (events[0..3]): before the metadata kernel, after it, after the RoPE
+ * prologue and after the attention kernel, so each stage can be timed with
+ * hipEventElapsedTime. Otherwise identical to mf_attn_packed.
+ */
+int mf_attn_packed_profiled(const void* q, const void* k, const void* v, const int32_t* cu_seqlens,
+                            const int32_t* grid_hw, const int32_t* text_len, void* out,
+                            int32_t n_seg, int64_t total_tokens, int32_t heads, int32_t head_dim,
+                            int32_t dtype, hipEvent_t const* events, hipStream_t stream);
+
+/* Bytes of workspace mf_attn_packed_ws needs for these sizes (0 if unsupported). */
+size_t mf_workspace_bytes(int64_t total_tokens, int32_t heads, int32_t head_dim, int32_t dtype,
+                          int32_t n_seg);
+
+/*
+ * Same as mf_attn_packed with a caller-provided device workspace of at least
+ * mf_workspace_bytes(...) bytes, 256-byte aligned. The workspace must stay
+ * alive until the enqueued work finishes; nothing is allocated.
+ */
+int mf_attn_packed_ws(const void* q, const void* k, const void* v, const int32_t* cu_seqlens,
+                      const int32_t* grid_hw, const int32_t* text_len, void* out, int32_t n_seg,
+                      int64_t total_tokens, int32_t heads, int32_t head_dim, int32_t dtype,
+                      void* workspace, size_t workspace_bytes, hipStream_t stream);
+
+/*
+ * Packing metadata alone (same conventions as above).
+ *   grid_hw, text_len  device int32 inputs
+ *   cu_seqlens_out     device int32 [n_seg + 1]
+ *   pos_out            device int32 [total_tokens][2] = (row, col)
+ *   seg_id_out         device int32 [total_tokens]
+ * total_tokens is the capacity of pos_out / seg_id_out and must equal the
+ * packed length; otherwise nothing past the capacity is written and the
+ * device error flag reports MF_ERR_METADATA.
+ */
+int mf_build_metadata(int32_t n_seg, const int32_t* grid_hw, const int32_t* text_len,
+                      int32_t* cu_seqlens_out, int32_t* pos_out, int32_t* seg_id_out,
+                      int64_t total_tokens, hipStream_t stream);
+
+/*
+ * 2D RoPE alone: x_out = R(pos) x_in, per token and head.
+ *   x_in, x_out device [total_tokens][heads][head_dim], dtype (may be the same buffer)
+ *   pos         device int32 [total_tokens][2], each in [0, 512)
+ * fp32 arithmetic with a cos/sin table computed on the host in double
+ * precision; bf16 results are rounded to nearest even. Positions outside
+ * [0, 512) leave the row unchanged and set the device error flag.
+ */
+int mf_rope_2d(const void* x_in, void* x_out, const int32_t* pos, int64_t total_tokens,
+               int32_t heads, int32_t head_dim, int32_t dtype, float theta, hipStream_t stream);
+
+/*
+ * Synchronizes `stream`, then returns MF_ERR_METADATA if the last enqueued
+ * metadata check on this device's library workspace failed, else MF_OK.
+ */
+int mf_get_device_error(hipStream_t stream);
+
+/* Same, for a caller-provided workspace of mf_attn_packed_ws. */
+int mf_get_workspace_error(const void* workspace, hipStream_t stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* MF_ATTN_H */

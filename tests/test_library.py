@@ -1,0 +1,81 @@
+"""Host-side checks of the C-ABI library (no GPU needed): it loads, exports every
+function the header declares, and rejects bad arguments before touching a device."""
+import ctypes
+import subprocess
+
+import pytest
+
+from text_image_diffusion_varlen_amd import binding
+
+
+def test_library_loads_and_exports_header_symbols():
+    lib = binding.lib()
+    names = binding.header_functions()
+    assert len(names) >= 9
+    for name in names:
+        assert hasattr(lib, name), name
+    out = subprocess.run(["nm", "-D", "--defined-only", binding.LIB_PATH], capture_output=True, text=True).stdout
+    exported = {line.split()[-1] for line in out.splitlines() if line.strip()}
+    assert set(names) <= exported
+    assert binding.version() == 100
+
+
+def test_workspace_bytes():
+    import torch
+    wb = binding.workspace_bytes
+    assert wb(4352, 24, 128, torch.bfloat16, 1) > 3 * 4352 * 24 * 128 * 2
+    assert wb(4352, 24, 128, torch.float32, 1) > wb(4352, 24, 128, torch.bfloat16, 1)
+    lib = binding.lib()
+    assert lib.mf_workspace_bytes(100, 2, 96, 0, 1) == 0  # unsupported head_dim
+    assert lib.mf_workspace_bytes(100, 2, 64, 7, 1) == 0  # unknown dtype
+    assert lib.mf_workspace_bytes(0, 2, 64, 0, 1) == 0
+    assert lib.mf_workspace_bytes(100, 2, 64, 0, 5000) == 0
+
+
+def _call(q=0x10000, k=0x20000, v=0x30000, cu=0x40000, grid=0x50000, text=0x60000, out=0x70000,
+          n=1, T=64, H=2, D=64, dtype=0):
+    lib = binding.lib()
+    P = ctypes.c_void_p
+    return lib.mf_attn_packed(P(q), P(k), P(v), P(cu), P(grid), P(text), P(out), n, T, H, D, dtype, None)
+
+
+@pytest.mark.parametrize("kwargs,code", [
+    (dict(q=0), binding.MF_ERR_INVALID_ARG),
+    (dict(out=0), binding.MF_ERR_INVALID_ARG),
+    (dict(n=0), binding.MF_ERR_INVALID_ARG),
+    (dict(n=5000), binding.MF_ERR_INVALID_ARG),
+    (dict(T=0), binding.MF_ERR_INVALID_ARG),
+    (dict(T=2**31), binding.MF_ERR_INVALID_ARG),
+    (dict(H=0), binding.MF_ERR_INVALID_ARG),
+    (dict(D=96), binding.MF_ERR_UNSUPPORTED),
+    (dict(dtype=3), binding.MF_ERR_UNSUPPORTED),
+    (dict(out=0x10000 + 64), binding.MF_ERR_INVALID_ARG),  # out overlaps q
+    (dict(out=0x40000), binding.MF_ERR_INVALID_ARG),  # out overlaps the offsets
+    (dict(q=0x10004), binding.MF_ERR_INVALID_ARG),  # misaligned
+])
+def test_attn_rejects_bad_arguments_on_host(kwargs, code):
+    assert _call(**kwargs) == code
+    assert binding.last_error() != ""
+
+
+def test_other_entry_points_reject_bad_arguments():
+    lib = binding.lib()
+    P = ctypes.c_void_p
+    assert lib.mf_build_metadata(0, P(1), P(2), P(3), P(4), P(5), 10, None) == binding.MF_ERR_INVALID_ARG
+    assert lib.mf_build_metadata(1, None, P(2), P(3), P(4), P(5), 10, None) == binding.MF_ERR_INVALID_ARG
+    assert lib.mf_rope_2d(P(16), P(4096), P(64), 10, 1, 96, 0, 10000.0, None) == binding.MF_ERR_UNSUPPORTED
+    assert lib.mf_rope_2d(P(16), P(4096), P(64), 10, 1, 64, 0, 0.5, None) == binding.MF_ERR_INVALID_ARG
+    assert lib.mf_rope_2d(P(16), P(32), P(64), 10, 1, 64, 0, 10000.0, None) == binding.MF_ERR_INVALID_ARG
+    ws = lib.mf_workspace_bytes(64, 2, 64, 0, 1)
+    assert lib.mf_attn_packed_ws(P(0x10000), P(0x20000), P(0x30000), P(0x40000), P(0x50000), P(0x60000),
+                                 P(0x70000), 1, 64, 2, 64, 0, None, ws, None) == binding.MF_ERR_INVALID_ARG
+    assert lib.mf_attn_packed_ws(P(0x10000), P(0x20000), P(0x30000), P(0x40000), P(0x50000), P(0x60000),
+                                 P(0x70000), 1, 64, 2, 64, 0, P(0x1000000), ws - 1, None) == binding.MF_ERR_INVALID_ARG
+    assert lib.mf_get_workspace_error(None, None) == binding.MF_ERR_INVALID_ARG
+
+
+def test_binding_rejects_host_tensors():
+    import torch
+    x = torch.zeros((4, 1, 64))
+    with pytest.raises(ValueError):
+        binding.rope_2d(x, torch.zeros((4, 2), dtype=torch.int32))

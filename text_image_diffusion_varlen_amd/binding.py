@@ -1,0 +1,206 @@
+"""ctypes binding of libmfattn.so (argument marshalling only).
+
+Every function here checks tensor properties, passes raw device pointers and
+the current HIP stream to the C ABI declared in include/mf_attn.h, and raises
+MFError on a negative status. All arithmetic runs in the library's kernels;
+there is no fallback path: without the built library every call raises.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import re
+
+import torch
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libmfattn.so")
+HEADER_PATH = os.path.join(os.path.dirname(_HERE), "include", "mf_attn.h")
+
+MF_OK = 0
+MF_ERR_INVALID_ARG = -1
+MF_ERR_METADATA = -2
+MF_ERR_UNSUPPORTED = -3
+MF_ERR_HIP = -4
+MF_ERR_OOM = -5
+MF_BF16 = 0
+MF_F32 = 1
+ROPE_THETA = 10000.0
+
+_DTYPES = {torch.bfloat16: MF_BF16, torch.float32: MF_F32}
+_lib = None
+
+
+class MFError(RuntimeError):
+    def __init__(self, code: int, message: str):
+        super().__init__(f"mfattn error {code}: {message}")
+        self.code = code
+
+
+def _declare(lib):
+    P, I32, I64, SZ, F = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64, ctypes.c_size_t, ctypes.c_float
+    sig = {
+        "mf_version": ([], ctypes.c_int),
+        "mf_last_error": ([], ctypes.c_char_p),
+        "mf_attn_packed": ([P, P, P, P, P, P, P, I32, I64, I32, I32, I32, P], ctypes.c_int),
+        "mf_attn_packed_profiled": ([P, P, P, P, P, P, P, I32, I64, I32, I32, I32, P, P], ctypes.c_int),
+        "mf_workspace_bytes": ([I64, I32, I32, I32, I32], SZ),
+        "mf_attn_packed_ws": ([P, P, P, P, P, P, P, I32, I64, I32, I32, I32, P, SZ, P], ctypes.c_int),
+        "mf_build_metadata": ([I32, P, P, P, P, P, I64, P], ctypes.c_int),
+        "mf_rope_2d": ([P, P, P, I64, I32, I32, I32, F, P], ctypes.c_int),
+        "mf_get_device_error": ([P], ctypes.c_int),
+        "mf_get_workspace_error": ([P, P], ctypes.c_int),
+    }
+    for name, (args, res) in sig.items():
+        fn = getattr(lib, name)
+        fn.argtypes = args
+        fn.restype = res
+    return lib
+
+
+def lib():
+    """The loaded library (raises if it has not been built)."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError(
+                f"{LIB_PATH} is not built; run `python -m text_image_diffusion_varlen_amd.build`")
+        _lib = _declare(ctypes.CDLL(LIB_PATH))
+    return _lib
+
+
+def header_functions():
+    """Names of the functions declared in include/mf_attn.h."""
+    with open(HEADER_PATH) as f:
+        text = f.read()
+    return sorted(set(re.findall(r"^\s*(?:const\s+)?\w+\*?\s+\*?(mf_\w+)\(", text, re.M)))
+
+
+def _check(rc: int):
+    if rc != MF_OK:
+        raise MFError(rc, lib().mf_last_error().decode())
+
+
+def _stream(stream):
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    return ctypes.c_void_p(stream.cuda_stream)
+
+
+def _ptr(t):
+    return ctypes.c_void_p(t.data_ptr())
+
+
+def _need(t, name, dtype=None, ndim=None, device=True):
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch.Tensor")
+    if device and not t.is_cuda:
+        raise ValueError(f"{name} must be a device tensor")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if dtype is not None and t.dtype != dtype:
+        raise ValueError(f"{name} must be {dtype}, got {t.dtype}")
+    if ndim is not None and t.dim() != ndim:
+        raise ValueError(f"{name} must have {ndim} dims, got {t.dim()}")
+
+
+def version() -> int:
+    return lib().mf_version()
+
+
+def workspace_bytes(total_tokens: int, heads: int, head_dim: int, dtype: torch.dtype, n_seg: int) -> int:
+    return int(lib().mf_workspace_bytes(total_tokens, heads, head_dim, _DTYPES[dtype], n_seg))
+
+
+def _attn_args(q, k, v, cu_seqlens, grid_hw, text_len, out):
+    for name, t in (("q", q), ("k", k), ("v", v)):
+        _need(t, name, ndim=3)
+    if q.dtype not in _DTYPES or k.dtype != q.dtype or v.dtype != q.dtype:
+        raise ValueError("q, k, v must share a dtype in {bfloat16, float32}")
+    if k.shape != q.shape or v.shape != q.shape:
+        raise ValueError("q, k, v must have the same [tokens, heads, head_dim] shape")
+    _need(cu_seqlens, "cu_seqlens", torch.int32, 1)
+    _need(grid_hw, "grid_hw", torch.int32, 2)
+    _need(text_len, "text_len", torch.int32, 1)
+    n = grid_hw.shape[0]
+    if grid_hw.shape[1] != 2 or text_len.shape[0] != n or cu_seqlens.shape[0] != n + 1:
+        raise ValueError("metadata shapes must be grid_hw [n,2], text_len [n], cu_seqlens [n+1]")
+    if out is None:
+        out = torch.empty_like(q)
+    _need(out, "out", q.dtype, 3)
+    if out.shape != q.shape:
+        raise ValueError("out must have the shape of q")
+    T, H, D = q.shape
+    return out, n, T, H, D
+
+
+def attn_packed(q, k, v, cu_seqlens, grid_hw, text_len, out=None, stream=None):
+    """Packed joint attention with 2D RoPE (mf_attn_packed). Returns out."""
+    out, n, T, H, D = _attn_args(q, k, v, cu_seqlens, grid_hw, text_len, out)
+    _check(lib().mf_attn_packed(_ptr(q), _ptr(k), _ptr(v), _ptr(cu_seqlens), _ptr(grid_hw), _ptr(text_len),
+                                _ptr(out), n, T, H, D, _DTYPES[q.dtype], _stream(stream)))
+    return out
+
+
+def attn_packed_profiled(q, k, v, cu_seqlens, grid_hw, text_len, events, out=None, stream=None):
+    """mf_attn_packed recording four hipEvent_t handles (ints) between its kernels."""
+    out, n, T, H, D = _attn_args(q, k, v, cu_seqlens, grid_hw, text_len, out)
+    arr = (ctypes.c_void_p * 4)(*events)
+    _check(lib().mf_attn_packed_profiled(_ptr(q), _ptr(k), _ptr(v), _ptr(cu_seqlens), _ptr(grid_hw),
+                                         _ptr(text_len), _ptr(out), n, T, H, D, _DTYPES[q.dtype],
+                                         ctypes.cast(arr, ctypes.c_void_p), _stream(stream)))
+    return out
+
+
+def attn_packed_ws(q, k, v, cu_seqlens, grid_hw, text_len, workspace, out=None, stream=None):
+    """mf_attn_packed_ws with a caller-owned uint8 device workspace."""
+    out, n, T, H, D = _attn_args(q, k, v, cu_seqlens, grid_hw, text_len, out)
+    _need(workspace, "workspace", torch.uint8, 1)
+    _check(lib().mf_attn_packed_ws(_ptr(q), _ptr(k), _ptr(v), _ptr(cu_seqlens), _ptr(grid_hw), _ptr(text_len),
+                                   _ptr(out), n, T, H, D, _DTYPES[q.dtype], _ptr(workspace),
+                                   workspace.numel(), _stream(stream)))
+    return out
+
+
+def build_metadata(grid_hw, text_len, total_tokens: int, stream=None):
+    """(cu_seqlens [n+1], pos [T,2], seg_id [T]) int32 device tensors (mf_build_metadata)."""
+    _need(grid_hw, "grid_hw", torch.int32, 2)
+    _need(text_len, "text_len", torch.int32, 1)
+    n = grid_hw.shape[0]
+    dev = grid_hw.device
+    cu = torch.empty(n + 1, dtype=torch.int32, device=dev)
+    pos = torch.empty((total_tokens, 2), dtype=torch.int32, device=dev)
+    seg = torch.empty(total_tokens, dtype=torch.int32, device=dev)
+    _check(lib().mf_build_metadata(n, _ptr(grid_hw), _ptr(text_len), _ptr(cu), _ptr(pos), _ptr(seg),
+                                   total_tokens, _stream(stream)))
+    return cu, pos, seg
+
+
+def rope_2d(x, pos, theta: float = ROPE_THETA, out=None, stream=None):
+    """2D RoPE of x [T, H, d] at pos [T, 2] (mf_rope_2d). Returns out."""
+    _need(x, "x", ndim=3)
+    _need(pos, "pos", torch.int32, 2)
+    if x.dtype not in _DTYPES:
+        raise ValueError("x must be bfloat16 or float32")
+    if out is None:
+        out = torch.empty_like(x)
+    _need(out, "out", x.dtype, 3)
+    T, H, D = x.shape
+    if pos.shape[0] != T or out.shape != x.shape:
+        raise ValueError("shape mismatch")
+    _check(lib().mf_rope_2d(_ptr(x), _ptr(out), _ptr(pos), T, H, D, _DTYPES[x.dtype], float(theta),
+                            _stream(stream)))
+    return out
+
+
+def get_device_error(stream=None) -> int:
+    """Synchronizes and returns the device-side check status (MF_OK or MF_ERR_METADATA)."""
+    return int(lib().mf_get_device_error(_stream(stream)))
+
+
+def get_workspace_error(workspace, stream=None) -> int:
+    return int(lib().mf_get_workspace_error(_ptr(workspace), _stream(stream)))
+
+
+def last_error() -> str:
+    return lib().mf_last_error().decode()

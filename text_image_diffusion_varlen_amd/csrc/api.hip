@@ -1,0 +1,365 @@
+// C ABI of libmfattn: argument checks, per-device state (workspace, cos/sin
+// tables, status flag) and the launch sequence of the packed attention path:
+//   meta_kernel      metadata check, padded offsets, longest-first tile table
+//   rope_pack_kernel 2D RoPE on q, k into the padded workspace (+ V transpose)
+//   attn_fwd_*       per-sample flash-style attention
+// Nothing here synchronizes except mf_get_device_error / mf_get_workspace_error
+// and the first-use allocations of the library-owned state.
+#include <cmath>
+#include <cstdarg>
+#include <cstdio>
+#include <cstdlib>
+#include <cstring>
+#include <map>
+#include <mutex>
+#include <string>
+#include <utility>
+#include <vector>
+
+#include "mf_attn.h"
+#include "mf_common.h"
+
+namespace mf {
+hipError_t launch_meta(const int32_t* grid_hw, const int32_t* text_len, const int32_t* cu_in,
+                       int32_t n, int64_t tokens, char* ws, const WsLayout& l, hipStream_t s);
+hipError_t launch_build_metadata(const int32_t* grid_hw, const int32_t* text_len, int32_t n,
+                                 int64_t tokens, int32_t* cu_out, int32_t* pos, int32_t* seg_id,
+                                 int32_t* status, hipStream_t s);
+hipError_t launch_rope_pack(const void* q, const void* k, const void* v, const int32_t* grid_hw,
+                            const int32_t* text_len, const char* ws, const WsLayout& l,
+                            const float2* cs, int32_t heads, int32_t head_dim, bool bf16,
+                            hipStream_t s);
+hipError_t launch_rope(const void* x, void* y, const int32_t* pos, int64_t tokens, int32_t heads,
+                       int32_t head_dim, bool bf16, const float2* cs, int32_t* status,
+                       hipStream_t s);
+hipError_t launch_attn_fwd(const char* ws, const WsLayout& l, void* out, int32_t heads,
+                           int32_t head_dim, bool bf16, float scale, hipStream_t s);
+}  // namespace mf
+
+namespace {
+
+thread_local std::string g_err;
+
+int fail(int code, const char* fmt, ...) __attribute__((format(printf, 2, 3)));
+int fail(int code, const char* fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof(buf), fmt, ap);
+  va_end(ap);
+  g_err = buf;
+  return code;
+}
+
+int hip_fail(hipError_t e, const char* what) {
+  return fail(MF_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
+}
+
+struct DeviceState {
+  int32_t* status = nullptr;  // sticky FLAG_* of the standalone metadata / RoPE calls
+  char* ws = nullptr;         // library workspace of mf_attn_packed
+  size_t ws_bytes = 0;
+  std::map<std::pair<int, uint32_t>, float2*> tables;  // (head_dim, theta bits) -> cos/sin
+};
+
+std::mutex g_mu;
+std::map<int, DeviceState> g_dev;
+
+int current_device(int* dev) {
+  const hipError_t e = hipGetDevice(dev);
+  return e == hipSuccess ? MF_OK : hip_fail(e, "hipGetDevice");
+}
+
+// Caller holds g_mu.
+int ensure_status(DeviceState& st) {
+  if (st.status) return MF_OK;
+  void* p = nullptr;
+  hipError_t e = hipMalloc(&p, 256);
+  if (e != hipSuccess) return fail(MF_ERR_OOM, "status buffer: %s", hipGetErrorString(e));
+  e = hipMemset(p, 0, 256);
+  if (e != hipSuccess) return hip_fail(e, "hipMemset(status)");
+  st.status = static_cast<int32_t*>(p);
+  return MF_OK;
+}
+
+// cos/sin table [ROPE_PMAX][head_dim/4]: entry (p, j) = (cos, sin) of
+// p * theta^(-2j/(head_dim/2)), evaluated in double and rounded to float.
+int ensure_table(DeviceState& st, int head_dim, float theta, const float2** out) {
+  uint32_t tb;
+  std::memcpy(&tb, &theta, 4);
+  const auto key = std::make_pair(head_dim, tb);
+  auto it = st.tables.find(key);
+  if (it != st.tables.end()) {
+    *out = it->second;
+    return MF_OK;
+  }
+  const int nf = head_dim / 4;
+  std::vector<float2> host(size_t(mf::ROPE_PMAX) * nf);
+  for (int p = 0; p < mf::ROPE_PMAX; ++p) {
+    for (int j = 0; j < nf; ++j) {
+      const double w = std::pow(double(theta), -2.0 * j / (head_dim / 2));
+      const double ang = double(p) * w;
+      host[size_t(p) * nf + j] = make_float2(float(std::cos(ang)), float(std::sin(ang)));
+    }
+  }
+  void* d = nullptr;
+  hipError_t e = hipMalloc(&d, host.size() * sizeof(float2));
+  if (e != hipSuccess) return fail(MF_ERR_OOM, "rope table: %s", hipGetErrorString(e));
+  e = hipMemcpy(d, host.data(), host.size() * sizeof(float2), hipMemcpyHostToDevice);
+  if (e != hipSuccess) {
+    (void)hipFree(d);
+    return hip_fail(e, "hipMemcpy(rope table)");
+  }
+  st.tables[key] = static_cast<float2*>(d);
+  *out = static_cast<float2*>(d);
+  return MF_OK;
+}
+
+int ensure_workspace(DeviceState& st, size_t bytes) {
+  if (st.ws_bytes >= bytes) return MF_OK;
+  const char* f = std::getenv("MF_FAULT_OOM");
+  if (f && f[0] == '1') return fail(MF_ERR_OOM, "workspace of %zu bytes: injected failure", bytes);
+  if (st.ws) {
+    // hipFree waits for the device, so no enqueued call still uses the old buffer.
+    const hipError_t e = hipFree(st.ws);
+    st.ws = nullptr;
+    st.ws_bytes = 0;
+    if (e != hipSuccess) return hip_fail(e, "hipFree(workspace)");
+  }
+  void* p = nullptr;
+  const hipError_t e = hipMalloc(&p, bytes);
+  if (e != hipSuccess) {
+    (void)hipGetLastError();
+    return fail(MF_ERR_OOM, "workspace of %zu bytes: %s", bytes, hipGetErrorString(e));
+  }
+  const hipError_t z = hipMemset(p, 0, sizeof(mf::WsHeader));
+  if (z != hipSuccess) {
+    (void)hipFree(p);
+    return hip_fail(z, "hipMemset(workspace header)");
+  }
+  st.ws = static_cast<char*>(p);
+  st.ws_bytes = bytes;
+  return MF_OK;
+}
+
+int elem_bytes(int32_t dtype) { return dtype == MF_BF16 ? 2 : dtype == MF_F32 ? 4 : 0; }
+
+bool overlaps(const void* a, size_t na, const void* b, size_t nb) {
+  const uintptr_t x = reinterpret_cast<uintptr_t>(a), y = reinterpret_cast<uintptr_t>(b);
+  return x < y + nb && y < x + na;
+}
+
+// Scalar checks shared by the attention entry points.
+int check_attn_args(const void* q, const void* k, const void* v, const int32_t* cu,
+                    const int32_t* grid_hw, const int32_t* text_len, const void* out,
+                    int32_t n_seg, int64_t tokens, int32_t heads, int32_t head_dim,
+                    int32_t dtype) {
+  if (!q || !k || !v || !cu || !grid_hw || !text_len || !out)
+    return fail(MF_ERR_INVALID_ARG, "null pointer argument");
+  if (n_seg < 1 || n_seg > MF_MAX_SEGMENTS)
+    return fail(MF_ERR_INVALID_ARG, "n_seg=%d outside [1, %d]", n_seg, MF_MAX_SEGMENTS);
+  if (tokens < 1 || tokens >= (int64_t(1) << 31))
+    return fail(MF_ERR_INVALID_ARG, "total_tokens=%lld outside [1, 2^31)", (long long)tokens);
+  if (heads < 1 || heads > 256) return fail(MF_ERR_INVALID_ARG, "heads=%d outside [1, 256]", heads);
+  if (head_dim != 64 && head_dim != 128)
+    return fail(MF_ERR_UNSUPPORTED, "head_dim=%d (supported: 64, 128)", head_dim);
+  const int eb = elem_bytes(dtype);
+  if (!eb) return fail(MF_ERR_UNSUPPORTED, "dtype=%d (supported: MF_BF16, MF_F32)", dtype);
+  const mf::WsLayout l = mf::ws_layout(tokens, heads, head_dim, eb, n_seg);
+  if (int64_t(heads) * l.rows * head_dim >= (int64_t(1) << 40) || l.n_tiles * heads >= (int64_t(1) << 31))
+    return fail(MF_ERR_UNSUPPORTED, "problem too large");
+  const size_t tb = size_t(tokens) * heads * head_dim * eb;
+  if (overlaps(out, tb, q, tb) || overlaps(out, tb, k, tb) || overlaps(out, tb, v, tb))
+    return fail(MF_ERR_INVALID_ARG, "out overlaps q, k or v");
+  if (overlaps(out, tb, cu, size_t(n_seg + 1) * 4) || overlaps(out, tb, grid_hw, size_t(n_seg) * 8) ||
+      overlaps(out, tb, text_len, size_t(n_seg) * 4))
+    return fail(MF_ERR_INVALID_ARG, "out overlaps the metadata");
+  const uintptr_t mis = reinterpret_cast<uintptr_t>(q) | reinterpret_cast<uintptr_t>(k) |
+                        reinterpret_cast<uintptr_t>(v) | reinterpret_cast<uintptr_t>(out);
+  if (mis & 15) return fail(MF_ERR_INVALID_ARG, "q, k, v and out must be 16-byte aligned");
+  return MF_OK;
+}
+
+int run_attn(const void* q, const void* k, const void* v, const int32_t* cu, const int32_t* grid_hw,
+             const int32_t* text_len, void* out, int32_t n_seg, int64_t tokens, int32_t heads,
+             int32_t head_dim, int32_t dtype, char* ws, const float2* cs, hipStream_t s,
+             hipEvent_t const* ev = nullptr) {
+  const bool bf16 = dtype == MF_BF16;
+  const mf::WsLayout l = mf::ws_layout(tokens, heads, head_dim, elem_bytes(dtype), n_seg);
+  hipError_t e;
+  if (ev && (e = hipEventRecord(ev[0], s)) != hipSuccess) return hip_fail(e, "hipEventRecord");
+  e = mf::launch_meta(grid_hw, text_len, cu, n_seg, tokens, ws, l, s);
+  if (e != hipSuccess) return hip_fail(e, "meta_kernel launch");
+  if (ev && (e = hipEventRecord(ev[1], s)) != hipSuccess) return hip_fail(e, "hipEventRecord");
+  e = mf::launch_rope_pack(q, k, v, grid_hw, text_len, ws, l, cs, heads, head_dim, bf16, s);
+  if (e != hipSuccess) return hip_fail(e, "rope_pack_kernel launch");
+  if (ev && (e = hipEventRecord(ev[2], s)) != hipSuccess) return hip_fail(e, "hipEventRecord");
+  e = mf::launch_attn_fwd(ws, l, out, heads, head_dim, bf16, float(1.0 / std::sqrt(double(head_dim))), s);
+  if (e != hipSuccess) return hip_fail(e, "attn_fwd launch");
+  if (ev && (e = hipEventRecord(ev[3], s)) != hipSuccess) return hip_fail(e, "hipEventRecord");
+  return MF_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int mf_version(void) { return 100; }
+
+const char* mf_last_error(void) { return g_err.c_str(); }
+
+size_t mf_workspace_bytes(int64_t total_tokens, int32_t heads, int32_t head_dim, int32_t dtype,
+                          int32_t n_seg) {
+  const int eb = elem_bytes(dtype);
+  if (!eb || (head_dim != 64 && head_dim != 128) || heads < 1 || heads > 256 || n_seg < 1 ||
+      n_seg > MF_MAX_SEGMENTS || total_tokens < 1 || total_tokens >= (int64_t(1) << 31))
+    return 0;
+  return size_t(mf::ws_layout(total_tokens, heads, head_dim, eb, n_seg).total);
+}
+
+int mf_attn_packed_profiled(const void* q, const void* k, const void* v, const int32_t* cu_seqlens,
+                            const int32_t* grid_hw, const int32_t* text_len, void* out,
+                            int32_t n_seg, int64_t total_tokens, int32_t heads, int32_t head_dim,
+                            int32_t dtype, hipEvent_t const* events, hipStream_t stream) {
+  int rc = check_attn_args(q, k, v, cu_seqlens, grid_hw, text_len, out, n_seg, total_tokens, heads,
+                           head_dim, dtype);
+  if (rc) return rc;
+  int dev;
+  if ((rc = current_device(&dev))) return rc;
+  const size_t need = mf_workspace_bytes(total_tokens, heads, head_dim, dtype, n_seg);
+  std::lock_guard<std::mutex> lock(g_mu);
+  DeviceState& st = g_dev[dev];
+  const float2* cs = nullptr;
+  if ((rc = ensure_table(st, head_dim, MF_ROPE_THETA, &cs))) return rc;
+  if ((rc = ensure_workspace(st, need))) return rc;
+  return run_attn(q, k, v, cu_seqlens, grid_hw, text_len, out, n_seg, total_tokens, heads, head_dim,
+                  dtype, st.ws, cs, stream, events);
+}
+
+int mf_attn_packed(const void* q, const void* k, const void* v, const int32_t* cu_seqlens,
+                   const int32_t* grid_hw, const int32_t* text_len, void* out, int32_t n_seg,
+                   int64_t total_tokens, int32_t heads, int32_t head_dim, int32_t dtype,
+                   hipStream_t stream) {
+  return mf_attn_packed_profiled(q, k, v, cu_seqlens, grid_hw, text_len, out, n_seg, total_tokens,
+                                 heads, head_dim, dtype, nullptr, stream);
+}
+
+int mf_attn_packed_ws(const void* q, const void* k, const void* v, const int32_t* cu_seqlens,
+                      const int32_t* grid_hw, const int32_t* text_len, void* out, int32_t n_seg,
+                      int64_t total_tokens, int32_t heads, int32_t head_dim, int32_t dtype,
+                      void* workspace, size_t workspace_bytes, hipStream_t stream) {
+  int rc = check_attn_args(q, k, v, cu_seqlens, grid_hw, text_len, out, n_seg, total_tokens, heads,
+                           head_dim, dtype);
+  if (rc) return rc;
+  if (!workspace) return fail(MF_ERR_INVALID_ARG, "null workspace");
+  if (reinterpret_cast<uintptr_t>(workspace) & 255)
+    return fail(MF_ERR_INVALID_ARG, "workspace must be 256-byte aligned");
+  const size_t need = mf_workspace_bytes(total_tokens, heads, head_dim, dtype, n_seg);
+  if (workspace_bytes < need)
+    return fail(MF_ERR_INVALID_ARG, "workspace of %zu bytes, %zu needed", workspace_bytes, need);
+  const size_t tb = size_t(total_tokens) * heads * head_dim * elem_bytes(dtype);
+  if (overlaps(workspace, need, out, tb) || overlaps(workspace, need, q, tb) ||
+      overlaps(workspace, need, k, tb) || overlaps(workspace, need, v, tb))
+    return fail(MF_ERR_INVALID_ARG, "workspace overlaps q, k, v or out");
+  int dev;
+  if ((rc = current_device(&dev))) return rc;
+  const float2* cs = nullptr;
+  {
+    std::lock_guard<std::mutex> lock(g_mu);
+    if ((rc = ensure_table(g_dev[dev], head_dim, MF_ROPE_THETA, &cs))) return rc;
+  }
+  return run_attn(q, k, v, cu_seqlens, grid_hw, text_len, out, n_seg, total_tokens, heads, head_dim,
+                  dtype, static_cast<char*>(workspace), cs, stream);
+}
+
+int mf_build_metadata(int32_t n_seg, const int32_t* grid_hw, const int32_t* text_len,
+                      int32_t* cu_seqlens_out, int32_t* pos_out, int32_t* seg_id_out,
+                      int64_t total_tokens, hipStream_t stream) {
+  if (!grid_hw || !text_len || !cu_seqlens_out || !pos_out || !seg_id_out)
+    return fail(MF_ERR_INVALID_ARG, "null pointer argument");
+  if (n_seg < 1 || n_seg > MF_MAX_SEGMENTS)
+    return fail(MF_ERR_INVALID_ARG, "n_seg=%d outside [1, %d]", n_seg, MF_MAX_SEGMENTS);
+  if (total_tokens < 1 || total_tokens >= (int64_t(1) << 31))
+    return fail(MF_ERR_INVALID_ARG, "total_tokens=%lld outside [1, 2^31)", (long long)total_tokens);
+  int dev, rc;
+  if ((rc = current_device(&dev))) return rc;
+  int32_t* status;
+  {
+    std::lock_guard<std::mutex> lock(g_mu);
+    if ((rc = ensure_status(g_dev[dev]))) return rc;
+    status = g_dev[dev].status;
+  }
+  const hipError_t e = mf::launch_build_metadata(grid_hw, text_len, n_seg, total_tokens,
+                                                 cu_seqlens_out, pos_out, seg_id_out, status, stream);
+  return e == hipSuccess ? MF_OK : hip_fail(e, "metadata kernels launch");
+}
+
+int mf_rope_2d(const void* x_in, void* x_out, const int32_t* pos, int64_t total_tokens,
+               int32_t heads, int32_t head_dim, int32_t dtype, float theta, hipStream_t stream) {
+  if (!x_in || !x_out || !pos) return fail(MF_ERR_INVALID_ARG, "null pointer argument");
+  if (total_tokens < 1 || total_tokens >= (int64_t(1) << 31))
+    return fail(MF_ERR_INVALID_ARG, "total_tokens=%lld outside [1, 2^31)", (long long)total_tokens);
+  if (heads < 1 || heads > 256) return fail(MF_ERR_INVALID_ARG, "heads=%d outside [1, 256]", heads);
+  if (head_dim != 64 && head_dim != 128)
+    return fail(MF_ERR_UNSUPPORTED, "head_dim=%d (supported: 64, 128)", head_dim);
+  const int eb = elem_bytes(dtype);
+  if (!eb) return fail(MF_ERR_UNSUPPORTED, "dtype=%d", dtype);
+  if (!(theta > 1.0f) || !std::isfinite(theta)) return fail(MF_ERR_INVALID_ARG, "theta must be > 1");
+  const size_t tb = size_t(total_tokens) * heads * head_dim * eb;
+  if (x_in != x_out && overlaps(x_in, tb, x_out, tb))
+    return fail(MF_ERR_INVALID_ARG, "x_in and x_out partially overlap");
+  if ((reinterpret_cast<uintptr_t>(x_in) | reinterpret_cast<uintptr_t>(x_out)) & 15)
+    return fail(MF_ERR_INVALID_ARG, "x_in and x_out must be 16-byte aligned");
+  int dev, rc;
+  if ((rc = current_device(&dev))) return rc;
+  const float2* cs;
+  int32_t* status;
+  {
+    std::lock_guard<std::mutex> lock(g_mu);
+    DeviceState& st = g_dev[dev];
+    if ((rc = ensure_status(st))) return rc;
+    if ((rc = ensure_table(st, head_dim, theta, &cs))) return rc;
+    status = st.status;
+  }
+  const hipError_t e = mf::launch_rope(x_in, x_out, pos, total_tokens, heads, head_dim,
+                                       dtype == MF_BF16, cs, status, stream);
+  return e == hipSuccess ? MF_OK : hip_fail(e, "rope_kernel launch");
+}
+
+int mf_get_device_error(hipStream_t stream) {
+  hipError_t e = hipStreamSynchronize(stream);
+  if (e != hipSuccess) return hip_fail(e, "hipStreamSynchronize");
+  int dev, rc;
+  if ((rc = current_device(&dev))) return rc;
+  std::lock_guard<std::mutex> lock(g_mu);
+  DeviceState& st = g_dev[dev];
+  int32_t flags = 0;
+  if (st.status) {
+    int32_t v = 0;
+    if ((e = hipMemcpy(&v, st.status, 4, hipMemcpyDeviceToHost)) != hipSuccess)
+      return hip_fail(e, "hipMemcpy(status)");
+    if (v && (e = hipMemset(st.status, 0, 4)) != hipSuccess) return hip_fail(e, "hipMemset(status)");
+    flags |= v;
+  }
+  if (st.ws) {
+    mf::WsHeader hdr;
+    if ((e = hipMemcpy(&hdr, st.ws, sizeof(hdr), hipMemcpyDeviceToHost)) != hipSuccess)
+      return hip_fail(e, "hipMemcpy(workspace header)");
+    flags |= hdr.flag;
+  }
+  if (flags) return fail(MF_ERR_METADATA, "device check failed (flags 0x%x)", unsigned(flags));
+  return MF_OK;
+}
+
+int mf_get_workspace_error(const void* workspace, hipStream_t stream) {
+  if (!workspace) return fail(MF_ERR_INVALID_ARG, "null workspace");
+  hipError_t e = hipStreamSynchronize(stream);
+  if (e != hipSuccess) return hip_fail(e, "hipStreamSynchronize");
+  mf::WsHeader hdr;
+  if ((e = hipMemcpy(&hdr, workspace, sizeof(hdr), hipMemcpyDeviceToHost)) != hipSuccess)
+    return hip_fail(e, "hipMemcpy(workspace header)");
+  if (hdr.flag) return fail(MF_ERR_METADATA, "device check failed (flags 0x%x)", unsigned(hdr.flag));
+  return MF_OK;
+}
+
+}  // extern "C"

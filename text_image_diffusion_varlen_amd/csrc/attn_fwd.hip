@@ -1,0 +1,317 @@
+// Packed joint attention forward on gfx950.
+//
+// Operation: for every sample i and head h, O = softmax(Q~ K~^T / sqrt(d)) V
+// over the sample's own L_i tokens only (Mage-Flow tech report, NR-MMDiT
+// section: per-sample cumulative offsets restrict attention to each sample;
+// mageflow.net architecture page, sections 2 and 8: text and image tokens in
+// one bidirectional sequence). Q~, K~ are the 2D-RoPE-rotated queries and
+// keys written by the prologue into the padded workspace layout, where every
+// sample starts on a KTILE boundary; query tiles are sample-relative, so a
+// workgroup only ever visits the key tiles of its own sample and the
+// cross-sample blocks of the packed score matrix are never touched.
+//
+// bf16 kernel (d = 64 or 128), one workgroup = 4 waves = QTILE (128) queries
+// of one (sample, head), each wave owning 32 query rows:
+//   S^T (64 keys x 32 queries) = K~ tile (LDS) x Q~^T (registers), on
+//       v_mfma_f32_32x32x16_bf16 with fp32 accumulation. In this orientation
+//       every lane holds one query row: 32 of the 64 keys in registers, the
+//       other 32 in lane ^ 32, so row max / sum need one cross-half exchange.
+//   online softmax in the exp2 domain (scale * log2(e) folded into one FMA),
+//       running max m, per-lane partial row sums (combined once at the end),
+//       accumulator rescale skipped when no row max moved;
+//   O^T (d x 32 queries) += V~^T tile (LDS) x P^T (registers, bf16 RNE).
+// K~ and V~^T tiles (KTILE x d each) are double-buffered in LDS: the global
+// loads of tile j+1 are issued before the math of tile j and written to the
+// other LDS buffer after it, one barrier per tile.
+//
+// f32 kernel: the same tiling of work with plain fp32 FMAs (no reduced
+// precision anywhere); each query row is split over two lanes (channel halves).
+#include "mf_common.h"
+
+namespace mf {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+
+struct AttnArgs {
+  const char* ws;
+  int64_t off_len, off_cu, off_pcu, off_tiles;
+  const void* qw;
+  const void* kw;
+  const void* vw;
+  void* out;
+  int32_t heads;
+  int64_t rows;      // padded rows per head in the workspace
+  float c_log2;      // softmax scale * log2(e)
+};
+
+__device__ inline uint32_t pack_bf16x2(float a, float b) {
+  typedef float f32x2 __attribute__((ext_vector_type(2)));
+  typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+  const f32x2 v = {a, b};
+  const bf16x2 r = __builtin_convertvector(v, bf16x2);  // v_cvt_pk_bf16_f32, round to nearest even
+  return __builtin_bit_cast(uint32_t, r);
+}
+
+template <int D>
+__global__ void __launch_bounds__(256, 2) attn_fwd_bf16_kernel(AttnArgs a) {
+  constexpr int CHUNKS = KTILE * D / 8;     // 16-byte chunks per K~ (or V~^T) tile
+  constexpr int PER_THREAD = CHUNKS / 256;  // 4 (d=128) or 2 (d=64)
+  constexpr int KSTEPS = D / 16;            // MFMA k-steps of the score product
+  constexpr int DBLK = D / 32;              // 32-channel blocks of the output
+
+  const WsHeader* hdr = reinterpret_cast<const WsHeader*>(a.ws);
+  const int32_t heads = a.heads;
+  const int h = int(blockIdx.x % unsigned(heads));
+  const int tile = int(blockIdx.x / unsigned(heads));
+  if (hdr->flag != FLAG_OK || tile >= hdr->n_tiles) return;
+  const int2 td = reinterpret_cast<const int2*>(a.ws + a.off_tiles)[tile];
+  const int32_t seg = td.x, qs = td.y;
+  const int32_t L = reinterpret_cast<const int32_t*>(a.ws + a.off_len)[seg];
+  const int32_t pb = reinterpret_cast<const int32_t*>(a.ws + a.off_pcu)[seg];
+  const int32_t cb = reinterpret_cast<const int32_t*>(a.ws + a.off_cu)[seg];
+
+  const int tid = threadIdx.x;
+  const int wave = tid >> 6, lane = tid & 63, hf = lane >> 5, l32 = lane & 31;
+  const int64_t head_row0 = int64_t(h) * a.rows + pb;  // first padded row of this (sample, head)
+
+  // Q~ rows of this lane as the B operand of S^T = K~ Q~^T: lane holds
+  // query l32, channels 16*ks + 8*hf .. +7 for every k-step ks.
+  const uint16_t* qw = static_cast<const uint16_t*>(a.qw);
+  bf16x8 qreg[KSTEPS];
+  {
+    const uint16_t* qrow = qw + (head_row0 + qs + 32 * wave + l32) * D + 8 * hf;
+#pragma unroll
+    for (int ks = 0; ks < KSTEPS; ++ks) qreg[ks] = *reinterpret_cast<const bf16x8*>(qrow + 16 * ks);
+  }
+
+  __shared__ __attribute__((aligned(16))) uint16_t lds[2][2][KTILE * D];
+  const u32x4* kg = reinterpret_cast<const u32x4*>(static_cast<const uint16_t*>(a.kw) + head_row0 * D);
+  const u32x4* vg = reinterpret_cast<const u32x4*>(static_cast<const uint16_t*>(a.vw) + head_row0 * D);
+  const int nkt = (L + KTILE - 1) / KTILE;
+
+  u32x4 stk[PER_THREAD], stv[PER_THREAD];
+#pragma unroll
+  for (int i = 0; i < PER_THREAD; ++i) {
+    stk[i] = kg[tid + 256 * i];
+    stv[i] = vg[tid + 256 * i];
+  }
+#pragma unroll
+  for (int i = 0; i < PER_THREAD; ++i) {
+    reinterpret_cast<u32x4*>(lds[0][0])[tid + 256 * i] = stk[i];
+    reinterpret_cast<u32x4*>(lds[0][1])[tid + 256 * i] = stv[i];
+  }
+  __syncthreads();
+
+  const float c = a.c_log2;
+  float m = -INFINITY;  // running row max, already multiplied by c
+  float lsum = 0.f;     // this lane's partial row sum (its 32 keys of every tile)
+  f32x16 acc[DBLK];
+#pragma unroll
+  for (int b = 0; b < DBLK; ++b) acc[b] = f32x16{};
+
+  for (int j = 0; j < nkt; ++j) {
+    const int buf = j & 1;
+    const bool more = j + 1 < nkt;
+    if (more) {
+      const u32x4* kn = kg + (j + 1) * CHUNKS;
+      const u32x4* vn = vg + (j + 1) * CHUNKS;
+#pragma unroll
+      for (int i = 0; i < PER_THREAD; ++i) {
+        stk[i] = kn[tid + 256 * i];
+        stv[i] = vn[tid + 256 * i];
+      }
+    }
+    const uint16_t* kt = lds[buf][0];
+    const uint16_t* vt = lds[buf][1];
+
+    // S^T for keys 0..31 (s0) and 32..63 (s1) of the tile.
+    f32x16 s0 = {}, s1 = {};
+#pragma unroll
+    for (int ks = 0; ks < KSTEPS; ++ks) {
+      const int ch = 2 * ks + hf;
+      const bf16x8 k0 = *reinterpret_cast<const bf16x8*>(kt + 8 * swz_chunk(l32 * (D / 8) + ch));
+      const bf16x8 k1 = *reinterpret_cast<const bf16x8*>(kt + 8 * swz_chunk((l32 + 32) * (D / 8) + ch));
+      s0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(k0, qreg[ks], s0, 0, 0, 0);
+      s1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(k1, qreg[ks], s1, 0, 0, 0);
+    }
+    // Accumulator entry e holds key 8*(e/4) + 4*hf + e%4 (s1: +32).
+    if (KTILE * (j + 1) > L) {
+      const int kbase = KTILE * j + 4 * hf;
+#pragma unroll
+      for (int e = 0; e < 16; ++e) {
+        const int key = kbase + 8 * (e >> 2) + (e & 3);
+        if (key >= L) s0[e] = -INFINITY;
+        if (key + 32 >= L) s1[e] = -INFINITY;
+      }
+    }
+    float mx = fmaxf(s0[0], s1[0]);
+#pragma unroll
+    for (int e = 1; e < 16; ++e) mx = fmaxf(mx, fmaxf(s0[e], s1[e]));
+    mx = fmaxf(mx, __shfl_xor(mx, 32));
+    const float mnew = fmaxf(m, mx * c);
+    const float alpha = __builtin_amdgcn_exp2f(m - mnew);
+    const float nm = -mnew;
+    float psum = 0.f;
+    uint32_t pk[4][4];  // P^T operand: k-step ks2 holds keys 16*ks2 + {4hf..4hf+3, 8+4hf..8+4hf+3}
+#pragma unroll
+    for (int e = 0; e < 16; e += 2) {
+      const float p0 = __builtin_amdgcn_exp2f(__builtin_fmaf(s0[e], c, nm));
+      const float p1 = __builtin_amdgcn_exp2f(__builtin_fmaf(s0[e + 1], c, nm));
+      const float p2 = __builtin_amdgcn_exp2f(__builtin_fmaf(s1[e], c, nm));
+      const float p3 = __builtin_amdgcn_exp2f(__builtin_fmaf(s1[e + 1], c, nm));
+      psum += (p0 + p1) + (p2 + p3);
+      pk[e >> 3][(e & 7) >> 1] = pack_bf16x2(p0, p1);
+      pk[2 + (e >> 3)][(e & 7) >> 1] = pack_bf16x2(p2, p3);
+    }
+    lsum = lsum * alpha + psum;
+    if (__any(mnew != m)) {
+#pragma unroll
+      for (int b = 0; b < DBLK; ++b) acc[b] *= alpha;
+    }
+    m = mnew;
+
+    // O^T += V~^T x P^T
+#pragma unroll
+    for (int ks2 = 0; ks2 < 4; ++ks2) {
+      const bf16x8 pb8 = __builtin_bit_cast(bf16x8, u32x4{pk[ks2][0], pk[ks2][1], pk[ks2][2], pk[ks2][3]});
+#pragma unroll
+      for (int b = 0; b < DBLK; ++b) {
+        const bf16x8 vv = *reinterpret_cast<const bf16x8*>(vt + 8 * swz_chunk((32 * b + l32) * 8 + 2 * ks2 + hf));
+        acc[b] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vv, pb8, acc[b], 0, 0, 0);
+      }
+    }
+
+    if (more) {
+#pragma unroll
+      for (int i = 0; i < PER_THREAD; ++i) {
+        reinterpret_cast<u32x4*>(lds[buf ^ 1][0])[tid + 256 * i] = stk[i];
+        reinterpret_cast<u32x4*>(lds[buf ^ 1][1])[tid + 256 * i] = stv[i];
+      }
+    }
+    __syncthreads();
+  }
+
+  // Epilogue: O = acc / l. Accumulator entry e of block b holds channel
+  // 32*b + 8*(e/4) + 4*hf + e%4 of query l32.
+  lsum += __shfl_xor(lsum, 32);
+  const float inv = 1.f / lsum;
+  const int32_t qrel = qs + 32 * wave + l32;
+  if (qrel < L) {
+    uint16_t* orow = static_cast<uint16_t*>(a.out) + (int64_t(cb + qrel) * heads + h) * D;
+#pragma unroll
+    for (int b = 0; b < DBLK; ++b) {
+#pragma unroll
+      for (int g = 0; g < 4; ++g) {
+        uint2 v2;
+        v2.x = pack_bf16x2(acc[b][4 * g] * inv, acc[b][4 * g + 1] * inv);
+        v2.y = pack_bf16x2(acc[b][4 * g + 2] * inv, acc[b][4 * g + 3] * inv);
+        *reinterpret_cast<uint2*>(orow + 32 * b + 8 * g + 4 * hf) = v2;
+      }
+    }
+  }
+}
+
+// fp32 path: 4 waves x 32 queries; lane = (query l32, channel half hf).
+template <int D>
+__global__ void __launch_bounds__(256) attn_fwd_f32_kernel(AttnArgs a) {
+  constexpr int HD = D / 2;
+  constexpr int KT = 32;  // keys per LDS tile
+  const WsHeader* hdr = reinterpret_cast<const WsHeader*>(a.ws);
+  const int32_t heads = a.heads;
+  const int h = int(blockIdx.x % unsigned(heads));
+  const int tile = int(blockIdx.x / unsigned(heads));
+  if (hdr->flag != FLAG_OK || tile >= hdr->n_tiles) return;
+  const int2 td = reinterpret_cast<const int2*>(a.ws + a.off_tiles)[tile];
+  const int32_t seg = td.x, qs = td.y;
+  const int32_t L = reinterpret_cast<const int32_t*>(a.ws + a.off_len)[seg];
+  const int32_t pb = reinterpret_cast<const int32_t*>(a.ws + a.off_pcu)[seg];
+  const int32_t cb = reinterpret_cast<const int32_t*>(a.ws + a.off_cu)[seg];
+  const int tid = threadIdx.x;
+  const int wave = tid >> 6, lane = tid & 63, hf = lane >> 5, l32 = lane & 31;
+  const int64_t head_row0 = int64_t(h) * a.rows + pb;
+  const float* qw = static_cast<const float*>(a.qw);
+  const float* kw = static_cast<const float*>(a.kw) + head_row0 * D;
+  const float* vw = static_cast<const float*>(a.vw) + head_row0 * D;
+
+  float qv[HD], acc[HD];
+  const float* qrow = qw + (head_row0 + qs + 32 * wave + l32) * D + HD * hf;
+#pragma unroll
+  for (int i = 0; i < HD; ++i) {
+    qv[i] = qrow[i];
+    acc[i] = 0.f;
+  }
+  __shared__ float ks[KT][D];
+  __shared__ float vs[KT][D];
+  const float c = a.c_log2;
+  float m = -INFINITY, lsum = 0.f;
+  const int nkt = (L + KT - 1) / KT;
+  for (int j = 0; j < nkt; ++j) {
+    __syncthreads();
+    for (int x = tid; x < KT * D; x += 256) {
+      ks[x / D][x % D] = kw[int64_t(j) * KT * D + x];
+      vs[x / D][x % D] = vw[int64_t(j) * KT * D + x];
+    }
+    __syncthreads();
+    float s[KT];
+    float mx = -INFINITY;
+#pragma unroll
+    for (int kk = 0; kk < KT; ++kk) {
+      float part = 0.f;
+#pragma unroll
+      for (int i = 0; i < HD; ++i) part = __builtin_fmaf(qv[i], ks[kk][HD * hf + i], part);
+      const float full = part + __shfl_xor(part, 32);
+      s[kk] = (KT * j + kk < L) ? full * c : -INFINITY;
+      mx = fmaxf(mx, s[kk]);
+    }
+    const float mnew = fmaxf(m, mx);
+    const float alpha = exp2f(m - mnew);
+    lsum *= alpha;
+#pragma unroll
+    for (int i = 0; i < HD; ++i) acc[i] *= alpha;
+#pragma unroll
+    for (int kk = 0; kk < KT; ++kk) {
+      const float p = exp2f(s[kk] - mnew);
+      lsum += p;
+#pragma unroll
+      for (int i = 0; i < HD; ++i) acc[i] = __builtin_fmaf(p, vs[kk][HD * hf + i], acc[i]);
+    }
+    m = mnew;
+  }
+  const int32_t qrel = qs + 32 * wave + l32;
+  if (qrel < L) {
+    float* orow = static_cast<float*>(a.out) + (int64_t(cb + qrel) * heads + h) * D + HD * hf;
+    const float inv = 1.f / lsum;
+#pragma unroll
+    for (int i = 0; i < HD; ++i) orow[i] = acc[i] * inv;
+  }
+}
+
+hipError_t launch_attn_fwd(const char* ws, const WsLayout& l, void* out, int32_t heads,
+                           int32_t head_dim, bool bf16, float scale, hipStream_t s) {
+  AttnArgs a;
+  a.ws = ws;
+  a.off_len = l.off_len;
+  a.off_cu = l.off_cu;
+  a.off_pcu = l.off_pcu;
+  a.off_tiles = l.off_tiles;
+  a.qw = ws + l.off_q;
+  a.kw = ws + l.off_k;
+  a.vw = ws + l.off_v;
+  a.out = out;
+  a.heads = heads;
+  a.rows = l.rows;
+  a.c_log2 = scale * 1.4426950408889634f;
+  const dim3 grid(unsigned(l.n_tiles * heads));
+  if (bf16) {
+    if (head_dim == 128) hipLaunchKernelGGL(attn_fwd_bf16_kernel<128>, grid, dim3(256), 0, s, a);
+    else hipLaunchKernelGGL(attn_fwd_bf16_kernel<64>, grid, dim3(256), 0, s, a);
+  } else {
+    if (head_dim == 128) hipLaunchKernelGGL(attn_fwd_f32_kernel<128>, grid, dim3(256), 0, s, a);
+    else hipLaunchKernelGGL(attn_fwd_f32_kernel<64>, grid, dim3(256), 0, s, a);
+  }
+  return hipGetLastError();
+}
+
+}  // namespace mf

@@ -1,0 +1,111 @@
+// Shared definitions of the HIP library: tile sizes, workspace layout, token
+// position rule and small device helpers. Included by every .hip source and
+// by the host API.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace mf {
+
+// Keys per K/V tile. Every sample starts on a multiple of KTILE in the padded
+// workspace layout, so tiles never straddle two samples.
+constexpr int KTILE = 64;
+// Queries per attention workgroup (both dtypes use the same tile table).
+constexpr int QTILE = 128;
+// Positions per axis covered by the cos/sin table.
+constexpr int ROPE_PMAX = 512;
+constexpr int MAX_SEGMENTS = 4096;
+
+enum : int32_t { FLAG_OK = 0, FLAG_METADATA = 1, FLAG_POSITION = 2 };
+
+__host__ __device__ inline int64_t round_up(int64_t x, int64_t m) { return (x + m - 1) / m * m; }
+__host__ __device__ inline int64_t ceil_div(int64_t x, int64_t m) { return (x + m - 1) / m; }
+
+// Rows per head of the padded Q~/K~/V^T buffers: every sample padded to a
+// multiple of KTILE (at most KTILE-1 extra rows each) plus one QTILE-KTILE
+// slack so the last query tile of the last sample stays inside the buffer.
+__host__ __device__ inline int64_t padded_rows(int64_t tokens, int32_t n_seg) {
+  return round_up(tokens + int64_t(n_seg) * (KTILE - 1), KTILE) + (QTILE - KTILE);
+}
+
+__host__ __device__ inline int64_t max_tiles(int64_t tokens, int32_t n_seg) {
+  return ceil_div(tokens, QTILE) + n_seg;
+}
+
+// Workspace: [header 256 B][len n][cu n+1][pcu n+1][tiles 2*max_tiles][Q~][K~][V~]
+// with every section 256-byte aligned. Q~, K~, V~ are [heads][rows][head_dim].
+struct WsHeader {
+  int32_t flag;          // FLAG_* of the last metadata check
+  int32_t n_tiles;       // valid entries of the tile table
+  int32_t padded_total;  // padded rows used by the samples (pcu[n])
+  int32_t n_seg;
+  int32_t pad[60];
+};
+static_assert(sizeof(WsHeader) == 256, "header is one 256-byte block");
+
+struct WsLayout {
+  int64_t off_len, off_cu, off_pcu, off_tiles, off_q, off_k, off_v, total;
+  int64_t rows;     // padded rows per head
+  int64_t n_tiles;  // capacity of the tile table
+};
+
+__host__ __device__ inline WsLayout ws_layout(int64_t tokens, int32_t heads, int32_t head_dim,
+                                              int32_t elem_bytes, int32_t n_seg) {
+  WsLayout l;
+  int64_t o = 256;
+  l.off_len = o;   o += round_up(int64_t(n_seg) * 4, 256);
+  l.off_cu = o;    o += round_up(int64_t(n_seg + 1) * 4, 256);
+  l.off_pcu = o;   o += round_up(int64_t(n_seg + 1) * 4, 256);
+  l.n_tiles = max_tiles(tokens, n_seg);
+  l.off_tiles = o; o += round_up(l.n_tiles * 8, 256);
+  l.rows = padded_rows(tokens, n_seg);
+  const int64_t buf = round_up(int64_t(heads) * l.rows * head_dim * elem_bytes, 256);
+  l.off_q = o; o += buf;
+  l.off_k = o; o += buf;
+  l.off_v = o; o += buf;
+  l.total = o;
+  return l;
+}
+
+// Position of token u (counted from the start of its sample): prompt tokens
+// at (0, 0), image token p = u - text_len at (p / w, p % w).
+__device__ inline void token_position(int32_t u, int32_t text_len, int32_t w, int32_t& row,
+                                      int32_t& col) {
+  if (u < text_len) {
+    row = 0;
+    col = 0;
+  } else {
+    const int32_t p = u - text_len;
+    row = p / w;
+    col = p - row * w;
+  }
+}
+
+// Largest i in [0, n) with a[i] <= x, for a non-decreasing a[0..n] with a[0] <= x.
+__device__ inline int32_t upper_segment(const int32_t* a, int32_t n, int64_t x) {
+  int32_t lo = 0, hi = n;  // invariant a[lo] <= x < a[hi] (a[n] treated as +inf if x beyond)
+  while (hi - lo > 1) {
+    const int32_t mid = (lo + hi) >> 1;
+    if (a[mid] <= x) lo = mid; else hi = mid;
+  }
+  return lo;
+}
+
+// bf16 helpers: round-to-nearest-even conversion and widening.
+__device__ inline uint16_t f32_to_bf16_rne(float f) {
+  uint32_t b = __float_as_uint(f);
+  b += 0x7FFFu + ((b >> 16) & 1u);
+  return uint16_t(b >> 16);
+}
+__device__ inline float bf16_to_f32(uint16_t h) { return __uint_as_float(uint32_t(h) << 16); }
+
+// Swizzled position of 16-byte chunk `c` inside a tile stored as 256-byte
+// lines: slot s of line L is stored at slot s ^ (L % 16). Rows read by
+// 16 consecutive lanes at one logical column then hit 16 distinct bank groups.
+__host__ __device__ inline int32_t swz_chunk(int32_t c) {
+  const int32_t line = c >> 4;
+  return (line << 4) | ((c & 15) ^ (line & 15));
+}
+
+}  // namespace mf

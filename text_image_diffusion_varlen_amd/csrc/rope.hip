@@ -1,0 +1,241 @@
+// 2D rotary position embedding on the device.
+//
+// Source: mageflow.net architecture page, section 2 (2D RoPE encodes the 2D
+// spatial position of every latent token natively, any aspect ratio, with no
+// interpolation onto a fixed grid). Layout taken: channels [0, d/2) turn by
+// the row, [d/2, d) by the column; adjacent pairs (2j, 2j+1) inside each half
+// at frequency theta^(-2j/(d/2)); (x0, x1) -> (x0 c - x1 s, x0 s + x1 c).
+// Prompt tokens sit at (0, 0) and are therefore left unrotated.
+//
+// cos/sin come from a float2 table [ROPE_PMAX][d/4] computed on the host in
+// double precision (entry (p, j) = cos/sin of p * theta^(-2j/(d/2))); the
+// device does the rotation in fp32.
+//
+// rope_pack_kernel is the prologue of the attention path. One workgroup per
+// (KTILE-row tile of the padded layout, head). It rotates q and k of every
+// token of the tile and writes them into the workspace:
+//   Q~  [head][row][d]           row-major
+//   K~  [head][row][d]           bf16: each KTILE x d tile stored as 256-byte
+//                                lines of 16-byte chunks with the chunk swizzle
+//                                of swz_chunk (conflict-free LDS reads later)
+//   V~  bf16: V transposed per tile, [d][KTILE] inside each tile, keys inside
+//       every group of 16 stored in the order 0-3, 8-11, 4-7, 12-15 (the order
+//       in which the MFMA accumulator of the score tile holds them), same
+//       chunk swizzle; f32: plain row-major copy.
+// Rows that belong to no token (padding up to KTILE, and the slack after the
+// last sample) are written as zeros.
+#include "mf_common.h"
+
+namespace mf {
+
+template <typename T> struct Elem;
+template <> struct Elem<uint16_t> {
+  static constexpr int PER_CHUNK = 8;
+  __device__ static float load(uint16_t x) { return bf16_to_f32(x); }
+  __device__ static uint16_t store(float x) { return f32_to_bf16_rne(x); }
+};
+template <> struct Elem<float> {
+  static constexpr int PER_CHUNK = 4;
+  __device__ static float load(float x) { return x; }
+  __device__ static float store(float x) { return x; }
+};
+
+template <typename T> struct alignas(16) Chunk { T v[16 / sizeof(T)]; };
+
+// Rotates one 16-byte chunk (channels d0 .. d0+E-1, E even) of a row at (row, col).
+template <typename T, int D>
+__device__ inline Chunk<T> rotate_chunk(const Chunk<T>& in, int d0, int32_t row, int32_t col,
+                                        const float2* __restrict__ cs) {
+  constexpr int E = Elem<T>::PER_CHUNK;
+  Chunk<T> out;
+#pragma unroll
+  for (int pp = 0; pp < E / 2; ++pp) {
+    const int d = d0 + 2 * pp;
+    const bool first_half = d < D / 2;
+    const int j = first_half ? d / 2 : (d - D / 2) / 2;
+    const int32_t p = first_half ? row : col;
+    const float2 r = cs[p * (D / 4) + j];
+    const float x0 = Elem<T>::load(in.v[2 * pp]);
+    const float x1 = Elem<T>::load(in.v[2 * pp + 1]);
+    out.v[2 * pp] = Elem<T>::store(x0 * r.x - x1 * r.y);
+    out.v[2 * pp + 1] = Elem<T>::store(x0 * r.y + x1 * r.x);
+  }
+  return out;
+}
+
+template <typename T, int D>
+__global__ void __launch_bounds__(256)
+rope_pack_kernel(const T* __restrict__ q, const T* __restrict__ k, const T* __restrict__ v,
+                 const int32_t* __restrict__ grid_hw, const int32_t* __restrict__ text_len,
+                 const char* __restrict__ ws, int64_t off_len, int64_t off_cu, int64_t off_pcu,
+                 T* __restrict__ qw, T* __restrict__ kw, T* __restrict__ vw,
+                 const float2* __restrict__ cs, int32_t heads, int64_t rows) {
+  constexpr int E = Elem<T>::PER_CHUNK;
+  constexpr int CPR = D / E;             // chunks per row
+  constexpr int CPT = KTILE * CPR;       // chunks per tile
+  const WsHeader* hdr = reinterpret_cast<const WsHeader*>(ws);
+  if (hdr->flag != FLAG_OK) return;
+  const int32_t* len = reinterpret_cast<const int32_t*>(ws + off_len);
+  const int32_t* cu = reinterpret_cast<const int32_t*>(ws + off_cu);
+  const int32_t* pcu = reinterpret_cast<const int32_t*>(ws + off_pcu);
+
+  const int64_t r0 = int64_t(blockIdx.x) * KTILE;
+  const int h = blockIdx.y;
+  const int32_t n = hdr->n_seg;
+  int32_t u0 = 0, L = 0, tl = 0, w = 1;
+  int64_t tok0 = 0;
+  if (r0 < hdr->padded_total) {
+    const int32_t s = upper_segment(pcu, n, r0);
+    u0 = int32_t(r0 - pcu[s]);
+    L = len[s];
+    tok0 = int64_t(cu[s]) + u0;
+    tl = text_len[s];
+    w = grid_hw[2 * s + 1];
+  }
+  const int64_t tile_off = (int64_t(h) * rows + r0) * D;
+  const int64_t src_stride = int64_t(heads) * D;  // elements between consecutive tokens
+
+  // Q and K: rotate, then row-major (Q, f32 K) or swizzled (bf16 K) stores.
+  for (int f = threadIdx.x; f < CPT; f += 256) {
+    const int rr = f / CPR, cc = f % CPR;
+    const int32_t u = u0 + rr;
+    Chunk<T> qo, ko;
+    if (u < L) {
+      int32_t row, col;
+      token_position(u, tl, w, row, col);
+      const int64_t src = (tok0 + rr) * src_stride + int64_t(h) * D + cc * E;
+      const Chunk<T> qi = *reinterpret_cast<const Chunk<T>*>(q + src);
+      const Chunk<T> ki = *reinterpret_cast<const Chunk<T>*>(k + src);
+      qo = rotate_chunk<T, D>(qi, cc * E, row, col, cs);
+      ko = rotate_chunk<T, D>(ki, cc * E, row, col, cs);
+    } else {
+#pragma unroll
+      for (int e = 0; e < E; ++e) qo.v[e] = ko.v[e] = T(0);
+    }
+    *reinterpret_cast<Chunk<T>*>(qw + tile_off + int64_t(f) * E) = qo;
+    const int kf = sizeof(T) == 2 ? swz_chunk(f) : f;
+    *reinterpret_cast<Chunk<T>*>(kw + tile_off + int64_t(kf) * E) = ko;
+  }
+
+  if constexpr (sizeof(T) == 4) {
+    // f32: V copied row-major into the padded layout.
+    for (int f = threadIdx.x; f < CPT; f += 256) {
+      const int rr = f / CPR, cc = f % CPR;
+      Chunk<T> vo;
+      if (u0 + rr < L) {
+        vo = *reinterpret_cast<const Chunk<T>*>(v + (tok0 + rr) * src_stride + int64_t(h) * D + cc * E);
+      } else {
+#pragma unroll
+        for (int e = 0; e < E; ++e) vo.v[e] = T(0);
+      }
+      *reinterpret_cast<Chunk<T>*>(vw + tile_off + int64_t(f) * E) = vo;
+    }
+  } else {
+    // bf16: V tile through LDS, written transposed ([d][KTILE]) in MFMA key order.
+    constexpr int VS = D + 2;  // padded LDS row (elements): consecutive keys fall in different banks
+    __shared__ uint16_t vs[KTILE * VS];
+    for (int f = threadIdx.x; f < CPT; f += 256) {
+      const int rr = f / CPR, cc = f % CPR;
+      Chunk<T> vi;
+      if (u0 + rr < L) {
+        vi = *reinterpret_cast<const Chunk<T>*>(v + (tok0 + rr) * src_stride + int64_t(h) * D + cc * E);
+      } else {
+#pragma unroll
+        for (int e = 0; e < E; ++e) vi.v[e] = T(0);
+      }
+      uint32_t* dst = reinterpret_cast<uint32_t*>(vs + rr * VS + cc * E);
+      const uint32_t* sv = reinterpret_cast<const uint32_t*>(vi.v);
+#pragma unroll
+      for (int e = 0; e < E / 2; ++e) dst[e] = sv[e];
+    }
+    __syncthreads();
+    // Output chunk f2 = c * 8 + g: channel c, keys of chunk g of the 64-key row.
+    for (int f2 = threadIdx.x; f2 < D * (KTILE / 8); f2 += 256) {
+      const int c = f2 >> 3, g = f2 & 7;
+      const int base = 16 * (g >> 1) + 4 * (g & 1);
+      Chunk<T> o;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        o.v[e] = vs[(base + e) * VS + c];
+        o.v[4 + e] = vs[(base + 8 + e) * VS + c];
+      }
+      *reinterpret_cast<Chunk<T>*>(vw + tile_off + int64_t(swz_chunk(f2)) * 8) = o;
+    }
+  }
+}
+
+// Standalone RoPE: x_out = R(pos) x_in for [tokens][heads][D]. Positions
+// outside [0, ROPE_PMAX) copy the row unchanged and flag FLAG_POSITION.
+template <typename T, int D>
+__global__ void __launch_bounds__(256)
+rope_kernel(const T* __restrict__ x, T* __restrict__ y, const int32_t* __restrict__ pos,
+            int64_t tokens, int32_t heads, const float2* __restrict__ cs, int32_t* status) {
+  constexpr int E = Elem<T>::PER_CHUNK;
+  constexpr int CPR = D / E;
+  const int64_t f = int64_t(blockIdx.x) * 256 + threadIdx.x;
+  if (f >= tokens * heads * CPR) return;
+  const int64_t t = f / (int64_t(heads) * CPR);
+  const int cc = int(f % CPR);
+  const int32_t row = pos[2 * t], col = pos[2 * t + 1];
+  const Chunk<T> in = *reinterpret_cast<const Chunk<T>*>(x + f * E);
+  Chunk<T> out;
+  if (row < 0 || col < 0 || row >= ROPE_PMAX || col >= ROPE_PMAX) {
+    out = in;
+    if (cc == 0) atomicOr(status, FLAG_POSITION);
+  } else {
+    out = rotate_chunk<T, D>(in, cc * E, row, col, cs);
+  }
+  *reinterpret_cast<Chunk<T>*>(y + f * E) = out;
+}
+
+template <typename T, int D>
+static hipError_t launch_rope_pack_t(const void* q, const void* k, const void* v,
+                                     const int32_t* grid_hw, const int32_t* text_len,
+                                     const char* ws, const WsLayout& l, const float2* cs,
+                                     int32_t heads, hipStream_t s) {
+  char* w = const_cast<char*>(ws);
+  dim3 grid(unsigned(l.rows / KTILE), unsigned(heads));
+  hipLaunchKernelGGL((rope_pack_kernel<T, D>), grid, dim3(256), 0, s,
+                     static_cast<const T*>(q), static_cast<const T*>(k), static_cast<const T*>(v),
+                     grid_hw, text_len, ws, l.off_len, l.off_cu, l.off_pcu,
+                     reinterpret_cast<T*>(w + l.off_q), reinterpret_cast<T*>(w + l.off_k),
+                     reinterpret_cast<T*>(w + l.off_v), cs, heads, l.rows);
+  return hipGetLastError();
+}
+
+hipError_t launch_rope_pack(const void* q, const void* k, const void* v, const int32_t* grid_hw,
+                            const int32_t* text_len, const char* ws, const WsLayout& l,
+                            const float2* cs, int32_t heads, int32_t head_dim, bool bf16,
+                            hipStream_t s) {
+  if (bf16) {
+    return head_dim == 128
+               ? launch_rope_pack_t<uint16_t, 128>(q, k, v, grid_hw, text_len, ws, l, cs, heads, s)
+               : launch_rope_pack_t<uint16_t, 64>(q, k, v, grid_hw, text_len, ws, l, cs, heads, s);
+  }
+  return head_dim == 128
+             ? launch_rope_pack_t<float, 128>(q, k, v, grid_hw, text_len, ws, l, cs, heads, s)
+             : launch_rope_pack_t<float, 64>(q, k, v, grid_hw, text_len, ws, l, cs, heads, s);
+}
+
+template <typename T, int D>
+static hipError_t launch_rope_t(const void* x, void* y, const int32_t* pos, int64_t tokens,
+                                int32_t heads, const float2* cs, int32_t* status, hipStream_t s) {
+  constexpr int CPR = D / Elem<T>::PER_CHUNK;
+  const int64_t chunks = tokens * heads * CPR;
+  hipLaunchKernelGGL((rope_kernel<T, D>), dim3(unsigned(ceil_div(chunks, 256))), dim3(256), 0, s,
+                     static_cast<const T*>(x), static_cast<T*>(y), pos, tokens, heads, cs, status);
+  return hipGetLastError();
+}
+
+hipError_t launch_rope(const void* x, void* y, const int32_t* pos, int64_t tokens, int32_t heads,
+                       int32_t head_dim, bool bf16, const float2* cs, int32_t* status,
+                       hipStream_t s) {
+  if (bf16) {
+    return head_dim == 128 ? launch_rope_t<uint16_t, 128>(x, y, pos, tokens, heads, cs, status, s)
+                           : launch_rope_t<uint16_t, 64>(x, y, pos, tokens, heads, cs, status, s);
+  }
+  return head_dim == 128 ? launch_rope_t<float, 128>(x, y, pos, tokens, heads, cs, status, s)
+                         : launch_rope_t<float, 64>(x, y, pos, tokens, heads, cs, status, s);
+}
+
+}  // namespace mf
