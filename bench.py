@@ -131,6 +131,8 @@ def main():
     ap.add_argument("--seed", type=int, default=None)
     ap.add_argument("--cpu-budget", type=float, default=15.0, help="seconds of oracle work for cpu_baseline")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--calibrate-copy", action="store_true",
+                    help="only run a plain device copy of 1 GiB (HBM-counter calibration for profiling)")
     args = ap.parse_args()
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
@@ -145,6 +147,16 @@ def main():
         print("bench.py needs a GPU", file=sys.stderr)
         sys.exit(1)
     torch.cuda.set_device(0)
+    if args.calibrate_copy:
+        n = 1 << 30
+        src = torch.ones(n, dtype=torch.uint8, device="cuda")
+        dst = torch.empty_like(src)
+        for _ in range(max(args.steps, 1)):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        print(json.dumps({"calibrate_copy_bytes_read": n, "calibrate_copy_bytes_written": n,
+                          "dispatches": max(args.steps, 1)}), flush=True)
+        return
     w = workloads.make_workload(args.config, seed=args.seed)
     dt = torch.bfloat16 if w.dtype == "bf16" else torch.float32
     q, k, v = (torch.from_numpy(x).to(dt).cuda() for x in (w.q, w.k, w.v))

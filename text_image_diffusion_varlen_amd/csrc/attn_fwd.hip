@@ -26,6 +26,8 @@
 //
 // f32 kernel: the same tiling of work with plain fp32 FMAs (no reduced
 // precision anywhere); each query row is split over two lanes (channel halves).
+#include <type_traits>
+
 #include "mf_common.h"
 
 namespace mf {
@@ -54,12 +56,154 @@ __device__ inline uint32_t pack_bf16x2(float a, float b) {
   return __builtin_bit_cast(uint32_t, r);
 }
 
+// Combine a value with the same register of lane ^ 32. v_permlane32_swap
+// exchanges the upper 32 lanes of its first operand with the lower 32 lanes of
+// its second; with both operands equal to x, every lane ends up holding x[l]
+// in one result and x[l ^ 32] in the other, so a symmetric combine of the two
+// results needs no lane test.
+__device__ inline float halves_max(float x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return __builtin_elementwise_maximum(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+// acc + p0 + p1 for a packed bf16 pair (v_dot2_f32_bf16 against (1, 1)).
+__device__ inline float dot2_bf16_sum(uint32_t pair, float acc) {
+  typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+  const bf16x2 one = {(__bf16)1.0f, (__bf16)1.0f};
+  return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, pair), one, acc, false);
+}
+__device__ inline float halves_sum(float x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+
+typedef __attribute__((address_space(3))) void* lds_ptr_t;
+
+// Copies one chunk-major tile (CHUNKS 16-byte chunks) from the workspace into
+// LDS with gfx950 direct-to-LDS loads: each wave moves CHUNKS/4 chunks, one
+// contiguous 1 KB per instruction, without passing through registers.
+template <int CHUNKS>
+__device__ inline void tile_to_lds(const u32x4* __restrict__ src, u32x4* dst, int wave, int lane) {
+  constexpr int PER_WAVE = CHUNKS / 4;
+#pragma unroll
+  for (int i = 0; i < PER_WAVE / 64; ++i) {
+    const int c = wave * PER_WAVE + i * 64;
+    __builtin_amdgcn_global_load_lds(src + c + lane, (lds_ptr_t)(dst + c), 16, 0, 0);
+  }
+}
+
+__device__ inline void wait_tile_and_sync() {
+  __builtin_amdgcn_s_waitcnt(0xF70);  // vmcnt(0): this wave's direct-to-LDS copies landed
+  __syncthreads();
+}
+
+template <int D>
+struct Bf16Tile {
+  static constexpr int CHUNKS = KTILE * D / 8;  // 16-byte chunks per K~ (or V~^T) tile
+  static constexpr int KSTEPS = D / 16;         // MFMA k-steps of the score product
+  static constexpr int DBLK = D / 32;           // 32-channel blocks of the output
+};
+
+// One 64-key tile of one wave's 32 query rows: S^T = K~ Q~^T, online softmax,
+// O^T += V~^T P^T. kt / vt point at the chunk-major K~ and V~^T tiles in LDS.
+template <int D, bool MASKED>
+__device__ inline void attend_tile(const u32x4* kt, const u32x4* vt, const bf16x8 (&qreg)[D / 16],
+                                   f32x16 (&acc)[D / 32], float& m, float& lsum, float c,
+                                   int kbase_key, int L, int hf, int l32) {
+  constexpr int KSTEPS = Bf16Tile<D>::KSTEPS;
+  constexpr int DBLK = Bf16Tile<D>::DBLK;
+  constexpr float REF_SLACK = 8.0f;
+  // K~ chunk (c, n) sits at c * KTILE + n: lane (l32, hf) reads key n = l32 (+32)
+  // and channel chunk 2*ks + hf, i.e. base + 2*KTILE*ks (+32).
+  const u32x4* kl = kt + hf * KTILE + l32;
+  // V~^T chunk (g, r) sits at g * D + r: lane reads channel r = 32*b + l32, key chunk 2*ks2 + hf.
+  const u32x4* vl = vt + hf * D + l32;
+
+  f32x16 s0 = {}, s1 = {};
+  bf16x8 kb0[4], kb1[4];
+#pragma unroll
+  for (int ks = 0; ks < 4; ++ks) {
+    kb0[ks] = __builtin_bit_cast(bf16x8, kl[2 * KTILE * ks]);
+    kb1[ks] = __builtin_bit_cast(bf16x8, kl[2 * KTILE * ks + 32]);
+  }
+#pragma unroll
+  for (int ks = 0; ks < KSTEPS; ++ks) {
+    const bf16x8 a0 = kb0[ks & 3], a1 = kb1[ks & 3];
+    if (ks + 4 < KSTEPS) {
+      kb0[ks & 3] = __builtin_bit_cast(bf16x8, kl[2 * KTILE * (ks + 4)]);
+      kb1[ks & 3] = __builtin_bit_cast(bf16x8, kl[2 * KTILE * (ks + 4) + 32]);
+    }
+    s0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a0, qreg[ks], s0, 0, 0, 0);
+    s1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a1, qreg[ks], s1, 0, 0, 0);
+  }
+  // V operands of the first two k-steps, read while the softmax runs.
+  bf16x8 vb[2][DBLK];
+#pragma unroll
+  for (int k2 = 0; k2 < 2; ++k2) {
+#pragma unroll
+    for (int b = 0; b < DBLK; ++b) vb[k2][b] = __builtin_bit_cast(bf16x8, vl[2 * D * k2 + 32 * b]);
+  }
+  // Accumulator entry e holds key 8*(e/4) + 4*hf + e%4 of the tile (s1: +32).
+  if constexpr (MASKED) {
+    const int kb = kbase_key + 4 * hf;
+#pragma unroll
+    for (int e = 0; e < 16; ++e) {
+      const int key = kb + 8 * (e >> 2) + (e & 3);
+      if (key >= L) s0[e] = -INFINITY;
+      if (key + 32 >= L) s1[e] = -INFINITY;
+    }
+  }
+  // Row max: this lane's 32 keys, then the other 32 from lane ^ 32.
+  float mx = __builtin_elementwise_maximum(s0[0], s1[0]);
+#pragma unroll
+  for (int e = 1; e < 16; ++e) mx = __builtin_elementwise_maximum(__builtin_elementwise_maximum(mx, s0[e]), s1[e]);
+  const float mt = halves_max(mx) * c;
+  // The reference max only moves when a tile's max exceeds it by more than
+  // REF_SLACK, so p = exp2(s*c - m) <= 2^REF_SLACK and the accumulator is
+  // rescaled only on those tiles; numerator and denominator share m.
+  const bool grow = mt > m + REF_SLACK;  // always true on the first tile (m = -inf)
+  if (__any(grow)) {
+    const float mnew = grow ? mt : m;
+    const float alpha = __builtin_amdgcn_exp2f(m - mnew);  // 0 on the first tile, 1 where unchanged
+    lsum *= alpha;
+#pragma unroll
+    for (int b = 0; b < DBLK; ++b) acc[b] *= alpha;
+    m = mnew;
+  }
+  const float nm = -m;
+  uint32_t pk[4][4];  // P^T operand: k-step ks2 holds keys 16*ks2 + {4hf..4hf+3, 8+4hf..8+4hf+3}
+#pragma unroll
+  for (int e = 0; e < 16; e += 2) {
+    const float p0 = __builtin_amdgcn_exp2f(__builtin_fmaf(s0[e], c, nm));
+    const float p1 = __builtin_amdgcn_exp2f(__builtin_fmaf(s0[e + 1], c, nm));
+    const float p2 = __builtin_amdgcn_exp2f(__builtin_fmaf(s1[e], c, nm));
+    const float p3 = __builtin_amdgcn_exp2f(__builtin_fmaf(s1[e + 1], c, nm));
+    pk[e >> 3][(e & 7) >> 1] = pack_bf16x2(p0, p1);
+    pk[2 + (e >> 3)][(e & 7) >> 1] = pack_bf16x2(p2, p3);
+  }
+  // Row sum of the bf16 P actually multiplied into V (two keys per v_dot2).
+#pragma unroll
+  for (int k2 = 0; k2 < 4; ++k2) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) lsum = dot2_bf16_sum(pk[k2][i], lsum);
+  }
+  // O^T += V~^T x P^T
+#pragma unroll
+  for (int ks2 = 0; ks2 < 4; ++ks2) {
+    const bf16x8 pb8 = __builtin_bit_cast(bf16x8, u32x4{pk[ks2][0], pk[ks2][1], pk[ks2][2], pk[ks2][3]});
+#pragma unroll
+    for (int b = 0; b < DBLK; ++b) {
+      const bf16x8 vv = vb[ks2 & 1][b];
+      if (ks2 + 2 < 4) vb[ks2 & 1][b] = __builtin_bit_cast(bf16x8, vl[2 * D * (ks2 + 2) + 32 * b]);
+      acc[b] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vv, pb8, acc[b], 0, 0, 0);
+    }
+  }
+}
+
 template <int D>
 __global__ void __launch_bounds__(256, 2) attn_fwd_bf16_kernel(AttnArgs a) {
-  constexpr int CHUNKS = KTILE * D / 8;     // 16-byte chunks per K~ (or V~^T) tile
-  constexpr int PER_THREAD = CHUNKS / 256;  // 4 (d=128) or 2 (d=64)
-  constexpr int KSTEPS = D / 16;            // MFMA k-steps of the score product
-  constexpr int DBLK = D / 32;              // 32-channel blocks of the output
+  constexpr int CHUNKS = Bf16Tile<D>::CHUNKS;
+  constexpr int KSTEPS = Bf16Tile<D>::KSTEPS;
+  constexpr int DBLK = Bf16Tile<D>::DBLK;
 
   const WsHeader* hdr = reinterpret_cast<const WsHeader*>(a.ws);
   const int32_t heads = a.heads;
@@ -78,124 +222,60 @@ __global__ void __launch_bounds__(256, 2) attn_fwd_bf16_kernel(AttnArgs a) {
 
   // Q~ rows of this lane as the B operand of S^T = K~ Q~^T: lane holds
   // query l32, channels 16*ks + 8*hf .. +7 for every k-step ks.
-  const uint16_t* qw = static_cast<const uint16_t*>(a.qw);
   bf16x8 qreg[KSTEPS];
   {
-    const uint16_t* qrow = qw + (head_row0 + qs + 32 * wave + l32) * D + 8 * hf;
+    const uint16_t* qrow = static_cast<const uint16_t*>(a.qw) + (head_row0 + qs + 32 * wave + l32) * D + 8 * hf;
 #pragma unroll
     for (int ks = 0; ks < KSTEPS; ++ks) qreg[ks] = *reinterpret_cast<const bf16x8*>(qrow + 16 * ks);
   }
+  // The tile copies share the in-order vector-memory counter with these
+  // loads: finish Q first so later waits only cover tile copies.
+  __builtin_amdgcn_sched_barrier(0);
+  __builtin_amdgcn_s_waitcnt(0xF70);  // vmcnt(0)
+  __builtin_amdgcn_sched_barrier(0);
 
-  __shared__ __attribute__((aligned(16))) uint16_t lds[2][2][KTILE * D];
+  // Two LDS buffers, each one K~ tile and one V~^T tile (chunk-major, verbatim copies).
+  __shared__ u32x4 kA[CHUNKS], vA[CHUNKS], kB[CHUNKS], vB[CHUNKS];
   const u32x4* kg = reinterpret_cast<const u32x4*>(static_cast<const uint16_t*>(a.kw) + head_row0 * D);
   const u32x4* vg = reinterpret_cast<const u32x4*>(static_cast<const uint16_t*>(a.vw) + head_row0 * D);
   const int nkt = (L + KTILE - 1) / KTILE;
 
-  u32x4 stk[PER_THREAD], stv[PER_THREAD];
-#pragma unroll
-  for (int i = 0; i < PER_THREAD; ++i) {
-    stk[i] = kg[tid + 256 * i];
-    stv[i] = vg[tid + 256 * i];
-  }
-#pragma unroll
-  for (int i = 0; i < PER_THREAD; ++i) {
-    reinterpret_cast<u32x4*>(lds[0][0])[tid + 256 * i] = stk[i];
-    reinterpret_cast<u32x4*>(lds[0][1])[tid + 256 * i] = stv[i];
-  }
-  __syncthreads();
-
   const float c = a.c_log2;
-  float m = -INFINITY;  // running row max, already multiplied by c
+  float m = -INFINITY;  // reference row max (log2 units)
   float lsum = 0.f;     // this lane's partial row sum (its 32 keys of every tile)
   f32x16 acc[DBLK];
 #pragma unroll
   for (int b = 0; b < DBLK; ++b) acc[b] = f32x16{};
 
-  for (int j = 0; j < nkt; ++j) {
-    const int buf = j & 1;
-    const bool more = j + 1 < nkt;
-    if (more) {
-      const u32x4* kn = kg + (j + 1) * CHUNKS;
-      const u32x4* vn = vg + (j + 1) * CHUNKS;
-#pragma unroll
-      for (int i = 0; i < PER_THREAD; ++i) {
-        stk[i] = kn[tid + 256 * i];
-        stv[i] = vn[tid + 256 * i];
-      }
-    }
-    const uint16_t* kt = lds[buf][0];
-    const uint16_t* vt = lds[buf][1];
-
-    // S^T for keys 0..31 (s0) and 32..63 (s1) of the tile.
-    f32x16 s0 = {}, s1 = {};
-#pragma unroll
-    for (int ks = 0; ks < KSTEPS; ++ks) {
-      const int ch = 2 * ks + hf;
-      const bf16x8 k0 = *reinterpret_cast<const bf16x8*>(kt + 8 * swz_chunk(l32 * (D / 8) + ch));
-      const bf16x8 k1 = *reinterpret_cast<const bf16x8*>(kt + 8 * swz_chunk((l32 + 32) * (D / 8) + ch));
-      s0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(k0, qreg[ks], s0, 0, 0, 0);
-      s1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(k1, qreg[ks], s1, 0, 0, 0);
-    }
-    // Accumulator entry e holds key 8*(e/4) + 4*hf + e%4 (s1: +32).
-    if (KTILE * (j + 1) > L) {
-      const int kbase = KTILE * j + 4 * hf;
-#pragma unroll
-      for (int e = 0; e < 16; ++e) {
-        const int key = kbase + 8 * (e >> 2) + (e & 3);
-        if (key >= L) s0[e] = -INFINITY;
-        if (key + 32 >= L) s1[e] = -INFINITY;
-      }
-    }
-    float mx = fmaxf(s0[0], s1[0]);
-#pragma unroll
-    for (int e = 1; e < 16; ++e) mx = fmaxf(mx, fmaxf(s0[e], s1[e]));
-    mx = fmaxf(mx, __shfl_xor(mx, 32));
-    const float mnew = fmaxf(m, mx * c);
-    const float alpha = __builtin_amdgcn_exp2f(m - mnew);
-    const float nm = -mnew;
-    float psum = 0.f;
-    uint32_t pk[4][4];  // P^T operand: k-step ks2 holds keys 16*ks2 + {4hf..4hf+3, 8+4hf..8+4hf+3}
-#pragma unroll
-    for (int e = 0; e < 16; e += 2) {
-      const float p0 = __builtin_amdgcn_exp2f(__builtin_fmaf(s0[e], c, nm));
-      const float p1 = __builtin_amdgcn_exp2f(__builtin_fmaf(s0[e + 1], c, nm));
-      const float p2 = __builtin_amdgcn_exp2f(__builtin_fmaf(s1[e], c, nm));
-      const float p3 = __builtin_amdgcn_exp2f(__builtin_fmaf(s1[e + 1], c, nm));
-      psum += (p0 + p1) + (p2 + p3);
-      pk[e >> 3][(e & 7) >> 1] = pack_bf16x2(p0, p1);
-      pk[2 + (e >> 3)][(e & 7) >> 1] = pack_bf16x2(p2, p3);
-    }
-    lsum = lsum * alpha + psum;
-    if (__any(mnew != m)) {
-#pragma unroll
-      for (int b = 0; b < DBLK; ++b) acc[b] *= alpha;
-    }
-    m = mnew;
-
-    // O^T += V~^T x P^T
-#pragma unroll
-    for (int ks2 = 0; ks2 < 4; ++ks2) {
-      const bf16x8 pb8 = __builtin_bit_cast(bf16x8, u32x4{pk[ks2][0], pk[ks2][1], pk[ks2][2], pk[ks2][3]});
-#pragma unroll
-      for (int b = 0; b < DBLK; ++b) {
-        const bf16x8 vv = *reinterpret_cast<const bf16x8*>(vt + 8 * swz_chunk((32 * b + l32) * 8 + 2 * ks2 + hf));
-        acc[b] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vv, pb8, acc[b], 0, 0, 0);
-      }
-    }
-
-    if (more) {
-#pragma unroll
-      for (int i = 0; i < PER_THREAD; ++i) {
-        reinterpret_cast<u32x4*>(lds[buf ^ 1][0])[tid + 256 * i] = stk[i];
-        reinterpret_cast<u32x4*>(lds[buf ^ 1][1])[tid + 256 * i] = stv[i];
-      }
-    }
-    __syncthreads();
+  tile_to_lds<CHUNKS>(kg, kA, wave, lane);
+  tile_to_lds<CHUNKS>(vg, vA, wave, lane);
+  wait_tile_and_sync();
+  // Tiles alternate between buffer A (even j) and B (odd j); the copy of tile
+  // j+1 runs while tile j is processed. The last tile carries the key mask.
+  int j = 0;
+  for (; j + 2 < nkt; j += 2) {
+    tile_to_lds<CHUNKS>(kg + (j + 1) * CHUNKS, kB, wave, lane);
+    tile_to_lds<CHUNKS>(vg + (j + 1) * CHUNKS, vB, wave, lane);
+    attend_tile<D, false>(kA, vA, qreg, acc, m, lsum, c, KTILE * j, L, hf, l32);
+    wait_tile_and_sync();
+    tile_to_lds<CHUNKS>(kg + (j + 2) * CHUNKS, kA, wave, lane);
+    tile_to_lds<CHUNKS>(vg + (j + 2) * CHUNKS, vA, wave, lane);
+    attend_tile<D, false>(kB, vB, qreg, acc, m, lsum, c, KTILE * (j + 1), L, hf, l32);
+    wait_tile_and_sync();
+  }
+  if (j + 1 < nkt) {
+    tile_to_lds<CHUNKS>(kg + (j + 1) * CHUNKS, kB, wave, lane);
+    tile_to_lds<CHUNKS>(vg + (j + 1) * CHUNKS, vB, wave, lane);
+    attend_tile<D, false>(kA, vA, qreg, acc, m, lsum, c, KTILE * j, L, hf, l32);
+    wait_tile_and_sync();
+    attend_tile<D, true>(kB, vB, qreg, acc, m, lsum, c, KTILE * (j + 1), L, hf, l32);
+  } else {
+    attend_tile<D, true>(kA, vA, qreg, acc, m, lsum, c, KTILE * j, L, hf, l32);
   }
 
   // Epilogue: O = acc / l. Accumulator entry e of block b holds channel
   // 32*b + 8*(e/4) + 4*hf + e%4 of query l32.
-  lsum += __shfl_xor(lsum, 32);
+  lsum = halves_sum(lsum);
   const float inv = 1.f / lsum;
   const int32_t qrel = qs + 32 * wave + l32;
   if (qrel < L) {

@@ -15,13 +15,17 @@
 // (KTILE-row tile of the padded layout, head). It rotates q and k of every
 // token of the tile and writes them into the workspace:
 //   Q~  [head][row][d]           row-major
-//   K~  [head][row][d]           bf16: each KTILE x d tile stored as 256-byte
-//                                lines of 16-byte chunks with the chunk swizzle
-//                                of swz_chunk (conflict-free LDS reads later)
+//   K~  bf16: each KTILE x d tile stored chunk-major: 16-byte chunk c (channels
+//       8c..8c+7) of tile row n at chunk index c * KTILE + n. f32: row-major.
 //   V~  bf16: V transposed per tile, [d][KTILE] inside each tile, keys inside
 //       every group of 16 stored in the order 0-3, 8-11, 4-7, 12-15 (the order
-//       in which the MFMA accumulator of the score tile holds them), same
-//       chunk swizzle; f32: plain row-major copy.
+//       in which the MFMA accumulator of the score tile holds them), and the
+//       tile stored chunk-major: chunk g (8 keys) of channel r at g * d + r.
+//       f32: plain row-major copy.
+// Chunk-major tiles are copied verbatim into LDS by the attention kernel;
+// there, the 16 lanes that read one MFMA operand row block touch 16
+// consecutive chunks (no bank conflicts) and every read is a fixed offset
+// from a per-lane base.
 // Rows that belong to no token (padding up to KTILE, and the slack after the
 // last sample) are written as zeros.
 #include "mf_common.h"
@@ -95,9 +99,13 @@ rope_pack_kernel(const T* __restrict__ q, const T* __restrict__ k, const T* __re
   const int64_t tile_off = (int64_t(h) * rows + r0) * D;
   const int64_t src_stride = int64_t(heads) * D;  // elements between consecutive tokens
 
-  // Q and K: rotate, then row-major (Q, f32 K) or swizzled (bf16 K) stores.
+  // Q and K: rotate, then row-major Q~ and (bf16) chunk-major K~. Chunk f of
+  // the loop covers tile row rr = (f / 4) % 64 and chunk cc = f % 4 + 4 * (f / 256):
+  // four lanes read 64 contiguous bytes of a row, sixteen lanes with the same
+  // cc write 256 contiguous bytes of K~.
   for (int f = threadIdx.x; f < CPT; f += 256) {
-    const int rr = f / CPR, cc = f % CPR;
+    const int rr = sizeof(T) == 2 ? (f >> 2) & (KTILE - 1) : f / CPR;
+    const int cc = sizeof(T) == 2 ? (f & 3) + 4 * (f >> 8) : f % CPR;
     const int32_t u = u0 + rr;
     Chunk<T> qo, ko;
     if (u < L) {
@@ -112,8 +120,8 @@ rope_pack_kernel(const T* __restrict__ q, const T* __restrict__ k, const T* __re
 #pragma unroll
       for (int e = 0; e < E; ++e) qo.v[e] = ko.v[e] = T(0);
     }
-    *reinterpret_cast<Chunk<T>*>(qw + tile_off + int64_t(f) * E) = qo;
-    const int kf = sizeof(T) == 2 ? swz_chunk(f) : f;
+    *reinterpret_cast<Chunk<T>*>(qw + tile_off + int64_t(rr * CPR + cc) * E) = qo;
+    const int kf = sizeof(T) == 2 ? cc * KTILE + rr : rr * CPR + cc;
     *reinterpret_cast<Chunk<T>*>(kw + tile_off + int64_t(kf) * E) = ko;
   }
 
@@ -149,9 +157,9 @@ rope_pack_kernel(const T* __restrict__ q, const T* __restrict__ k, const T* __re
       for (int e = 0; e < E / 2; ++e) dst[e] = sv[e];
     }
     __syncthreads();
-    // Output chunk f2 = c * 8 + g: channel c, keys of chunk g of the 64-key row.
+    // Output chunk f2 = g * D + c: channel c, keys of chunk g of the 64-key row.
     for (int f2 = threadIdx.x; f2 < D * (KTILE / 8); f2 += 256) {
-      const int c = f2 >> 3, g = f2 & 7;
+      const int g = f2 / D, c = f2 % D;
       const int base = 16 * (g >> 1) + 4 * (g & 1);
       Chunk<T> o;
 #pragma unroll
@@ -159,7 +167,7 @@ rope_pack_kernel(const T* __restrict__ q, const T* __restrict__ k, const T* __re
         o.v[e] = vs[(base + e) * VS + c];
         o.v[4 + e] = vs[(base + 8 + e) * VS + c];
       }
-      *reinterpret_cast<Chunk<T>*>(vw + tile_off + int64_t(swz_chunk(f2)) * 8) = o;
+      *reinterpret_cast<Chunk<T>*>(vw + tile_off + int64_t(f2) * 8) = o;
     }
   }
 }
