@@ -10,7 +10,7 @@
 // workgroup only ever visits the key tiles of its own sample and the
 // cross-sample blocks of the packed score matrix are never touched.
 //
-// bf16 kernel (d = 64 or 128), one workgroup = 4 waves = QTILE (128) queries
+// bf16 kernel (d = 64 or 128), one workgroup = QTILE / 32 waves = QTILE queries
 // of one (sample, head), each wave owning 32 query rows:
 //   S^T (64 keys x 32 queries) = K~ tile (LDS) x Q~^T (registers), on
 //       v_mfma_f32_32x32x16_bf16 with fp32 accumulation. In this orientation
@@ -79,11 +79,12 @@ __device__ inline float halves_sum(float x) {
 typedef __attribute__((address_space(3))) void* lds_ptr_t;
 
 // Copies one chunk-major tile (CHUNKS 16-byte chunks) from the workspace into
-// LDS with gfx950 direct-to-LDS loads: each wave moves CHUNKS/4 chunks, one
+// LDS with gfx950 direct-to-LDS loads: each wave moves CHUNKS/ATTN_WAVES chunks, one
 // contiguous 1 KB per instruction, without passing through registers.
 template <int CHUNKS>
 __device__ inline void tile_to_lds(const u32x4* __restrict__ src, u32x4* dst, int wave, int lane) {
-  constexpr int PER_WAVE = CHUNKS / 4;
+  constexpr int PER_WAVE = CHUNKS / ATTN_WAVES;
+  static_assert(PER_WAVE % 64 == 0, "whole 1 KB copies per wave");
 #pragma unroll
   for (int i = 0; i < PER_WAVE / 64; ++i) {
     const int c = wave * PER_WAVE + i * 64;
@@ -200,7 +201,7 @@ __device__ inline void attend_tile(const u32x4* kt, const u32x4* vt, const bf16x
 }
 
 template <int D>
-__global__ void __launch_bounds__(256, 2) attn_fwd_bf16_kernel(AttnArgs a) {
+__global__ void __launch_bounds__(ATTN_THREADS, 2) attn_fwd_bf16_kernel(AttnArgs a) {
   constexpr int CHUNKS = Bf16Tile<D>::CHUNKS;
   constexpr int KSTEPS = Bf16Tile<D>::KSTEPS;
   constexpr int DBLK = Bf16Tile<D>::DBLK;
@@ -293,9 +294,9 @@ __global__ void __launch_bounds__(256, 2) attn_fwd_bf16_kernel(AttnArgs a) {
   }
 }
 
-// fp32 path: 4 waves x 32 queries; lane = (query l32, channel half hf).
+// fp32 path: QTILE / 32 waves x 32 queries; lane = (query l32, channel half hf).
 template <int D>
-__global__ void __launch_bounds__(256) attn_fwd_f32_kernel(AttnArgs a) {
+__global__ void __launch_bounds__(ATTN_THREADS) attn_fwd_f32_kernel(AttnArgs a) {
   constexpr int HD = D / 2;
   constexpr int KT = 32;  // keys per LDS tile
   const WsHeader* hdr = reinterpret_cast<const WsHeader*>(a.ws);
@@ -329,7 +330,7 @@ __global__ void __launch_bounds__(256) attn_fwd_f32_kernel(AttnArgs a) {
   const int nkt = (L + KT - 1) / KT;
   for (int j = 0; j < nkt; ++j) {
     __syncthreads();
-    for (int x = tid; x < KT * D; x += 256) {
+    for (int x = tid; x < KT * D; x += ATTN_THREADS) {
       ks[x / D][x % D] = kw[int64_t(j) * KT * D + x];
       vs[x / D][x % D] = vw[int64_t(j) * KT * D + x];
     }
@@ -385,11 +386,11 @@ hipError_t launch_attn_fwd(const char* ws, const WsLayout& l, void* out, int32_t
   a.c_log2 = scale * 1.4426950408889634f;
   const dim3 grid(unsigned(l.n_tiles * heads));
   if (bf16) {
-    if (head_dim == 128) hipLaunchKernelGGL(attn_fwd_bf16_kernel<128>, grid, dim3(256), 0, s, a);
-    else hipLaunchKernelGGL(attn_fwd_bf16_kernel<64>, grid, dim3(256), 0, s, a);
+    if (head_dim == 128) hipLaunchKernelGGL(attn_fwd_bf16_kernel<128>, grid, dim3(ATTN_THREADS), 0, s, a);
+    else hipLaunchKernelGGL(attn_fwd_bf16_kernel<64>, grid, dim3(ATTN_THREADS), 0, s, a);
   } else {
-    if (head_dim == 128) hipLaunchKernelGGL(attn_fwd_f32_kernel<128>, grid, dim3(256), 0, s, a);
-    else hipLaunchKernelGGL(attn_fwd_f32_kernel<64>, grid, dim3(256), 0, s, a);
+    if (head_dim == 128) hipLaunchKernelGGL(attn_fwd_f32_kernel<128>, grid, dim3(ATTN_THREADS), 0, s, a);
+    else hipLaunchKernelGGL(attn_fwd_f32_kernel<64>, grid, dim3(ATTN_THREADS), 0, s, a);
   }
   return hipGetLastError();
 }

@@ -11,8 +11,14 @@ namespace mf {
 // Keys per K/V tile. Every sample starts on a multiple of KTILE in the padded
 // workspace layout, so tiles never straddle two samples.
 constexpr int KTILE = 64;
-// Queries per attention workgroup (both dtypes use the same tile table).
-constexpr int QTILE = 128;
+// Queries per attention workgroup (both dtypes use the same tile table): one
+// wave per 32 query rows.
+#ifndef MF_QTILE
+#define MF_QTILE 256
+#endif
+constexpr int QTILE = MF_QTILE;
+constexpr int ATTN_WAVES = QTILE / 32;
+constexpr int ATTN_THREADS = 64 * ATTN_WAVES;
 // Positions per axis covered by the cos/sin table.
 constexpr int ROPE_PMAX = 512;
 constexpr int MAX_SEGMENTS = 4096;
