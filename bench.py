@@ -204,7 +204,9 @@ def main():
 
     attn_s = stage["attn"] / 1e3
     achieved = flops / attn_s
-    rope_bytes = 6.0 * w.tokens * w.heads * w.head_dim * elem
+    # prologue: bf16 reads k, v and writes K~, V~ (queries are rotated inside the attention kernel);
+    # f32 also reads q and writes Q~
+    rope_bytes = (4.0 if w.dtype == "bf16" else 6.0) * w.tokens * w.heads * w.head_dim * elem
     result = {
         "metric": "packed joint-attn TFLOP/s (bf16, 2D RoPE) + % of MFMA peak; tokens/s",
         "value": round(flops / (ms / 1e3) / 1e12, 2),

@@ -32,7 +32,8 @@ hipError_t launch_rope_pack(const void* q, const void* k, const void* v, const i
 hipError_t launch_rope(const void* x, void* y, const int32_t* pos, int64_t tokens, int32_t heads,
                        int32_t head_dim, bool bf16, const float2* cs, int32_t* status,
                        hipStream_t s);
-hipError_t launch_attn_fwd(const char* ws, const WsLayout& l, void* out, int32_t heads,
+hipError_t launch_attn_fwd(const char* ws, const WsLayout& l, const void* q, const int32_t* grid_hw,
+                           const int32_t* text_len, const float2* cs, void* out, int32_t heads,
                            int32_t head_dim, bool bf16, float scale, hipStream_t s);
 }  // namespace mf
 
@@ -194,7 +195,8 @@ int run_attn(const void* q, const void* k, const void* v, const int32_t* cu, con
   e = mf::launch_rope_pack(q, k, v, grid_hw, text_len, ws, l, cs, heads, head_dim, bf16, s);
   if (e != hipSuccess) return hip_fail(e, "rope_pack_kernel launch");
   if (ev && (e = hipEventRecord(ev[2], s)) != hipSuccess) return hip_fail(e, "hipEventRecord");
-  e = mf::launch_attn_fwd(ws, l, out, heads, head_dim, bf16, float(1.0 / std::sqrt(double(head_dim))), s);
+  e = mf::launch_attn_fwd(ws, l, q, grid_hw, text_len, cs, out, heads, head_dim, bf16,
+                          float(1.0 / std::sqrt(double(head_dim))), s);
   if (e != hipSuccess) return hip_fail(e, "attn_fwd launch");
   if (ev && (e = hipEventRecord(ev[3], s)) != hipSuccess) return hip_fail(e, "hipEventRecord");
   return MF_OK;

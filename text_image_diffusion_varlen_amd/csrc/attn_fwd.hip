@@ -5,12 +5,13 @@
 // section: per-sample cumulative offsets restrict attention to each sample;
 // mageflow.net architecture page, sections 2 and 8: text and image tokens in
 // one bidirectional sequence). Q~, K~ are the 2D-RoPE-rotated queries and
-// keys written by the prologue into the padded workspace layout, where every
+// keys; K~ (and V~^T) are written by the prologue into the padded workspace layout, where every
 // sample starts on a KTILE boundary; query tiles are sample-relative, so a
 // workgroup only ever visits the key tiles of its own sample and the
 // cross-sample blocks of the packed score matrix are never touched.
 //
 // bf16 kernel (d = 64 or 128), one workgroup = QTILE / 32 waves = QTILE queries
+// (the queries are read from the caller's q and rotated while loading)
 // of one (sample, head), each wave owning 32 query rows:
 //   S^T (64 keys x 32 queries) = K~ tile (LDS) x Q~^T (registers), on
 //       v_mfma_f32_32x32x16_bf16 with fp32 accumulation. In this orientation
@@ -29,6 +30,7 @@
 #include <type_traits>
 
 #include "mf_common.h"
+#include "rope_math.h"
 
 namespace mf {
 
@@ -39,7 +41,11 @@ typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 struct AttnArgs {
   const char* ws;
   int64_t off_len, off_cu, off_pcu, off_tiles;
-  const void* qw;
+  const void* q;            // caller's queries [T][heads][d] (bf16 kernel rotates them on load)
+  const int32_t* grid_hw;   // caller's (h, w) per sample
+  const int32_t* text_len;  // caller's prompt length per sample
+  const float2* cs;         // cos/sin table [ROPE_PMAX][d/4]
+  const void* qw;           // rotated queries in the workspace (f32 kernel)
   const void* kw;
   const void* vw;
   void* out;
@@ -221,13 +227,21 @@ __global__ void __launch_bounds__(ATTN_THREADS, 2) attn_fwd_bf16_kernel(AttnArgs
   const int wave = tid >> 6, lane = tid & 63, hf = lane >> 5, l32 = lane & 31;
   const int64_t head_row0 = int64_t(h) * a.rows + pb;  // first padded row of this (sample, head)
 
-  // Q~ rows of this lane as the B operand of S^T = K~ Q~^T: lane holds
-  // query l32, channels 16*ks + 8*hf .. +7 for every k-step ks.
+  // Rotated query row of this lane as the B operand of S^T = K~ Q~^T: lane
+  // holds query l32, channels 16*ks + 8*hf .. +7 for every k-step ks. The row
+  // is read from the caller's q and rotated here (once per workgroup); rows
+  // past the sample's end read its last token and are never stored.
   bf16x8 qreg[KSTEPS];
   {
-    const uint16_t* qrow = static_cast<const uint16_t*>(a.qw) + (head_row0 + qs + 32 * wave + l32) * D + 8 * hf;
+    const int32_t u = min(qs + 32 * wave + l32, L - 1);
+    int32_t row, col;
+    token_position(u, a.text_len[seg], a.grid_hw[2 * seg + 1], row, col);
+    const uint16_t* qrow = static_cast<const uint16_t*>(a.q) + (int64_t(cb + u) * heads + h) * D + 8 * hf;
 #pragma unroll
-    for (int ks = 0; ks < KSTEPS; ++ks) qreg[ks] = *reinterpret_cast<const bf16x8*>(qrow + 16 * ks);
+    for (int ks = 0; ks < KSTEPS; ++ks) {
+      const Chunk<uint16_t> raw = *reinterpret_cast<const Chunk<uint16_t>*>(qrow + 16 * ks);
+      qreg[ks] = __builtin_bit_cast(bf16x8, rotate_chunk<uint16_t, D>(raw, 16 * ks + 8 * hf, row, col, a.cs));
+    }
   }
   // The tile copies share the in-order vector-memory counter with these
   // loads: finish Q first so later waits only cover tile copies.
@@ -369,10 +383,15 @@ __global__ void __launch_bounds__(ATTN_THREADS) attn_fwd_f32_kernel(AttnArgs a) 
   }
 }
 
-hipError_t launch_attn_fwd(const char* ws, const WsLayout& l, void* out, int32_t heads,
+hipError_t launch_attn_fwd(const char* ws, const WsLayout& l, const void* q, const int32_t* grid_hw,
+                           const int32_t* text_len, const float2* cs, void* out, int32_t heads,
                            int32_t head_dim, bool bf16, float scale, hipStream_t s) {
   AttnArgs a;
   a.ws = ws;
+  a.q = q;
+  a.grid_hw = grid_hw;
+  a.text_len = text_len;
+  a.cs = cs;
   a.off_len = l.off_len;
   a.off_cu = l.off_cu;
   a.off_pcu = l.off_pcu;

@@ -105,6 +105,78 @@ __device__ inline void offsets(int32_t n, int64_t tokens, MetaShared& sh) {
   __syncthreads();
 }
 
+// Inclusive prefix sum across the 64 lanes of a wave.
+__device__ inline int64_t wave_inclusive_scan(int64_t x) {
+  const int lane = threadIdx.x & 63;
+#pragma unroll
+  for (int off = 1; off < 64; off <<= 1) {
+    const int64_t y = __shfl_up(x, off);
+    if (lane >= off) x += y;
+  }
+  return x;
+}
+
+// The same derivation as meta_kernel for n <= 64, by the first wave alone:
+// lane i owns sample i. No LDS and no workgroup barriers.
+__device__ inline void meta_small(const int32_t* __restrict__ grid_hw, const int32_t* __restrict__ text_len,
+                                  const int32_t* __restrict__ cu_in, int32_t n, int64_t tokens,
+                                  WsHeader* hdr, int32_t* len, int32_t* cu, int32_t* pcu, int2* tiles) {
+  const int i = threadIdx.x;
+  const bool mine = i < n;
+  int32_t L = 0;
+  bool ok = true;
+  if (mine) {
+    const int32_t h = grid_hw[2 * i], w = grid_hw[2 * i + 1], tl = text_len[i];
+    ok = h >= 1 && w >= 1 && h <= ROPE_PMAX && w <= ROPE_PMAX && tl >= 0 && tl <= MAX_TEXT_LEN;
+    L = ok ? tl + h * w : 1;
+  }
+  const int64_t incl = wave_inclusive_scan(L);
+  const int64_t total = __shfl(incl, 63);
+  const int64_t excl = incl - L;
+  if (mine && int64_t(cu_in[i]) != excl) ok = false;
+  if (i == 0 && (int64_t(cu_in[n]) != total || total != tokens || total >= (int64_t(1) << 31))) ok = false;
+  if (__any(!ok)) {
+    if (i == 0) {
+      hdr->flag = FLAG_METADATA;
+      hdr->n_tiles = 0;
+      hdr->padded_total = 0;
+      hdr->n_seg = n;
+    }
+    return;
+  }
+  const int32_t padded = int32_t(round_up(L, KTILE));
+  const int64_t pincl = wave_inclusive_scan(padded);
+  // Longest-first rank, ties by index; tiles of sample i start after those of
+  // every sample ranked before it.
+  const int32_t ct = mine ? int32_t(ceil_div(L, QTILE)) : 0;
+  int32_t rank = 0, toff = 0;
+  for (int j = 0; j < n; ++j) {
+    const int32_t lj = __shfl(L, j);
+    const int32_t cj = __shfl(ct, j);
+    const bool before = (lj > L) || (lj == L && j < i);
+    rank += before;
+    toff += before ? cj : 0;
+  }
+  (void)rank;
+  // Shuffles run with the whole wave active, before any lane-dependent branch.
+  const int32_t total_tiles = int32_t(__shfl(wave_inclusive_scan(ct), 63));
+  const int32_t padded_total = int32_t(__shfl(pincl, 63));
+  if (mine) {
+    len[i] = L;
+    cu[i] = int32_t(excl);
+    pcu[i] = int32_t(pincl - padded);
+    for (int32_t x = 0; x < ct; ++x) tiles[toff + x] = make_int2(i, x * QTILE);
+  }
+  if (i == 0) {
+    cu[n] = int32_t(total);
+    pcu[n] = padded_total;
+    hdr->flag = FLAG_OK;
+    hdr->n_tiles = total_tiles;
+    hdr->padded_total = padded_total;
+    hdr->n_seg = n;
+  }
+}
+
 // Validates and derives the packing metadata of one call into the workspace.
 __global__ void __launch_bounds__(META_THREADS)
 meta_kernel(const int32_t* __restrict__ grid_hw, const int32_t* __restrict__ text_len,
@@ -118,6 +190,11 @@ meta_kernel(const int32_t* __restrict__ grid_hw, const int32_t* __restrict__ tex
   int32_t* pcu = reinterpret_cast<int32_t*>(ws + off_pcu);
   int2* tiles = reinterpret_cast<int2*>(ws + off_tiles);
   const int t = threadIdx.x;
+  if (n <= 64) {
+    // Up to 64 samples: one wave, one lane per sample, wave-level scans.
+    if (t < 64) meta_small(grid_hw, text_len, cu_in, n, tokens, hdr, len, cu, pcu, tiles);
+    return;
+  }
 
   load_lengths(grid_hw, text_len, n, sh);
   offsets(n, tokens, sh);

@@ -12,9 +12,10 @@
 // device does the rotation in fp32.
 //
 // rope_pack_kernel is the prologue of the attention path. One workgroup per
-// (KTILE-row tile of the padded layout, head). It rotates q and k of every
-// token of the tile and writes them into the workspace:
-//   Q~  [head][row][d]           row-major
+// (KTILE-row tile of the padded layout, head). It rotates the keys (and, for
+// f32, the queries) of every token of the tile and writes into the workspace:
+//   Q~  f32 only: [head][row][d] row-major (the bf16 attention kernel rotates
+//       its query rows itself while loading them)
 //   K~  bf16: each KTILE x d tile stored chunk-major: 16-byte chunk c (channels
 //       8c..8c+7) of tile row n at chunk index c * KTILE + n. f32: row-major.
 //   V~  bf16: V transposed per tile, [d][KTILE] inside each tile, keys inside
@@ -29,43 +30,9 @@
 // Rows that belong to no token (padding up to KTILE, and the slack after the
 // last sample) are written as zeros.
 #include "mf_common.h"
+#include "rope_math.h"
 
 namespace mf {
-
-template <typename T> struct Elem;
-template <> struct Elem<uint16_t> {
-  static constexpr int PER_CHUNK = 8;
-  __device__ static float load(uint16_t x) { return bf16_to_f32(x); }
-  __device__ static uint16_t store(float x) { return f32_to_bf16_rne(x); }
-};
-template <> struct Elem<float> {
-  static constexpr int PER_CHUNK = 4;
-  __device__ static float load(float x) { return x; }
-  __device__ static float store(float x) { return x; }
-};
-
-template <typename T> struct alignas(16) Chunk { T v[16 / sizeof(T)]; };
-
-// Rotates one 16-byte chunk (channels d0 .. d0+E-1, E even) of a row at (row, col).
-template <typename T, int D>
-__device__ inline Chunk<T> rotate_chunk(const Chunk<T>& in, int d0, int32_t row, int32_t col,
-                                        const float2* __restrict__ cs) {
-  constexpr int E = Elem<T>::PER_CHUNK;
-  Chunk<T> out;
-#pragma unroll
-  for (int pp = 0; pp < E / 2; ++pp) {
-    const int d = d0 + 2 * pp;
-    const bool first_half = d < D / 2;
-    const int j = first_half ? d / 2 : (d - D / 2) / 2;
-    const int32_t p = first_half ? row : col;
-    const float2 r = cs[p * (D / 4) + j];
-    const float x0 = Elem<T>::load(in.v[2 * pp]);
-    const float x1 = Elem<T>::load(in.v[2 * pp + 1]);
-    out.v[2 * pp] = Elem<T>::store(x0 * r.x - x1 * r.y);
-    out.v[2 * pp + 1] = Elem<T>::store(x0 * r.y + x1 * r.x);
-  }
-  return out;
-}
 
 template <typename T, int D>
 __global__ void __launch_bounds__(256)
@@ -99,30 +66,25 @@ rope_pack_kernel(const T* __restrict__ q, const T* __restrict__ k, const T* __re
   const int64_t tile_off = (int64_t(h) * rows + r0) * D;
   const int64_t src_stride = int64_t(heads) * D;  // elements between consecutive tokens
 
-  // Q and K: rotate, then row-major Q~ and (bf16) chunk-major K~. Chunk f of
-  // the loop covers tile row rr = (f / 4) % 64 and chunk cc = f % 4 + 4 * (f / 256):
-  // four lanes read 64 contiguous bytes of a row, sixteen lanes with the same
-  // cc write 256 contiguous bytes of K~.
-  for (int f = threadIdx.x; f < CPT; f += 256) {
-    const int rr = sizeof(T) == 2 ? (f >> 2) & (KTILE - 1) : f / CPR;
-    const int cc = sizeof(T) == 2 ? (f & 3) + 4 * (f >> 8) : f % CPR;
-    const int32_t u = u0 + rr;
-    Chunk<T> qo, ko;
-    if (u < L) {
-      int32_t row, col;
-      token_position(u, tl, w, row, col);
-      const int64_t src = (tok0 + rr) * src_stride + int64_t(h) * D + cc * E;
-      const Chunk<T> qi = *reinterpret_cast<const Chunk<T>*>(q + src);
-      const Chunk<T> ki = *reinterpret_cast<const Chunk<T>*>(k + src);
-      qo = rotate_chunk<T, D>(qi, cc * E, row, col, cs);
-      ko = rotate_chunk<T, D>(ki, cc * E, row, col, cs);
-    } else {
+  if constexpr (sizeof(T) == 4) {
+    // f32: Q~ and K~ rotated, row-major.
+    for (int f = threadIdx.x; f < CPT; f += 256) {
+      const int rr = f / CPR, cc = f % CPR;
+      const int32_t u = u0 + rr;
+      Chunk<T> qo, ko;
+      if (u < L) {
+        int32_t row, col;
+        token_position(u, tl, w, row, col);
+        const int64_t src = (tok0 + rr) * src_stride + int64_t(h) * D + cc * E;
+        qo = rotate_chunk<T, D>(*reinterpret_cast<const Chunk<T>*>(q + src), cc * E, row, col, cs);
+        ko = rotate_chunk<T, D>(*reinterpret_cast<const Chunk<T>*>(k + src), cc * E, row, col, cs);
+      } else {
 #pragma unroll
-      for (int e = 0; e < E; ++e) qo.v[e] = ko.v[e] = T(0);
+        for (int e = 0; e < E; ++e) qo.v[e] = ko.v[e] = T(0);
+      }
+      *reinterpret_cast<Chunk<T>*>(qw + tile_off + int64_t(f) * E) = qo;
+      *reinterpret_cast<Chunk<T>*>(kw + tile_off + int64_t(f) * E) = ko;
     }
-    *reinterpret_cast<Chunk<T>*>(qw + tile_off + int64_t(rr * CPR + cc) * E) = qo;
-    const int kf = sizeof(T) == 2 ? cc * KTILE + rr : rr * CPR + cc;
-    *reinterpret_cast<Chunk<T>*>(kw + tile_off + int64_t(kf) * E) = ko;
   }
 
   if constexpr (sizeof(T) == 4) {
@@ -139,22 +101,39 @@ rope_pack_kernel(const T* __restrict__ q, const T* __restrict__ k, const T* __re
       *reinterpret_cast<Chunk<T>*>(vw + tile_off + int64_t(f) * E) = vo;
     }
   } else {
-    // bf16: V tile through LDS, written transposed ([d][KTILE]) in MFMA key order.
-    constexpr int VS = D + 2;  // padded LDS row (elements): consecutive keys fall in different banks
+    // bf16 (queries are rotated by the attention kernel itself): the K tile is
+    // rotated and staged through LDS, then written chunk-major; the V tile goes
+    // through LDS and is written transposed ([d][KTILE]) in MFMA key order.
+    // Loads read whole rows (16 lanes x 16 B), stores write consecutive chunks.
+    constexpr int KS = KTILE + 1;  // LDS stride (chunks) between channel chunks: no bank conflicts
+    constexpr int VS = D + 2;      // padded LDS row (elements): consecutive keys fall in different banks
+    __shared__ Chunk<T> ks[CPR * KS];
     __shared__ uint16_t vs[KTILE * VS];
     for (int f = threadIdx.x; f < CPT; f += 256) {
       const int rr = f / CPR, cc = f % CPR;
-      Chunk<T> vi;
-      if (u0 + rr < L) {
-        vi = *reinterpret_cast<const Chunk<T>*>(v + (tok0 + rr) * src_stride + int64_t(h) * D + cc * E);
+      const int32_t u = u0 + rr;
+      Chunk<T> ko, vi;
+      if (u < L) {
+        int32_t row, col;
+        token_position(u, tl, w, row, col);
+        const int64_t src = (tok0 + rr) * src_stride + int64_t(h) * D + cc * E;
+        ko = rotate_chunk<T, D>(*reinterpret_cast<const Chunk<T>*>(k + src), cc * E, row, col, cs);
+        vi = *reinterpret_cast<const Chunk<T>*>(v + src);
       } else {
 #pragma unroll
-        for (int e = 0; e < E; ++e) vi.v[e] = T(0);
+        for (int e = 0; e < E; ++e) ko.v[e] = vi.v[e] = T(0);
       }
+      ks[cc * KS + rr] = ko;
       uint32_t* dst = reinterpret_cast<uint32_t*>(vs + rr * VS + cc * E);
       const uint32_t* sv = reinterpret_cast<const uint32_t*>(vi.v);
 #pragma unroll
       for (int e = 0; e < E / 2; ++e) dst[e] = sv[e];
+    }
+    __syncthreads();
+    // K~ chunk f2 = cc * KTILE + rr (chunk-major).
+    for (int f2 = threadIdx.x; f2 < CPT; f2 += 256) {
+      const int cc = f2 / KTILE, rr = f2 % KTILE;
+      *reinterpret_cast<Chunk<T>*>(kw + tile_off + int64_t(f2) * E) = ks[cc * KS + rr];
     }
     __syncthreads();
     // Output chunk f2 = g * D + c: channel c, keys of chunk g of the 64-key row.

@@ -1,0 +1,47 @@
+// 2D RoPE arithmetic shared by the prologue, the standalone RoPE kernel and
+// the attention kernel (which rotates its query rows as it loads them).
+// Layout: channels [0, d/2) turn by the row, [d/2, d) by the column; adjacent
+// pairs (2j, 2j+1) inside each half at frequency theta^(-2j/(d/2)), read from a
+// float2 cos/sin table [ROPE_PMAX][d/4]; (x0, x1) -> (x0 c - x1 s, x0 s + x1 c).
+#pragma once
+
+#include "mf_common.h"
+
+namespace mf {
+
+template <typename T> struct Elem;
+template <> struct Elem<uint16_t> {
+  static constexpr int PER_CHUNK = 8;
+  __device__ static float load(uint16_t x) { return bf16_to_f32(x); }
+  __device__ static uint16_t store(float x) { return f32_to_bf16_rne(x); }
+};
+template <> struct Elem<float> {
+  static constexpr int PER_CHUNK = 4;
+  __device__ static float load(float x) { return x; }
+  __device__ static float store(float x) { return x; }
+};
+
+template <typename T> struct alignas(16) Chunk { T v[16 / sizeof(T)]; };
+
+// Rotates one 16-byte chunk (channels d0 .. d0+E-1, E even) of a row at (row, col).
+template <typename T, int D>
+__device__ inline Chunk<T> rotate_chunk(const Chunk<T>& in, int d0, int32_t row, int32_t col,
+                                        const float2* __restrict__ cs) {
+  constexpr int E = Elem<T>::PER_CHUNK;
+  Chunk<T> out;
+#pragma unroll
+  for (int pp = 0; pp < E / 2; ++pp) {
+    const int d = d0 + 2 * pp;
+    const bool first_half = d < D / 2;
+    const int j = first_half ? d / 2 : (d - D / 2) / 2;
+    const int32_t p = first_half ? row : col;
+    const float2 r = cs[p * (D / 4) + j];
+    const float x0 = Elem<T>::load(in.v[2 * pp]);
+    const float x1 = Elem<T>::load(in.v[2 * pp + 1]);
+    out.v[2 * pp] = Elem<T>::store(x0 * r.x - x1 * r.y);
+    out.v[2 * pp + 1] = Elem<T>::store(x0 * r.y + x1 * r.x);
+  }
+  return out;
+}
+
+}  // namespace mf
