@@ -103,6 +103,25 @@ def test_packed_equals_each_sample_alone_bitwise():
         assert torch.equal(alone, packed[a:b]), f"sample {i} differs"
 
 
+def test_no_leakage_between_samples_bitwise():
+    """Scale every other sample's keys and values by 256: any attention weight
+    that crossed a sample boundary would move this sample's output. Tiles are
+    sample-relative, so the sample's output bits must not change at all."""
+    w = workloads.make_workload("mixed", seed=23)
+    base = run_attention(w)
+    cu = np.concatenate([[0], np.cumsum(w.text_len + w.grid_hw[:, 0] * w.grid_hw[:, 1])])
+    i = 2
+    a, b = int(cu[i]), int(cu[i + 1])
+    k2, v2 = w.k.copy(), w.v.copy()
+    big = np.float32(256.0)  # exact in bf16
+    for arr in (k2, v2):
+        arr[:a] *= big
+        arr[b:] *= big
+    wl = workloads.Workload("loud", w.grid_hw, w.text_len, w.heads, w.head_dim, w.dtype, w.q, k2, v2)
+    loud = run_attention(wl)
+    assert torch.equal(loud[a:b], base[a:b])
+
+
 def test_sample_permutation_permutes_output_bitwise():
     w = workloads.make_workload("mixed", seed=21)
     base = run_attention(w)
