@@ -144,6 +144,41 @@ int mf_rope_2d(const void* x_in, void* x_out, const int32_t* pos, int64_t total_
                int32_t heads, int32_t head_dim, int32_t dtype, float theta, hipStream_t stream);
 
 /*
+ * Guided rectified-flow Euler step over a packed classifier-free-guidance batch.
+ * Sources: Mage-Flow tech report, NR-MMDiT section (the conditional and the
+ * unconditional branch are packed together and evaluated in one forward pass);
+ * mageflow.net architecture page, section 3 (straight rectified-flow paths
+ * sampled with Euler steps). The guided velocity is v_u + s * (v_c - v_u) (the
+ * pages do not print it; this is the standard form), and the step is
+ *   z <- z + dt * (v_u + guidance * (v_c - v_u)).
+ *   z           device float [image_tokens][channels]: the images' latent tokens
+ *               back to back in image order, each image's grid row-major;
+ *               updated in place
+ *   v           device [total_tokens][channels], dtype: the velocity predicted
+ *               for every token of the packed batch
+ *   cu_seqlens, grid_hw, text_len  device int32, the packed batch's metadata
+ *               (same conventions as mf_attn_packed, n_seg samples)
+ *   cond_seg    device int32 [n_img]: sample holding image b with its prompt
+ *   uncond_seg  device int32 [n_img]: sample holding image b without it, or -1
+ *               for no guidance (then the step uses v_c alone)
+ * Image b owns h*w tokens of z, (h, w) = grid_hw[cond_seg[b]]. channels is a
+ * positive multiple of 8 (at most 4096), image_tokens * channels / 8 < 2^31, z
+ * and v are 16-byte aligned, n_img <= MF_MAX_SEGMENTS and grid sides are at
+ * most MF_MAX_GRID_SIDE. One kernel launch; it first checks on the device that
+ * every index is in range, that both samples of an image have the same grid,
+ * that cu_seqlens agrees with grid_hw/text_len for the samples used and ends
+ * inside total_tokens, and that the images' tokens add up to image_tokens. If
+ * any check fails nothing is written and the device flag read by
+ * mf_get_device_error is set. Arithmetic in fp32. Uses no library workspace,
+ * so calls on different streams that touch disjoint z buffers may overlap.
+ */
+int mf_rf_cfg_euler_step(float* z, const void* v, const int32_t* cu_seqlens, const int32_t* grid_hw,
+                         const int32_t* text_len, int32_t n_seg, int64_t total_tokens,
+                         const int32_t* cond_seg, const int32_t* uncond_seg, int32_t n_img,
+                         int64_t image_tokens, int32_t channels, int32_t dtype, float guidance,
+                         float dt, hipStream_t stream);
+
+/*
  * Synchronizes `stream`, then returns MF_ERR_METADATA if the last enqueued
  * metadata check on this device's library workspace failed, else MF_OK.
  */

@@ -18,6 +18,8 @@ from __future__ import annotations
 
 import numpy as np
 
+from .packing import cu_seqlens
+
 
 def interpolate(z0, z1, t):
     """z_t = t * z_1 + (1 - t) * z_0."""
@@ -73,3 +75,29 @@ def cfg_combine(v_uncond, v_cond, guidance: float):
     vu = np.asarray(v_uncond, dtype=np.float64)
     vc = np.asarray(v_cond, dtype=np.float64)
     return vu + guidance * (vc - vu)
+
+
+def packed_cfg_euler_step(z, v, grid_hw, text_len, cond_seg, uncond_seg, guidance: float, dt: float):
+    """One guided Euler step for every image of a packed CFG batch.
+
+    The batch packs samples [prompt; h*w image tokens] back to back (tech report,
+    NR-MMDiT section: conditional and unconditional branches in one pass).
+    Image b's conditional velocities are the image rows of sample cond_seg[b],
+    its unconditional ones those of uncond_seg[b] (or the conditional ones when
+    that is -1). z holds the images' tokens back to back in image order; each
+    image moves by dt * cfg_combine(v_u, v_c, guidance).
+    """
+    grid_hw = np.asarray(grid_hw).reshape(-1, 2)
+    text_len = np.asarray(text_len)
+    v = np.asarray(v, dtype=np.float64)
+    cu = cu_seqlens(grid_hw, text_len)
+    out = np.array(z, dtype=np.float64)
+    start = 0
+    for b in range(len(cond_seg)):
+        cs, us = int(cond_seg[b]), int(uncond_seg[b])
+        n = int(grid_hw[cs, 0]) * int(grid_hw[cs, 1])
+        vc = v[cu[cs] + text_len[cs]: cu[cs + 1]]
+        vu = vc if us < 0 else v[cu[us] + text_len[us]: cu[us + 1]]
+        out[start:start + n] += dt * cfg_combine(vu, vc, guidance)
+        start += n
+    return out

@@ -79,3 +79,29 @@ def test_binding_rejects_host_tensors():
     x = torch.zeros((4, 1, 64))
     with pytest.raises(ValueError):
         binding.rope_2d(x, torch.zeros((4, 2), dtype=torch.int32))
+
+
+def test_cfg_step_rejects_bad_arguments_on_host():
+    lib = binding.lib()
+    P = ctypes.c_void_p
+
+    def call(z=0x10000, v=0x200000, n_seg=2, T=40, n_img=1, img=16, C=8, dtype=0, s=5.0, dt=0.25, cs=0x300000):
+        return lib.mf_rf_cfg_euler_step(P(z), P(v), P(0x400000), P(0x500000), P(0x600000), n_seg, T, P(cs),
+                                        P(0x700000), n_img, img, C, dtype, s, dt, None)
+
+    bad = binding.MF_ERR_INVALID_ARG
+    assert call(z=0) == bad
+    assert call(cs=0) == bad
+    assert call(n_seg=0) == bad
+    assert call(n_img=0) == bad
+    assert call(n_img=5000) == bad
+    assert call(T=0) == bad
+    assert call(img=0) == bad
+    assert call(C=12) == binding.MF_ERR_UNSUPPORTED
+    assert call(C=0) == binding.MF_ERR_UNSUPPORTED
+    assert call(dtype=5) == binding.MF_ERR_UNSUPPORTED
+    assert call(s=float("nan")) == bad
+    assert call(dt=float("inf")) == bad
+    assert call(z=0x10004) == bad  # misaligned
+    assert call(v=0x10000 + 64) == bad  # z overlaps v
+    assert binding.last_error() != ""

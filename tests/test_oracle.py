@@ -413,3 +413,54 @@ def test_rf_loss_and_cfg():
     np.testing.assert_allclose(rectified_flow.cfg_combine(vu, vc, 0.0), vu)
     np.testing.assert_allclose(rectified_flow.cfg_combine(vu, vc, 1.0), vc, atol=1e-15)
     np.testing.assert_allclose(rectified_flow.cfg_combine(vu, vc, 5.0), 5 * vc - 4 * vu, atol=1e-13)
+
+
+# ---------------------------------------------------------------- packed CFG step
+
+from cfg_common import guided_field  # noqa: E402
+
+
+@pytest.mark.parametrize("layout", ["interleaved", "blocks", "shuffled"])
+@pytest.mark.parametrize("guidance", [5.0, 1.0, -2.0])
+def test_packed_cfg_euler_lands_on_data(layout, guidance):
+    """Four guided Euler steps along the constructed field follow the straight
+    path t z1 + (1 - t) z0 and land on z1 (closed form of the straight path)."""
+    batch = workloads.make_cfg_batch([(3, 5), (1, 1), (4, 2), (2, 7)], [4, 0, 9, 2], [0, 3, 1, 0], layout,
+                                     channels=8, dtype="f32", seed=11, guided=[1, 1, 0, 1])
+    rng = np.random.default_rng(12)
+    z0 = batch.z.astype(np.float64)
+    z1 = rng.standard_normal(z0.shape)
+    z = z0
+    grid = rectified_flow.uniform_grid(4)
+    for k in range(4):
+        t, dt = grid[k], grid[k + 1] - grid[k]
+        v = guided_field(batch, z, z1, t, guidance, rng.standard_normal(batch.v.shape))
+        z = rectified_flow.packed_cfg_euler_step(z, v, batch.grid_hw, batch.text_len, batch.cond_seg,
+                                                 batch.uncond_seg, guidance, dt)
+        np.testing.assert_allclose(z, grid[k + 1] * z1 + (1 - grid[k + 1]) * z0, atol=1e-12)
+    np.testing.assert_allclose(z, z1, atol=1e-12)
+
+
+def test_packed_cfg_euler_special_cases():
+    batch = workloads.make_cfg_batch([(3, 4), (2, 2)], [5, 1], [2, 0], "shuffled", channels=8, dtype="f32",
+                                     seed=13)
+    args = (batch.grid_hw, batch.text_len, batch.cond_seg, batch.uncond_seg)
+    step = rectified_flow.packed_cfg_euler_step
+    z, v = batch.z, batch.v
+    # dt = 0 leaves z alone; text rows never matter
+    np.testing.assert_array_equal(step(z, v, *args, 5.0, 0.0), z)
+    v2 = v.copy()
+    run = 0
+    for (h, w), t in zip(batch.grid_hw.tolist(), batch.text_len.tolist()):
+        v2[run:run + t] = 1e6
+        run += t + h * w
+    np.testing.assert_array_equal(step(z, v2, *args, 5.0, 0.5), step(z, v, *args, 5.0, 0.5))
+    # guidance 0 / no unconditional sample: the unguided step of the matching branch
+    nog = np.full_like(batch.uncond_seg, -1)
+    a = step(z, v, batch.grid_hw, batch.text_len, batch.uncond_seg, nog, 7.0, 0.5)
+    np.testing.assert_allclose(step(z, v, *args, 0.0, 0.5), a, atol=1e-14)
+    c = step(z, v, batch.grid_hw, batch.text_len, batch.cond_seg, nog, 7.0, 0.5)
+    np.testing.assert_allclose(step(z, v, *args, 1.0, 0.5), c, atol=1e-14)
+    # the step is affine in dt
+    d1, d2 = step(z, v, *args, 3.0, 0.25) - z, step(z, v, *args, 3.0, 0.75) - z
+    np.testing.assert_allclose(3 * d1, d2, atol=1e-13)

@@ -48,6 +48,7 @@ def _declare(lib):
         "mf_attn_packed_ws": ([P, P, P, P, P, P, P, I32, I64, I32, I32, I32, P, SZ, P], ctypes.c_int),
         "mf_build_metadata": ([I32, P, P, P, P, P, I64, P], ctypes.c_int),
         "mf_rope_2d": ([P, P, P, I64, I32, I32, I32, F, P], ctypes.c_int),
+        "mf_rf_cfg_euler_step": ([P, P, P, P, P, I32, I64, P, P, I32, I64, I32, I32, F, F, P], ctypes.c_int),
         "mf_get_device_error": ([P], ctypes.c_int),
         "mf_get_workspace_error": ([P, P], ctypes.c_int),
     }
@@ -191,6 +192,36 @@ def rope_2d(x, pos, theta: float = ROPE_THETA, out=None, stream=None):
     _check(lib().mf_rope_2d(_ptr(x), _ptr(out), _ptr(pos), T, H, D, _DTYPES[x.dtype], float(theta),
                             _stream(stream)))
     return out
+
+
+def rf_cfg_euler_step(z, v, cu_seqlens, grid_hw, text_len, cond_seg, uncond_seg, guidance: float, dt: float,
+                      stream=None):
+    """In-place guided Euler step z += dt * (v_u + guidance * (v_c - v_u)) (mf_rf_cfg_euler_step).
+
+    z [image_tokens, C] float32; v [total_tokens, C] bfloat16/float32; cond_seg,
+    uncond_seg [n_img] int32 sample indices (uncond -1: no guidance). Returns z.
+    """
+    _need(z, "z", torch.float32, 2)
+    _need(v, "v", ndim=2)
+    if v.dtype not in _DTYPES:
+        raise ValueError("v must be bfloat16 or float32")
+    if v.shape[1] != z.shape[1]:
+        raise ValueError("z and v must have the same channel count")
+    _need(cu_seqlens, "cu_seqlens", torch.int32, 1)
+    _need(grid_hw, "grid_hw", torch.int32, 2)
+    _need(text_len, "text_len", torch.int32, 1)
+    _need(cond_seg, "cond_seg", torch.int32, 1)
+    _need(uncond_seg, "uncond_seg", torch.int32, 1)
+    n = grid_hw.shape[0]
+    if grid_hw.shape[1] != 2 or text_len.shape[0] != n or cu_seqlens.shape[0] != n + 1:
+        raise ValueError("metadata shapes must be grid_hw [n,2], text_len [n], cu_seqlens [n+1]")
+    if uncond_seg.shape != cond_seg.shape:
+        raise ValueError("cond_seg and uncond_seg must have the same length")
+    _check(lib().mf_rf_cfg_euler_step(_ptr(z), _ptr(v), _ptr(cu_seqlens), _ptr(grid_hw), _ptr(text_len), n,
+                                      v.shape[0], _ptr(cond_seg), _ptr(uncond_seg), cond_seg.shape[0],
+                                      z.shape[0], z.shape[1], _DTYPES[v.dtype], float(guidance), float(dt),
+                                      _stream(stream)))
+    return z
 
 
 def get_device_error(stream=None) -> int:

@@ -5,6 +5,7 @@
 //   attn_fwd_*       per-sample flash-style attention
 // Nothing here synchronizes except mf_get_device_error / mf_get_workspace_error
 // and the first-use allocations of the library-owned state.
+#include <algorithm>
 #include <cmath>
 #include <cstdarg>
 #include <cstdio>
@@ -35,6 +36,11 @@ hipError_t launch_rope(const void* x, void* y, const int32_t* pos, int64_t token
 hipError_t launch_attn_fwd(const char* ws, const WsLayout& l, const void* q, const int32_t* grid_hw,
                            const int32_t* text_len, const float2* cs, void* out, int32_t heads,
                            int32_t head_dim, bool bf16, float scale, hipStream_t s);
+hipError_t launch_cfg_euler(float* z, const void* v, const int32_t* cu, const int32_t* grid_hw,
+                            const int32_t* text_len, int32_t n_seg, int64_t total_tokens,
+                            const int32_t* cond_seg, const int32_t* uncond_seg, int32_t n_img,
+                            int64_t image_tokens, int32_t channels, bool bf16, float guidance, float dt,
+                            int32_t* status, hipStream_t s);
 }  // namespace mf
 
 namespace {
@@ -57,7 +63,7 @@ int hip_fail(hipError_t e, const char* what) {
 }
 
 struct DeviceState {
-  int32_t* status = nullptr;  // sticky FLAG_* of the standalone metadata / RoPE calls
+  int32_t* status = nullptr;  // sticky FLAG_* of the standalone metadata / RoPE / sampler calls
   char* ws = nullptr;         // library workspace of mf_attn_packed
   size_t ws_bytes = 0;
   std::map<std::pair<int, uint32_t>, float2*> tables;  // (head_dim, theta bits) -> cos/sin
@@ -326,6 +332,51 @@ int mf_rope_2d(const void* x_in, void* x_out, const int32_t* pos, int64_t total_
   const hipError_t e = mf::launch_rope(x_in, x_out, pos, total_tokens, heads, head_dim,
                                        dtype == MF_BF16, cs, status, stream);
   return e == hipSuccess ? MF_OK : hip_fail(e, "rope_kernel launch");
+}
+
+int mf_rf_cfg_euler_step(float* z, const void* v, const int32_t* cu_seqlens, const int32_t* grid_hw,
+                         const int32_t* text_len, int32_t n_seg, int64_t total_tokens,
+                         const int32_t* cond_seg, const int32_t* uncond_seg, int32_t n_img,
+                         int64_t image_tokens, int32_t channels, int32_t dtype, float guidance,
+                         float dt, hipStream_t stream) {
+  if (!z || !v || !cu_seqlens || !grid_hw || !text_len || !cond_seg || !uncond_seg)
+    return fail(MF_ERR_INVALID_ARG, "null pointer argument");
+  if (n_seg < 1 || n_seg > MF_MAX_SEGMENTS)
+    return fail(MF_ERR_INVALID_ARG, "n_seg=%d outside [1, %d]", n_seg, MF_MAX_SEGMENTS);
+  if (n_img < 1 || n_img > MF_MAX_SEGMENTS)
+    return fail(MF_ERR_INVALID_ARG, "n_img=%d outside [1, %d]", n_img, MF_MAX_SEGMENTS);
+  if (total_tokens < 1 || total_tokens >= (int64_t(1) << 31))
+    return fail(MF_ERR_INVALID_ARG, "total_tokens=%lld outside [1, 2^31)", (long long)total_tokens);
+  if (image_tokens < 1 || image_tokens >= (int64_t(1) << 31))
+    return fail(MF_ERR_INVALID_ARG, "image_tokens=%lld outside [1, 2^31)", (long long)image_tokens);
+  if (channels < 8 || channels > 4096 || channels % 8)
+    return fail(MF_ERR_UNSUPPORTED, "channels=%d (need a multiple of 8 in [8, 4096])", channels);
+  const int64_t chunks = image_tokens * (channels / 8);
+  if (chunks >= (int64_t(1) << 31)) return fail(MF_ERR_INVALID_ARG, "image_tokens * channels / 8 >= 2^31");
+  const int eb = elem_bytes(dtype);
+  if (!eb) return fail(MF_ERR_UNSUPPORTED, "dtype=%d", dtype);
+  if (!std::isfinite(guidance) || !std::isfinite(dt))
+    return fail(MF_ERR_INVALID_ARG, "guidance and dt must be finite");
+  if ((reinterpret_cast<uintptr_t>(z) | reinterpret_cast<uintptr_t>(v)) & 15)
+    return fail(MF_ERR_INVALID_ARG, "z and v must be 16-byte aligned");
+  const size_t zb = size_t(image_tokens) * channels * 4, vb = size_t(total_tokens) * channels * eb;
+  if (overlaps(z, zb, v, vb) || overlaps(z, zb, cu_seqlens, size_t(n_seg + 1) * 4) ||
+      overlaps(z, zb, grid_hw, size_t(n_seg) * 8) || overlaps(z, zb, text_len, size_t(n_seg) * 4) ||
+      overlaps(z, zb, cond_seg, size_t(n_img) * 4) || overlaps(z, zb, uncond_seg, size_t(n_img) * 4))
+    return fail(MF_ERR_INVALID_ARG, "z overlaps another argument");
+  int dev, rc;
+  if ((rc = current_device(&dev))) return rc;
+  int32_t* status;
+  {
+    std::lock_guard<std::mutex> lock(g_mu);
+    DeviceState& st = g_dev[dev];
+    if ((rc = ensure_status(st))) return rc;
+    status = st.status;
+  }
+  const hipError_t e = mf::launch_cfg_euler(z, v, cu_seqlens, grid_hw, text_len, n_seg, total_tokens, cond_seg,
+                                            uncond_seg, n_img, image_tokens, channels, dtype == MF_BF16,
+                                            guidance, dt, status, stream);
+  return e == hipSuccess ? MF_OK : hip_fail(e, "cfg_euler_kernel launch");
 }
 
 int mf_get_device_error(hipStream_t stream) {

@@ -30,6 +30,10 @@ __all__ = [
     "make_workload",
     "make_segments",
     "make_custom",
+    "CfgBatch",
+    "CFG_CONFIGS",
+    "make_cfg_batch",
+    "make_cfg_config",
     "f32_to_bf16_bits",
     "bf16_bits_to_f32",
 ]
@@ -178,3 +182,106 @@ def make_custom(grid_hw, text_len, heads, head_dim, dtype="bf16", seed=0, scale=
     n_tokens = int(text_len.astype(np.int64).sum() + (grid_hw[:, 0].astype(np.int64) * grid_hw[:, 1]).sum())
     q, k, v = _draw_qkv(rng, n_tokens, heads, head_dim, dtype, scale)
     return Workload(name, grid_hw, text_len, heads, head_dim, dtype, q, k, v, seed)
+
+
+@dataclass
+class CfgBatch:
+    """A packed classifier-free-guidance batch for one sampler step.
+
+    Every image owns a conditional sample (its prompt, then its latent grid)
+    and optionally an unconditional sample (unconditional prompt, same grid).
+    ``z`` holds the images' latent tokens back to back (image order, each grid
+    row-major); ``v`` holds a velocity for every token of the packed batch.
+    """
+
+    name: str
+    grid_hw: np.ndarray  # int32 [n_seg, 2]
+    text_len: np.ndarray  # int32 [n_seg]
+    cond_seg: np.ndarray  # int32 [n_img]
+    uncond_seg: np.ndarray  # int32 [n_img], -1: no unconditional sample
+    channels: int
+    dtype: str  # dtype of v: "bf16" or "f32"; z is always float32
+    z: np.ndarray = field(repr=False)  # float32 [image_tokens, channels]
+    v: np.ndarray = field(repr=False)  # float32 [tokens, channels], exactly representable in dtype
+    seed: int = 0
+
+    @property
+    def n_seg(self) -> int:
+        return int(self.grid_hw.shape[0])
+
+    @property
+    def n_img(self) -> int:
+        return int(self.cond_seg.shape[0])
+
+    @property
+    def tokens(self) -> int:
+        return int(self.v.shape[0])
+
+    @property
+    def image_tokens(self) -> int:
+        return int(self.z.shape[0])
+
+
+# Packed CFG batches: 1024x1024 images (64x64 latent grids, 128 latent channels
+# per token), prompts uniform in [77, 256] tokens, unconditional prompt empty.
+CFG_CONFIGS = {
+    "cfg1024": dict(grids=[(64, 64)] * 8, uncond_text=0, channels=128, dtype="bf16", seed=6),
+    "cfg_mixed": dict(grids=[(32, 128), (128, 32), (48, 84), (64, 64), (32, 32)], uncond_text=0, channels=128,
+                      dtype="bf16", seed=7),
+}
+
+
+def make_cfg_batch(grids, cond_text=None, uncond_text=0, layout="interleaved", channels=128, dtype="bf16",
+                   seed=0, guided=None, name="cfg", rng=None) -> CfgBatch:
+    """Pack a CFG batch.
+
+    grids: (h, w) per image. cond_text: prompt length per image, drawn uniformly
+    in [77, 256] when None. uncond_text: prompt length of the unconditional
+    samples (an int or one per image). guided: bool per image (default all);
+    an unguided image has no unconditional sample. layout: "interleaved"
+    (c0 u0 c1 u1 ...), "blocks" (all conditional samples, then all
+    unconditional ones) or "shuffled" (a seeded permutation of the samples).
+    Draw order: prompt lengths, permutation, then z ~ N(0, 1) and v ~ N(0, 1)
+    as float32 (v rounded to bf16 for bf16 batches).
+    """
+    rng = np.random.default_rng(seed) if rng is None else rng
+    grids = [tuple(int(x) for x in g) for g in grids]
+    n_img = len(grids)
+    if cond_text is None:
+        cond_text = rng.integers(77, 257, size=n_img).tolist()
+    if np.isscalar(uncond_text):
+        uncond_text = [int(uncond_text)] * n_img
+    guided = [True] * n_img if guided is None else [bool(g) for g in guided]
+    samples = []  # (image, is_cond)
+    if layout == "blocks":
+        samples = [(b, True) for b in range(n_img)] + [(b, False) for b in range(n_img) if guided[b]]
+    else:
+        for b in range(n_img):
+            samples.append((b, True))
+            if guided[b]:
+                samples.append((b, False))
+        if layout == "shuffled":
+            samples = [samples[i] for i in rng.permutation(len(samples))]
+        elif layout != "interleaved":
+            raise ValueError(f"unknown layout {layout}")
+    grid_hw = np.array([grids[b] for b, _ in samples], dtype=np.int32).reshape(-1, 2)
+    text_len = np.array([cond_text[b] if c else uncond_text[b] for b, c in samples], dtype=np.int32)
+    cond_seg = np.full(n_img, -1, dtype=np.int32)
+    uncond_seg = np.full(n_img, -1, dtype=np.int32)
+    for i, (b, c) in enumerate(samples):
+        (cond_seg if c else uncond_seg)[b] = i
+    image_tokens = sum(h * w for h, w in grids)
+    tokens = int(text_len.astype(np.int64).sum() + (grid_hw[:, 0].astype(np.int64) * grid_hw[:, 1]).sum())
+    z = rng.standard_normal((image_tokens, channels), dtype=np.float32)
+    v = rng.standard_normal((tokens, channels), dtype=np.float32)
+    if dtype == "bf16":
+        v = bf16_bits_to_f32(f32_to_bf16_bits(v))
+    return CfgBatch(name, grid_hw, text_len, cond_seg, uncond_seg, channels, dtype, z, v, seed)
+
+
+def make_cfg_config(config: str, seed: int | None = None, layout="interleaved") -> CfgBatch:
+    """The seeded CFG batch of a named config."""
+    c = CFG_CONFIGS[config]
+    seed = c["seed"] if seed is None else seed
+    return make_cfg_batch(c["grids"], None, c["uncond_text"], layout, c["channels"], c["dtype"], seed,
+                          name=config)
