@@ -119,6 +119,60 @@ int mf_attn_packed_ws(const void* q, const void* k, const void* v, const int32_t
                       void* workspace, size_t workspace_bytes, hipStream_t stream);
 
 /*
+ * Forward for training: mf_attn_packed that also stores each query row's
+ * log-sum-exp of its scaled scores, the statistic the backward recomputes P
+ * from (no score matrix is kept).
+ *   lse  device float [heads][total_tokens]: ln sum_k exp(q~.k~ / sqrt(d)) over
+ *        the row's own sample; must not overlap the other arguments
+ * Same sources, checks and workspace as mf_attn_packed.
+ */
+int mf_attn_packed_lse(const void* q, const void* k, const void* v, const int32_t* cu_seqlens,
+                       const int32_t* grid_hw, const int32_t* text_len, void* out, float* lse,
+                       int32_t n_seg, int64_t total_tokens, int32_t heads, int32_t head_dim,
+                       int32_t dtype, hipStream_t stream);
+
+/*
+ * Packed backward: gradients of mf_attn_packed with respect to q, k and v.
+ * Sources: Mage-Flow tech report, NR-MMDiT section (training on packed
+ * native-resolution batches, attention restricted to each sample by its
+ * cumulative offsets); mageflow.net architecture page, section 2 (2D RoPE).
+ * With P the per-sample softmax, D = rowsum(d_out * out):
+ *   dv = P^T d_out, dX = P * (d_out v^T - D), dq = R^T (dX R(k)) / sqrt(d),
+ *   dk = R^T (dX^T R(q)) / sqrt(d).
+ *   q, k, v, out, d_out  device [total_tokens][heads][head_dim], MF_BF16
+ *               (out is the forward's output; d_out the upstream gradient)
+ *   lse         device float [heads][total_tokens] from mf_attn_packed_lse
+ *   cu_seqlens, grid_hw, text_len  as for mf_attn_packed
+ *   dq, dk, dv  device [total_tokens][heads][head_dim], MF_BF16, written in
+ *               full; must not overlap each other, the inputs or the metadata
+ * bf16 only (MF_F32 returns MF_ERR_UNSUPPORTED); head_dim 64 or 128. The
+ * metadata is checked on the device as for the forward: on a mismatch nothing
+ * is written and mf_get_device_error() reports MF_ERR_METADATA. Uses a second
+ * library-owned per-device workspace (mf_bwd_workspace_bytes), with the same
+ * stream-order rule as mf_attn_packed. Deterministic: no atomics.
+ */
+int mf_attn_packed_bwd(const void* q, const void* k, const void* v, const void* out, const void* d_out,
+                       const float* lse, const int32_t* cu_seqlens, const int32_t* grid_hw,
+                       const int32_t* text_len, void* dq, void* dk, void* dv, int32_t n_seg,
+                       int64_t total_tokens, int32_t heads, int32_t head_dim, int32_t dtype,
+                       hipStream_t stream);
+
+/*
+ * mf_attn_packed_bwd that records four caller-created hipEvent_t on `stream`:
+ * before the metadata kernel, after the backward prologue, after the dK/dV
+ * kernel and after the dQ kernel. Otherwise identical.
+ */
+int mf_attn_packed_bwd_profiled(const void* q, const void* k, const void* v, const void* out,
+                                const void* d_out, const float* lse, const int32_t* cu_seqlens,
+                                const int32_t* grid_hw, const int32_t* text_len, void* dq, void* dk,
+                                void* dv, int32_t n_seg, int64_t total_tokens, int32_t heads,
+                                int32_t head_dim, int32_t dtype, hipEvent_t const* events,
+                                hipStream_t stream);
+
+/* Bytes of the backward's library-owned workspace for these sizes (0 if unsupported). */
+size_t mf_bwd_workspace_bytes(int64_t total_tokens, int32_t heads, int32_t head_dim, int32_t n_seg);
+
+/*
  * Packing metadata alone (same conventions as above).
  *   grid_hw, text_len  device int32 inputs
  *   cu_seqlens_out     device int32 [n_seg + 1]

@@ -173,6 +173,21 @@ def packed_attention_backward(q, k, v, d_out, cu_seqlens, scale: float | None = 
     return dq, dk, dv
 
 
+def joint_attention_lse(q, k, grid_hw, text_len, theta: float = rope.DEFAULT_THETA,
+                        scale: float | None = None) -> np.ndarray:
+    """Row log-sum-exp of the joint path's scaled scores, [H, T] (natural log):
+    2D RoPE on q and k, then ``sample_attention_lse`` per sample."""
+    cu = packing.cu_seqlens(grid_hw, text_len)
+    pos, _ = packing.token_positions(grid_hw, text_len)
+    qr = rope.rope2d(q, pos, theta)
+    kr = rope.rope2d(k, pos, theta)
+    out = np.empty((np.shape(q)[1], np.shape(q)[0]), dtype=np.float64)
+    for i in range(cu.shape[0] - 1):
+        a, b = int(cu[i]), int(cu[i + 1])
+        out[:, a:b] = sample_attention_lse(qr[a:b], kr[a:b], scale).T
+    return out
+
+
 def joint_attention_backward(q, k, v, d_out, grid_hw, text_len, theta: float = rope.DEFAULT_THETA,
                              scale: float | None = None):
     """Gradients of ``joint_attention`` with respect to the unrotated q, k and v.

@@ -342,6 +342,41 @@ def test_lse_matches_brute_force():
         assert abs(lse[i, 0] - math.log(sum(math.exp(x) for x in s))) < 1e-12
 
 
+def test_joint_lse_brute_force_with_complex_rotation():
+    """Joint LSE against a pure-Python evaluation: positions enumerated by hand,
+    each channel pair rotated as a complex number times e^{i p w_j}, scores and
+    log-sum-exp summed term by term per sample."""
+    grid, text = [[2, 3], [1, 2]], [2, 1]
+    d, H = 8, 2
+    rng = np.random.default_rng(21)
+    T = sum(t + h * w for (h, w), t in zip(grid, text))
+    q, k = rng.standard_normal((T, H, d)), rng.standard_normal((T, H, d))
+    lse = attention.joint_attention_lse(q, k, grid, text)
+    samples, start = [], 0
+    for (h, w), t in zip(grid, text):
+        pos = [(0, 0)] * t + [(r, c) for r in range(h) for c in range(w)]
+        samples.append((start, pos))
+        start += t + h * w
+
+    def rot(x, p):
+        out = []
+        for j in range(d // 2):
+            half, jj = divmod(j, d // 4)
+            ang = p[half] * 10000.0 ** (-2 * jj / (d // 2))
+            z = complex(x[2 * j], x[2 * j + 1]) * complex(math.cos(ang), math.sin(ang))
+            out += [z.real, z.imag]
+        return out
+
+    for start, pos in samples:
+        n = len(pos)
+        for hh in range(H):
+            qr = [rot(q[start + i, hh], pos[i]) for i in range(n)]
+            kr = [rot(k[start + i, hh], pos[i]) for i in range(n)]
+            for i in range(n):
+                s = [sum(a * b for a, b in zip(qr[i], kr[j])) / math.sqrt(d) for j in range(n)]
+                assert abs(lse[hh, start + i] - math.log(sum(math.exp(x) for x in s))) < 1e-12
+
+
 def _numeric_grad(f, x, eps=1e-6):
     g = np.zeros_like(x)
     for idx in itertools.product(*map(range, x.shape)):

@@ -46,6 +46,10 @@ def _declare(lib):
         "mf_attn_packed_profiled": ([P, P, P, P, P, P, P, I32, I64, I32, I32, I32, P, P], ctypes.c_int),
         "mf_workspace_bytes": ([I64, I32, I32, I32, I32], SZ),
         "mf_attn_packed_ws": ([P, P, P, P, P, P, P, I32, I64, I32, I32, I32, P, SZ, P], ctypes.c_int),
+        "mf_attn_packed_lse": ([P, P, P, P, P, P, P, P, I32, I64, I32, I32, I32, P], ctypes.c_int),
+        "mf_attn_packed_bwd": ([P] * 12 + [I32, I64, I32, I32, I32, P], ctypes.c_int),
+        "mf_attn_packed_bwd_profiled": ([P] * 12 + [I32, I64, I32, I32, I32, P, P], ctypes.c_int),
+        "mf_bwd_workspace_bytes": ([I64, I32, I32, I32], SZ),
         "mf_build_metadata": ([I32, P, P, P, P, P, I64, P], ctypes.c_int),
         "mf_rope_2d": ([P, P, P, I64, I32, I32, I32, F, P], ctypes.c_int),
         "mf_rf_cfg_euler_step": ([P, P, P, P, P, I32, I64, P, P, I32, I64, I32, I32, F, F, P], ctypes.c_int),
@@ -161,6 +165,57 @@ def attn_packed_ws(q, k, v, cu_seqlens, grid_hw, text_len, workspace, out=None, 
                                    _ptr(out), n, T, H, D, _DTYPES[q.dtype], _ptr(workspace),
                                    workspace.numel(), _stream(stream)))
     return out
+
+
+def attn_packed_lse(q, k, v, cu_seqlens, grid_hw, text_len, out=None, lse=None, stream=None):
+    """Forward that also returns the row log-sum-exp (mf_attn_packed_lse): (out, lse [H, T] float32)."""
+    out, n, T, H, D = _attn_args(q, k, v, cu_seqlens, grid_hw, text_len, out)
+    if lse is None:
+        lse = torch.empty((H, T), dtype=torch.float32, device=q.device)
+    _need(lse, "lse", torch.float32, 2)
+    if lse.shape != (H, T):
+        raise ValueError("lse must be [heads, tokens]")
+    _check(lib().mf_attn_packed_lse(_ptr(q), _ptr(k), _ptr(v), _ptr(cu_seqlens), _ptr(grid_hw), _ptr(text_len),
+                                    _ptr(out), _ptr(lse), n, T, H, D, _DTYPES[q.dtype], _stream(stream)))
+    return out, lse
+
+
+def _bwd_args(q, k, v, out, d_out, lse, cu_seqlens, grid_hw, text_len, grads):
+    _, n, T, H, D = _attn_args(q, k, v, cu_seqlens, grid_hw, text_len, out)
+    _need(d_out, "d_out", q.dtype, 3)
+    if d_out.shape != q.shape:
+        raise ValueError("d_out must have the shape of q")
+    _need(lse, "lse", torch.float32, 2)
+    if lse.shape != (H, T):
+        raise ValueError("lse must be [heads, tokens]")
+    if grads is None:
+        grads = tuple(torch.empty_like(q) for _ in range(3))
+    for name, g in zip(("dq", "dk", "dv"), grads):
+        _need(g, name, q.dtype, 3)
+        if g.shape != q.shape:
+            raise ValueError(f"{name} must have the shape of q")
+    return grads, n, T, H, D
+
+
+def attn_packed_bwd(q, k, v, out, d_out, lse, cu_seqlens, grid_hw, text_len, grads=None, stream=None):
+    """Packed backward (mf_attn_packed_bwd). Returns (dq, dk, dv)."""
+    (dq, dk, dv), n, T, H, D = _bwd_args(q, k, v, out, d_out, lse, cu_seqlens, grid_hw, text_len, grads)
+    _check(lib().mf_attn_packed_bwd(_ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(d_out), _ptr(lse),
+                                    _ptr(cu_seqlens), _ptr(grid_hw), _ptr(text_len), _ptr(dq), _ptr(dk),
+                                    _ptr(dv), n, T, H, D, _DTYPES[q.dtype], _stream(stream)))
+    return dq, dk, dv
+
+
+def attn_packed_bwd_profiled(q, k, v, out, d_out, lse, cu_seqlens, grid_hw, text_len, events, grads=None,
+                             stream=None):
+    """mf_attn_packed_bwd recording four hipEvent_t handles (ints) between its kernels."""
+    (dq, dk, dv), n, T, H, D = _bwd_args(q, k, v, out, d_out, lse, cu_seqlens, grid_hw, text_len, grads)
+    arr = (ctypes.c_void_p * 4)(*events)
+    _check(lib().mf_attn_packed_bwd_profiled(_ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(d_out), _ptr(lse),
+                                             _ptr(cu_seqlens), _ptr(grid_hw), _ptr(text_len), _ptr(dq),
+                                             _ptr(dk), _ptr(dv), n, T, H, D, _DTYPES[q.dtype],
+                                             ctypes.cast(arr, ctypes.c_void_p), _stream(stream)))
+    return dq, dk, dv
 
 
 def build_metadata(grid_hw, text_len, total_tokens: int, stream=None):

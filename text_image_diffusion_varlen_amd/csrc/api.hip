@@ -34,8 +34,14 @@ hipError_t launch_rope(const void* x, void* y, const int32_t* pos, int64_t token
                        int32_t head_dim, bool bf16, const float2* cs, int32_t* status,
                        hipStream_t s);
 hipError_t launch_attn_fwd(const char* ws, const WsLayout& l, const void* q, const int32_t* grid_hw,
-                           const int32_t* text_len, const float2* cs, void* out, int32_t heads,
-                           int32_t head_dim, bool bf16, float scale, hipStream_t s);
+                           const int32_t* text_len, const float2* cs, void* out, float* lse,
+                           int64_t tokens, int32_t heads, int32_t head_dim, bool bf16, float scale,
+                           hipStream_t s);
+hipError_t launch_attn_bwd(const void* q, const void* k, const void* v, const void* o, const void* dout,
+                           const float* lse, const int32_t* grid_hw, const int32_t* text_len,
+                           const float2* cs, char* ws, const BwdLayout& l, void* dq, void* dk, void* dv,
+                           int64_t tokens, int32_t heads, int32_t head_dim, float scale, hipStream_t s,
+                           hipEvent_t const* ev);
 hipError_t launch_cfg_euler(float* z, const void* v, const int32_t* cu, const int32_t* grid_hw,
                             const int32_t* text_len, int32_t n_seg, int64_t total_tokens,
                             const int32_t* cond_seg, const int32_t* uncond_seg, int32_t n_img,
@@ -66,6 +72,8 @@ struct DeviceState {
   int32_t* status = nullptr;  // sticky FLAG_* of the standalone metadata / RoPE / sampler calls
   char* ws = nullptr;         // library workspace of mf_attn_packed
   size_t ws_bytes = 0;
+  char* bws = nullptr;        // library workspace of mf_attn_packed_bwd
+  size_t bws_bytes = 0;
   std::map<std::pair<int, uint32_t>, float2*> tables;  // (head_dim, theta bits) -> cos/sin
 };
 
@@ -122,15 +130,17 @@ int ensure_table(DeviceState& st, int head_dim, float theta, const float2** out)
   return MF_OK;
 }
 
-int ensure_workspace(DeviceState& st, size_t bytes) {
-  if (st.ws_bytes >= bytes) return MF_OK;
+// Grows a library-owned workspace (buf, have) to at least `bytes`; a new
+// buffer starts with a zeroed header.
+int ensure_buffer(char*& buf, size_t& have, size_t bytes) {
+  if (have >= bytes) return MF_OK;
   const char* f = std::getenv("MF_FAULT_OOM");
   if (f && f[0] == '1') return fail(MF_ERR_OOM, "workspace of %zu bytes: injected failure", bytes);
-  if (st.ws) {
+  if (buf) {
     // hipFree waits for the device, so no enqueued call still uses the old buffer.
-    const hipError_t e = hipFree(st.ws);
-    st.ws = nullptr;
-    st.ws_bytes = 0;
+    const hipError_t e = hipFree(buf);
+    buf = nullptr;
+    have = 0;
     if (e != hipSuccess) return hip_fail(e, "hipFree(workspace)");
   }
   void* p = nullptr;
@@ -144,10 +154,12 @@ int ensure_workspace(DeviceState& st, size_t bytes) {
     (void)hipFree(p);
     return hip_fail(z, "hipMemset(workspace header)");
   }
-  st.ws = static_cast<char*>(p);
-  st.ws_bytes = bytes;
+  buf = static_cast<char*>(p);
+  have = bytes;
   return MF_OK;
 }
+
+int ensure_workspace(DeviceState& st, size_t bytes) { return ensure_buffer(st.ws, st.ws_bytes, bytes); }
 
 int elem_bytes(int32_t dtype) { return dtype == MF_BF16 ? 2 : dtype == MF_F32 ? 4 : 0; }
 
@@ -190,7 +202,7 @@ int check_attn_args(const void* q, const void* k, const void* v, const int32_t* 
 int run_attn(const void* q, const void* k, const void* v, const int32_t* cu, const int32_t* grid_hw,
              const int32_t* text_len, void* out, int32_t n_seg, int64_t tokens, int32_t heads,
              int32_t head_dim, int32_t dtype, char* ws, const float2* cs, hipStream_t s,
-             hipEvent_t const* ev = nullptr) {
+             hipEvent_t const* ev = nullptr, float* lse = nullptr) {
   const bool bf16 = dtype == MF_BF16;
   const mf::WsLayout l = mf::ws_layout(tokens, heads, head_dim, elem_bytes(dtype), n_seg);
   hipError_t e;
@@ -201,7 +213,7 @@ int run_attn(const void* q, const void* k, const void* v, const int32_t* cu, con
   e = mf::launch_rope_pack(q, k, v, grid_hw, text_len, ws, l, cs, heads, head_dim, bf16, s);
   if (e != hipSuccess) return hip_fail(e, "rope_pack_kernel launch");
   if (ev && (e = hipEventRecord(ev[2], s)) != hipSuccess) return hip_fail(e, "hipEventRecord");
-  e = mf::launch_attn_fwd(ws, l, q, grid_hw, text_len, cs, out, heads, head_dim, bf16,
+  e = mf::launch_attn_fwd(ws, l, q, grid_hw, text_len, cs, out, lse, tokens, heads, head_dim, bf16,
                           float(1.0 / std::sqrt(double(head_dim))), s);
   if (e != hipSuccess) return hip_fail(e, "attn_fwd launch");
   if (ev && (e = hipEventRecord(ev[3], s)) != hipSuccess) return hip_fail(e, "hipEventRecord");
@@ -278,6 +290,98 @@ int mf_attn_packed_ws(const void* q, const void* k, const void* v, const int32_t
   }
   return run_attn(q, k, v, cu_seqlens, grid_hw, text_len, out, n_seg, total_tokens, heads, head_dim,
                   dtype, static_cast<char*>(workspace), cs, stream);
+}
+
+int mf_attn_packed_lse(const void* q, const void* k, const void* v, const int32_t* cu_seqlens,
+                       const int32_t* grid_hw, const int32_t* text_len, void* out, float* lse,
+                       int32_t n_seg, int64_t total_tokens, int32_t heads, int32_t head_dim,
+                       int32_t dtype, hipStream_t stream) {
+  int rc = check_attn_args(q, k, v, cu_seqlens, grid_hw, text_len, out, n_seg, total_tokens, heads,
+                           head_dim, dtype);
+  if (rc) return rc;
+  if (!lse) return fail(MF_ERR_INVALID_ARG, "null lse");
+  if (reinterpret_cast<uintptr_t>(lse) & 3) return fail(MF_ERR_INVALID_ARG, "lse must be 4-byte aligned");
+  const size_t tb = size_t(total_tokens) * heads * head_dim * elem_bytes(dtype);
+  const size_t lb = size_t(total_tokens) * heads * 4;
+  if (overlaps(lse, lb, out, tb) || overlaps(lse, lb, q, tb) || overlaps(lse, lb, k, tb) ||
+      overlaps(lse, lb, v, tb))
+    return fail(MF_ERR_INVALID_ARG, "lse overlaps q, k, v or out");
+  int dev;
+  if ((rc = current_device(&dev))) return rc;
+  const size_t need = mf_workspace_bytes(total_tokens, heads, head_dim, dtype, n_seg);
+  std::lock_guard<std::mutex> lock(g_mu);
+  DeviceState& st = g_dev[dev];
+  const float2* cs = nullptr;
+  if ((rc = ensure_table(st, head_dim, MF_ROPE_THETA, &cs))) return rc;
+  if ((rc = ensure_workspace(st, need))) return rc;
+  return run_attn(q, k, v, cu_seqlens, grid_hw, text_len, out, n_seg, total_tokens, heads, head_dim,
+                  dtype, st.ws, cs, stream, nullptr, lse);
+}
+
+size_t mf_bwd_workspace_bytes(int64_t total_tokens, int32_t heads, int32_t head_dim, int32_t n_seg) {
+  if ((head_dim != 64 && head_dim != 128) || heads < 1 || heads > 256 || n_seg < 1 ||
+      n_seg > MF_MAX_SEGMENTS || total_tokens < 1 || total_tokens >= (int64_t(1) << 31))
+    return 0;
+  return size_t(mf::bwd_layout(total_tokens, heads, head_dim, n_seg).total);
+}
+
+int mf_attn_packed_bwd_profiled(const void* q, const void* k, const void* v, const void* out,
+                                const void* d_out, const float* lse, const int32_t* cu_seqlens,
+                                const int32_t* grid_hw, const int32_t* text_len, void* dq, void* dk,
+                                void* dv, int32_t n_seg, int64_t total_tokens, int32_t heads,
+                                int32_t head_dim, int32_t dtype, hipEvent_t const* events,
+                                hipStream_t stream) {
+  int rc = check_attn_args(q, k, v, cu_seqlens, grid_hw, text_len, dq, n_seg, total_tokens, heads,
+                           head_dim, dtype);
+  if (rc) return rc;
+  if (dtype != MF_BF16) return fail(MF_ERR_UNSUPPORTED, "backward supports MF_BF16 only");
+  if (!out || !d_out || !lse || !dk || !dv) return fail(MF_ERR_INVALID_ARG, "null pointer argument");
+  const size_t tb = size_t(total_tokens) * heads * head_dim * 2;
+  const size_t lb = size_t(total_tokens) * heads * 4;
+  const void* ins[6] = {q, k, v, out, d_out, lse};
+  const size_t in_bytes[6] = {tb, tb, tb, tb, tb, lb};
+  void* outs[3] = {dq, dk, dv};
+  for (int i = 0; i < 3; ++i) {
+    for (int j = 0; j < 6; ++j)
+      if (overlaps(outs[i], tb, ins[j], in_bytes[j]))
+        return fail(MF_ERR_INVALID_ARG, "a gradient output overlaps an input");
+    for (int j = i + 1; j < 3; ++j)
+      if (overlaps(outs[i], tb, outs[j], tb)) return fail(MF_ERR_INVALID_ARG, "gradient outputs overlap");
+    if (overlaps(outs[i], tb, cu_seqlens, size_t(n_seg + 1) * 4) ||
+        overlaps(outs[i], tb, grid_hw, size_t(n_seg) * 8) || overlaps(outs[i], tb, text_len, size_t(n_seg) * 4))
+      return fail(MF_ERR_INVALID_ARG, "a gradient output overlaps the metadata");
+  }
+  const uintptr_t mis = reinterpret_cast<uintptr_t>(out) | reinterpret_cast<uintptr_t>(d_out) |
+                        reinterpret_cast<uintptr_t>(dk) | reinterpret_cast<uintptr_t>(dv);
+  if ((mis & 15) || (reinterpret_cast<uintptr_t>(lse) & 3))
+    return fail(MF_ERR_INVALID_ARG, "out, d_out, dk, dv must be 16-byte aligned and lse 4-byte aligned");
+  int dev;
+  if ((rc = current_device(&dev))) return rc;
+  const mf::BwdLayout l = mf::bwd_layout(total_tokens, heads, head_dim, n_seg);
+  std::lock_guard<std::mutex> lock(g_mu);
+  DeviceState& st = g_dev[dev];
+  const float2* cs = nullptr;
+  if ((rc = ensure_table(st, head_dim, MF_ROPE_THETA, &cs))) return rc;
+  if ((rc = ensure_buffer(st.bws, st.bws_bytes, size_t(l.total)))) return rc;
+  hipError_t e;
+  if (events && (e = hipEventRecord(events[0], stream)) != hipSuccess) return hip_fail(e, "hipEventRecord");
+  e = mf::launch_meta(grid_hw, text_len, cu_seqlens, n_seg, total_tokens, st.bws, l.m, stream);
+  if (e != hipSuccess) return hip_fail(e, "meta_kernel launch");
+  e = mf::launch_attn_bwd(q, k, v, out, d_out, lse, grid_hw, text_len, cs, st.bws, l, dq, dk, dv,
+                          total_tokens, heads, head_dim, float(1.0 / std::sqrt(double(head_dim))), stream,
+                          events ? events + 1 : nullptr);
+  if (e != hipSuccess) return hip_fail(e, "backward kernels launch");
+  if (events && (e = hipEventRecord(events[3], stream)) != hipSuccess) return hip_fail(e, "hipEventRecord");
+  return MF_OK;
+}
+
+int mf_attn_packed_bwd(const void* q, const void* k, const void* v, const void* out, const void* d_out,
+                       const float* lse, const int32_t* cu_seqlens, const int32_t* grid_hw,
+                       const int32_t* text_len, void* dq, void* dk, void* dv, int32_t n_seg,
+                       int64_t total_tokens, int32_t heads, int32_t head_dim, int32_t dtype,
+                       hipStream_t stream) {
+  return mf_attn_packed_bwd_profiled(q, k, v, out, d_out, lse, cu_seqlens, grid_hw, text_len, dq, dk, dv,
+                                     n_seg, total_tokens, heads, head_dim, dtype, nullptr, stream);
 }
 
 int mf_build_metadata(int32_t n_seg, const int32_t* grid_hw, const int32_t* text_len,
@@ -394,9 +498,10 @@ int mf_get_device_error(hipStream_t stream) {
     if (v && (e = hipMemset(st.status, 0, 4)) != hipSuccess) return hip_fail(e, "hipMemset(status)");
     flags |= v;
   }
-  if (st.ws) {
+  for (char* w : {st.ws, st.bws}) {
+    if (!w) continue;
     mf::WsHeader hdr;
-    if ((e = hipMemcpy(&hdr, st.ws, sizeof(hdr), hipMemcpyDeviceToHost)) != hipSuccess)
+    if ((e = hipMemcpy(&hdr, w, sizeof(hdr), hipMemcpyDeviceToHost)) != hipSuccess)
       return hip_fail(e, "hipMemcpy(workspace header)");
     flags |= hdr.flag;
   }

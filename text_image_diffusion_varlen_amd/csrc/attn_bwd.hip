@@ -1,0 +1,553 @@
+// Packed joint attention backward on gfx950.
+//
+// Gradients of O = softmax(X) V, X = scale * Q~ K~^T, per sample and head
+// (the packed samples are independent: Mage-Flow tech report, NR-MMDiT
+// section, per-sample cumulative offsets; training runs on such packed
+// batches, same section). With P = softmax(X), the upstream gradient dO and
+// D_q = sum_c dO[q][c] O[q][c]:
+//   dV = P^T dO,  dP = dO V^T,  dX = P * (dP - D),
+//   dQ~ = scale * dX K~,  dK~ = scale * dX^T Q~,
+// and the 2D RoPE rotation (orthogonal, mageflow.net architecture page,
+// section 2) is undone on dQ~, dK~: dq = R(pos)^T dQ~, dk = R(pos)^T dK~.
+// P is recomputed from the forward's saved row log-sum-exp (natural log,
+// [heads][tokens]); no score matrix is stored.
+//
+// Three kernels:
+//   bwd_pack_kernel  one workgroup per (KTILE padded rows, head): rotates q and
+//                    k, and writes Q~, dO, K~, V chunk-major, Q~^T, dO^T, K~^T
+//                    in MFMA order (as the forward's V~^T) and per-row
+//                    log2-domain LSE and D into the backward workspace.
+//   bwd_kv_kernel    one workgroup per (128 keys of a sample, head), 4 waves x
+//                    32 keys, keys resident in registers; loops over all the
+//                    sample's 64-query tiles (double-buffered in LDS):
+//                      S = Q~ K~^T, dP = dO V^T (lane = key, entries = queries),
+//                      dV^T += dO^T P, dK^T += Q~^T dX.
+//   bwd_q_kernel     one workgroup per (256 queries of a sample, head), 8 waves
+//                    x 32 queries, queries resident in registers; loops over
+//                    the sample's 64-key tiles:
+//                      S^T = K~ Q~^T, dP^T = V dO^T (lane = query),
+//                      dQ^T += K~^T dX^T.
+// Every product runs on v_mfma_f32_32x32x16_bf16 with fp32 accumulation; P
+// and dX are rounded to bf16 (RNE) as MFMA operands. Nothing is accumulated
+// across workgroups, so results are deterministic.
+#include "mf_common.h"
+#include "mfma_util.h"
+#include "rope_math.h"
+
+namespace mf {
+
+constexpr float LOG2E = 1.4426950408889634f;
+constexpr int KV_WAVES = 4;                 // waves of bwd_kv_kernel, 32 keys each
+constexpr int KV_KEYS = 32 * KV_WAVES;      // keys per bwd_kv workgroup
+constexpr int Q_WAVES = QTILE / 32;         // waves of bwd_q_kernel, 32 queries each
+static_assert(QTILE == 2 * KV_KEYS, "two key blocks per entry of the tile table");
+
+struct BwdArgs {
+  const char* ws;
+  int64_t off_len, off_cu, off_pcu, off_tiles;
+  const uint16_t* q;     // caller tensors [tokens][heads][d]
+  const uint16_t* k;
+  const uint16_t* v;
+  const uint16_t* o;
+  const uint16_t* dout;
+  const float* lse;      // [heads][tokens], natural log
+  const int32_t* grid_hw;
+  const int32_t* text_len;
+  const float2* cs;      // cos/sin table [ROPE_PMAX][d/4]
+  uint16_t* qc;
+  uint16_t* qt;
+  uint16_t* oc;
+  uint16_t* ot;
+  uint16_t* kc;
+  uint16_t* kt;
+  uint16_t* vc;
+  float* st;
+  uint16_t* dq;
+  uint16_t* dk;
+  uint16_t* dv;
+  int32_t heads;
+  int64_t rows;      // padded rows per head
+  int64_t tokens;
+  float c_log2;      // scale * log2(e)
+  float scale;
+};
+
+// ---------------------------------------------------------------- prologue
+
+template <int D>
+__global__ void __launch_bounds__(256) bwd_pack_kernel(BwdArgs a) {
+  constexpr int CPR = D / 8;             // 16-byte chunks per row
+  constexpr int CPT = KTILE * CPR;       // chunks per tile
+  constexpr int VS = D + 2;              // staged row stride (elements): column reads hit distinct banks
+  const WsHeader* hdr = reinterpret_cast<const WsHeader*>(a.ws);
+  if (hdr->flag != FLAG_OK) return;
+  const int32_t* len = reinterpret_cast<const int32_t*>(a.ws + a.off_len);
+  const int32_t* cu = reinterpret_cast<const int32_t*>(a.ws + a.off_cu);
+  const int32_t* pcu = reinterpret_cast<const int32_t*>(a.ws + a.off_pcu);
+
+  const int64_t r0 = int64_t(blockIdx.x) * KTILE;
+  const int h = blockIdx.y;
+  int32_t u0 = 0, L = 0, tl = 0, w = 1;
+  int64_t tok0 = 0;
+  if (r0 < hdr->padded_total) {
+    const int32_t s = upper_segment(pcu, hdr->n_seg, r0);
+    u0 = int32_t(r0 - pcu[s]);
+    L = len[s];
+    tok0 = int64_t(cu[s]) + u0;
+    tl = a.text_len[s];
+    w = a.grid_hw[2 * s + 1];
+  }
+  const int64_t tile_off = (int64_t(h) * a.rows + r0) * D;  // element offset of this tile
+  const int64_t stride = int64_t(a.heads) * D;              // elements between tokens
+  __shared__ uint16_t tile[KTILE * VS];
+  __shared__ float dsum[KTILE];
+  const int tid = threadIdx.x;
+
+  // Stage a KTILE x D tile of `src` (rotated when asked) into LDS; zero rows
+  // past the sample. For dO also form D = rowsum(dO * O) (the CPR threads of
+  // one row are consecutive lanes, 64 % CPR == 0).
+  auto stage = [&](const uint16_t* src, bool rotate, bool with_dsum) {
+#pragma unroll
+    for (int i = 0; i < CPT / 256; ++i) {
+      const int f = tid + 256 * i;
+      const int rr = f / CPR, cc = f % CPR;
+      const int32_t u = u0 + rr;
+      Chunk<uint16_t> x;
+      float part = 0.f;
+      if (u < L) {
+        const int64_t off = (tok0 + rr) * stride + int64_t(h) * D + cc * 8;
+        x = *reinterpret_cast<const Chunk<uint16_t>*>(src + off);
+        if (rotate) {
+          int32_t row, col;
+          token_position(u, tl, w, row, col);
+          x = rotate_chunk<uint16_t, D>(x, cc * 8, row, col, a.cs);
+        }
+        if (with_dsum) {
+          const Chunk<uint16_t> y = *reinterpret_cast<const Chunk<uint16_t>*>(a.o + off);
+#pragma unroll
+          for (int e = 0; e < 8; ++e) part = __builtin_fmaf(bf16_to_f32(x.v[e]), bf16_to_f32(y.v[e]), part);
+        }
+      } else {
+#pragma unroll
+        for (int e = 0; e < 8; ++e) x.v[e] = 0;
+      }
+      uint32_t* dst = reinterpret_cast<uint32_t*>(tile + rr * VS + cc * 8);
+      const uint32_t* sv = reinterpret_cast<const uint32_t*>(x.v);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) dst[e] = sv[e];
+      if (with_dsum) {
+#pragma unroll
+        for (int o = CPR / 2; o >= 1; o >>= 1) part += __shfl_xor(part, o, 64);
+        if (cc == 0) dsum[rr] = part;
+      }
+    }
+    __syncthreads();
+  };
+  // Chunk f2 = c * KTILE + n holds channels 8c .. 8c+7 of row n.
+  auto write_chunk_major = [&](uint16_t* dst) {
+    for (int f2 = tid; f2 < CPT; f2 += 256) {
+      const int cc = f2 / KTILE, rr = f2 % KTILE;
+      const uint32_t* sv = reinterpret_cast<const uint32_t*>(tile + rr * VS + cc * 8);
+      u32x4 o = {sv[0], sv[1], sv[2], sv[3]};
+      *reinterpret_cast<u32x4*>(dst + tile_off + int64_t(f2) * 8) = o;
+    }
+  };
+  // Transposed tile [D][KTILE], rows inside every group of 16 in the order
+  // 0-3, 8-11, 4-7, 12-15, chunk-major: chunk g (8 rows) of channel c at g * D + c.
+  auto write_transposed = [&](uint16_t* dst) {
+    for (int f2 = tid; f2 < D * (KTILE / 8); f2 += 256) {
+      const int g = f2 / D, c = f2 % D;
+      const int base = 16 * (g >> 1) + 4 * (g & 1);
+      Chunk<uint16_t> o;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        o.v[e] = tile[(base + e) * VS + c];
+        o.v[4 + e] = tile[(base + 8 + e) * VS + c];
+      }
+      *reinterpret_cast<Chunk<uint16_t>*>(dst + tile_off + int64_t(f2) * 8) = o;
+    }
+  };
+
+  stage(a.q, true, false);
+  write_chunk_major(a.qc);
+  write_transposed(a.qt);
+  __syncthreads();
+  stage(a.k, true, false);
+  write_chunk_major(a.kc);
+  write_transposed(a.kt);
+  __syncthreads();
+  stage(a.dout, false, true);
+  write_chunk_major(a.oc);
+  write_transposed(a.ot);
+  __syncthreads();
+  stage(a.v, false, false);
+  write_chunk_major(a.vc);
+  if (tid < KTILE) {
+    const int32_t u = u0 + tid;
+    float* st = a.st + (int64_t(h) * a.rows + r0) * 2;  // tile index * 2 * KTILE
+    st[tid] = u < L ? a.lse[int64_t(h) * a.tokens + tok0 + tid] * LOG2E : INFINITY;
+    st[KTILE + tid] = u < L ? dsum[tid] : 0.f;
+  }
+}
+
+// ---------------------------------------------------------------- dK, dV
+
+template <int D>
+struct BwdTile {
+  static constexpr int CH = KTILE * D / 8;  // 16-byte chunks per KTILE x D tile
+  static constexpr int KSTEPS = D / 16;
+  static constexpr int DBLK = D / 32;
+};
+
+// One 64-query tile for one wave's 32 keys. T: LDS tile set [qc | oc | qt | ot | stats].
+template <int D>
+__device__ inline void kv_step(const u32x4* T, const bf16x8 (&kreg)[D / 16], const bf16x8 (&vreg)[D / 16],
+                               f32x16 (&dk)[D / 32], f32x16 (&dv)[D / 32], float c, int hf, int l32) {
+  constexpr int CH = BwdTile<D>::CH, KSTEPS = BwdTile<D>::KSTEPS, DBLK = BwdTile<D>::DBLK;
+  const u32x4* qcl = T + hf * KTILE + l32;           // Q~ chunk (2ks+hf) of query 32qb + l32
+  const u32x4* ocl = T + CH + hf * KTILE + l32;      // dO, same layout
+  const u32x4* qtl = T + 2 * CH + hf * D + l32;      // Q~^T chunk (2ks+hf) of channel 32b + l32
+  const u32x4* otl = T + 3 * CH + hf * D + l32;      // dO^T, same layout
+  const float* stl = reinterpret_cast<const float*>(T + 4 * CH);
+
+  // S (queries x keys) and dP, two 32-query blocks each; lane = key l32,
+  // entry e of block qb = query 32qb + 8(e/4) + 4hf + e%4.
+  f32x16 s[2] = {}, dp[2] = {};
+#pragma unroll
+  for (int ks = 0; ks < KSTEPS; ++ks) {
+#pragma unroll
+    for (int qb = 0; qb < 2; ++qb) {
+      s[qb] = mfma32(as_bf16x8(qcl[2 * KTILE * ks + 32 * qb]), kreg[ks], s[qb]);
+      dp[qb] = mfma32(as_bf16x8(ocl[2 * KTILE * ks + 32 * qb]), vreg[ks], dp[qb]);
+    }
+  }
+  // P = 2^(S c - lse2), dX = P (dP - D); packed to bf16 as the B operands of
+  // the two products below: k-step ks (queries 16ks .. 16ks+15) takes entries
+  // 8(ks%2) .. +7 of block ks/2, which are the queries the MFMA-order tiles
+  // (qt, ot) hold in chunk 2ks + hf.
+  uint32_t pp[4][4], pd[4][4];
+#pragma unroll
+  for (int qb = 0; qb < 2; ++qb) {
+#pragma unroll
+    for (int g = 0; g < 4; ++g) {
+      const int q0 = 32 * qb + 8 * g + 4 * hf;
+      const float4 l4 = *reinterpret_cast<const float4*>(stl + q0);
+      const float4 d4 = *reinterpret_cast<const float4*>(stl + KTILE + q0);
+      const float lq[4] = {l4.x, l4.y, l4.z, l4.w};
+      const float dq[4] = {d4.x, d4.y, d4.z, d4.w};
+      float p[4], x[4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        p[i] = __builtin_amdgcn_exp2f(__builtin_fmaf(s[qb][4 * g + i], c, -lq[i]));
+        x[i] = p[i] * (dp[qb][4 * g + i] - dq[i]);
+      }
+      const int ks = 2 * qb + (g >> 1), slot = 2 * (g & 1);
+      pp[ks][slot] = pack_bf16x2(p[0], p[1]);
+      pp[ks][slot + 1] = pack_bf16x2(p[2], p[3]);
+      pd[ks][slot] = pack_bf16x2(x[0], x[1]);
+      pd[ks][slot + 1] = pack_bf16x2(x[2], x[3]);
+    }
+  }
+  // dV^T (channels x keys) += dO^T P;  dK^T += Q~^T dX.
+#pragma unroll
+  for (int ks = 0; ks < 4; ++ks) {
+    const bf16x8 p8 = __builtin_bit_cast(bf16x8, u32x4{pp[ks][0], pp[ks][1], pp[ks][2], pp[ks][3]});
+    const bf16x8 x8 = __builtin_bit_cast(bf16x8, u32x4{pd[ks][0], pd[ks][1], pd[ks][2], pd[ks][3]});
+#pragma unroll
+    for (int b = 0; b < DBLK; ++b) {
+      dv[b] = mfma32(as_bf16x8(otl[2 * D * ks + 32 * b]), p8, dv[b]);
+      dk[b] = mfma32(as_bf16x8(qtl[2 * D * ks + 32 * b]), x8, dk[b]);
+    }
+  }
+}
+
+// Undo the rotation of four consecutive channels ch0 .. ch0+3 (two pairs) at
+// (row, col) and scale: (x0, x1) -> (x0 c + x1 s, -x0 s + x1 c) * scale.
+template <int D>
+__device__ inline uint2 unrotate4(const float (&x)[4], int ch0, int32_t row, int32_t col, float scale,
+                                  const float2* __restrict__ cs) {
+  float y[4];
+#pragma unroll
+  for (int pp = 0; pp < 2; ++pp) {
+    const int d = ch0 + 2 * pp;
+    const bool first_half = d < D / 2;
+    const int j = first_half ? d / 2 : (d - D / 2) / 2;
+    const float2 r = cs[(first_half ? row : col) * (D / 4) + j];
+    const float x0 = x[2 * pp], x1 = x[2 * pp + 1];
+    y[2 * pp] = (x0 * r.x + x1 * r.y) * scale;
+    y[2 * pp + 1] = (x1 * r.x - x0 * r.y) * scale;
+  }
+  uint2 o;
+  o.x = pack_bf16x2(y[0], y[1]);
+  o.y = pack_bf16x2(y[2], y[3]);
+  return o;
+}
+
+template <int D>
+__global__ void __launch_bounds__(64 * KV_WAVES, 1) bwd_kv_kernel(BwdArgs a) {
+  constexpr int CH = BwdTile<D>::CH, KSTEPS = BwdTile<D>::KSTEPS, DBLK = BwdTile<D>::DBLK;
+  constexpr int SET = 4 * CH + 2 * KTILE / 4;  // chunks of one LDS tile set (4 tiles + stats)
+  const WsHeader* hdr = reinterpret_cast<const WsHeader*>(a.ws);
+  const int32_t heads = a.heads;
+  const int h = int(blockIdx.x % unsigned(heads));
+  const int rest = int(blockIdx.x / unsigned(heads));
+  const int tile = rest >> 1;
+  if (hdr->flag != FLAG_OK || tile >= hdr->n_tiles) return;
+  const int2 td = reinterpret_cast<const int2*>(a.ws + a.off_tiles)[tile];
+  const int32_t seg = td.x, k0 = td.y + KV_KEYS * (rest & 1);
+  const int32_t L = reinterpret_cast<const int32_t*>(a.ws + a.off_len)[seg];
+  if (k0 >= L) return;
+  const int32_t pb = reinterpret_cast<const int32_t*>(a.ws + a.off_pcu)[seg];
+  const int32_t cb = reinterpret_cast<const int32_t*>(a.ws + a.off_cu)[seg];
+  const int tid = threadIdx.x;
+  const int wave = tid >> 6, lane = tid & 63, hf = lane >> 5, l32 = lane & 31;
+  const int64_t tile0 = (int64_t(h) * a.rows + pb) / KTILE;  // first KTILE tile of this (sample, head)
+
+  // This lane's key as the B operand of S = Q~ K~^T and dP = dO V^T: key
+  // k0 + 32 wave + l32, channels 16ks + 8hf .. +7, read from the chunk-major
+  // K~ and V tiles. Keys past the sample are zero (never stored).
+  const int32_t key = k0 + 32 * wave + l32;
+  bf16x8 kreg[KSTEPS], vreg[KSTEPS];
+  {
+    const int64_t r = tile0 * KTILE + key;
+    const u32x4* kp = reinterpret_cast<const u32x4*>(a.kc) + (r / KTILE) * CH + hf * KTILE + (r % KTILE);
+    const u32x4* vp = reinterpret_cast<const u32x4*>(a.vc) + (r / KTILE) * CH + hf * KTILE + (r % KTILE);
+#pragma unroll
+    for (int ks = 0; ks < KSTEPS; ++ks) {
+      kreg[ks] = key < L ? as_bf16x8(kp[2 * KTILE * ks]) : bf16x8{};
+      vreg[ks] = key < L ? as_bf16x8(vp[2 * KTILE * ks]) : bf16x8{};
+    }
+  }
+  __builtin_amdgcn_sched_barrier(0);
+  __builtin_amdgcn_s_waitcnt(0xF70);  // vmcnt(0): later waits cover tile copies only
+  __builtin_amdgcn_sched_barrier(0);
+
+  __shared__ u32x4 sets[2 * SET];
+  const u32x4* qcg = reinterpret_cast<const u32x4*>(a.qc) + tile0 * CH;
+  const u32x4* ocg = reinterpret_cast<const u32x4*>(a.oc) + tile0 * CH;
+  const u32x4* qtg = reinterpret_cast<const u32x4*>(a.qt) + tile0 * CH;
+  const u32x4* otg = reinterpret_cast<const u32x4*>(a.ot) + tile0 * CH;
+  const u32x4* stg = reinterpret_cast<const u32x4*>(a.st) + tile0 * (2 * KTILE / 4);
+  auto load_set = [&](int j, u32x4* dst) {
+    copy_to_lds<CH, KV_WAVES>(qcg + int64_t(j) * CH, dst, wave, lane);
+    copy_to_lds<CH, KV_WAVES>(ocg + int64_t(j) * CH, dst + CH, wave, lane);
+    copy_to_lds<CH, KV_WAVES>(qtg + int64_t(j) * CH, dst + 2 * CH, wave, lane);
+    copy_to_lds<CH, KV_WAVES>(otg + int64_t(j) * CH, dst + 3 * CH, wave, lane);
+    if (wave == 0 && lane < 2 * KTILE / 4)
+      __builtin_amdgcn_global_load_lds(stg + int64_t(j) * (2 * KTILE / 4) + lane, (lds_ptr_t)(dst + 4 * CH), 16, 0, 0);
+  };
+
+  f32x16 dk[DBLK], dv[DBLK];
+#pragma unroll
+  for (int b = 0; b < DBLK; ++b) dk[b] = dv[b] = f32x16{};
+  const int nqt = (L + KTILE - 1) / KTILE;
+  load_set(0, sets);
+  wait_vm_and_sync();
+  for (int j = 0; j < nqt; ++j) {
+    const u32x4* cur = sets + (j & 1) * SET;
+    if (j + 1 < nqt) load_set(j + 1, sets + ((j + 1) & 1) * SET);
+    kv_step<D>(cur, kreg, vreg, dk, dv, a.c_log2, hf, l32);
+    wait_vm_and_sync();
+  }
+
+  // Epilogue: entry e of block b is channel 32b + 8(e/4) + 4hf + e%4 of this lane's key.
+  if (key < L) {
+    int32_t row, col;
+    token_position(key, a.text_len[seg], a.grid_hw[2 * seg + 1], row, col);
+    const int64_t off = (int64_t(cb + key) * heads + h) * D;
+#pragma unroll
+    for (int b = 0; b < DBLK; ++b) {
+#pragma unroll
+      for (int g = 0; g < 4; ++g) {
+        const int ch = 32 * b + 8 * g + 4 * hf;
+        const float xk[4] = {dk[b][4 * g], dk[b][4 * g + 1], dk[b][4 * g + 2], dk[b][4 * g + 3]};
+        *reinterpret_cast<uint2*>(a.dk + off + ch) = unrotate4<D>(xk, ch, row, col, a.scale, a.cs);
+        uint2 o;
+        o.x = pack_bf16x2(dv[b][4 * g], dv[b][4 * g + 1]);
+        o.y = pack_bf16x2(dv[b][4 * g + 2], dv[b][4 * g + 3]);
+        *reinterpret_cast<uint2*>(a.dv + off + ch) = o;
+      }
+    }
+  }
+}
+
+// ---------------------------------------------------------------- dQ
+
+// One 64-key tile for one wave's 32 queries. T: LDS tile set [kc | vc | kt].
+template <int D, bool MASKED>
+__device__ inline void q_step(const u32x4* T, const bf16x8 (&qreg)[D / 16], const bf16x8 (&oreg)[D / 16],
+                              f32x16 (&acc)[D / 32], float c, float lse2, float dsum, int kbase, int L,
+                              int hf, int l32) {
+  constexpr int CH = BwdTile<D>::CH, KSTEPS = BwdTile<D>::KSTEPS, DBLK = BwdTile<D>::DBLK;
+  const u32x4* kcl = T + hf * KTILE + l32;
+  const u32x4* vcl = T + CH + hf * KTILE + l32;
+  const u32x4* ktl = T + 2 * CH + hf * D + l32;
+  // S^T and dP^T (keys x queries), two 32-key blocks; lane = query l32,
+  // entry e of block kb = key 32kb + 8(e/4) + 4hf + e%4.
+  f32x16 s[2] = {}, dp[2] = {};
+#pragma unroll
+  for (int ks = 0; ks < KSTEPS; ++ks) {
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb) {
+      s[kb] = mfma32(as_bf16x8(kcl[2 * KTILE * ks + 32 * kb]), qreg[ks], s[kb]);
+      dp[kb] = mfma32(as_bf16x8(vcl[2 * KTILE * ks + 32 * kb]), oreg[ks], dp[kb]);
+    }
+  }
+  uint32_t pd[4][4];
+#pragma unroll
+  for (int kb = 0; kb < 2; ++kb) {
+#pragma unroll
+    for (int e = 0; e < 16; e += 2) {
+      float p0 = __builtin_amdgcn_exp2f(__builtin_fmaf(s[kb][e], c, -lse2));
+      float p1 = __builtin_amdgcn_exp2f(__builtin_fmaf(s[kb][e + 1], c, -lse2));
+      if constexpr (MASKED) {
+        const int key = kbase + 32 * kb + 8 * (e >> 2) + 4 * hf + (e & 3);
+        if (key >= L) p0 = 0.f;
+        if (key + 1 >= L) p1 = 0.f;
+      }
+      pd[2 * kb + (e >> 3)][(e & 7) >> 1] = pack_bf16x2(p0 * (dp[kb][e] - dsum), p1 * (dp[kb][e + 1] - dsum));
+    }
+  }
+  // dQ^T (channels x queries) += K~^T dX^T
+#pragma unroll
+  for (int ks = 0; ks < 4; ++ks) {
+    const bf16x8 x8 = __builtin_bit_cast(bf16x8, u32x4{pd[ks][0], pd[ks][1], pd[ks][2], pd[ks][3]});
+#pragma unroll
+    for (int b = 0; b < DBLK; ++b) acc[b] = mfma32(as_bf16x8(ktl[2 * D * ks + 32 * b]), x8, acc[b]);
+  }
+}
+
+template <int D>
+__global__ void __launch_bounds__(64 * Q_WAVES, 2) bwd_q_kernel(BwdArgs a) {
+  constexpr int CH = BwdTile<D>::CH, KSTEPS = BwdTile<D>::KSTEPS, DBLK = BwdTile<D>::DBLK;
+  constexpr int SET = 3 * CH;
+  const WsHeader* hdr = reinterpret_cast<const WsHeader*>(a.ws);
+  const int32_t heads = a.heads;
+  const int h = int(blockIdx.x % unsigned(heads));
+  const int tile = int(blockIdx.x / unsigned(heads));
+  if (hdr->flag != FLAG_OK || tile >= hdr->n_tiles) return;
+  const int2 td = reinterpret_cast<const int2*>(a.ws + a.off_tiles)[tile];
+  const int32_t seg = td.x, qs = td.y;
+  const int32_t L = reinterpret_cast<const int32_t*>(a.ws + a.off_len)[seg];
+  const int32_t pb = reinterpret_cast<const int32_t*>(a.ws + a.off_pcu)[seg];
+  const int32_t cb = reinterpret_cast<const int32_t*>(a.ws + a.off_cu)[seg];
+  const int tid = threadIdx.x;
+  const int wave = tid >> 6, lane = tid & 63, hf = lane >> 5, l32 = lane & 31;
+  const int64_t tile0 = (int64_t(h) * a.rows + pb) / KTILE;
+
+  // This lane's query (rotated) and its dO row as B operands, plus its LSE
+  // and D. Query rows past the sample are never stored; they get P = 0.
+  const int32_t qrel = qs + 32 * wave + l32;
+  const int64_t r = tile0 * KTILE + qrel;  // inside the padded buffer (its slack covers a whole tile)
+  bf16x8 qreg[KSTEPS], oreg[KSTEPS];
+  {
+    const u32x4* qp = reinterpret_cast<const u32x4*>(a.qc) + (r / KTILE) * CH + hf * KTILE + (r % KTILE);
+    const u32x4* op = reinterpret_cast<const u32x4*>(a.oc) + (r / KTILE) * CH + hf * KTILE + (r % KTILE);
+#pragma unroll
+    for (int ks = 0; ks < KSTEPS; ++ks) {
+      qreg[ks] = as_bf16x8(qp[2 * KTILE * ks]);
+      oreg[ks] = as_bf16x8(op[2 * KTILE * ks]);
+    }
+  }
+  const float* stp = a.st + (r / KTILE) * (2 * KTILE) + (r % KTILE);
+  const float lse2 = qrel < L ? stp[0] : INFINITY;
+  const float dsum = qrel < L ? stp[KTILE] : 0.f;
+  __builtin_amdgcn_sched_barrier(0);
+  __builtin_amdgcn_s_waitcnt(0xF70);  // vmcnt(0)
+  __builtin_amdgcn_sched_barrier(0);
+
+  __shared__ u32x4 sets[2 * SET];
+  const u32x4* kcg = reinterpret_cast<const u32x4*>(a.kc) + tile0 * CH;
+  const u32x4* vcg = reinterpret_cast<const u32x4*>(a.vc) + tile0 * CH;
+  const u32x4* ktg = reinterpret_cast<const u32x4*>(a.kt) + tile0 * CH;
+  auto load_set = [&](int j, u32x4* dst) {
+    copy_to_lds<CH, Q_WAVES>(kcg + int64_t(j) * CH, dst, wave, lane);
+    copy_to_lds<CH, Q_WAVES>(vcg + int64_t(j) * CH, dst + CH, wave, lane);
+    copy_to_lds<CH, Q_WAVES>(ktg + int64_t(j) * CH, dst + 2 * CH, wave, lane);
+  };
+
+  f32x16 acc[DBLK];
+#pragma unroll
+  for (int b = 0; b < DBLK; ++b) acc[b] = f32x16{};
+  const int nkt = (L + KTILE - 1) / KTILE;
+  load_set(0, sets);
+  wait_vm_and_sync();
+  for (int j = 0; j + 1 < nkt; ++j) {
+    load_set(j + 1, sets + ((j + 1) & 1) * SET);
+    q_step<D, false>(sets + (j & 1) * SET, qreg, oreg, acc, a.c_log2, lse2, dsum, KTILE * j, L, hf, l32);
+    wait_vm_and_sync();
+  }
+  q_step<D, true>(sets + ((nkt - 1) & 1) * SET, qreg, oreg, acc, a.c_log2, lse2, dsum, KTILE * (nkt - 1), L,
+                  hf, l32);
+
+  if (qrel < L) {
+    int32_t row, col;
+    token_position(qrel, a.text_len[seg], a.grid_hw[2 * seg + 1], row, col);
+    const int64_t off = (int64_t(cb + qrel) * heads + h) * D;
+#pragma unroll
+    for (int b = 0; b < DBLK; ++b) {
+#pragma unroll
+      for (int g = 0; g < 4; ++g) {
+        const int ch = 32 * b + 8 * g + 4 * hf;
+        const float x[4] = {acc[b][4 * g], acc[b][4 * g + 1], acc[b][4 * g + 2], acc[b][4 * g + 3]};
+        *reinterpret_cast<uint2*>(a.dq + off + ch) = unrotate4<D>(x, ch, row, col, a.scale, a.cs);
+      }
+    }
+  }
+}
+
+// ---------------------------------------------------------------- launch
+
+template <int D>
+static hipError_t launch_bwd_t(const BwdArgs& a, const BwdLayout& l, hipStream_t s, hipEvent_t const* ev) {
+  hipError_t e;
+  hipLaunchKernelGGL(bwd_pack_kernel<D>, dim3(unsigned(l.m.rows / KTILE), unsigned(a.heads)), dim3(256), 0, s, a);
+  if ((e = hipGetLastError()) != hipSuccess) return e;
+  if (ev && (e = hipEventRecord(ev[0], s)) != hipSuccess) return e;
+  hipLaunchKernelGGL(bwd_kv_kernel<D>, dim3(unsigned(2 * l.m.n_tiles * a.heads)), dim3(64 * KV_WAVES), 0, s, a);
+  if ((e = hipGetLastError()) != hipSuccess) return e;
+  if (ev && (e = hipEventRecord(ev[1], s)) != hipSuccess) return e;
+  hipLaunchKernelGGL(bwd_q_kernel<D>, dim3(unsigned(l.m.n_tiles * a.heads)), dim3(64 * Q_WAVES), 0, s, a);
+  return hipGetLastError();
+}
+
+hipError_t launch_attn_bwd(const void* q, const void* k, const void* v, const void* o, const void* dout,
+                           const float* lse, const int32_t* grid_hw, const int32_t* text_len,
+                           const float2* cs, char* ws, const BwdLayout& l, void* dq, void* dk, void* dv,
+                           int64_t tokens, int32_t heads, int32_t head_dim, float scale, hipStream_t s,
+                           hipEvent_t const* ev) {
+  BwdArgs a;
+  a.ws = ws;
+  a.off_len = l.m.off_len;
+  a.off_cu = l.m.off_cu;
+  a.off_pcu = l.m.off_pcu;
+  a.off_tiles = l.m.off_tiles;
+  a.q = static_cast<const uint16_t*>(q);
+  a.k = static_cast<const uint16_t*>(k);
+  a.v = static_cast<const uint16_t*>(v);
+  a.o = static_cast<const uint16_t*>(o);
+  a.dout = static_cast<const uint16_t*>(dout);
+  a.lse = lse;
+  a.grid_hw = grid_hw;
+  a.text_len = text_len;
+  a.cs = cs;
+  a.qc = reinterpret_cast<uint16_t*>(ws + l.off_qc);
+  a.qt = reinterpret_cast<uint16_t*>(ws + l.off_qt);
+  a.oc = reinterpret_cast<uint16_t*>(ws + l.off_oc);
+  a.ot = reinterpret_cast<uint16_t*>(ws + l.off_ot);
+  a.kc = reinterpret_cast<uint16_t*>(ws + l.off_kc);
+  a.kt = reinterpret_cast<uint16_t*>(ws + l.off_kt);
+  a.vc = reinterpret_cast<uint16_t*>(ws + l.off_vc);
+  a.st = reinterpret_cast<float*>(ws + l.off_st);
+  a.dq = static_cast<uint16_t*>(dq);
+  a.dk = static_cast<uint16_t*>(dk);
+  a.dv = static_cast<uint16_t*>(dv);
+  a.heads = heads;
+  a.rows = l.m.rows;
+  a.tokens = tokens;
+  a.c_log2 = scale * LOG2E;
+  a.scale = scale;
+  return head_dim == 128 ? launch_bwd_t<128>(a, l, s, ev) : launch_bwd_t<64>(a, l, s, ev);
+}
+
+}  // namespace mf

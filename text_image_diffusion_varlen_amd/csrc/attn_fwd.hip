@@ -30,13 +30,10 @@
 #include <type_traits>
 
 #include "mf_common.h"
+#include "mfma_util.h"
 #include "rope_math.h"
 
 namespace mf {
-
-typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
-typedef float f32x16 __attribute__((ext_vector_type(16)));
-typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 
 struct AttnArgs {
   const char* ws;
@@ -49,59 +46,21 @@ struct AttnArgs {
   const void* kw;
   const void* vw;
   void* out;
+  float* lse;        // optional [heads][tokens] natural-log row sum-exp of the scaled scores
+  int64_t tokens;
   int32_t heads;
   int64_t rows;      // padded rows per head in the workspace
   float c_log2;      // softmax scale * log2(e)
 };
 
-__device__ inline uint32_t pack_bf16x2(float a, float b) {
-  typedef float f32x2 __attribute__((ext_vector_type(2)));
-  typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
-  const f32x2 v = {a, b};
-  const bf16x2 r = __builtin_convertvector(v, bf16x2);  // v_cvt_pk_bf16_f32, round to nearest even
-  return __builtin_bit_cast(uint32_t, r);
-}
-
-// Combine a value with the same register of lane ^ 32. v_permlane32_swap
-// exchanges the upper 32 lanes of its first operand with the lower 32 lanes of
-// its second; with both operands equal to x, every lane ends up holding x[l]
-// in one result and x[l ^ 32] in the other, so a symmetric combine of the two
-// results needs no lane test.
-__device__ inline float halves_max(float x) {
-  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
-  return __builtin_elementwise_maximum(__uint_as_float(r[0]), __uint_as_float(r[1]));
-}
-// acc + p0 + p1 for a packed bf16 pair (v_dot2_f32_bf16 against (1, 1)).
-__device__ inline float dot2_bf16_sum(uint32_t pair, float acc) {
-  typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
-  const bf16x2 one = {(__bf16)1.0f, (__bf16)1.0f};
-  return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, pair), one, acc, false);
-}
-__device__ inline float halves_sum(float x) {
-  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
-  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
-}
-
-typedef __attribute__((address_space(3))) void* lds_ptr_t;
-
 // Copies one chunk-major tile (CHUNKS 16-byte chunks) from the workspace into
-// LDS with gfx950 direct-to-LDS loads: each wave moves CHUNKS/ATTN_WAVES chunks, one
-// contiguous 1 KB per instruction, without passing through registers.
+// LDS with direct-to-LDS loads spread over the workgroup's waves.
 template <int CHUNKS>
 __device__ inline void tile_to_lds(const u32x4* __restrict__ src, u32x4* dst, int wave, int lane) {
-  constexpr int PER_WAVE = CHUNKS / ATTN_WAVES;
-  static_assert(PER_WAVE % 64 == 0, "whole 1 KB copies per wave");
-#pragma unroll
-  for (int i = 0; i < PER_WAVE / 64; ++i) {
-    const int c = wave * PER_WAVE + i * 64;
-    __builtin_amdgcn_global_load_lds(src + c + lane, (lds_ptr_t)(dst + c), 16, 0, 0);
-  }
+  copy_to_lds<CHUNKS, ATTN_WAVES>(src, dst, wave, lane);
 }
 
-__device__ inline void wait_tile_and_sync() {
-  __builtin_amdgcn_s_waitcnt(0xF70);  // vmcnt(0): this wave's direct-to-LDS copies landed
-  __syncthreads();
-}
+__device__ inline void wait_tile_and_sync() { wait_vm_and_sync(); }
 
 template <int D>
 struct Bf16Tile {
@@ -293,6 +252,9 @@ __global__ void __launch_bounds__(ATTN_THREADS, 2) attn_fwd_bf16_kernel(AttnArgs
   lsum = halves_sum(lsum);
   const float inv = 1.f / lsum;
   const int32_t qrel = qs + 32 * wave + l32;
+  // log-sum-exp in natural-log units: p = 2^(s c - m) / lsum, so
+  // ln sum_k e^(s_k * scale) = (m + log2 lsum) * ln 2.
+  if (a.lse && qrel < L && hf == 0) a.lse[int64_t(h) * a.tokens + cb + qrel] = (m + log2f(lsum)) * 0.6931471805599453f;
   if (qrel < L) {
     uint16_t* orow = static_cast<uint16_t*>(a.out) + (int64_t(cb + qrel) * heads + h) * D;
 #pragma unroll
@@ -375,6 +337,7 @@ __global__ void __launch_bounds__(ATTN_THREADS) attn_fwd_f32_kernel(AttnArgs a) 
     m = mnew;
   }
   const int32_t qrel = qs + 32 * wave + l32;
+  if (a.lse && qrel < L && hf == 0) a.lse[int64_t(h) * a.tokens + cb + qrel] = (m + log2f(lsum)) * 0.6931471805599453f;
   if (qrel < L) {
     float* orow = static_cast<float*>(a.out) + (int64_t(cb + qrel) * heads + h) * D + HD * hf;
     const float inv = 1.f / lsum;
@@ -384,8 +347,9 @@ __global__ void __launch_bounds__(ATTN_THREADS) attn_fwd_f32_kernel(AttnArgs a) 
 }
 
 hipError_t launch_attn_fwd(const char* ws, const WsLayout& l, const void* q, const int32_t* grid_hw,
-                           const int32_t* text_len, const float2* cs, void* out, int32_t heads,
-                           int32_t head_dim, bool bf16, float scale, hipStream_t s) {
+                           const int32_t* text_len, const float2* cs, void* out, float* lse,
+                           int64_t tokens, int32_t heads, int32_t head_dim, bool bf16, float scale,
+                           hipStream_t s) {
   AttnArgs a;
   a.ws = ws;
   a.q = q;
@@ -400,6 +364,8 @@ hipError_t launch_attn_fwd(const char* ws, const WsLayout& l, const void* q, con
   a.kw = ws + l.off_k;
   a.vw = ws + l.off_v;
   a.out = out;
+  a.lse = lse;
+  a.tokens = tokens;
   a.heads = heads;
   a.rows = l.rows;
   a.c_log2 = scale * 1.4426950408889634f;

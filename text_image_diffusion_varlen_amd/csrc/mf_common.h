@@ -74,6 +74,38 @@ __host__ __device__ inline WsLayout ws_layout(int64_t tokens, int32_t heads, int
   return l;
 }
 
+// Backward workspace: the same header, metadata and tile-table sections as
+// ws_layout, then seven bf16 buffers [heads][rows][head_dim] and per-row
+// statistics. Buffers (tiles of KTILE padded rows):
+//   qc  Q~ chunk-major          qt  Q~^T, MFMA-order, chunk-major
+//   oc  dO chunk-major          ot  dO^T, MFMA-order, chunk-major
+//   kc  K~ chunk-major          kt  K~^T, MFMA-order, chunk-major
+//   vc  V chunk-major
+//   st  f32 [heads][rows / KTILE][2 * KTILE]: per tile, log2-domain LSE of
+//       the KTILE rows (+inf on padding rows), then D = rowsum(dO * O).
+struct BwdLayout {
+  WsLayout m;  // metadata sections (its off_q / off_k / off_v / total are not used)
+  int64_t off_qc, off_qt, off_oc, off_ot, off_kc, off_kt, off_vc, off_st, total;
+};
+
+__host__ __device__ inline BwdLayout bwd_layout(int64_t tokens, int32_t heads, int32_t head_dim,
+                                                int32_t n_seg) {
+  BwdLayout b;
+  b.m = ws_layout(tokens, heads, head_dim, 2, n_seg);
+  const int64_t buf = round_up(int64_t(heads) * b.m.rows * head_dim * 2, 256);
+  int64_t o = b.m.off_q;
+  b.off_qc = o; o += buf;
+  b.off_qt = o; o += buf;
+  b.off_oc = o; o += buf;
+  b.off_ot = o; o += buf;
+  b.off_kc = o; o += buf;
+  b.off_kt = o; o += buf;
+  b.off_vc = o; o += buf;
+  b.off_st = o; o += round_up(int64_t(heads) * b.m.rows * 2 * 4, 256);
+  b.total = o;
+  return b;
+}
+
 // Position of token u (counted from the start of its sample): prompt tokens
 // at (0, 0), image token p = u - text_len at (p / w, p % w).
 __device__ inline void token_position(int32_t u, int32_t text_len, int32_t w, int32_t& row,
