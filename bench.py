@@ -186,6 +186,59 @@ def sampler_bench(steps: int, warmup: int):
     }
 
 
+def backward_bench(w, q, k, v, cu, grid, text, steps: int, warmup: int):
+    """Packed backward on the same batch: one step = mf_attn_packed_bwd (metadata,
+    prologue, dK/dV kernel, dQ kernel) with the forward's out and LSE resident.
+    TFLOP/s count the algorithmic 10 * sum_i L_i^2 * d * H (the five products of
+    the backward; the kernels' recomputation of S and dP is not counted)."""
+    import torch
+    from text_image_diffusion_varlen_amd import binding
+
+    out, lse = binding.attn_packed_lse(q, k, v, cu, grid, text)
+    gen = torch.Generator(device="cuda").manual_seed(5)
+    d_out = torch.randn(q.shape, generator=gen, device="cuda", dtype=torch.float32).to(q.dtype)
+    grads = tuple(torch.empty_like(q) for _ in range(3))
+    for _ in range(warmup):
+        binding.attn_packed_bwd(q, k, v, out, d_out, lse, cu, grid, text, grads=grads)
+    torch.cuda.synchronize()
+    start, stop = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    start.record()
+    for _ in range(steps):
+        binding.attn_packed_bwd(q, k, v, out, d_out, lse, cu, grid, text, grads=grads)
+    stop.record()
+    torch.cuda.synchronize()
+    ms = start.elapsed_time(stop) / steps
+    ev = HipEvents(4 * steps)
+    for st in range(steps):
+        binding.attn_packed_bwd_profiled(q, k, v, out, d_out, lse, cu, grid, text, ev.ev[4 * st:4 * st + 4],
+                                         grads=grads)
+    torch.cuda.synchronize()
+    if binding.get_device_error() != binding.MF_OK:
+        raise RuntimeError(binding.last_error())
+    stage = {"meta_pack": 0.0, "dkdv": 0.0, "dq": 0.0}
+    for st in range(steps):
+        b = 4 * st
+        stage["meta_pack"] += ev.elapsed_ms(b, b + 1) / steps
+        stage["dkdv"] += ev.elapsed_ms(b + 1, b + 2) / steps
+        stage["dq"] += ev.elapsed_ms(b + 2, b + 3) / steps
+    ev.close()
+    lengths = sample_lengths(w)
+    per = sum(L * L for L in lengths) * w.head_dim * w.heads
+    flops = 10.0 * per
+    # MFMA work the two kernels execute (S and dP are recomputed by the dQ kernel):
+    # dK/dV kernel S, dP, dV, dK = 8 L^2 d H; dQ kernel S, dP, dQ = 6 L^2 d H
+    kv_flops, q_flops = 8.0 * per, 6.0 * per
+    return {
+        "tflops": round(flops / (ms / 1e3) / 1e12, 2),
+        "ms_per_step": round(ms, 4),
+        "flop_per_step": flops,
+        "stages_ms": {k2: round(v2, 4) for k2, v2 in stage.items()},
+        "dkdv_executed_tflops": round(kv_flops / (stage["dkdv"] / 1e3) / 1e12, 1),
+        "dq_executed_tflops": round(q_flops / (stage["dq"] / 1e3) / 1e12, 1),
+        "pct_mfma_peak_executed": round(100.0 * (kv_flops + q_flops) / ((stage["dkdv"] + stage["dq"]) / 1e3) / PEAK["bf16"], 2),
+    }
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -196,6 +249,7 @@ def main():
     ap.add_argument("--cpu-budget", type=float, default=15.0, help="seconds of oracle work for cpu_baseline")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-sampler", action="store_true", help="skip the packed CFG Euler-step measurement")
+    ap.add_argument("--no-backward", action="store_true", help="skip the packed backward measurement")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="only run a plain device copy of 1 GiB (HBM-counter calibration for profiling)")
     args = ap.parse_args()
@@ -309,6 +363,8 @@ def main():
             "algorithmic_bytes": qkvo_bytes,
         },
     }
+    if w.dtype == "bf16" and not args.no_backward:
+        result["backward"] = backward_bench(w, q, k, v, cu, grid, text, args.steps, args.warmup)
     if not args.no_sampler:
         result["cfg_euler_step"] = sampler_bench(args.steps, args.warmup)
     if not args.no_cpu_baseline:

@@ -17,11 +17,13 @@
 //                    k, and writes Q~, dO, K~, V chunk-major, Q~^T, dO^T, K~^T
 //                    in MFMA order (as the forward's V~^T) and per-row
 //                    log2-domain LSE and D into the backward workspace.
-//   bwd_kv_kernel    one workgroup per (128 keys of a sample, head), 4 waves x
-//                    32 keys, keys resident in registers; loops over all the
-//                    sample's 64-query tiles (double-buffered in LDS):
-//                      S = Q~ K~^T, dP = dO V^T (lane = key, entries = queries),
-//                      dV^T += dO^T P, dK^T += Q~^T dX.
+//   bwd_kv_kernel    one workgroup per (128 keys of a sample, head), 8 waves:
+//                    each 32-key group has a dV wave (S, P, dV^T += dO^T P)
+//                    and a dK wave (dP, dX, dK^T += Q~^T dX) that receives P
+//                    through LDS, so two waves per SIMD fit in registers and
+//                    nothing is computed twice; keys resident in registers;
+//                    loops over all the sample's 64-query tiles
+//                    (double-buffered in LDS); lane = key, entries = queries.
 //   bwd_q_kernel     one workgroup per (256 queries of a sample, head), 8 waves
 //                    x 32 queries, queries resident in registers; loops over
 //                    the sample's 64-key tiles:
@@ -37,10 +39,12 @@
 namespace mf {
 
 constexpr float LOG2E = 1.4426950408889634f;
-constexpr int KV_WAVES = 4;                 // waves of bwd_kv_kernel, 32 keys each
-constexpr int KV_KEYS = 32 * KV_WAVES;      // keys per bwd_kv workgroup
+constexpr int KV_WAVES = 8;                 // waves of bwd_kv_kernel
+constexpr int KV_GROUPS = KV_WAVES / 2;     // 32-key groups: one dV wave and one dK wave each
+constexpr int KV_KEYS = 32 * KV_GROUPS;     // keys per bwd_kv workgroup
+constexpr int KV_SPLIT = QTILE / KV_KEYS;   // key blocks per entry of the tile table
 constexpr int Q_WAVES = QTILE / 32;         // waves of bwd_q_kernel, 32 queries each
-static_assert(QTILE == 2 * KV_KEYS, "two key blocks per entry of the tile table");
+static_assert(QTILE % KV_KEYS == 0, "whole key blocks per entry of the tile table");
 
 struct BwdArgs {
   const char* ws;
@@ -199,65 +203,94 @@ struct BwdTile {
   static constexpr int DBLK = D / 32;
 };
 
-// One 64-query tile for one wave's 32 keys. T: LDS tile set [qc | oc | qt | ot | stats].
+// One 64-query tile for one 32-key group, split over the group's two waves
+// and two phases with a workgroup barrier between them. T: LDS tile set
+// [qc | oc | qt | ot | stats]; pl: this group's P exchange slot (4 KB).
+// Entry e of a 32-query half qb of a product with lane = key l32 is query
+// 32qb + 8(e/4) + 4hf + e%4; k-step kk of half qb (queries 32qb + 16kk .. +15)
+// of the B operands takes entries 8kk .. 8kk+7, which are the queries the
+// MFMA-order tiles (qt, ot) hold in chunk 2(2qb + kk) + hf.
+//   dV wave, phase 1: S = Q~ K~^T, P = 2^(S c - lse2) packed to bf16, kept in
+//                     registers and stored to pl.
+//   dK wave, phase 1: dP = dO V^T (kept in registers).
+//   dV wave, phase 2: dV^T += dO^T P.
+//   dK wave, phase 2: P from pl, dX = P (dP - D) packed to bf16, dK^T += Q~^T dX.
 template <int D>
-__device__ inline void kv_step(const u32x4* T, const bf16x8 (&kreg)[D / 16], const bf16x8 (&vreg)[D / 16],
-                               f32x16 (&dk)[D / 32], f32x16 (&dv)[D / 32], float c, int hf, int l32) {
-  constexpr int CH = BwdTile<D>::CH, KSTEPS = BwdTile<D>::KSTEPS, DBLK = BwdTile<D>::DBLK;
-  const u32x4* qcl = T + hf * KTILE + l32;           // Q~ chunk (2ks+hf) of query 32qb + l32
-  const u32x4* ocl = T + CH + hf * KTILE + l32;      // dO, same layout
-  const u32x4* qtl = T + 2 * CH + hf * D + l32;      // Q~^T chunk (2ks+hf) of channel 32b + l32
-  const u32x4* otl = T + 3 * CH + hf * D + l32;      // dO^T, same layout
+__device__ inline void kv_phase1_dv(const u32x4* T, u32x4* pl, const bf16x8 (&kreg)[D / 16], u32x4 (&pk)[4],
+                                    float c, int hf, int l32, int lane) {
+  constexpr int KSTEPS = BwdTile<D>::KSTEPS, CH = BwdTile<D>::CH;
+  const u32x4* qcl = T + hf * KTILE + l32;
   const float* stl = reinterpret_cast<const float*>(T + 4 * CH);
+#pragma unroll
+  for (int qb = 0; qb < 2; ++qb) {
+    f32x16 s = {};
+#pragma unroll
+    for (int ks = 0; ks < KSTEPS; ++ks) s = mfma32(as_bf16x8(qcl[2 * KTILE * ks + 32 * qb]), kreg[ks], s);
+#pragma unroll
+    for (int g = 0; g < 4; ++g) {
+      const float4 l4 = *reinterpret_cast<const float4*>(stl + 32 * qb + 8 * g + 4 * hf);
+      const float p0 = __builtin_amdgcn_exp2f(__builtin_fmaf(s[4 * g], c, -l4.x));
+      const float p1 = __builtin_amdgcn_exp2f(__builtin_fmaf(s[4 * g + 1], c, -l4.y));
+      const float p2 = __builtin_amdgcn_exp2f(__builtin_fmaf(s[4 * g + 2], c, -l4.z));
+      const float p3 = __builtin_amdgcn_exp2f(__builtin_fmaf(s[4 * g + 3], c, -l4.w));
+      const int kk = 2 * qb + (g >> 1), slot = 2 * (g & 1);
+      pk[kk][slot] = pack_bf16x2(p0, p1);
+      pk[kk][slot + 1] = pack_bf16x2(p2, p3);
+    }
+  }
+#pragma unroll
+  for (int kk = 0; kk < 4; ++kk) pl[64 * kk + lane] = pk[kk];
+}
 
-  // S (queries x keys) and dP, two 32-query blocks each; lane = key l32,
-  // entry e of block qb = query 32qb + 8(e/4) + 4hf + e%4.
-  f32x16 s[2] = {}, dp[2] = {};
+template <int D>
+__device__ inline void kv_phase1_dk(const u32x4* T, const bf16x8 (&vreg)[D / 16], f32x16 (&dp)[2], int hf,
+                                    int l32) {
+  constexpr int KSTEPS = BwdTile<D>::KSTEPS, CH = BwdTile<D>::CH;
+  const u32x4* ocl = T + CH + hf * KTILE + l32;
+  dp[0] = dp[1] = f32x16{};
 #pragma unroll
   for (int ks = 0; ks < KSTEPS; ++ks) {
 #pragma unroll
-    for (int qb = 0; qb < 2; ++qb) {
-      s[qb] = mfma32(as_bf16x8(qcl[2 * KTILE * ks + 32 * qb]), kreg[ks], s[qb]);
-      dp[qb] = mfma32(as_bf16x8(ocl[2 * KTILE * ks + 32 * qb]), vreg[ks], dp[qb]);
-    }
+    for (int qb = 0; qb < 2; ++qb) dp[qb] = mfma32(as_bf16x8(ocl[2 * KTILE * ks + 32 * qb]), vreg[ks], dp[qb]);
   }
-  // P = 2^(S c - lse2), dX = P (dP - D); packed to bf16 as the B operands of
-  // the two products below: k-step ks (queries 16ks .. 16ks+15) takes entries
-  // 8(ks%2) .. +7 of block ks/2, which are the queries the MFMA-order tiles
-  // (qt, ot) hold in chunk 2ks + hf.
-  uint32_t pp[4][4], pd[4][4];
-#pragma unroll
-  for (int qb = 0; qb < 2; ++qb) {
-#pragma unroll
-    for (int g = 0; g < 4; ++g) {
-      const int q0 = 32 * qb + 8 * g + 4 * hf;
-      const float4 l4 = *reinterpret_cast<const float4*>(stl + q0);
-      const float4 d4 = *reinterpret_cast<const float4*>(stl + KTILE + q0);
-      const float lq[4] = {l4.x, l4.y, l4.z, l4.w};
-      const float dq[4] = {d4.x, d4.y, d4.z, d4.w};
-      float p[4], x[4];
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        p[i] = __builtin_amdgcn_exp2f(__builtin_fmaf(s[qb][4 * g + i], c, -lq[i]));
-        x[i] = p[i] * (dp[qb][4 * g + i] - dq[i]);
-      }
-      const int ks = 2 * qb + (g >> 1), slot = 2 * (g & 1);
-      pp[ks][slot] = pack_bf16x2(p[0], p[1]);
-      pp[ks][slot + 1] = pack_bf16x2(p[2], p[3]);
-      pd[ks][slot] = pack_bf16x2(x[0], x[1]);
-      pd[ks][slot + 1] = pack_bf16x2(x[2], x[3]);
-    }
-  }
-  // dV^T (channels x keys) += dO^T P;  dK^T += Q~^T dX.
+}
+
+template <int D>
+__device__ inline void kv_phase2_dv(const u32x4* T, const u32x4 (&pk)[4], f32x16 (&acc)[D / 32], int hf, int l32) {
+  constexpr int CH = BwdTile<D>::CH, DBLK = BwdTile<D>::DBLK;
+  const u32x4* otl = T + 3 * CH + hf * D + l32;
 #pragma unroll
   for (int ks = 0; ks < 4; ++ks) {
-    const bf16x8 p8 = __builtin_bit_cast(bf16x8, u32x4{pp[ks][0], pp[ks][1], pp[ks][2], pp[ks][3]});
-    const bf16x8 x8 = __builtin_bit_cast(bf16x8, u32x4{pd[ks][0], pd[ks][1], pd[ks][2], pd[ks][3]});
+    const bf16x8 p8 = as_bf16x8(pk[ks]);
 #pragma unroll
-    for (int b = 0; b < DBLK; ++b) {
-      dv[b] = mfma32(as_bf16x8(otl[2 * D * ks + 32 * b]), p8, dv[b]);
-      dk[b] = mfma32(as_bf16x8(qtl[2 * D * ks + 32 * b]), x8, dk[b]);
+    for (int b = 0; b < DBLK; ++b) acc[b] = mfma32(as_bf16x8(otl[2 * D * ks + 32 * b]), p8, acc[b]);
+  }
+}
+
+template <int D>
+__device__ inline void kv_phase2_dk(const u32x4* T, const u32x4* pl, const f32x16 (&dp)[2], f32x16 (&acc)[D / 32],
+                                    int hf, int l32, int lane) {
+  constexpr int CH = BwdTile<D>::CH, DBLK = BwdTile<D>::DBLK;
+  const u32x4* qtl = T + 2 * CH + hf * D + l32;
+  const float* stl = reinterpret_cast<const float*>(T + 4 * CH);
+#pragma unroll
+  for (int ks = 0; ks < 4; ++ks) {
+    const int qb = ks >> 1;
+    const u32x4 p = pl[64 * ks + lane];
+    uint32_t x[4];
+#pragma unroll
+    for (int gg = 0; gg < 2; ++gg) {
+      const int g = 2 * (ks & 1) + gg;
+      const float4 d4 = *reinterpret_cast<const float4*>(stl + KTILE + 32 * qb + 8 * g + 4 * hf);
+      const uint32_t w0 = p[2 * gg], w1 = p[2 * gg + 1];
+      x[2 * gg] = pack_bf16x2(__uint_as_float(w0 << 16) * (dp[qb][4 * g] - d4.x),
+                              __uint_as_float(w0 & 0xFFFF0000u) * (dp[qb][4 * g + 1] - d4.y));
+      x[2 * gg + 1] = pack_bf16x2(__uint_as_float(w1 << 16) * (dp[qb][4 * g + 2] - d4.z),
+                                  __uint_as_float(w1 & 0xFFFF0000u) * (dp[qb][4 * g + 3] - d4.w));
     }
+    const bf16x8 x8 = __builtin_bit_cast(bf16x8, u32x4{x[0], x[1], x[2], x[3]});
+#pragma unroll
+    for (int b = 0; b < DBLK; ++b) acc[b] = mfma32(as_bf16x8(qtl[2 * D * ks + 32 * b]), x8, acc[b]);
   }
 }
 
@@ -284,29 +317,32 @@ __device__ inline uint2 unrotate4(const float (&x)[4], int ch0, int32_t row, int
 }
 
 template <int D>
-__global__ void __launch_bounds__(64 * KV_WAVES, 1) bwd_kv_kernel(BwdArgs a) {
+__global__ void __launch_bounds__(64 * KV_WAVES, 2) bwd_kv_kernel(BwdArgs a) {
   constexpr int CH = BwdTile<D>::CH, KSTEPS = BwdTile<D>::KSTEPS, DBLK = BwdTile<D>::DBLK;
   constexpr int SET = 4 * CH + 2 * KTILE / 4;  // chunks of one LDS tile set (4 tiles + stats)
   const WsHeader* hdr = reinterpret_cast<const WsHeader*>(a.ws);
   const int32_t heads = a.heads;
   const int h = int(blockIdx.x % unsigned(heads));
   const int rest = int(blockIdx.x / unsigned(heads));
-  const int tile = rest >> 1;
+  const int tile = rest / KV_SPLIT;
   if (hdr->flag != FLAG_OK || tile >= hdr->n_tiles) return;
   const int2 td = reinterpret_cast<const int2*>(a.ws + a.off_tiles)[tile];
-  const int32_t seg = td.x, k0 = td.y + KV_KEYS * (rest & 1);
+  const int32_t seg = td.x, k0 = td.y + KV_KEYS * (rest % KV_SPLIT);
   const int32_t L = reinterpret_cast<const int32_t*>(a.ws + a.off_len)[seg];
   if (k0 >= L) return;
   const int32_t pb = reinterpret_cast<const int32_t*>(a.ws + a.off_pcu)[seg];
   const int32_t cb = reinterpret_cast<const int32_t*>(a.ws + a.off_cu)[seg];
   const int tid = threadIdx.x;
   const int wave = tid >> 6, lane = tid & 63, hf = lane >> 5, l32 = lane & 31;
+  // Waves [0, KV_GROUPS) accumulate dV, the others dK, of the same key groups.
+  const bool dv_wave = wave < KV_GROUPS;
+  const int group = dv_wave ? wave : wave - KV_GROUPS;
   const int64_t tile0 = (int64_t(h) * a.rows + pb) / KTILE;  // first KTILE tile of this (sample, head)
 
   // This lane's key as the B operand of S = Q~ K~^T and dP = dO V^T: key
-  // k0 + 32 wave + l32, channels 16ks + 8hf .. +7, read from the chunk-major
+  // k0 + 32 group + l32, channels 16ks + 8hf .. +7, read from the chunk-major
   // K~ and V tiles. Keys past the sample are zero (never stored).
-  const int32_t key = k0 + 32 * wave + l32;
+  const int32_t key = k0 + 32 * group + l32;
   bf16x8 kreg[KSTEPS], vreg[KSTEPS];
   {
     const int64_t r = tile0 * KTILE + key;
@@ -314,8 +350,8 @@ __global__ void __launch_bounds__(64 * KV_WAVES, 1) bwd_kv_kernel(BwdArgs a) {
     const u32x4* vp = reinterpret_cast<const u32x4*>(a.vc) + (r / KTILE) * CH + hf * KTILE + (r % KTILE);
 #pragma unroll
     for (int ks = 0; ks < KSTEPS; ++ks) {
-      kreg[ks] = key < L ? as_bf16x8(kp[2 * KTILE * ks]) : bf16x8{};
-      vreg[ks] = key < L ? as_bf16x8(vp[2 * KTILE * ks]) : bf16x8{};
+      kreg[ks] = key < L && dv_wave ? as_bf16x8(kp[2 * KTILE * ks]) : bf16x8{};
+      vreg[ks] = key < L && !dv_wave ? as_bf16x8(vp[2 * KTILE * ks]) : bf16x8{};
     }
   }
   __builtin_amdgcn_sched_barrier(0);
@@ -323,6 +359,8 @@ __global__ void __launch_bounds__(64 * KV_WAVES, 1) bwd_kv_kernel(BwdArgs a) {
   __builtin_amdgcn_sched_barrier(0);
 
   __shared__ u32x4 sets[2 * SET];
+  __shared__ u32x4 pex[KV_GROUPS * 4 * 64];  // P exchange: 4 KB per key group
+  u32x4* pl = pex + group * 4 * 64;
   const u32x4* qcg = reinterpret_cast<const u32x4*>(a.qc) + tile0 * CH;
   const u32x4* ocg = reinterpret_cast<const u32x4*>(a.oc) + tile0 * CH;
   const u32x4* qtg = reinterpret_cast<const u32x4*>(a.qt) + tile0 * CH;
@@ -337,35 +375,44 @@ __global__ void __launch_bounds__(64 * KV_WAVES, 1) bwd_kv_kernel(BwdArgs a) {
       __builtin_amdgcn_global_load_lds(stg + int64_t(j) * (2 * KTILE / 4) + lane, (lds_ptr_t)(dst + 4 * CH), 16, 0, 0);
   };
 
-  f32x16 dk[DBLK], dv[DBLK];
+  f32x16 acc[DBLK];
 #pragma unroll
-  for (int b = 0; b < DBLK; ++b) dk[b] = dv[b] = f32x16{};
+  for (int b = 0; b < DBLK; ++b) acc[b] = f32x16{};
   const int nqt = (L + KTILE - 1) / KTILE;
   load_set(0, sets);
   wait_vm_and_sync();
+  u32x4 pk[4];     // dV waves: this step's P (bf16), as the B operand of its four k-steps
+  f32x16 dp[2];    // dK waves: this step's dP, two 32-query halves
   for (int j = 0; j < nqt; ++j) {
     const u32x4* cur = sets + (j & 1) * SET;
     if (j + 1 < nqt) load_set(j + 1, sets + ((j + 1) & 1) * SET);
-    kv_step<D>(cur, kreg, vreg, dk, dv, a.c_log2, hf, l32);
-    wait_vm_and_sync();
+    if (dv_wave) kv_phase1_dv<D>(cur, pl, kreg, pk, a.c_log2, hf, l32, lane);
+    else kv_phase1_dk<D>(cur, vreg, dp, hf, l32);
+    __syncthreads();  // P of this step is in pl
+    if (dv_wave) kv_phase2_dv<D>(cur, pk, acc, hf, l32);
+    else kv_phase2_dk<D>(cur, pl, dp, acc, hf, l32, lane);
+    wait_vm_and_sync();  // next tile set landed; pl and the current set may be overwritten
   }
 
   // Epilogue: entry e of block b is channel 32b + 8(e/4) + 4hf + e%4 of this lane's key.
   if (key < L) {
-    int32_t row, col;
-    token_position(key, a.text_len[seg], a.grid_hw[2 * seg + 1], row, col);
+    int32_t row = 0, col = 0;
+    if (!dv_wave) token_position(key, a.text_len[seg], a.grid_hw[2 * seg + 1], row, col);
     const int64_t off = (int64_t(cb + key) * heads + h) * D;
 #pragma unroll
     for (int b = 0; b < DBLK; ++b) {
 #pragma unroll
       for (int g = 0; g < 4; ++g) {
         const int ch = 32 * b + 8 * g + 4 * hf;
-        const float xk[4] = {dk[b][4 * g], dk[b][4 * g + 1], dk[b][4 * g + 2], dk[b][4 * g + 3]};
-        *reinterpret_cast<uint2*>(a.dk + off + ch) = unrotate4<D>(xk, ch, row, col, a.scale, a.cs);
-        uint2 o;
-        o.x = pack_bf16x2(dv[b][4 * g], dv[b][4 * g + 1]);
-        o.y = pack_bf16x2(dv[b][4 * g + 2], dv[b][4 * g + 3]);
-        *reinterpret_cast<uint2*>(a.dv + off + ch) = o;
+        if (dv_wave) {
+          uint2 o;
+          o.x = pack_bf16x2(acc[b][4 * g], acc[b][4 * g + 1]);
+          o.y = pack_bf16x2(acc[b][4 * g + 2], acc[b][4 * g + 3]);
+          *reinterpret_cast<uint2*>(a.dv + off + ch) = o;
+        } else {
+          const float xk[4] = {acc[b][4 * g], acc[b][4 * g + 1], acc[b][4 * g + 2], acc[b][4 * g + 3]};
+          *reinterpret_cast<uint2*>(a.dk + off + ch) = unrotate4<D>(xk, ch, row, col, a.scale, a.cs);
+        }
       }
     }
   }
@@ -504,7 +551,8 @@ static hipError_t launch_bwd_t(const BwdArgs& a, const BwdLayout& l, hipStream_t
   hipLaunchKernelGGL(bwd_pack_kernel<D>, dim3(unsigned(l.m.rows / KTILE), unsigned(a.heads)), dim3(256), 0, s, a);
   if ((e = hipGetLastError()) != hipSuccess) return e;
   if (ev && (e = hipEventRecord(ev[0], s)) != hipSuccess) return e;
-  hipLaunchKernelGGL(bwd_kv_kernel<D>, dim3(unsigned(2 * l.m.n_tiles * a.heads)), dim3(64 * KV_WAVES), 0, s, a);
+  hipLaunchKernelGGL(bwd_kv_kernel<D>, dim3(unsigned(KV_SPLIT * l.m.n_tiles * a.heads)), dim3(64 * KV_WAVES), 0,
+                     s, a);
   if ((e = hipGetLastError()) != hipSuccess) return e;
   if (ev && (e = hipEventRecord(ev[1], s)) != hipSuccess) return e;
   hipLaunchKernelGGL(bwd_q_kernel<D>, dim3(unsigned(l.m.n_tiles * a.heads)), dim3(64 * Q_WAVES), 0, s, a);
