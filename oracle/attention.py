@@ -199,3 +199,48 @@ def joint_attention_backward(q, k, v, d_out, grid_hw, text_len, theta: float = r
     kr = rope.rope2d(k, pos, theta)
     dqr, dkr, dv = packed_attention_backward(qr, kr, v, d_out, cu, scale)
     return rope.rope2d_inverse(dqr, pos, theta), rope.rope2d_inverse(dkr, pos, theta), dv
+
+
+# ---------------------------------------------------------------- editing (frame-aware) variant
+#
+# Tech report, NR-MMDiT editing paragraph: an editing sample is the condition
+# followed by the source latents and the target latents, and the 2D RoPE is
+# extended with the image index f: every visual token sits at (h, w, f).
+# ``split`` gives the channels turned by row, column and frame (contiguous
+# blocks in that order; the pages do not fix it).
+
+
+def _positions_3d(grid_hw, text_len, frames):
+    cu = packing.cu_seqlens(grid_hw, text_len, frames)
+    pos3, _ = packing.token_positions_3d(grid_hw, text_len, frames)
+    return cu, pos3
+
+
+def joint_attention_3d(q, k, v, grid_hw, text_len, frames, split, theta: float = rope.DEFAULT_THETA,
+                       scale: float | None = None) -> np.ndarray:
+    """Packed joint attention of editing samples with frame-aware RoPE."""
+    cu, pos3 = _positions_3d(grid_hw, text_len, frames)
+    if int(cu[-1]) != np.shape(q)[0]:
+        raise ValueError("q has %d tokens, metadata describes %d" % (np.shape(q)[0], int(cu[-1])))
+    return packed_attention(rope.rope3d(q, pos3, split, theta), rope.rope3d(k, pos3, split, theta), v, cu, scale)
+
+
+def joint_attention_3d_lse(q, k, grid_hw, text_len, frames, split, theta: float = rope.DEFAULT_THETA,
+                           scale: float | None = None) -> np.ndarray:
+    """Row log-sum-exp [H, T] of ``joint_attention_3d``'s scaled scores."""
+    cu, pos3 = _positions_3d(grid_hw, text_len, frames)
+    qr, kr = rope.rope3d(q, pos3, split, theta), rope.rope3d(k, pos3, split, theta)
+    out = np.empty((np.shape(q)[1], np.shape(q)[0]), dtype=np.float64)
+    for i in range(cu.shape[0] - 1):
+        a, b = int(cu[i]), int(cu[i + 1])
+        out[:, a:b] = sample_attention_lse(qr[a:b], kr[a:b], scale).T
+    return out
+
+
+def joint_attention_3d_backward(q, k, v, d_out, grid_hw, text_len, frames, split,
+                                theta: float = rope.DEFAULT_THETA, scale: float | None = None):
+    """Gradients of ``joint_attention_3d`` with respect to the unrotated q, k and v."""
+    cu, pos3 = _positions_3d(grid_hw, text_len, frames)
+    qr, kr = rope.rope3d(q, pos3, split, theta), rope.rope3d(k, pos3, split, theta)
+    dqr, dkr, dv = packed_attention_backward(qr, kr, v, d_out, cu, scale)
+    return rope.rope3d_inverse(dqr, pos3, split, theta), rope.rope3d_inverse(dkr, pos3, split, theta), dv

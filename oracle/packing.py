@@ -16,26 +16,36 @@ Readings taken where the pages are silent:
 * the image grid is flattened row-major (row outer, column inner);
 * positions are zero-based integers with no centring or rescaling;
 * prompt tokens carry position (0, 0).
+
+Editing samples (tech report, NR-MMDiT editing paragraph): the sequence is
+the condition tau, then the latents of the source image(s), then the noisy
+target latents, and every visual token has a 3D position (h, w, f) with f the
+image index over the sources and the target. Readings: all images of a
+sample share its grid (h, w) (the paragraph keeps source-target spatial
+correspondence); frames are numbered 0, 1, ... in sequence order (sources
+first, the target last); prompt tokens sit at (0, 0, 0).
 """
 from __future__ import annotations
 
 import numpy as np
 
 
-def segment_lengths(grid_hw, text_len) -> np.ndarray:
-    """L_i = text_len_i + h_i * w_i for every sample (int64)."""
+def segment_lengths(grid_hw, text_len, frames=None) -> np.ndarray:
+    """L_i = text_len_i + f_i * h_i * w_i for every sample (int64); f_i = 1
+    (one image per sample) unless ``frames`` gives the images per sample."""
     g = np.asarray(grid_hw, dtype=np.int64).reshape(-1, 2)
     t = np.asarray(text_len, dtype=np.int64).reshape(-1)
-    if g.shape[0] != t.shape[0]:
-        raise ValueError("grid_hw and text_len disagree on the number of samples")
-    if (g < 1).any() or (t < 0).any():
-        raise ValueError("grid sides must be >= 1 and prompt lengths >= 0")
-    return t + g[:, 0] * g[:, 1]
+    f = np.ones_like(t) if frames is None else np.asarray(frames, dtype=np.int64).reshape(-1)
+    if g.shape[0] != t.shape[0] or f.shape[0] != t.shape[0]:
+        raise ValueError("grid_hw, text_len and frames disagree on the number of samples")
+    if (g < 1).any() or (t < 0).any() or (f < 1).any():
+        raise ValueError("grid sides and frame counts must be >= 1 and prompt lengths >= 0")
+    return t + f * g[:, 0] * g[:, 1]
 
 
-def cu_seqlens(grid_hw, text_len) -> np.ndarray:
+def cu_seqlens(grid_hw, text_len, frames=None) -> np.ndarray:
     """Per-sample cumulative offsets: cu[0] = 0, cu[i+1] = cu[i] + L_i (int32)."""
-    lengths = segment_lengths(grid_hw, text_len)
+    lengths = segment_lengths(grid_hw, text_len, frames)
     cu = np.zeros(lengths.shape[0] + 1, dtype=np.int64)
     for i, length in enumerate(lengths):
         cu[i + 1] = cu[i] + length
@@ -67,4 +77,31 @@ def token_positions(grid_hw, text_len):
         pos[start + n_text : start + n_text + h * w, 0] = p // w
         pos[start + n_text : start + n_text + h * w, 1] = p % w
         start += n_text + h * w
+    return pos, seg
+
+
+def token_positions_3d(grid_hw, text_len, frames):
+    """Per-token (row, col, frame) of a packed batch of editing samples.
+
+    Returns ``pos3`` int32 [T, 3] and ``seg_id`` int32 [T]. Token u of sample i
+    is a prompt token at (0, 0, 0) when u < text_len_i; otherwise it is visual
+    token p = u - text_len_i of image f = p // (h_i w_i), at row
+    (p mod h_i w_i) // w_i and column p mod w_i.
+    """
+    g = np.asarray(grid_hw, dtype=np.int64).reshape(-1, 2)
+    t = np.asarray(text_len, dtype=np.int64).reshape(-1)
+    f = np.asarray(frames, dtype=np.int64).reshape(-1)
+    lengths = segment_lengths(g, t, f)
+    pos = np.zeros((int(lengths.sum()), 3), dtype=np.int32)
+    seg = np.zeros(int(lengths.sum()), dtype=np.int32)
+    start = 0
+    for i in range(g.shape[0]):
+        h, w, n_text, n_img = int(g[i, 0]), int(g[i, 1]), int(t[i]), int(f[i])
+        seg[start : start + int(lengths[i])] = i
+        p = np.arange(n_img * h * w, dtype=np.int64)
+        a = start + n_text
+        pos[a : a + n_img * h * w, 0] = (p % (h * w)) // w
+        pos[a : a + n_img * h * w, 1] = p % w
+        pos[a : a + n_img * h * w, 2] = p // (h * w)
+        start += int(lengths[i])
     return pos, seg

@@ -88,3 +88,9 @@ def rope3d(x: np.ndarray, pos3: np.ndarray, split, theta: float = DEFAULT_THETA)
     """Apply frame-aware (row, col, frame) RoPE to x [T, H, d]."""
     x = np.asarray(x, dtype=np.float64)
     return _rotate_pairs(x, angles_3d(pos3, x.shape[-1], split, theta))
+
+
+def rope3d_inverse(x: np.ndarray, pos3: np.ndarray, split, theta: float = DEFAULT_THETA) -> np.ndarray:
+    """Transpose (= inverse) of ``rope3d``: rotation by the negated angles."""
+    x = np.asarray(x, dtype=np.float64)
+    return _rotate_pairs(x, -angles_3d(pos3, x.shape[-1], split, theta))

@@ -499,3 +499,122 @@ def test_packed_cfg_euler_special_cases():
     # the step is affine in dt
     d1, d2 = step(z, v, *args, 3.0, 0.25) - z, step(z, v, *args, 3.0, 0.75) - z
     np.testing.assert_allclose(3 * d1, d2, atol=1e-13)
+
+
+# ---------------------------------------------------------------- frame-aware (editing) variant
+
+
+def test_positions_3d_enumeration():
+    grid, text, frames = [[2, 3], [1, 1], [3, 2]], [2, 0, 1], [2, 3, 1]
+    pos3, seg = packing.token_positions_3d(grid, text, frames)
+    exp, eseg = [], []
+    for i, ((h, w), t, f) in enumerate(zip(grid, text, frames)):
+        for _ in range(t):
+            exp.append((0, 0, 0))
+            eseg.append(i)
+        for fr in range(f):
+            for r in range(h):
+                for c in range(w):
+                    exp.append((r, c, fr))
+                    eseg.append(i)
+    assert pos3.tolist() == [list(x) for x in exp]
+    assert seg.tolist() == eseg
+    assert packing.cu_seqlens(grid, text, frames).tolist() == [0, 14, 17, 24]
+    # one image per sample: the 2D positions at frame 0
+    p2, s2 = packing.token_positions(grid, text)
+    p1, s1 = packing.token_positions_3d(grid, text, [1, 1, 1])
+    assert np.array_equal(p1[:, :2], p2) and not p1[:, 2].any() and np.array_equal(s1, s2)
+
+
+@pytest.mark.parametrize("split", [(4, 6, 6), (8, 4, 4), (6, 6, 4)])
+def test_rope3d_is_complex_rotation(split):
+    d = 16
+    rng = np.random.default_rng(40)
+    x = rng.standard_normal((5, 2, d))
+    p3 = rng.integers(0, 40, size=(5, 3))
+    y = rope.rope3d(x, p3, split)
+    bounds = np.cumsum([0] + list(split))
+    for t in range(5):
+        for a in range(3):
+            m = split[a]
+            for j in range(m // 2):
+                ch = bounds[a] + 2 * j
+                ang = p3[t, a] * 10000.0 ** (-2.0 * j / m)
+                z = (x[t, :, ch] + 1j * x[t, :, ch + 1]) * np.exp(1j * ang)
+                np.testing.assert_allclose(y[t, :, ch], z.real, atol=1e-12)
+                np.testing.assert_allclose(y[t, :, ch + 1], z.imag, atol=1e-12)
+    np.testing.assert_allclose(rope.rope3d_inverse(y, p3, split), x, atol=1e-12)
+
+
+def test_rope3d_relative_in_every_axis():
+    rng = np.random.default_rng(41)
+    q, k = rng.standard_normal((2, 1, 1, 24))
+    for delta in ([0, 0, 3], [2, 5, 0], [7, 1, 9]):
+        p, pp = np.array([[3, 4, 1]]), np.array([[1, 9, 2]])
+        a = np.sum(rope.rope3d(q, p, (8, 8, 8)) * rope.rope3d(k, pp, (8, 8, 8)))
+        b = np.sum(rope.rope3d(q, p + delta, (8, 8, 8)) * rope.rope3d(k, pp + delta, (8, 8, 8)))
+        assert abs(a - b) < 1e-12
+
+
+def test_joint_attention_3d_reduces_to_2d():
+    grid, text = [[3, 4], [2, 2]], [5, 0]
+    rng = np.random.default_rng(42)
+    T = 5 + 12 + 4
+    q, k, v = (rng.standard_normal((T, 2, 8)) for _ in range(3))
+    a = attention.joint_attention(q, k, v, grid, text)
+    b = attention.joint_attention_3d(q, k, v, grid, text, [1, 1], (4, 4, 0))
+    np.testing.assert_allclose(a, b, atol=1e-12)
+
+
+def test_joint_attention_3d_brute_force():
+    """Output and LSE of a two-image editing sample against pure-Python loops
+    (complex rotation per channel pair, explicit softmax)."""
+    grid, text, frames, split = [[2, 2], [1, 3]], [2, 1], [2, 3], (2, 2, 4)
+    d, H = 8, 1
+    rng = np.random.default_rng(43)
+    T = 2 + 8 + 1 + 9
+    q, k, v = (rng.standard_normal((T, H, d)) for _ in range(3))
+    out = attention.joint_attention_3d(q, k, v, grid, text, frames, split)
+    lse = attention.joint_attention_3d_lse(q, k, grid, text, frames, split)
+
+    def rot(x, p):
+        res, base = [], 0
+        for a, m in enumerate(split):
+            for j in range(m // 2):
+                z = complex(x[base + 2 * j], x[base + 2 * j + 1]) * complex(
+                    math.cos(p[a] * 10000.0 ** (-2 * j / m)), math.sin(p[a] * 10000.0 ** (-2 * j / m)))
+                res += [z.real, z.imag]
+            base += m
+        return res
+
+    start = 0
+    for (h, w), t, f in zip(grid, text, frames):
+        pos = [(0, 0, 0)] * t + [(r, c, fr) for fr in range(f) for r in range(h) for c in range(w)]
+        n = len(pos)
+        qr = [rot(q[start + i, 0], pos[i]) for i in range(n)]
+        kr = [rot(k[start + i, 0], pos[i]) for i in range(n)]
+        for i in range(n):
+            s = [sum(a * b for a, b in zip(qr[i], kr[j])) / math.sqrt(d) for j in range(n)]
+            m = max(s)
+            e = [math.exp(x - m) for x in s]
+            z = sum(e)
+            assert abs(lse[0, start + i] - (m + math.log(z))) < 1e-12
+            for c in range(d):
+                ref = sum(e[j] * v[start + j, 0, c] for j in range(n)) / z
+                assert abs(out[start + i, 0, c] - ref) < 1e-12
+        start += n
+
+
+def test_attention_3d_backward_finite_differences():
+    grid, text, frames, split = [[1, 2], [2, 1]], [1, 0], [2, 2], (2, 2, 4)
+    T = 5 + 4
+    rng = np.random.default_rng(44)
+    q, k, v, w = (rng.standard_normal((T, 1, 8)) for _ in range(4))
+
+    def loss(qq, kk, vv):
+        return float(np.sum(attention.joint_attention_3d(qq, kk, vv, grid, text, frames, split) * w))
+
+    dq, dk, dv = attention.joint_attention_3d_backward(q, k, v, w, grid, text, frames, split)
+    np.testing.assert_allclose(dq, _numeric_grad(lambda x: loss(x, k, v), q), atol=1e-7)
+    np.testing.assert_allclose(dk, _numeric_grad(lambda x: loss(q, x, v), k), atol=1e-7)
+    np.testing.assert_allclose(dv, _numeric_grad(lambda x: loss(q, k, x), v), atol=1e-7)
