@@ -37,6 +37,10 @@ DESCRIPTIONS = {
     "mixed": "5 mixed-aspect images (32x128, 128x32, 48x84, 64x64, 32x32 grids) + prompts of 77-256 tokens, 24 heads x 128, bf16",
     "2048sq": "one 2048x2048 image (128x128 grid) + 256 prompt tokens, L=16640, 24 heads x 128, bf16",
     "train65k": "training-style packed block under a 65536-token budget, 24 heads x 128, bf16",
+    "edit1024": "one 1024x1024 edit: 256-token instruction + source and target 64x64 grids (frames 0, 1), "
+                "L=8448, frame-aware RoPE split 48/48/32, 24 heads x 128, bf16",
+    "edit_mixed": "three edits (32x128 x2 frames, 64x64 x3, 48x84 x2) + instructions of 77-256 tokens, "
+                  "frame-aware RoPE split 48/48/32, 24 heads x 128, bf16",
 }
 
 
@@ -88,7 +92,8 @@ class HipEvents:
 
 
 def sample_lengths(w):
-    return (w.text_len.astype("int64") + w.grid_hw[:, 0].astype("int64") * w.grid_hw[:, 1]).tolist()
+    f = 1 if w.frames is None else w.frames.astype("int64")
+    return (w.text_len.astype("int64") + f * w.grid_hw[:, 0].astype("int64") * w.grid_hw[:, 1]).tolist()
 
 
 def cpu_baseline(w, budget_s: float):
@@ -108,7 +113,11 @@ def cpu_baseline(w, budget_s: float):
     heads = 0
     while heads < w.heads:
         h = slice(heads, heads + 1)
-        attention.joint_attention(w.q[:, h], w.k[:, h], w.v[:, h], w.grid_hw, w.text_len)
+        if w.frames is None:
+            attention.joint_attention(w.q[:, h], w.k[:, h], w.v[:, h], w.grid_hw, w.text_len)
+        else:
+            attention.joint_attention_3d(w.q[:, h], w.k[:, h], w.v[:, h], w.grid_hw, w.text_len, w.frames,
+                                         w.rope_split)
         heads += 1
         if time.perf_counter() - t0 > budget_s:
             break
@@ -186,7 +195,7 @@ def sampler_bench(steps: int, warmup: int):
     }
 
 
-def backward_bench(w, q, k, v, cu, grid, text, steps: int, warmup: int):
+def backward_bench(w, q, k, v, cu, grid, text, steps: int, warmup: int, frames=None):
     """Packed backward on the same batch: one step = mf_attn_packed_bwd (metadata,
     prologue, dK/dV kernel, dQ kernel) with the forward's out and LSE resident.
     TFLOP/s count the algorithmic 10 * sum_i L_i^2 * d * H (the five products of
@@ -194,20 +203,36 @@ def backward_bench(w, q, k, v, cu, grid, text, steps: int, warmup: int):
     import torch
     from text_image_diffusion_varlen_amd import binding
 
-    out, lse = binding.attn_packed_lse(q, k, v, cu, grid, text)
+    if frames is None:
+        out, lse = binding.attn_packed_lse(q, k, v, cu, grid, text)
+    else:
+        out, lse = binding.attn_packed_3d(q, k, v, cu, grid, text, frames, w.rope_split, lse=True)
     gen = torch.Generator(device="cuda").manual_seed(5)
     d_out = torch.randn(q.shape, generator=gen, device="cuda", dtype=torch.float32).to(q.dtype)
     grads = tuple(torch.empty_like(q) for _ in range(3))
+
+    def bwd():
+        if frames is None:
+            binding.attn_packed_bwd(q, k, v, out, d_out, lse, cu, grid, text, grads=grads)
+        else:
+            binding.attn_packed_3d_bwd(q, k, v, out, d_out, lse, cu, grid, text, frames, w.rope_split, grads=grads)
     for _ in range(warmup):
-        binding.attn_packed_bwd(q, k, v, out, d_out, lse, cu, grid, text, grads=grads)
+        bwd()
     torch.cuda.synchronize()
     start, stop = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     start.record()
     for _ in range(steps):
-        binding.attn_packed_bwd(q, k, v, out, d_out, lse, cu, grid, text, grads=grads)
+        bwd()
     stop.record()
     torch.cuda.synchronize()
     ms = start.elapsed_time(stop) / steps
+    lengths = sample_lengths(w)
+    per = sum(L * L for L in lengths) * w.head_dim * w.heads
+    if frames is not None:
+        if binding.get_device_error() != binding.MF_OK:
+            raise RuntimeError(binding.last_error())
+        return {"tflops": round(10.0 * per / (ms / 1e3) / 1e12, 2), "ms_per_step": round(ms, 4),
+                "flop_per_step": 10.0 * per}
     ev = HipEvents(4 * steps)
     for st in range(steps):
         binding.attn_packed_bwd_profiled(q, k, v, out, d_out, lse, cu, grid, text, ev.ev[4 * st:4 * st + 4],
@@ -222,8 +247,6 @@ def backward_bench(w, q, k, v, cu, grid, text, steps: int, warmup: int):
         stage["dkdv"] += ev.elapsed_ms(b + 1, b + 2) / steps
         stage["dq"] += ev.elapsed_ms(b + 2, b + 3) / steps
     ev.close()
-    lengths = sample_lengths(w)
-    per = sum(L * L for L in lengths) * w.head_dim * w.heads
     flops = 10.0 * per
     # MFMA work the two kernels execute (S and dP are recomputed by the dQ kernel):
     # dK/dV kernel S, dP, dV, dK = 8 L^2 d H; dQ kernel S, dP, dQ = 6 L^2 d H
@@ -276,12 +299,17 @@ def main():
         print(json.dumps({"calibrate_copy_bytes_read": n, "calibrate_copy_bytes_written": n,
                           "dispatches": max(args.steps, 1)}), flush=True)
         return
-    w = workloads.make_workload(args.config, seed=args.seed)
+    edit = args.config in workloads.EDIT_CONFIGS
+    w = workloads.make_edit(args.config, seed=args.seed) if edit else workloads.make_workload(args.config, seed=args.seed)
     dt = torch.bfloat16 if w.dtype == "bf16" else torch.float32
     q, k, v = (torch.from_numpy(x).to(dt).cuda() for x in (w.q, w.k, w.v))
     grid = torch.from_numpy(w.grid_hw).cuda()
     text = torch.from_numpy(w.text_len).cuda()
-    cu, _, _ = binding.build_metadata(grid, text, w.tokens)
+    if edit:
+        frames = torch.from_numpy(w.frames).cuda()
+        cu, _, _ = binding.build_metadata_3d(grid, text, frames, w.tokens)
+    else:
+        cu, _, _ = binding.build_metadata(grid, text, w.tokens)
     out = torch.empty_like(q)
     torch.cuda.synchronize()
     if binding.get_device_error() != binding.MF_OK:
@@ -292,8 +320,14 @@ def main():
     elem = 2 if w.dtype == "bf16" else 4
     qkvo_bytes = 4.0 * w.tokens * w.heads * w.head_dim * elem
 
+    if edit:
+        def step():
+            binding.attn_packed_3d(q, k, v, cu, grid, text, frames, w.rope_split, out=out)
+    else:
+        def step():
+            binding.attn_packed(q, k, v, cu, grid, text, out=out)
     for _ in range(args.warmup):
-        binding.attn_packed(q, k, v, cu, grid, text, out=out)
+        step()
     torch.cuda.synchronize()
 
     # Timed region: K whole steps, torch events on the stream the library launches on.
@@ -301,25 +335,29 @@ def main():
     torch.cuda.synchronize()
     start.record()
     for _ in range(args.steps):
-        binding.attn_packed(q, k, v, cu, grid, text, out=out)
+        step()
     stop.record()
     torch.cuda.synchronize()
     ms = start.elapsed_time(stop) / args.steps
     if binding.get_device_error() != binding.MF_OK:
         raise RuntimeError(binding.last_error())
 
-    # Per-kernel durations: the same calls with HIP events between the three kernels.
-    ev = HipEvents(4 * args.steps)
-    for s in range(args.steps):
-        binding.attn_packed_profiled(q, k, v, cu, grid, text, ev.ev[4 * s : 4 * s + 4], out=out)
-    torch.cuda.synchronize()
-    stage = {"meta": 0.0, "rope_pack": 0.0, "attn": 0.0}
-    for s in range(args.steps):
-        b = 4 * s
-        stage["meta"] += ev.elapsed_ms(b, b + 1) / args.steps
-        stage["rope_pack"] += ev.elapsed_ms(b + 1, b + 2) / args.steps
-        stage["attn"] += ev.elapsed_ms(b + 2, b + 3) / args.steps
-    ev.close()
+    # Per-kernel durations: the same calls with HIP events between the three
+    # kernels (2D path; the frame-aware batches report the whole step).
+    if edit:
+        stage = {"meta": 0.0, "rope_pack": 0.0, "attn": ms}
+    else:
+        ev = HipEvents(4 * args.steps)
+        for s in range(args.steps):
+            binding.attn_packed_profiled(q, k, v, cu, grid, text, ev.ev[4 * s : 4 * s + 4], out=out)
+        torch.cuda.synchronize()
+        stage = {"meta": 0.0, "rope_pack": 0.0, "attn": 0.0}
+        for s in range(args.steps):
+            b = 4 * s
+            stage["meta"] += ev.elapsed_ms(b, b + 1) / args.steps
+            stage["rope_pack"] += ev.elapsed_ms(b + 1, b + 2) / args.steps
+            stage["attn"] += ev.elapsed_ms(b + 2, b + 3) / args.steps
+        ev.close()
 
     attn_s = stage["attn"] / 1e3
     achieved = flops / attn_s
@@ -351,9 +389,10 @@ def main():
         "pct_mfma_peak": round(100.0 * flops / (ms / 1e3) / PEAK[w.dtype], 2),
         "tokens_per_s": round(w.tokens / (ms / 1e3), 1),
         "stages_ms": {k2: round(v2, 4) for k2, v2 in stage.items()},
-        "rope_pack_gbps": round(rope_bytes / (stage["rope_pack"] / 1e3) / 1e9, 1),
+        "rope_pack_gbps": round(rope_bytes / (stage["rope_pack"] / 1e3) / 1e9, 1) if not edit else None,
         "roofline": {
-            "kernel": f"attn_fwd_{w.dtype}_kernel<{w.head_dim}>",
+            "kernel": f"attn_fwd_{w.dtype}_kernel<{w.head_dim}, {'true' if edit else 'false'}>"
+                      + (" (whole step: no per-kernel events on the frame-aware path)" if edit else ""),
             "bound": "mfma" if w.dtype == "bf16" else "alu",
             "achieved": round(achieved / 1e12, 2),
             "peak": PEAK[w.dtype] / 1e12,
@@ -364,7 +403,8 @@ def main():
         },
     }
     if w.dtype == "bf16" and not args.no_backward:
-        result["backward"] = backward_bench(w, q, k, v, cu, grid, text, args.steps, args.warmup)
+        result["backward"] = backward_bench(w, q, k, v, cu, grid, text, args.steps, args.warmup,
+                                            frames if edit else None)
     if not args.no_sampler:
         result["cfg_euler_step"] = sampler_bench(args.steps, args.warmup)
     if not args.no_cpu_baseline:

@@ -173,6 +173,53 @@ int mf_attn_packed_bwd_profiled(const void* q, const void* k, const void* v, con
 size_t mf_bwd_workspace_bytes(int64_t total_tokens, int32_t heads, int32_t head_dim, int32_t n_seg);
 
 /*
+ * Frame-aware variants for editing samples. Source: Mage-Flow tech report,
+ * NR-MMDiT section, editing paragraph: the sequence of an editing sample is
+ * the condition, then the source image latents, then the target latents, and
+ * the 2D RoPE gains the image index f, so every visual token sits at
+ * (h, w, f). Readings (the pages fix neither): all images of a sample share
+ * its grid; frames are numbered 0, 1, ... in sequence order; prompt tokens
+ * sit at (0, 0, 0); the head dimension is split into three contiguous channel
+ * blocks turned by row, column and frame, each with its own frequency ladder
+ * theta^(-2j/m) (m = channels of the block), adjacent pairs as in 2D.
+ *   frames      device int32 [n_seg]: images per sample, 1 .. 512
+ *               (L_i = text_len_i + frames_i * h_i * w_i)
+ *   split_row, split_col, split_frame  host: channels per block, even, >= 0,
+ *               summing to head_dim; (head_dim/2, head_dim/2, 0) with all
+ *               frames 1 gives exactly mf_attn_packed's result
+ *   lse         optional (NULL allowed) device float [heads][total_tokens]
+ * Everything else as mf_attn_packed / mf_attn_packed_lse.
+ */
+int mf_attn_packed_3d(const void* q, const void* k, const void* v, const int32_t* cu_seqlens,
+                      const int32_t* grid_hw, const int32_t* text_len, const int32_t* frames, int32_t split_row,
+                      int32_t split_col, int32_t split_frame, void* out, float* lse, int32_t n_seg,
+                      int64_t total_tokens, int32_t heads, int32_t head_dim, int32_t dtype, hipStream_t stream);
+
+/* Backward of mf_attn_packed_3d (lse required), as mf_attn_packed_bwd. */
+int mf_attn_packed_3d_bwd(const void* q, const void* k, const void* v, const void* out, const void* d_out,
+                          const float* lse, const int32_t* cu_seqlens, const int32_t* grid_hw,
+                          const int32_t* text_len, const int32_t* frames, int32_t split_row, int32_t split_col,
+                          int32_t split_frame, void* dq, void* dk, void* dv, int32_t n_seg, int64_t total_tokens,
+                          int32_t heads, int32_t head_dim, int32_t dtype, hipStream_t stream);
+
+/*
+ * Metadata of editing samples: as mf_build_metadata with frames, and pos_out
+ * device int32 [total_tokens][3] = (row, col, frame).
+ */
+int mf_build_metadata_3d(int32_t n_seg, const int32_t* grid_hw, const int32_t* text_len, const int32_t* frames,
+                         int32_t* cu_seqlens_out, int32_t* pos_out, int32_t* seg_id_out, int64_t total_tokens,
+                         hipStream_t stream);
+
+/*
+ * Frame-aware RoPE alone: x_out = R(pos) x_in with pos device int32
+ * [total_tokens][3] = (row, col, frame), each in [0, 512), and the channel
+ * split above. Otherwise as mf_rope_2d.
+ */
+int mf_rope_3d(const void* x_in, void* x_out, const int32_t* pos, int64_t total_tokens, int32_t heads,
+               int32_t head_dim, int32_t dtype, float theta, int32_t split_row, int32_t split_col,
+               int32_t split_frame, hipStream_t stream);
+
+/*
  * Packing metadata alone (same conventions as above).
  *   grid_hw, text_len  device int32 inputs
  *   cu_seqlens_out     device int32 [n_seg + 1]

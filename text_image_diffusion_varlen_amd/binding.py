@@ -50,6 +50,10 @@ def _declare(lib):
         "mf_attn_packed_bwd": ([P] * 12 + [I32, I64, I32, I32, I32, P], ctypes.c_int),
         "mf_attn_packed_bwd_profiled": ([P] * 12 + [I32, I64, I32, I32, I32, P, P], ctypes.c_int),
         "mf_bwd_workspace_bytes": ([I64, I32, I32, I32], SZ),
+        "mf_attn_packed_3d": ([P] * 7 + [I32, I32, I32, P, P, I32, I64, I32, I32, I32, P], ctypes.c_int),
+        "mf_attn_packed_3d_bwd": ([P] * 10 + [I32, I32, I32, P, P, P, I32, I64, I32, I32, I32, P], ctypes.c_int),
+        "mf_build_metadata_3d": ([I32, P, P, P, P, P, P, I64, P], ctypes.c_int),
+        "mf_rope_3d": ([P, P, P, I64, I32, I32, I32, F, I32, I32, I32, P], ctypes.c_int),
         "mf_build_metadata": ([I32, P, P, P, P, P, I64, P], ctypes.c_int),
         "mf_rope_2d": ([P, P, P, I64, I32, I32, I32, F, P], ctypes.c_int),
         "mf_rf_cfg_euler_step": ([P, P, P, P, P, I32, I64, P, P, I32, I64, I32, I32, F, F, P], ctypes.c_int),
@@ -216,6 +220,80 @@ def attn_packed_bwd_profiled(q, k, v, out, d_out, lse, cu_seqlens, grid_hw, text
                                              _ptr(dk), _ptr(dv), n, T, H, D, _DTYPES[q.dtype],
                                              ctypes.cast(arr, ctypes.c_void_p), _stream(stream)))
     return dq, dk, dv
+
+
+def _split(split, head_dim):
+    split = tuple(int(x) for x in split)
+    if len(split) != 3:
+        raise ValueError("split must have three entries (row, col, frame)")
+    return split
+
+
+def attn_packed_3d(q, k, v, cu_seqlens, grid_hw, text_len, frames, split, out=None, lse=False, stream=None):
+    """Frame-aware packed attention (mf_attn_packed_3d). Returns out, or (out, lse) when lse is True
+    or a [H, T] float32 tensor."""
+    out, n, T, H, D = _attn_args(q, k, v, cu_seqlens, grid_hw, text_len, out)
+    _need(frames, "frames", torch.int32, 1)
+    if frames.shape[0] != n:
+        raise ValueError("frames must be [n]")
+    sr, sc, sf = _split(split, D)
+    want = lse is not False and lse is not None
+    if lse is True:
+        lse = torch.empty((H, T), dtype=torch.float32, device=q.device)
+    if want:
+        _need(lse, "lse", torch.float32, 2)
+        if lse.shape != (H, T):
+            raise ValueError("lse must be [heads, tokens]")
+    _check(lib().mf_attn_packed_3d(_ptr(q), _ptr(k), _ptr(v), _ptr(cu_seqlens), _ptr(grid_hw), _ptr(text_len),
+                                   _ptr(frames), sr, sc, sf, _ptr(out), _ptr(lse) if want else None, n, T, H, D,
+                                   _DTYPES[q.dtype], _stream(stream)))
+    return (out, lse) if want else out
+
+
+def attn_packed_3d_bwd(q, k, v, out, d_out, lse, cu_seqlens, grid_hw, text_len, frames, split, grads=None,
+                       stream=None):
+    """Backward of the frame-aware attention (mf_attn_packed_3d_bwd). Returns (dq, dk, dv)."""
+    (dq, dk, dv), n, T, H, D = _bwd_args(q, k, v, out, d_out, lse, cu_seqlens, grid_hw, text_len, grads)
+    _need(frames, "frames", torch.int32, 1)
+    sr, sc, sf = _split(split, D)
+    _check(lib().mf_attn_packed_3d_bwd(_ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(d_out), _ptr(lse),
+                                       _ptr(cu_seqlens), _ptr(grid_hw), _ptr(text_len), _ptr(frames), sr, sc, sf,
+                                       _ptr(dq), _ptr(dk), _ptr(dv), n, T, H, D, _DTYPES[q.dtype],
+                                       _stream(stream)))
+    return dq, dk, dv
+
+
+def build_metadata_3d(grid_hw, text_len, frames, total_tokens: int, stream=None):
+    """(cu_seqlens [n+1], pos [T,3], seg_id [T]) for editing samples (mf_build_metadata_3d)."""
+    _need(grid_hw, "grid_hw", torch.int32, 2)
+    _need(text_len, "text_len", torch.int32, 1)
+    _need(frames, "frames", torch.int32, 1)
+    n = grid_hw.shape[0]
+    dev = grid_hw.device
+    cu = torch.empty(n + 1, dtype=torch.int32, device=dev)
+    pos = torch.empty((total_tokens, 3), dtype=torch.int32, device=dev)
+    seg = torch.empty(total_tokens, dtype=torch.int32, device=dev)
+    _check(lib().mf_build_metadata_3d(n, _ptr(grid_hw), _ptr(text_len), _ptr(frames), _ptr(cu), _ptr(pos),
+                                      _ptr(seg), total_tokens, _stream(stream)))
+    return cu, pos, seg
+
+
+def rope_3d(x, pos, split, theta: float = ROPE_THETA, out=None, stream=None):
+    """Frame-aware RoPE of x [T, H, d] at pos [T, 3] (mf_rope_3d). Returns out."""
+    _need(x, "x", ndim=3)
+    _need(pos, "pos", torch.int32, 2)
+    if x.dtype not in _DTYPES:
+        raise ValueError("x must be bfloat16 or float32")
+    if out is None:
+        out = torch.empty_like(x)
+    _need(out, "out", x.dtype, 3)
+    T, H, D = x.shape
+    if pos.shape != (T, 3) or out.shape != x.shape:
+        raise ValueError("shape mismatch")
+    sr, sc, sf = _split(split, D)
+    _check(lib().mf_rope_3d(_ptr(x), _ptr(out), _ptr(pos), T, H, D, _DTYPES[x.dtype], float(theta), sr, sc, sf,
+                            _stream(stream)))
+    return out
 
 
 def build_metadata(grid_hw, text_len, total_tokens: int, stream=None):

@@ -14,33 +14,36 @@
 #include <map>
 #include <mutex>
 #include <string>
+#include <tuple>
 #include <utility>
 #include <vector>
 
 #include "mf_attn.h"
 #include "mf_common.h"
+#include "rope_math.h"
 
 namespace mf {
-hipError_t launch_meta(const int32_t* grid_hw, const int32_t* text_len, const int32_t* cu_in,
-                       int32_t n, int64_t tokens, char* ws, const WsLayout& l, hipStream_t s);
-hipError_t launch_build_metadata(const int32_t* grid_hw, const int32_t* text_len, int32_t n,
-                                 int64_t tokens, int32_t* cu_out, int32_t* pos, int32_t* seg_id,
+hipError_t launch_meta(const int32_t* grid_hw, const int32_t* text_len, const int32_t* frames,
+                       const int32_t* cu_in, int32_t n, int64_t tokens, char* ws, const WsLayout& l,
+                       hipStream_t s);
+hipError_t launch_build_metadata(const int32_t* grid_hw, const int32_t* text_len, const int32_t* frames,
+                                 int32_t n, int64_t tokens, int32_t* cu_out, int32_t* pos, int32_t* seg_id,
                                  int32_t* status, hipStream_t s);
 hipError_t launch_rope_pack(const void* q, const void* k, const void* v, const int32_t* grid_hw,
                             const int32_t* text_len, const char* ws, const WsLayout& l,
-                            const float2* cs, int32_t heads, int32_t head_dim, bool bf16,
+                            const float2* cs, const Rope3* r3, int32_t heads, int32_t head_dim, bool bf16,
                             hipStream_t s);
 hipError_t launch_rope(const void* x, void* y, const int32_t* pos, int64_t tokens, int32_t heads,
-                       int32_t head_dim, bool bf16, const float2* cs, int32_t* status,
+                       int32_t head_dim, bool bf16, const float2* cs, const Rope3* r3, int32_t* status,
                        hipStream_t s);
 hipError_t launch_attn_fwd(const char* ws, const WsLayout& l, const void* q, const int32_t* grid_hw,
-                           const int32_t* text_len, const float2* cs, void* out, float* lse,
+                           const int32_t* text_len, const float2* cs, const Rope3* r3, void* out, float* lse,
                            int64_t tokens, int32_t heads, int32_t head_dim, bool bf16, float scale,
                            hipStream_t s);
 hipError_t launch_attn_bwd(const void* q, const void* k, const void* v, const void* o, const void* dout,
                            const float* lse, const int32_t* grid_hw, const int32_t* text_len,
-                           const float2* cs, char* ws, const BwdLayout& l, void* dq, void* dk, void* dv,
-                           int64_t tokens, int32_t heads, int32_t head_dim, float scale, hipStream_t s,
+                           const float2* cs, const Rope3* r3, char* ws, const BwdLayout& l, void* dq, void* dk,
+                           void* dv, int64_t tokens, int32_t heads, int32_t head_dim, float scale, hipStream_t s,
                            hipEvent_t const* ev);
 hipError_t launch_cfg_euler(float* z, const void* v, const int32_t* cu, const int32_t* grid_hw,
                             const int32_t* text_len, int32_t n_seg, int64_t total_tokens,
@@ -74,7 +77,9 @@ struct DeviceState {
   size_t ws_bytes = 0;
   char* bws = nullptr;        // library workspace of mf_attn_packed_bwd
   size_t bws_bytes = 0;
-  std::map<std::pair<int, uint32_t>, float2*> tables;  // (head_dim, theta bits) -> cos/sin
+  // (head_dim, theta bits, row channels, column channels) -> cos/sin table;
+  // row channels -1 marks the 2D table
+  std::map<std::tuple<int, uint32_t, int, int>, float2*> tables;
 };
 
 std::mutex g_mu;
@@ -97,12 +102,28 @@ int ensure_status(DeviceState& st) {
   return MF_OK;
 }
 
-// cos/sin table [ROPE_PMAX][head_dim/4]: entry (p, j) = (cos, sin) of
+int upload_table(DeviceState& st, std::tuple<int, uint32_t, int, int> key, const std::vector<float2>& host,
+                 const float2** out) {
+  void* d = nullptr;
+  hipError_t e = hipMalloc(&d, host.size() * sizeof(float2));
+  if (e != hipSuccess) return fail(MF_ERR_OOM, "rope table: %s", hipGetErrorString(e));
+  e = hipMemcpy(d, host.data(), host.size() * sizeof(float2), hipMemcpyHostToDevice);
+  if (e != hipSuccess) {
+    (void)hipFree(d);
+    return hip_fail(e, "hipMemcpy(rope table)");
+  }
+  st.tables[key] = static_cast<float2*>(d);
+  *out = static_cast<float2*>(d);
+  return MF_OK;
+}
+
+// 2D cos/sin table [ROPE_PMAX][head_dim/4]: entry (p, j) = (cos, sin) of
 // p * theta^(-2j/(head_dim/2)), evaluated in double and rounded to float.
+// Caller holds g_mu.
 int ensure_table(DeviceState& st, int head_dim, float theta, const float2** out) {
   uint32_t tb;
   std::memcpy(&tb, &theta, 4);
-  const auto key = std::make_pair(head_dim, tb);
+  const auto key = std::make_tuple(head_dim, tb, -1, -1);
   auto it = st.tables.find(key);
   if (it != st.tables.end()) {
     *out = it->second;
@@ -117,16 +138,43 @@ int ensure_table(DeviceState& st, int head_dim, float theta, const float2** out)
       host[size_t(p) * nf + j] = make_float2(float(std::cos(ang)), float(std::sin(ang)));
     }
   }
-  void* d = nullptr;
-  hipError_t e = hipMalloc(&d, host.size() * sizeof(float2));
-  if (e != hipSuccess) return fail(MF_ERR_OOM, "rope table: %s", hipGetErrorString(e));
-  e = hipMemcpy(d, host.data(), host.size() * sizeof(float2), hipMemcpyHostToDevice);
-  if (e != hipSuccess) {
-    (void)hipFree(d);
-    return hip_fail(e, "hipMemcpy(rope table)");
+  return upload_table(st, key, host, out);
+}
+
+// Frame-aware cos/sin table [ROPE_PMAX][head_dim/2] for the channel split
+// (row, col, head_dim - row - col): pair k of block a (channels m_a, local
+// index j) has frequency theta^(-2j/m_a); entry (p, k) = (cos, sin) of p times
+// it, evaluated in double. Caller holds g_mu.
+int ensure_table3(DeviceState& st, int head_dim, float theta, int s_row, int s_col, const float2** out) {
+  uint32_t tb;
+  std::memcpy(&tb, &theta, 4);
+  const auto key = std::make_tuple(head_dim, tb, s_row, s_col);
+  auto it = st.tables.find(key);
+  if (it != st.tables.end()) {
+    *out = it->second;
+    return MF_OK;
   }
-  st.tables[key] = static_cast<float2*>(d);
-  *out = static_cast<float2*>(d);
+  const int np = head_dim / 2;
+  const int bound[3] = {s_row / 2, (s_row + s_col) / 2, np};
+  const int m[3] = {s_row, s_col, head_dim - s_row - s_col};
+  std::vector<float2> host(size_t(mf::ROPE_PMAX) * np);
+  for (int k = 0; k < np; ++k) {
+    const int a = k < bound[0] ? 0 : (k < bound[1] ? 1 : 2);
+    const int j = k - (a == 0 ? 0 : bound[a - 1]);
+    const double w = std::pow(double(theta), -2.0 * j / m[a]);
+    for (int p = 0; p < mf::ROPE_PMAX; ++p) {
+      const double ang = double(p) * w;
+      host[size_t(p) * np + k] = make_float2(float(std::cos(ang)), float(std::sin(ang)));
+    }
+  }
+  return upload_table(st, key, host, out);
+}
+
+int check_split(int32_t head_dim, int32_t s_row, int32_t s_col, int32_t s_frame) {
+  if (s_row < 0 || s_col < 0 || s_frame < 0 || (s_row | s_col | s_frame) & 1 ||
+      int64_t(s_row) + s_col + s_frame != head_dim)
+    return fail(MF_ERR_INVALID_ARG, "rope split (%d, %d, %d) must be even, >= 0 and sum to head_dim=%d", s_row,
+                s_col, s_frame, head_dim);
   return MF_OK;
 }
 
@@ -202,18 +250,19 @@ int check_attn_args(const void* q, const void* k, const void* v, const int32_t* 
 int run_attn(const void* q, const void* k, const void* v, const int32_t* cu, const int32_t* grid_hw,
              const int32_t* text_len, void* out, int32_t n_seg, int64_t tokens, int32_t heads,
              int32_t head_dim, int32_t dtype, char* ws, const float2* cs, hipStream_t s,
-             hipEvent_t const* ev = nullptr, float* lse = nullptr) {
+             hipEvent_t const* ev = nullptr, float* lse = nullptr, const int32_t* frames = nullptr,
+             const mf::Rope3* r3 = nullptr) {
   const bool bf16 = dtype == MF_BF16;
   const mf::WsLayout l = mf::ws_layout(tokens, heads, head_dim, elem_bytes(dtype), n_seg);
   hipError_t e;
   if (ev && (e = hipEventRecord(ev[0], s)) != hipSuccess) return hip_fail(e, "hipEventRecord");
-  e = mf::launch_meta(grid_hw, text_len, cu, n_seg, tokens, ws, l, s);
+  e = mf::launch_meta(grid_hw, text_len, frames, cu, n_seg, tokens, ws, l, s);
   if (e != hipSuccess) return hip_fail(e, "meta_kernel launch");
   if (ev && (e = hipEventRecord(ev[1], s)) != hipSuccess) return hip_fail(e, "hipEventRecord");
-  e = mf::launch_rope_pack(q, k, v, grid_hw, text_len, ws, l, cs, heads, head_dim, bf16, s);
+  e = mf::launch_rope_pack(q, k, v, grid_hw, text_len, ws, l, cs, r3, heads, head_dim, bf16, s);
   if (e != hipSuccess) return hip_fail(e, "rope_pack_kernel launch");
   if (ev && (e = hipEventRecord(ev[2], s)) != hipSuccess) return hip_fail(e, "hipEventRecord");
-  e = mf::launch_attn_fwd(ws, l, q, grid_hw, text_len, cs, out, lse, tokens, heads, head_dim, bf16,
+  e = mf::launch_attn_fwd(ws, l, q, grid_hw, text_len, cs, r3, out, lse, tokens, heads, head_dim, bf16,
                           float(1.0 / std::sqrt(double(head_dim))), s);
   if (e != hipSuccess) return hip_fail(e, "attn_fwd launch");
   if (ev && (e = hipEventRecord(ev[3], s)) != hipSuccess) return hip_fail(e, "hipEventRecord");
@@ -292,30 +341,200 @@ int mf_attn_packed_ws(const void* q, const void* k, const void* v, const int32_t
                   dtype, static_cast<char*>(workspace), cs, stream);
 }
 
-int mf_attn_packed_lse(const void* q, const void* k, const void* v, const int32_t* cu_seqlens,
-                       const int32_t* grid_hw, const int32_t* text_len, void* out, float* lse,
-                       int32_t n_seg, int64_t total_tokens, int32_t heads, int32_t head_dim,
-                       int32_t dtype, hipStream_t stream) {
+}  // extern "C"
+
+namespace {
+
+// Forward with optional LSE; frames/split select the frame-aware RoPE.
+int attn_impl(const void* q, const void* k, const void* v, const int32_t* cu_seqlens, const int32_t* grid_hw,
+              const int32_t* text_len, const int32_t* frames, const int32_t* split, void* out, float* lse,
+              int32_t n_seg, int64_t total_tokens, int32_t heads, int32_t head_dim, int32_t dtype,
+              hipStream_t stream) {
   int rc = check_attn_args(q, k, v, cu_seqlens, grid_hw, text_len, out, n_seg, total_tokens, heads,
                            head_dim, dtype);
   if (rc) return rc;
-  if (!lse) return fail(MF_ERR_INVALID_ARG, "null lse");
-  if (reinterpret_cast<uintptr_t>(lse) & 3) return fail(MF_ERR_INVALID_ARG, "lse must be 4-byte aligned");
+  if (split && (rc = check_split(head_dim, split[0], split[1], split[2]))) return rc;
+  if (split && !frames) return fail(MF_ERR_INVALID_ARG, "null frames");
   const size_t tb = size_t(total_tokens) * heads * head_dim * elem_bytes(dtype);
-  const size_t lb = size_t(total_tokens) * heads * 4;
-  if (overlaps(lse, lb, out, tb) || overlaps(lse, lb, q, tb) || overlaps(lse, lb, k, tb) ||
-      overlaps(lse, lb, v, tb))
-    return fail(MF_ERR_INVALID_ARG, "lse overlaps q, k, v or out");
+  if (lse) {
+    if (reinterpret_cast<uintptr_t>(lse) & 3) return fail(MF_ERR_INVALID_ARG, "lse must be 4-byte aligned");
+    const size_t lb = size_t(total_tokens) * heads * 4;
+    if (overlaps(lse, lb, out, tb) || overlaps(lse, lb, q, tb) || overlaps(lse, lb, k, tb) ||
+        overlaps(lse, lb, v, tb))
+      return fail(MF_ERR_INVALID_ARG, "lse overlaps q, k, v or out");
+  }
+  if (frames && overlaps(out, tb, frames, size_t(n_seg) * 4))
+    return fail(MF_ERR_INVALID_ARG, "out overlaps frames");
   int dev;
   if ((rc = current_device(&dev))) return rc;
   const size_t need = mf_workspace_bytes(total_tokens, heads, head_dim, dtype, n_seg);
   std::lock_guard<std::mutex> lock(g_mu);
   DeviceState& st = g_dev[dev];
   const float2* cs = nullptr;
-  if ((rc = ensure_table(st, head_dim, MF_ROPE_THETA, &cs))) return rc;
+  mf::Rope3 r3{nullptr, 0, 0};
+  if (split) {
+    if ((rc = ensure_table3(st, head_dim, MF_ROPE_THETA, split[0], split[1], &r3.cs))) return rc;
+    r3.b1 = split[0] / 2;
+    r3.b2 = (split[0] + split[1]) / 2;
+  } else if ((rc = ensure_table(st, head_dim, MF_ROPE_THETA, &cs))) {
+    return rc;
+  }
   if ((rc = ensure_workspace(st, need))) return rc;
-  return run_attn(q, k, v, cu_seqlens, grid_hw, text_len, out, n_seg, total_tokens, heads, head_dim,
-                  dtype, st.ws, cs, stream, nullptr, lse);
+  return run_attn(q, k, v, cu_seqlens, grid_hw, text_len, out, n_seg, total_tokens, heads, head_dim, dtype,
+                  st.ws, cs, stream, nullptr, lse, frames, split ? &r3 : nullptr);
+}
+
+int bwd_impl(const void* q, const void* k, const void* v, const void* out, const void* d_out, const float* lse,
+             const int32_t* cu_seqlens, const int32_t* grid_hw, const int32_t* text_len, const int32_t* frames,
+             const int32_t* split, void* dq, void* dk, void* dv, int32_t n_seg, int64_t total_tokens,
+             int32_t heads, int32_t head_dim, int32_t dtype, hipEvent_t const* events, hipStream_t stream) {
+  int rc = check_attn_args(q, k, v, cu_seqlens, grid_hw, text_len, dq, n_seg, total_tokens, heads,
+                           head_dim, dtype);
+  if (rc) return rc;
+  if (dtype != MF_BF16) return fail(MF_ERR_UNSUPPORTED, "backward supports MF_BF16 only");
+  if (!out || !d_out || !lse || !dk || !dv) return fail(MF_ERR_INVALID_ARG, "null pointer argument");
+  if (split && (rc = check_split(head_dim, split[0], split[1], split[2]))) return rc;
+  if (split && !frames) return fail(MF_ERR_INVALID_ARG, "null frames");
+  const size_t tb = size_t(total_tokens) * heads * head_dim * 2;
+  const size_t lb = size_t(total_tokens) * heads * 4;
+  const void* ins[6] = {q, k, v, out, d_out, lse};
+  const size_t in_bytes[6] = {tb, tb, tb, tb, tb, lb};
+  void* outs[3] = {dq, dk, dv};
+  for (int i = 0; i < 3; ++i) {
+    for (int j = 0; j < 6; ++j)
+      if (overlaps(outs[i], tb, ins[j], in_bytes[j]))
+        return fail(MF_ERR_INVALID_ARG, "a gradient output overlaps an input");
+    for (int j = i + 1; j < 3; ++j)
+      if (overlaps(outs[i], tb, outs[j], tb)) return fail(MF_ERR_INVALID_ARG, "gradient outputs overlap");
+    if (overlaps(outs[i], tb, cu_seqlens, size_t(n_seg + 1) * 4) ||
+        overlaps(outs[i], tb, grid_hw, size_t(n_seg) * 8) || overlaps(outs[i], tb, text_len, size_t(n_seg) * 4) ||
+        (frames && overlaps(outs[i], tb, frames, size_t(n_seg) * 4)))
+      return fail(MF_ERR_INVALID_ARG, "a gradient output overlaps the metadata");
+  }
+  const uintptr_t mis = reinterpret_cast<uintptr_t>(out) | reinterpret_cast<uintptr_t>(d_out) |
+                        reinterpret_cast<uintptr_t>(dk) | reinterpret_cast<uintptr_t>(dv);
+  if ((mis & 15) || (reinterpret_cast<uintptr_t>(lse) & 3))
+    return fail(MF_ERR_INVALID_ARG, "out, d_out, dk, dv must be 16-byte aligned and lse 4-byte aligned");
+  int dev;
+  if ((rc = current_device(&dev))) return rc;
+  const mf::BwdLayout l = mf::bwd_layout(total_tokens, heads, head_dim, n_seg);
+  std::lock_guard<std::mutex> lock(g_mu);
+  DeviceState& st = g_dev[dev];
+  const float2* cs = nullptr;
+  mf::Rope3 r3{nullptr, 0, 0};
+  if (split) {
+    if ((rc = ensure_table3(st, head_dim, MF_ROPE_THETA, split[0], split[1], &r3.cs))) return rc;
+    r3.b1 = split[0] / 2;
+    r3.b2 = (split[0] + split[1]) / 2;
+  } else if ((rc = ensure_table(st, head_dim, MF_ROPE_THETA, &cs))) {
+    return rc;
+  }
+  if ((rc = ensure_buffer(st.bws, st.bws_bytes, size_t(l.total)))) return rc;
+  hipError_t e;
+  if (events && (e = hipEventRecord(events[0], stream)) != hipSuccess) return hip_fail(e, "hipEventRecord");
+  e = mf::launch_meta(grid_hw, text_len, frames, cu_seqlens, n_seg, total_tokens, st.bws, l.m, stream);
+  if (e != hipSuccess) return hip_fail(e, "meta_kernel launch");
+  e = mf::launch_attn_bwd(q, k, v, out, d_out, lse, grid_hw, text_len, cs, split ? &r3 : nullptr, st.bws, l, dq,
+                          dk, dv, total_tokens, heads, head_dim, float(1.0 / std::sqrt(double(head_dim))), stream,
+                          events ? events + 1 : nullptr);
+  if (e != hipSuccess) return hip_fail(e, "backward kernels launch");
+  if (events && (e = hipEventRecord(events[3], stream)) != hipSuccess) return hip_fail(e, "hipEventRecord");
+  return MF_OK;
+}
+
+int metadata_impl(int32_t n_seg, const int32_t* grid_hw, const int32_t* text_len, const int32_t* frames,
+                  int32_t* cu_seqlens_out, int32_t* pos_out, int32_t* seg_id_out, int64_t total_tokens,
+                  hipStream_t stream) {
+  if (!grid_hw || !text_len || !cu_seqlens_out || !pos_out || !seg_id_out)
+    return fail(MF_ERR_INVALID_ARG, "null pointer argument");
+  if (n_seg < 1 || n_seg > MF_MAX_SEGMENTS)
+    return fail(MF_ERR_INVALID_ARG, "n_seg=%d outside [1, %d]", n_seg, MF_MAX_SEGMENTS);
+  if (total_tokens < 1 || total_tokens >= (int64_t(1) << 31))
+    return fail(MF_ERR_INVALID_ARG, "total_tokens=%lld outside [1, 2^31)", (long long)total_tokens);
+  int dev, rc;
+  if ((rc = current_device(&dev))) return rc;
+  int32_t* status;
+  {
+    std::lock_guard<std::mutex> lock(g_mu);
+    if ((rc = ensure_status(g_dev[dev]))) return rc;
+    status = g_dev[dev].status;
+  }
+  const hipError_t e = mf::launch_build_metadata(grid_hw, text_len, frames, n_seg, total_tokens, cu_seqlens_out,
+                                                 pos_out, seg_id_out, status, stream);
+  return e == hipSuccess ? MF_OK : hip_fail(e, "metadata kernels launch");
+}
+
+int rope_impl(const void* x_in, void* x_out, const int32_t* pos, const int32_t* split, int64_t total_tokens,
+              int32_t heads, int32_t head_dim, int32_t dtype, float theta, hipStream_t stream) {
+  if (!x_in || !x_out || !pos) return fail(MF_ERR_INVALID_ARG, "null pointer argument");
+  if (total_tokens < 1 || total_tokens >= (int64_t(1) << 31))
+    return fail(MF_ERR_INVALID_ARG, "total_tokens=%lld outside [1, 2^31)", (long long)total_tokens);
+  if (heads < 1 || heads > 256) return fail(MF_ERR_INVALID_ARG, "heads=%d outside [1, 256]", heads);
+  if (head_dim != 64 && head_dim != 128)
+    return fail(MF_ERR_UNSUPPORTED, "head_dim=%d (supported: 64, 128)", head_dim);
+  const int eb = elem_bytes(dtype);
+  if (!eb) return fail(MF_ERR_UNSUPPORTED, "dtype=%d", dtype);
+  if (!(theta > 1.0f) || !std::isfinite(theta)) return fail(MF_ERR_INVALID_ARG, "theta must be > 1");
+  int rc;
+  if (split && (rc = check_split(head_dim, split[0], split[1], split[2]))) return rc;
+  const size_t tb = size_t(total_tokens) * heads * head_dim * eb;
+  if (x_in != x_out && overlaps(x_in, tb, x_out, tb))
+    return fail(MF_ERR_INVALID_ARG, "x_in and x_out partially overlap");
+  if ((reinterpret_cast<uintptr_t>(x_in) | reinterpret_cast<uintptr_t>(x_out)) & 15)
+    return fail(MF_ERR_INVALID_ARG, "x_in and x_out must be 16-byte aligned");
+  int dev;
+  if ((rc = current_device(&dev))) return rc;
+  const float2* cs = nullptr;
+  mf::Rope3 r3{nullptr, 0, 0};
+  int32_t* status;
+  {
+    std::lock_guard<std::mutex> lock(g_mu);
+    DeviceState& st = g_dev[dev];
+    if ((rc = ensure_status(st))) return rc;
+    if (split) {
+      if ((rc = ensure_table3(st, head_dim, theta, split[0], split[1], &r3.cs))) return rc;
+      r3.b1 = split[0] / 2;
+      r3.b2 = (split[0] + split[1]) / 2;
+    } else if ((rc = ensure_table(st, head_dim, theta, &cs))) {
+      return rc;
+    }
+    status = st.status;
+  }
+  const hipError_t e = mf::launch_rope(x_in, x_out, pos, total_tokens, heads, head_dim, dtype == MF_BF16, cs,
+                                       split ? &r3 : nullptr, status, stream);
+  return e == hipSuccess ? MF_OK : hip_fail(e, "rope_kernel launch");
+}
+
+}  // namespace
+
+extern "C" {
+
+int mf_attn_packed_lse(const void* q, const void* k, const void* v, const int32_t* cu_seqlens,
+                       const int32_t* grid_hw, const int32_t* text_len, void* out, float* lse,
+                       int32_t n_seg, int64_t total_tokens, int32_t heads, int32_t head_dim,
+                       int32_t dtype, hipStream_t stream) {
+  if (!lse) return fail(MF_ERR_INVALID_ARG, "null lse");
+  return attn_impl(q, k, v, cu_seqlens, grid_hw, text_len, nullptr, nullptr, out, lse, n_seg, total_tokens, heads,
+                   head_dim, dtype, stream);
+}
+
+int mf_attn_packed_3d(const void* q, const void* k, const void* v, const int32_t* cu_seqlens,
+                      const int32_t* grid_hw, const int32_t* text_len, const int32_t* frames, int32_t split_row,
+                      int32_t split_col, int32_t split_frame, void* out, float* lse, int32_t n_seg,
+                      int64_t total_tokens, int32_t heads, int32_t head_dim, int32_t dtype, hipStream_t stream) {
+  const int32_t split[3] = {split_row, split_col, split_frame};
+  return attn_impl(q, k, v, cu_seqlens, grid_hw, text_len, frames, split, out, lse, n_seg, total_tokens, heads,
+                   head_dim, dtype, stream);
+}
+
+int mf_attn_packed_3d_bwd(const void* q, const void* k, const void* v, const void* out, const void* d_out,
+                          const float* lse, const int32_t* cu_seqlens, const int32_t* grid_hw,
+                          const int32_t* text_len, const int32_t* frames, int32_t split_row, int32_t split_col,
+                          int32_t split_frame, void* dq, void* dk, void* dv, int32_t n_seg, int64_t total_tokens,
+                          int32_t heads, int32_t head_dim, int32_t dtype, hipStream_t stream) {
+  const int32_t split[3] = {split_row, split_col, split_frame};
+  return bwd_impl(q, k, v, out, d_out, lse, cu_seqlens, grid_hw, text_len, frames, split, dq, dk, dv, n_seg,
+                  total_tokens, heads, head_dim, dtype, nullptr, stream);
 }
 
 size_t mf_bwd_workspace_bytes(int64_t total_tokens, int32_t heads, int32_t head_dim, int32_t n_seg) {
@@ -331,48 +550,8 @@ int mf_attn_packed_bwd_profiled(const void* q, const void* k, const void* v, con
                                 void* dv, int32_t n_seg, int64_t total_tokens, int32_t heads,
                                 int32_t head_dim, int32_t dtype, hipEvent_t const* events,
                                 hipStream_t stream) {
-  int rc = check_attn_args(q, k, v, cu_seqlens, grid_hw, text_len, dq, n_seg, total_tokens, heads,
-                           head_dim, dtype);
-  if (rc) return rc;
-  if (dtype != MF_BF16) return fail(MF_ERR_UNSUPPORTED, "backward supports MF_BF16 only");
-  if (!out || !d_out || !lse || !dk || !dv) return fail(MF_ERR_INVALID_ARG, "null pointer argument");
-  const size_t tb = size_t(total_tokens) * heads * head_dim * 2;
-  const size_t lb = size_t(total_tokens) * heads * 4;
-  const void* ins[6] = {q, k, v, out, d_out, lse};
-  const size_t in_bytes[6] = {tb, tb, tb, tb, tb, lb};
-  void* outs[3] = {dq, dk, dv};
-  for (int i = 0; i < 3; ++i) {
-    for (int j = 0; j < 6; ++j)
-      if (overlaps(outs[i], tb, ins[j], in_bytes[j]))
-        return fail(MF_ERR_INVALID_ARG, "a gradient output overlaps an input");
-    for (int j = i + 1; j < 3; ++j)
-      if (overlaps(outs[i], tb, outs[j], tb)) return fail(MF_ERR_INVALID_ARG, "gradient outputs overlap");
-    if (overlaps(outs[i], tb, cu_seqlens, size_t(n_seg + 1) * 4) ||
-        overlaps(outs[i], tb, grid_hw, size_t(n_seg) * 8) || overlaps(outs[i], tb, text_len, size_t(n_seg) * 4))
-      return fail(MF_ERR_INVALID_ARG, "a gradient output overlaps the metadata");
-  }
-  const uintptr_t mis = reinterpret_cast<uintptr_t>(out) | reinterpret_cast<uintptr_t>(d_out) |
-                        reinterpret_cast<uintptr_t>(dk) | reinterpret_cast<uintptr_t>(dv);
-  if ((mis & 15) || (reinterpret_cast<uintptr_t>(lse) & 3))
-    return fail(MF_ERR_INVALID_ARG, "out, d_out, dk, dv must be 16-byte aligned and lse 4-byte aligned");
-  int dev;
-  if ((rc = current_device(&dev))) return rc;
-  const mf::BwdLayout l = mf::bwd_layout(total_tokens, heads, head_dim, n_seg);
-  std::lock_guard<std::mutex> lock(g_mu);
-  DeviceState& st = g_dev[dev];
-  const float2* cs = nullptr;
-  if ((rc = ensure_table(st, head_dim, MF_ROPE_THETA, &cs))) return rc;
-  if ((rc = ensure_buffer(st.bws, st.bws_bytes, size_t(l.total)))) return rc;
-  hipError_t e;
-  if (events && (e = hipEventRecord(events[0], stream)) != hipSuccess) return hip_fail(e, "hipEventRecord");
-  e = mf::launch_meta(grid_hw, text_len, cu_seqlens, n_seg, total_tokens, st.bws, l.m, stream);
-  if (e != hipSuccess) return hip_fail(e, "meta_kernel launch");
-  e = mf::launch_attn_bwd(q, k, v, out, d_out, lse, grid_hw, text_len, cs, st.bws, l, dq, dk, dv,
-                          total_tokens, heads, head_dim, float(1.0 / std::sqrt(double(head_dim))), stream,
-                          events ? events + 1 : nullptr);
-  if (e != hipSuccess) return hip_fail(e, "backward kernels launch");
-  if (events && (e = hipEventRecord(events[3], stream)) != hipSuccess) return hip_fail(e, "hipEventRecord");
-  return MF_OK;
+  return bwd_impl(q, k, v, out, d_out, lse, cu_seqlens, grid_hw, text_len, nullptr, nullptr, dq, dk, dv, n_seg,
+                  total_tokens, heads, head_dim, dtype, events, stream);
 }
 
 int mf_attn_packed_bwd(const void* q, const void* k, const void* v, const void* out, const void* d_out,
@@ -387,55 +566,28 @@ int mf_attn_packed_bwd(const void* q, const void* k, const void* v, const void* 
 int mf_build_metadata(int32_t n_seg, const int32_t* grid_hw, const int32_t* text_len,
                       int32_t* cu_seqlens_out, int32_t* pos_out, int32_t* seg_id_out,
                       int64_t total_tokens, hipStream_t stream) {
-  if (!grid_hw || !text_len || !cu_seqlens_out || !pos_out || !seg_id_out)
-    return fail(MF_ERR_INVALID_ARG, "null pointer argument");
-  if (n_seg < 1 || n_seg > MF_MAX_SEGMENTS)
-    return fail(MF_ERR_INVALID_ARG, "n_seg=%d outside [1, %d]", n_seg, MF_MAX_SEGMENTS);
-  if (total_tokens < 1 || total_tokens >= (int64_t(1) << 31))
-    return fail(MF_ERR_INVALID_ARG, "total_tokens=%lld outside [1, 2^31)", (long long)total_tokens);
-  int dev, rc;
-  if ((rc = current_device(&dev))) return rc;
-  int32_t* status;
-  {
-    std::lock_guard<std::mutex> lock(g_mu);
-    if ((rc = ensure_status(g_dev[dev]))) return rc;
-    status = g_dev[dev].status;
-  }
-  const hipError_t e = mf::launch_build_metadata(grid_hw, text_len, n_seg, total_tokens,
-                                                 cu_seqlens_out, pos_out, seg_id_out, status, stream);
-  return e == hipSuccess ? MF_OK : hip_fail(e, "metadata kernels launch");
+  return metadata_impl(n_seg, grid_hw, text_len, nullptr, cu_seqlens_out, pos_out, seg_id_out, total_tokens,
+                       stream);
+}
+
+int mf_build_metadata_3d(int32_t n_seg, const int32_t* grid_hw, const int32_t* text_len, const int32_t* frames,
+                         int32_t* cu_seqlens_out, int32_t* pos_out, int32_t* seg_id_out, int64_t total_tokens,
+                         hipStream_t stream) {
+  if (!frames) return fail(MF_ERR_INVALID_ARG, "null frames");
+  return metadata_impl(n_seg, grid_hw, text_len, frames, cu_seqlens_out, pos_out, seg_id_out, total_tokens,
+                       stream);
 }
 
 int mf_rope_2d(const void* x_in, void* x_out, const int32_t* pos, int64_t total_tokens,
                int32_t heads, int32_t head_dim, int32_t dtype, float theta, hipStream_t stream) {
-  if (!x_in || !x_out || !pos) return fail(MF_ERR_INVALID_ARG, "null pointer argument");
-  if (total_tokens < 1 || total_tokens >= (int64_t(1) << 31))
-    return fail(MF_ERR_INVALID_ARG, "total_tokens=%lld outside [1, 2^31)", (long long)total_tokens);
-  if (heads < 1 || heads > 256) return fail(MF_ERR_INVALID_ARG, "heads=%d outside [1, 256]", heads);
-  if (head_dim != 64 && head_dim != 128)
-    return fail(MF_ERR_UNSUPPORTED, "head_dim=%d (supported: 64, 128)", head_dim);
-  const int eb = elem_bytes(dtype);
-  if (!eb) return fail(MF_ERR_UNSUPPORTED, "dtype=%d", dtype);
-  if (!(theta > 1.0f) || !std::isfinite(theta)) return fail(MF_ERR_INVALID_ARG, "theta must be > 1");
-  const size_t tb = size_t(total_tokens) * heads * head_dim * eb;
-  if (x_in != x_out && overlaps(x_in, tb, x_out, tb))
-    return fail(MF_ERR_INVALID_ARG, "x_in and x_out partially overlap");
-  if ((reinterpret_cast<uintptr_t>(x_in) | reinterpret_cast<uintptr_t>(x_out)) & 15)
-    return fail(MF_ERR_INVALID_ARG, "x_in and x_out must be 16-byte aligned");
-  int dev, rc;
-  if ((rc = current_device(&dev))) return rc;
-  const float2* cs;
-  int32_t* status;
-  {
-    std::lock_guard<std::mutex> lock(g_mu);
-    DeviceState& st = g_dev[dev];
-    if ((rc = ensure_status(st))) return rc;
-    if ((rc = ensure_table(st, head_dim, theta, &cs))) return rc;
-    status = st.status;
-  }
-  const hipError_t e = mf::launch_rope(x_in, x_out, pos, total_tokens, heads, head_dim,
-                                       dtype == MF_BF16, cs, status, stream);
-  return e == hipSuccess ? MF_OK : hip_fail(e, "rope_kernel launch");
+  return rope_impl(x_in, x_out, pos, nullptr, total_tokens, heads, head_dim, dtype, theta, stream);
+}
+
+int mf_rope_3d(const void* x_in, void* x_out, const int32_t* pos, int64_t total_tokens, int32_t heads,
+               int32_t head_dim, int32_t dtype, float theta, int32_t split_row, int32_t split_col,
+               int32_t split_frame, hipStream_t stream) {
+  const int32_t split[3] = {split_row, split_col, split_frame};
+  return rope_impl(x_in, x_out, pos, split, total_tokens, heads, head_dim, dtype, theta, stream);
 }
 
 int mf_rf_cfg_euler_step(float* z, const void* v, const int32_t* cu_seqlens, const int32_t* grid_hw,

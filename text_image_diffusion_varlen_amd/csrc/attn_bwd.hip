@@ -58,6 +58,7 @@ struct BwdArgs {
   const int32_t* grid_hw;
   const int32_t* text_len;
   const float2* cs;      // cos/sin table [ROPE_PMAX][d/4]
+  Rope3 r3;              // frame-aware RoPE of editing samples (R3 kernels)
   uint16_t* qc;
   uint16_t* qt;
   uint16_t* oc;
@@ -78,7 +79,7 @@ struct BwdArgs {
 
 // ---------------------------------------------------------------- prologue
 
-template <int D>
+template <int D, bool R3>
 __global__ void __launch_bounds__(256) bwd_pack_kernel(BwdArgs a) {
   constexpr int CPR = D / 8;             // 16-byte chunks per row
   constexpr int CPT = KTILE * CPR;       // chunks per tile
@@ -91,7 +92,7 @@ __global__ void __launch_bounds__(256) bwd_pack_kernel(BwdArgs a) {
 
   const int64_t r0 = int64_t(blockIdx.x) * KTILE;
   const int h = blockIdx.y;
-  int32_t u0 = 0, L = 0, tl = 0, w = 1;
+  int32_t u0 = 0, L = 0, tl = 0, w = 1, gh = 1;
   int64_t tok0 = 0;
   if (r0 < hdr->padded_total) {
     const int32_t s = upper_segment(pcu, hdr->n_seg, r0);
@@ -99,6 +100,7 @@ __global__ void __launch_bounds__(256) bwd_pack_kernel(BwdArgs a) {
     L = len[s];
     tok0 = int64_t(cu[s]) + u0;
     tl = a.text_len[s];
+    gh = a.grid_hw[2 * s];
     w = a.grid_hw[2 * s + 1];
   }
   const int64_t tile_off = (int64_t(h) * a.rows + r0) * D;  // element offset of this tile
@@ -122,9 +124,15 @@ __global__ void __launch_bounds__(256) bwd_pack_kernel(BwdArgs a) {
         const int64_t off = (tok0 + rr) * stride + int64_t(h) * D + cc * 8;
         x = *reinterpret_cast<const Chunk<uint16_t>*>(src + off);
         if (rotate) {
-          int32_t row, col;
-          token_position(u, tl, w, row, col);
-          x = rotate_chunk<uint16_t, D>(x, cc * 8, row, col, a.cs);
+          if constexpr (R3) {
+            int32_t row, col, frame;
+            token_position3(u, tl, gh, w, row, col, frame);
+            x = rotate_chunk3<uint16_t, D>(x, cc * 8, row, col, frame, a.r3);
+          } else {
+            int32_t row, col;
+            token_position(u, tl, w, row, col);
+            x = rotate_chunk<uint16_t, D>(x, cc * 8, row, col, a.cs);
+          }
         }
         if (with_dsum) {
           const Chunk<uint16_t> y = *reinterpret_cast<const Chunk<uint16_t>*>(a.o + off);
@@ -294,18 +302,34 @@ __device__ inline void kv_phase2_dk(const u32x4* T, const u32x4* pl, const f32x1
   }
 }
 
+// Position of a sample token for the epilogue rotations.
+struct TokPos {
+  int32_t row, col, frame;
+};
+template <bool R3>
+__device__ inline TokPos token_pos(int32_t u, int32_t seg, const BwdArgs& a) {
+  TokPos p{0, 0, 0};
+  if constexpr (R3) token_position3(u, a.text_len[seg], a.grid_hw[2 * seg], a.grid_hw[2 * seg + 1], p.row, p.col, p.frame);
+  else token_position(u, a.text_len[seg], a.grid_hw[2 * seg + 1], p.row, p.col);
+  return p;
+}
+
 // Undo the rotation of four consecutive channels ch0 .. ch0+3 (two pairs) at
-// (row, col) and scale: (x0, x1) -> (x0 c + x1 s, -x0 s + x1 c) * scale.
-template <int D>
-__device__ inline uint2 unrotate4(const float (&x)[4], int ch0, int32_t row, int32_t col, float scale,
-                                  const float2* __restrict__ cs) {
+// position p and scale: (x0, x1) -> (x0 c + x1 s, -x0 s + x1 c) * scale.
+template <int D, bool R3>
+__device__ inline uint2 unrotate4(const float (&x)[4], int ch0, const TokPos& p, float scale, const BwdArgs& a) {
   float y[4];
 #pragma unroll
   for (int pp = 0; pp < 2; ++pp) {
     const int d = ch0 + 2 * pp;
-    const bool first_half = d < D / 2;
-    const int j = first_half ? d / 2 : (d - D / 2) / 2;
-    const float2 r = cs[(first_half ? row : col) * (D / 4) + j];
+    float2 r;
+    if constexpr (R3) {
+      r = rope3_cs(a.r3, D, d / 2, p.row, p.col, p.frame);
+    } else {
+      const bool first_half = d < D / 2;
+      const int j = first_half ? d / 2 : (d - D / 2) / 2;
+      r = a.cs[(first_half ? p.row : p.col) * (D / 4) + j];
+    }
     const float x0 = x[2 * pp], x1 = x[2 * pp + 1];
     y[2 * pp] = (x0 * r.x + x1 * r.y) * scale;
     y[2 * pp + 1] = (x1 * r.x - x0 * r.y) * scale;
@@ -316,7 +340,7 @@ __device__ inline uint2 unrotate4(const float (&x)[4], int ch0, int32_t row, int
   return o;
 }
 
-template <int D>
+template <int D, bool R3>
 __global__ void __launch_bounds__(64 * KV_WAVES, 2) bwd_kv_kernel(BwdArgs a) {
   constexpr int CH = BwdTile<D>::CH, KSTEPS = BwdTile<D>::KSTEPS, DBLK = BwdTile<D>::DBLK;
   constexpr int SET = 4 * CH + 2 * KTILE / 4;  // chunks of one LDS tile set (4 tiles + stats)
@@ -396,8 +420,7 @@ __global__ void __launch_bounds__(64 * KV_WAVES, 2) bwd_kv_kernel(BwdArgs a) {
 
   // Epilogue: entry e of block b is channel 32b + 8(e/4) + 4hf + e%4 of this lane's key.
   if (key < L) {
-    int32_t row = 0, col = 0;
-    if (!dv_wave) token_position(key, a.text_len[seg], a.grid_hw[2 * seg + 1], row, col);
+    const TokPos pos = token_pos<R3>(key, seg, a);
     const int64_t off = (int64_t(cb + key) * heads + h) * D;
 #pragma unroll
     for (int b = 0; b < DBLK; ++b) {
@@ -411,7 +434,7 @@ __global__ void __launch_bounds__(64 * KV_WAVES, 2) bwd_kv_kernel(BwdArgs a) {
           *reinterpret_cast<uint2*>(a.dv + off + ch) = o;
         } else {
           const float xk[4] = {acc[b][4 * g], acc[b][4 * g + 1], acc[b][4 * g + 2], acc[b][4 * g + 3]};
-          *reinterpret_cast<uint2*>(a.dk + off + ch) = unrotate4<D>(xk, ch, row, col, a.scale, a.cs);
+          *reinterpret_cast<uint2*>(a.dk + off + ch) = unrotate4<D, R3>(xk, ch, pos, a.scale, a);
         }
       }
     }
@@ -464,7 +487,7 @@ __device__ inline void q_step(const u32x4* T, const bf16x8 (&qreg)[D / 16], cons
   }
 }
 
-template <int D>
+template <int D, bool R3>
 __global__ void __launch_bounds__(64 * Q_WAVES, 2) bwd_q_kernel(BwdArgs a) {
   constexpr int CH = BwdTile<D>::CH, KSTEPS = BwdTile<D>::KSTEPS, DBLK = BwdTile<D>::DBLK;
   constexpr int SET = 3 * CH;
@@ -528,8 +551,7 @@ __global__ void __launch_bounds__(64 * Q_WAVES, 2) bwd_q_kernel(BwdArgs a) {
                   hf, l32);
 
   if (qrel < L) {
-    int32_t row, col;
-    token_position(qrel, a.text_len[seg], a.grid_hw[2 * seg + 1], row, col);
+    const TokPos pos = token_pos<R3>(qrel, seg, a);
     const int64_t off = (int64_t(cb + qrel) * heads + h) * D;
 #pragma unroll
     for (int b = 0; b < DBLK; ++b) {
@@ -537,7 +559,7 @@ __global__ void __launch_bounds__(64 * Q_WAVES, 2) bwd_q_kernel(BwdArgs a) {
       for (int g = 0; g < 4; ++g) {
         const int ch = 32 * b + 8 * g + 4 * hf;
         const float x[4] = {acc[b][4 * g], acc[b][4 * g + 1], acc[b][4 * g + 2], acc[b][4 * g + 3]};
-        *reinterpret_cast<uint2*>(a.dq + off + ch) = unrotate4<D>(x, ch, row, col, a.scale, a.cs);
+        *reinterpret_cast<uint2*>(a.dq + off + ch) = unrotate4<D, R3>(x, ch, pos, a.scale, a);
       }
     }
   }
@@ -545,24 +567,25 @@ __global__ void __launch_bounds__(64 * Q_WAVES, 2) bwd_q_kernel(BwdArgs a) {
 
 // ---------------------------------------------------------------- launch
 
-template <int D>
+template <int D, bool R3>
 static hipError_t launch_bwd_t(const BwdArgs& a, const BwdLayout& l, hipStream_t s, hipEvent_t const* ev) {
   hipError_t e;
-  hipLaunchKernelGGL(bwd_pack_kernel<D>, dim3(unsigned(l.m.rows / KTILE), unsigned(a.heads)), dim3(256), 0, s, a);
-  if ((e = hipGetLastError()) != hipSuccess) return e;
-  if (ev && (e = hipEventRecord(ev[0], s)) != hipSuccess) return e;
-  hipLaunchKernelGGL(bwd_kv_kernel<D>, dim3(unsigned(KV_SPLIT * l.m.n_tiles * a.heads)), dim3(64 * KV_WAVES), 0,
+  hipLaunchKernelGGL((bwd_pack_kernel<D, R3>), dim3(unsigned(l.m.rows / KTILE), unsigned(a.heads)), dim3(256), 0,
                      s, a);
   if ((e = hipGetLastError()) != hipSuccess) return e;
+  if (ev && (e = hipEventRecord(ev[0], s)) != hipSuccess) return e;
+  hipLaunchKernelGGL((bwd_kv_kernel<D, R3>), dim3(unsigned(KV_SPLIT * l.m.n_tiles * a.heads)), dim3(64 * KV_WAVES),
+                     0, s, a);
+  if ((e = hipGetLastError()) != hipSuccess) return e;
   if (ev && (e = hipEventRecord(ev[1], s)) != hipSuccess) return e;
-  hipLaunchKernelGGL(bwd_q_kernel<D>, dim3(unsigned(l.m.n_tiles * a.heads)), dim3(64 * Q_WAVES), 0, s, a);
+  hipLaunchKernelGGL((bwd_q_kernel<D, R3>), dim3(unsigned(l.m.n_tiles * a.heads)), dim3(64 * Q_WAVES), 0, s, a);
   return hipGetLastError();
 }
 
 hipError_t launch_attn_bwd(const void* q, const void* k, const void* v, const void* o, const void* dout,
                            const float* lse, const int32_t* grid_hw, const int32_t* text_len,
-                           const float2* cs, char* ws, const BwdLayout& l, void* dq, void* dk, void* dv,
-                           int64_t tokens, int32_t heads, int32_t head_dim, float scale, hipStream_t s,
+                           const float2* cs, const Rope3* r3, char* ws, const BwdLayout& l, void* dq, void* dk,
+                           void* dv, int64_t tokens, int32_t heads, int32_t head_dim, float scale, hipStream_t s,
                            hipEvent_t const* ev) {
   BwdArgs a;
   a.ws = ws;
@@ -579,6 +602,7 @@ hipError_t launch_attn_bwd(const void* q, const void* k, const void* v, const vo
   a.grid_hw = grid_hw;
   a.text_len = text_len;
   a.cs = cs;
+  a.r3 = r3 ? *r3 : Rope3{nullptr, 0, 0};
   a.qc = reinterpret_cast<uint16_t*>(ws + l.off_qc);
   a.qt = reinterpret_cast<uint16_t*>(ws + l.off_qt);
   a.oc = reinterpret_cast<uint16_t*>(ws + l.off_oc);
@@ -595,7 +619,8 @@ hipError_t launch_attn_bwd(const void* q, const void* k, const void* v, const vo
   a.tokens = tokens;
   a.c_log2 = scale * LOG2E;
   a.scale = scale;
-  return head_dim == 128 ? launch_bwd_t<128>(a, l, s, ev) : launch_bwd_t<64>(a, l, s, ev);
+  if (r3) return head_dim == 128 ? launch_bwd_t<128, true>(a, l, s, ev) : launch_bwd_t<64, true>(a, l, s, ev);
+  return head_dim == 128 ? launch_bwd_t<128, false>(a, l, s, ev) : launch_bwd_t<64, false>(a, l, s, ev);
 }
 
 }  // namespace mf

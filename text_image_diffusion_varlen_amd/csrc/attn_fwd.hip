@@ -42,6 +42,7 @@ struct AttnArgs {
   const int32_t* grid_hw;   // caller's (h, w) per sample
   const int32_t* text_len;  // caller's prompt length per sample
   const float2* cs;         // cos/sin table [ROPE_PMAX][d/4]
+  Rope3 r3;                 // frame-aware RoPE of editing samples (R3 kernels)
   const void* qw;           // rotated queries in the workspace (f32 kernel)
   const void* kw;
   const void* vw;
@@ -165,7 +166,7 @@ __device__ inline void attend_tile(const u32x4* kt, const u32x4* vt, const bf16x
   }
 }
 
-template <int D>
+template <int D, bool R3>
 __global__ void __launch_bounds__(ATTN_THREADS, 2) attn_fwd_bf16_kernel(AttnArgs a) {
   constexpr int CHUNKS = Bf16Tile<D>::CHUNKS;
   constexpr int KSTEPS = Bf16Tile<D>::KSTEPS;
@@ -193,13 +194,17 @@ __global__ void __launch_bounds__(ATTN_THREADS, 2) attn_fwd_bf16_kernel(AttnArgs
   bf16x8 qreg[KSTEPS];
   {
     const int32_t u = min(qs + 32 * wave + l32, L - 1);
-    int32_t row, col;
-    token_position(u, a.text_len[seg], a.grid_hw[2 * seg + 1], row, col);
+    int32_t row, col, frame = 0;
+    if constexpr (R3) token_position3(u, a.text_len[seg], a.grid_hw[2 * seg], a.grid_hw[2 * seg + 1], row, col, frame);
+    else token_position(u, a.text_len[seg], a.grid_hw[2 * seg + 1], row, col);
     const uint16_t* qrow = static_cast<const uint16_t*>(a.q) + (int64_t(cb + u) * heads + h) * D + 8 * hf;
 #pragma unroll
     for (int ks = 0; ks < KSTEPS; ++ks) {
       const Chunk<uint16_t> raw = *reinterpret_cast<const Chunk<uint16_t>*>(qrow + 16 * ks);
-      qreg[ks] = __builtin_bit_cast(bf16x8, rotate_chunk<uint16_t, D>(raw, 16 * ks + 8 * hf, row, col, a.cs));
+      if constexpr (R3)
+        qreg[ks] = __builtin_bit_cast(bf16x8, rotate_chunk3<uint16_t, D>(raw, 16 * ks + 8 * hf, row, col, frame, a.r3));
+      else
+        qreg[ks] = __builtin_bit_cast(bf16x8, rotate_chunk<uint16_t, D>(raw, 16 * ks + 8 * hf, row, col, a.cs));
     }
   }
   // The tile copies share the in-order vector-memory counter with these
@@ -347,7 +352,7 @@ __global__ void __launch_bounds__(ATTN_THREADS) attn_fwd_f32_kernel(AttnArgs a) 
 }
 
 hipError_t launch_attn_fwd(const char* ws, const WsLayout& l, const void* q, const int32_t* grid_hw,
-                           const int32_t* text_len, const float2* cs, void* out, float* lse,
+                           const int32_t* text_len, const float2* cs, const Rope3* r3, void* out, float* lse,
                            int64_t tokens, int32_t heads, int32_t head_dim, bool bf16, float scale,
                            hipStream_t s) {
   AttnArgs a;
@@ -356,6 +361,7 @@ hipError_t launch_attn_fwd(const char* ws, const WsLayout& l, const void* q, con
   a.grid_hw = grid_hw;
   a.text_len = text_len;
   a.cs = cs;
+  a.r3 = r3 ? *r3 : Rope3{nullptr, 0, 0};
   a.off_len = l.off_len;
   a.off_cu = l.off_cu;
   a.off_pcu = l.off_pcu;
@@ -371,8 +377,13 @@ hipError_t launch_attn_fwd(const char* ws, const WsLayout& l, const void* q, con
   a.c_log2 = scale * 1.4426950408889634f;
   const dim3 grid(unsigned(l.n_tiles * heads));
   if (bf16) {
-    if (head_dim == 128) hipLaunchKernelGGL(attn_fwd_bf16_kernel<128>, grid, dim3(ATTN_THREADS), 0, s, a);
-    else hipLaunchKernelGGL(attn_fwd_bf16_kernel<64>, grid, dim3(ATTN_THREADS), 0, s, a);
+    if (r3) {
+      if (head_dim == 128) hipLaunchKernelGGL((attn_fwd_bf16_kernel<128, true>), grid, dim3(ATTN_THREADS), 0, s, a);
+      else hipLaunchKernelGGL((attn_fwd_bf16_kernel<64, true>), grid, dim3(ATTN_THREADS), 0, s, a);
+    } else {
+      if (head_dim == 128) hipLaunchKernelGGL((attn_fwd_bf16_kernel<128, false>), grid, dim3(ATTN_THREADS), 0, s, a);
+      else hipLaunchKernelGGL((attn_fwd_bf16_kernel<64, false>), grid, dim3(ATTN_THREADS), 0, s, a);
+    }
   } else {
     if (head_dim == 128) hipLaunchKernelGGL(attn_fwd_f32_kernel<128>, grid, dim3(ATTN_THREADS), 0, s, a);
     else hipLaunchKernelGGL(attn_fwd_f32_kernel<64>, grid, dim3(ATTN_THREADS), 0, s, a);

@@ -3,7 +3,10 @@
 // Samples are packed back to back and attention is kept inside each sample
 // by per-sample cumulative offsets (Mage-Flow tech report, NR-MMDiT section,
 // native-resolution packing paragraph). Sample i is its prompt followed by
-// its flattened h_i x w_i latent grid, so L_i = text_len_i + h_i * w_i.
+// its flattened h_i x w_i latent grid, so L_i = text_len_i + h_i * w_i; an
+// editing sample (same section, editing paragraph) carries f_i images of one
+// grid after its prompt, L_i = text_len_i + f_i * h_i * w_i (f_i = 1 when no
+// frame counts are given).
 //
 // meta_kernel (one workgroup) validates the caller's offsets and builds what
 // the prologue and the attention kernel need:
@@ -13,7 +16,8 @@
 //   tiles[]  = (sample, first query row) of every QTILE-row query tile,
 //              samples in order of decreasing L_i (longest processing time
 //              first), so the heaviest workgroups are dispatched first.
-// positions_kernel writes the per-token (row, col) and sample id.
+// positions_kernel writes the per-token (row, col) (or (row, col, frame)) and
+// sample id.
 #include "mf_common.h"
 
 namespace mf {
@@ -68,18 +72,26 @@ struct MetaShared {
   int32_t bad;
 };
 
-// L_i of every sample into sh.len (1 for an invalid sample) and the range
-// checks: 1 <= h, w <= ROPE_PMAX, 0 <= text_len <= 2^30.
-__device__ inline void load_lengths(const int32_t* grid_hw, const int32_t* text_len, int32_t n,
-                                    MetaShared& sh) {
+// L_i of sample i and its range checks: 1 <= h, w <= ROPE_PMAX,
+// 0 <= text_len <= 2^30, 1 <= frames <= ROPE_PMAX (frames == nullptr: one image).
+__device__ inline int32_t sample_length(const int32_t* grid_hw, const int32_t* text_len, const int32_t* frames,
+                                        int i, bool& ok) {
+  const int32_t h = grid_hw[2 * i], w = grid_hw[2 * i + 1], tl = text_len[i];
+  const int32_t f = frames ? frames[i] : 1;
+  ok = h >= 1 && w >= 1 && h <= ROPE_PMAX && w <= ROPE_PMAX && tl >= 0 && tl <= MAX_TEXT_LEN && f >= 1 &&
+       f <= ROPE_PMAX;
+  return ok ? tl + f * h * w : 1;  // f h w <= 2^27: no overflow
+}
+
+// L_i of every sample into sh.len (1 for an invalid sample) and the range checks.
+__device__ inline void load_lengths(const int32_t* grid_hw, const int32_t* text_len, const int32_t* frames,
+                                    int32_t n, MetaShared& sh) {
   const int t = threadIdx.x;
   if (t == 0) sh.bad = 0;
   __syncthreads();
   for (int i = t; i < n; i += META_THREADS) {
-    const int32_t h = grid_hw[2 * i], w = grid_hw[2 * i + 1], tl = text_len[i];
-    const bool ok = h >= 1 && w >= 1 && h <= ROPE_PMAX && w <= ROPE_PMAX && tl >= 0 &&
-                    tl <= MAX_TEXT_LEN;
-    sh.len[i] = ok ? tl + h * w : 1;
+    bool ok;
+    sh.len[i] = sample_length(grid_hw, text_len, frames, i, ok);
     if (!ok) atomicOr(&sh.bad, 1);
   }
   __syncthreads();
@@ -119,17 +131,14 @@ __device__ inline int64_t wave_inclusive_scan(int64_t x) {
 // The same derivation as meta_kernel for n <= 64, by the first wave alone:
 // lane i owns sample i. No LDS and no workgroup barriers.
 __device__ inline void meta_small(const int32_t* __restrict__ grid_hw, const int32_t* __restrict__ text_len,
-                                  const int32_t* __restrict__ cu_in, int32_t n, int64_t tokens,
+                                  const int32_t* __restrict__ frames, const int32_t* __restrict__ cu_in,
+                                  int32_t n, int64_t tokens,
                                   WsHeader* hdr, int32_t* len, int32_t* cu, int32_t* pcu, int2* tiles) {
   const int i = threadIdx.x;
   const bool mine = i < n;
   int32_t L = 0;
   bool ok = true;
-  if (mine) {
-    const int32_t h = grid_hw[2 * i], w = grid_hw[2 * i + 1], tl = text_len[i];
-    ok = h >= 1 && w >= 1 && h <= ROPE_PMAX && w <= ROPE_PMAX && tl >= 0 && tl <= MAX_TEXT_LEN;
-    L = ok ? tl + h * w : 1;
-  }
+  if (mine) L = sample_length(grid_hw, text_len, frames, i, ok);
   const int64_t incl = wave_inclusive_scan(L);
   const int64_t total = __shfl(incl, 63);
   const int64_t excl = incl - L;
@@ -180,7 +189,8 @@ __device__ inline void meta_small(const int32_t* __restrict__ grid_hw, const int
 // Validates and derives the packing metadata of one call into the workspace.
 __global__ void __launch_bounds__(META_THREADS)
 meta_kernel(const int32_t* __restrict__ grid_hw, const int32_t* __restrict__ text_len,
-            const int32_t* __restrict__ cu_in, int32_t n, int64_t tokens, char* __restrict__ ws,
+            const int32_t* __restrict__ frames, const int32_t* __restrict__ cu_in, int32_t n, int64_t tokens,
+            char* __restrict__ ws,
             int64_t off_len, int64_t off_cu, int64_t off_pcu, int64_t off_tiles,
             int64_t tile_capacity) {
   __shared__ MetaShared sh;
@@ -192,11 +202,11 @@ meta_kernel(const int32_t* __restrict__ grid_hw, const int32_t* __restrict__ tex
   const int t = threadIdx.x;
   if (n <= 64) {
     // Up to 64 samples: one wave, one lane per sample, wave-level scans.
-    if (t < 64) meta_small(grid_hw, text_len, cu_in, n, tokens, hdr, len, cu, pcu, tiles);
+    if (t < 64) meta_small(grid_hw, text_len, frames, cu_in, n, tokens, hdr, len, cu, pcu, tiles);
     return;
   }
 
-  load_lengths(grid_hw, text_len, n, sh);
+  load_lengths(grid_hw, text_len, frames, n, sh);
   offsets(n, tokens, sh);
   // The caller's offsets must be exactly these prefix sums.
   for (int i = t; i <= n; i += META_THREADS) {
@@ -276,16 +286,19 @@ meta_kernel(const int32_t* __restrict__ grid_hw, const int32_t* __restrict__ tex
 // FLAG_METADATA into *status when a sample is out of range or the packed
 // length differs from `tokens`.
 __global__ void __launch_bounds__(META_THREADS)
-offsets_kernel(const int32_t* __restrict__ grid_hw, const int32_t* __restrict__ text_len, int32_t n,
-               int64_t tokens, int32_t* __restrict__ cu_out, int32_t* __restrict__ status) {
+offsets_kernel(const int32_t* __restrict__ grid_hw, const int32_t* __restrict__ text_len,
+               const int32_t* __restrict__ frames, int32_t n, int64_t tokens, int32_t* __restrict__ cu_out,
+               int32_t* __restrict__ status) {
   __shared__ MetaShared sh;
-  load_lengths(grid_hw, text_len, n, sh);
+  load_lengths(grid_hw, text_len, frames, n, sh);
   offsets(n, tokens, sh);
   for (int i = threadIdx.x; i <= n; i += META_THREADS) cu_out[i] = sh.pre[i];
   if (threadIdx.x == 0 && sh.bad) atomicOr(status, FLAG_METADATA);
 }
 
-// Per-token position and sample id, for tokens below both the capacity and cu[n].
+// Per-token position and sample id, for tokens below both the capacity and
+// cu[n]. THREE: (row, col, frame) per token, else (row, col).
+template <bool THREE>
 __global__ void __launch_bounds__(256)
 positions_kernel(const int32_t* __restrict__ grid_hw, const int32_t* __restrict__ text_len,
                  const int32_t* __restrict__ cu, int32_t n, int64_t tokens,
@@ -293,28 +306,40 @@ positions_kernel(const int32_t* __restrict__ grid_hw, const int32_t* __restrict_
   const int64_t x = int64_t(blockIdx.x) * blockDim.x + threadIdx.x;
   if (x >= tokens || x >= cu[n]) return;
   const int32_t i = upper_segment(cu, n, x);
-  int32_t r, c;
-  token_position(int32_t(x - cu[i]), text_len[i], max(grid_hw[2 * i + 1], 1), r, c);
-  pos[2 * x] = r;
-  pos[2 * x + 1] = c;
+  int32_t r, c, f;
+  token_position3(int32_t(x - cu[i]), text_len[i], max(grid_hw[2 * i], 1), max(grid_hw[2 * i + 1], 1), r, c, f);
+  if (THREE) {
+    pos[3 * x] = r;
+    pos[3 * x + 1] = c;
+    pos[3 * x + 2] = f;
+  } else {
+    pos[2 * x] = r;
+    pos[2 * x + 1] = c;
+  }
   seg_id[x] = i;
 }
 
-hipError_t launch_meta(const int32_t* grid_hw, const int32_t* text_len, const int32_t* cu_in,
-                       int32_t n, int64_t tokens, char* ws, const WsLayout& l, hipStream_t s) {
-  hipLaunchKernelGGL(meta_kernel, dim3(1), dim3(META_THREADS), 0, s, grid_hw, text_len, cu_in, n,
+hipError_t launch_meta(const int32_t* grid_hw, const int32_t* text_len, const int32_t* frames,
+                       const int32_t* cu_in, int32_t n, int64_t tokens, char* ws, const WsLayout& l,
+                       hipStream_t s) {
+  hipLaunchKernelGGL(meta_kernel, dim3(1), dim3(META_THREADS), 0, s, grid_hw, text_len, frames, cu_in, n,
                      tokens, ws, l.off_len, l.off_cu, l.off_pcu, l.off_tiles, l.n_tiles);
   return hipGetLastError();
 }
 
-hipError_t launch_build_metadata(const int32_t* grid_hw, const int32_t* text_len, int32_t n,
-                                 int64_t tokens, int32_t* cu_out, int32_t* pos, int32_t* seg_id,
+hipError_t launch_build_metadata(const int32_t* grid_hw, const int32_t* text_len, const int32_t* frames,
+                                 int32_t n, int64_t tokens, int32_t* cu_out, int32_t* pos, int32_t* seg_id,
                                  int32_t* status, hipStream_t s) {
-  hipLaunchKernelGGL(offsets_kernel, dim3(1), dim3(META_THREADS), 0, s, grid_hw, text_len, n,
+  hipLaunchKernelGGL(offsets_kernel, dim3(1), dim3(META_THREADS), 0, s, grid_hw, text_len, frames, n,
                      tokens, cu_out, status);
   const int64_t blocks = ceil_div(tokens, 256);
-  hipLaunchKernelGGL(positions_kernel, dim3(unsigned(blocks)), dim3(256), 0, s, grid_hw, text_len,
-                     cu_out, n, tokens, pos, seg_id);
+  if (frames) {
+    hipLaunchKernelGGL(positions_kernel<true>, dim3(unsigned(blocks)), dim3(256), 0, s, grid_hw, text_len,
+                       cu_out, n, tokens, pos, seg_id);
+  } else {
+    hipLaunchKernelGGL(positions_kernel<false>, dim3(unsigned(blocks)), dim3(256), 0, s, grid_hw, text_len,
+                       cu_out, n, tokens, pos, seg_id);
+  }
   return hipGetLastError();
 }
 

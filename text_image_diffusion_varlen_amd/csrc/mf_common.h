@@ -120,6 +120,22 @@ __device__ inline void token_position(int32_t u, int32_t text_len, int32_t w, in
   }
 }
 
+// Position of token u of an editing sample (prompt, then `frames` images of
+// one h x w grid): prompt tokens at (0, 0, 0), visual token p = u - text_len
+// of image f = p / (h w) at (row, col) = ((p mod h w) / w, p mod w).
+__device__ inline void token_position3(int32_t u, int32_t text_len, int32_t h, int32_t w, int32_t& row,
+                                       int32_t& col, int32_t& frame) {
+  if (u < text_len) {
+    row = col = frame = 0;
+  } else {
+    const int32_t p = u - text_len, hw = h * w;
+    frame = p / hw;
+    const int32_t q = p - frame * hw;
+    row = q / w;
+    col = q - row * w;
+  }
+}
+
 // Largest i in [0, n) with a[i] <= x, for a non-decreasing a[0..n] with a[0] <= x.
 __device__ inline int32_t upper_segment(const int32_t* a, int32_t n, int64_t x) {
   int32_t lo = 0, hi = n;  // invariant a[lo] <= x < a[hi] (a[n] treated as +inf if x beyond)

@@ -11,6 +11,10 @@
 // double precision (entry (p, j) = cos/sin of p * theta^(-2j/(d/2))); the
 // device does the rotation in fp32.
 //
+// Editing samples (tech report, NR-MMDiT editing paragraph) use the
+// frame-aware variant: (row, col, frame) positions, three channel blocks
+// (rope_math.h, Rope3).
+//
 // rope_pack_kernel is the prologue of the attention path. One workgroup per
 // (KTILE-row tile of the padded layout, head). It rotates the keys (and, for
 // f32, the queries) of every token of the tile and writes into the workspace:
@@ -34,13 +38,14 @@
 
 namespace mf {
 
-template <typename T, int D>
+// R3: editing samples with frame-aware (row, col, frame) RoPE (r3), else 2D (cs).
+template <typename T, int D, bool R3>
 __global__ void __launch_bounds__(256)
 rope_pack_kernel(const T* __restrict__ q, const T* __restrict__ k, const T* __restrict__ v,
                  const int32_t* __restrict__ grid_hw, const int32_t* __restrict__ text_len,
                  const char* __restrict__ ws, int64_t off_len, int64_t off_cu, int64_t off_pcu,
                  T* __restrict__ qw, T* __restrict__ kw, T* __restrict__ vw,
-                 const float2* __restrict__ cs, int32_t heads, int64_t rows) {
+                 const float2* __restrict__ cs, Rope3 r3, int32_t heads, int64_t rows) {
   constexpr int E = Elem<T>::PER_CHUNK;
   constexpr int CPR = D / E;             // chunks per row
   constexpr int CPT = KTILE * CPR;       // chunks per tile
@@ -53,7 +58,7 @@ rope_pack_kernel(const T* __restrict__ q, const T* __restrict__ k, const T* __re
   const int64_t r0 = int64_t(blockIdx.x) * KTILE;
   const int h = blockIdx.y;
   const int32_t n = hdr->n_seg;
-  int32_t u0 = 0, L = 0, tl = 0, w = 1;
+  int32_t u0 = 0, L = 0, tl = 0, w = 1, gh = 1;
   int64_t tok0 = 0;
   if (r0 < hdr->padded_total) {
     const int32_t s = upper_segment(pcu, n, r0);
@@ -61,8 +66,21 @@ rope_pack_kernel(const T* __restrict__ q, const T* __restrict__ k, const T* __re
     L = len[s];
     tok0 = int64_t(cu[s]) + u0;
     tl = text_len[s];
+    gh = grid_hw[2 * s];
     w = grid_hw[2 * s + 1];
   }
+  // Rotation of chunk cc (channels cc*E ..) of sample token u.
+  auto rotate = [&](const Chunk<T>& x, int cc, int32_t u) {
+    if constexpr (R3) {
+      int32_t row, col, frame;
+      token_position3(u, tl, gh, w, row, col, frame);
+      return rotate_chunk3<T, D>(x, cc * E, row, col, frame, r3);
+    } else {
+      int32_t row, col;
+      token_position(u, tl, w, row, col);
+      return rotate_chunk<T, D>(x, cc * E, row, col, cs);
+    }
+  };
   const int64_t tile_off = (int64_t(h) * rows + r0) * D;
   const int64_t src_stride = int64_t(heads) * D;  // elements between consecutive tokens
 
@@ -73,11 +91,9 @@ rope_pack_kernel(const T* __restrict__ q, const T* __restrict__ k, const T* __re
       const int32_t u = u0 + rr;
       Chunk<T> qo, ko;
       if (u < L) {
-        int32_t row, col;
-        token_position(u, tl, w, row, col);
         const int64_t src = (tok0 + rr) * src_stride + int64_t(h) * D + cc * E;
-        qo = rotate_chunk<T, D>(*reinterpret_cast<const Chunk<T>*>(q + src), cc * E, row, col, cs);
-        ko = rotate_chunk<T, D>(*reinterpret_cast<const Chunk<T>*>(k + src), cc * E, row, col, cs);
+        qo = rotate(*reinterpret_cast<const Chunk<T>*>(q + src), cc, u);
+        ko = rotate(*reinterpret_cast<const Chunk<T>*>(k + src), cc, u);
       } else {
 #pragma unroll
         for (int e = 0; e < E; ++e) qo.v[e] = ko.v[e] = T(0);
@@ -114,10 +130,8 @@ rope_pack_kernel(const T* __restrict__ q, const T* __restrict__ k, const T* __re
       const int32_t u = u0 + rr;
       Chunk<T> ko, vi;
       if (u < L) {
-        int32_t row, col;
-        token_position(u, tl, w, row, col);
         const int64_t src = (tok0 + rr) * src_stride + int64_t(h) * D + cc * E;
-        ko = rotate_chunk<T, D>(*reinterpret_cast<const Chunk<T>*>(k + src), cc * E, row, col, cs);
+        ko = rotate(*reinterpret_cast<const Chunk<T>*>(k + src), cc, u);
         vi = *reinterpret_cast<const Chunk<T>*>(v + src);
       } else {
 #pragma unroll
@@ -151,78 +165,99 @@ rope_pack_kernel(const T* __restrict__ q, const T* __restrict__ k, const T* __re
   }
 }
 
-// Standalone RoPE: x_out = R(pos) x_in for [tokens][heads][D]. Positions
-// outside [0, ROPE_PMAX) copy the row unchanged and flag FLAG_POSITION.
-template <typename T, int D>
+// Standalone RoPE: x_out = R(pos) x_in for [tokens][heads][D]; pos is
+// [tokens][2] (2D) or [tokens][3] (R3: row, col, frame). Positions outside
+// [0, ROPE_PMAX) copy the row unchanged and flag FLAG_POSITION.
+template <typename T, int D, bool R3>
 __global__ void __launch_bounds__(256)
 rope_kernel(const T* __restrict__ x, T* __restrict__ y, const int32_t* __restrict__ pos,
-            int64_t tokens, int32_t heads, const float2* __restrict__ cs, int32_t* status) {
+            int64_t tokens, int32_t heads, const float2* __restrict__ cs, Rope3 r3, int32_t* status) {
   constexpr int E = Elem<T>::PER_CHUNK;
   constexpr int CPR = D / E;
+  constexpr int NP = R3 ? 3 : 2;
   const int64_t f = int64_t(blockIdx.x) * 256 + threadIdx.x;
   if (f >= tokens * heads * CPR) return;
   const int64_t t = f / (int64_t(heads) * CPR);
   const int cc = int(f % CPR);
-  const int32_t row = pos[2 * t], col = pos[2 * t + 1];
+  const int32_t row = pos[NP * t], col = pos[NP * t + 1], frame = R3 ? pos[NP * t + 2] : 0;
   const Chunk<T> in = *reinterpret_cast<const Chunk<T>*>(x + f * E);
   Chunk<T> out;
-  if (row < 0 || col < 0 || row >= ROPE_PMAX || col >= ROPE_PMAX) {
+  if (row < 0 || col < 0 || frame < 0 || row >= ROPE_PMAX || col >= ROPE_PMAX || frame >= ROPE_PMAX) {
     out = in;
     if (cc == 0) atomicOr(status, FLAG_POSITION);
+  } else if constexpr (R3) {
+    out = rotate_chunk3<T, D>(in, cc * E, row, col, frame, r3);
   } else {
     out = rotate_chunk<T, D>(in, cc * E, row, col, cs);
   }
   *reinterpret_cast<Chunk<T>*>(y + f * E) = out;
 }
 
-template <typename T, int D>
+template <typename T, int D, bool R3>
 static hipError_t launch_rope_pack_t(const void* q, const void* k, const void* v,
                                      const int32_t* grid_hw, const int32_t* text_len,
-                                     const char* ws, const WsLayout& l, const float2* cs,
+                                     const char* ws, const WsLayout& l, const float2* cs, Rope3 r3,
                                      int32_t heads, hipStream_t s) {
   char* w = const_cast<char*>(ws);
   dim3 grid(unsigned(l.rows / KTILE), unsigned(heads));
-  hipLaunchKernelGGL((rope_pack_kernel<T, D>), grid, dim3(256), 0, s,
+  hipLaunchKernelGGL((rope_pack_kernel<T, D, R3>), grid, dim3(256), 0, s,
                      static_cast<const T*>(q), static_cast<const T*>(k), static_cast<const T*>(v),
                      grid_hw, text_len, ws, l.off_len, l.off_cu, l.off_pcu,
                      reinterpret_cast<T*>(w + l.off_q), reinterpret_cast<T*>(w + l.off_k),
-                     reinterpret_cast<T*>(w + l.off_v), cs, heads, l.rows);
+                     reinterpret_cast<T*>(w + l.off_v), cs, r3, heads, l.rows);
   return hipGetLastError();
 }
 
+template <typename T, bool R3>
+static hipError_t launch_rope_pack_d(const void* q, const void* k, const void* v, const int32_t* grid_hw,
+                                     const int32_t* text_len, const char* ws, const WsLayout& l,
+                                     const float2* cs, Rope3 r3, int32_t heads, int32_t head_dim, hipStream_t s) {
+  return head_dim == 128 ? launch_rope_pack_t<T, 128, R3>(q, k, v, grid_hw, text_len, ws, l, cs, r3, heads, s)
+                         : launch_rope_pack_t<T, 64, R3>(q, k, v, grid_hw, text_len, ws, l, cs, r3, heads, s);
+}
+
+// r3 == nullptr: 2D RoPE with the table cs; else frame-aware RoPE.
 hipError_t launch_rope_pack(const void* q, const void* k, const void* v, const int32_t* grid_hw,
                             const int32_t* text_len, const char* ws, const WsLayout& l,
-                            const float2* cs, int32_t heads, int32_t head_dim, bool bf16,
+                            const float2* cs, const Rope3* r3, int32_t heads, int32_t head_dim, bool bf16,
                             hipStream_t s) {
+  const Rope3 r = r3 ? *r3 : Rope3{nullptr, 0, 0};
   if (bf16) {
-    return head_dim == 128
-               ? launch_rope_pack_t<uint16_t, 128>(q, k, v, grid_hw, text_len, ws, l, cs, heads, s)
-               : launch_rope_pack_t<uint16_t, 64>(q, k, v, grid_hw, text_len, ws, l, cs, heads, s);
+    return r3 ? launch_rope_pack_d<uint16_t, true>(q, k, v, grid_hw, text_len, ws, l, cs, r, heads, head_dim, s)
+              : launch_rope_pack_d<uint16_t, false>(q, k, v, grid_hw, text_len, ws, l, cs, r, heads, head_dim, s);
   }
-  return head_dim == 128
-             ? launch_rope_pack_t<float, 128>(q, k, v, grid_hw, text_len, ws, l, cs, heads, s)
-             : launch_rope_pack_t<float, 64>(q, k, v, grid_hw, text_len, ws, l, cs, heads, s);
+  return r3 ? launch_rope_pack_d<float, true>(q, k, v, grid_hw, text_len, ws, l, cs, r, heads, head_dim, s)
+            : launch_rope_pack_d<float, false>(q, k, v, grid_hw, text_len, ws, l, cs, r, heads, head_dim, s);
 }
 
-template <typename T, int D>
+template <typename T, int D, bool R3>
 static hipError_t launch_rope_t(const void* x, void* y, const int32_t* pos, int64_t tokens,
-                                int32_t heads, const float2* cs, int32_t* status, hipStream_t s) {
+                                int32_t heads, const float2* cs, Rope3 r3, int32_t* status, hipStream_t s) {
   constexpr int CPR = D / Elem<T>::PER_CHUNK;
   const int64_t chunks = tokens * heads * CPR;
-  hipLaunchKernelGGL((rope_kernel<T, D>), dim3(unsigned(ceil_div(chunks, 256))), dim3(256), 0, s,
-                     static_cast<const T*>(x), static_cast<T*>(y), pos, tokens, heads, cs, status);
+  hipLaunchKernelGGL((rope_kernel<T, D, R3>), dim3(unsigned(ceil_div(chunks, 256))), dim3(256), 0, s,
+                     static_cast<const T*>(x), static_cast<T*>(y), pos, tokens, heads, cs, r3, status);
   return hipGetLastError();
 }
 
-hipError_t launch_rope(const void* x, void* y, const int32_t* pos, int64_t tokens, int32_t heads,
-                       int32_t head_dim, bool bf16, const float2* cs, int32_t* status,
-                       hipStream_t s) {
+template <bool R3>
+static hipError_t launch_rope_r(const void* x, void* y, const int32_t* pos, int64_t tokens, int32_t heads,
+                                int32_t head_dim, bool bf16, const float2* cs, Rope3 r3, int32_t* status,
+                                hipStream_t s) {
   if (bf16) {
-    return head_dim == 128 ? launch_rope_t<uint16_t, 128>(x, y, pos, tokens, heads, cs, status, s)
-                           : launch_rope_t<uint16_t, 64>(x, y, pos, tokens, heads, cs, status, s);
+    return head_dim == 128 ? launch_rope_t<uint16_t, 128, R3>(x, y, pos, tokens, heads, cs, r3, status, s)
+                           : launch_rope_t<uint16_t, 64, R3>(x, y, pos, tokens, heads, cs, r3, status, s);
   }
-  return head_dim == 128 ? launch_rope_t<float, 128>(x, y, pos, tokens, heads, cs, status, s)
-                         : launch_rope_t<float, 64>(x, y, pos, tokens, heads, cs, status, s);
+  return head_dim == 128 ? launch_rope_t<float, 128, R3>(x, y, pos, tokens, heads, cs, r3, status, s)
+                         : launch_rope_t<float, 64, R3>(x, y, pos, tokens, heads, cs, r3, status, s);
+}
+
+// r3 == nullptr: 2D positions [tokens][2] with table cs; else [tokens][3].
+hipError_t launch_rope(const void* x, void* y, const int32_t* pos, int64_t tokens, int32_t heads,
+                       int32_t head_dim, bool bf16, const float2* cs, const Rope3* r3, int32_t* status,
+                       hipStream_t s) {
+  if (r3) return launch_rope_r<true>(x, y, pos, tokens, heads, head_dim, bf16, cs, *r3, status, s);
+  return launch_rope_r<false>(x, y, pos, tokens, heads, head_dim, bf16, cs, Rope3{nullptr, 0, 0}, status, s);
 }
 
 }  // namespace mf

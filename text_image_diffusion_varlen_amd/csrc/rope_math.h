@@ -44,4 +44,36 @@ __device__ inline Chunk<T> rotate_chunk(const Chunk<T>& in, int d0, int32_t row,
   return out;
 }
 
+// Frame-aware RoPE (editing samples: (row, col, frame) positions). Channel
+// pairs k = 0 .. D/2-1 in three contiguous blocks: [0, b1) turn by the row,
+// [b1, b2) by the column, [b2, D/2) by the frame; each block has its own
+// frequency ladder theta^(-2j/m), m = channels of the block. The cos/sin
+// table is [ROPE_PMAX][D/2], entry (p, k) = cos/sin of p times pair k's
+// frequency, computed on the host in double precision.
+struct Rope3 {
+  const float2* cs;
+  int32_t b1, b2;
+};
+
+__device__ inline float2 rope3_cs(const Rope3& r, int D, int k, int32_t row, int32_t col, int32_t frame) {
+  const int32_t p = k < r.b1 ? row : (k < r.b2 ? col : frame);
+  return r.cs[p * (D / 2) + k];
+}
+
+template <typename T, int D>
+__device__ inline Chunk<T> rotate_chunk3(const Chunk<T>& in, int d0, int32_t row, int32_t col, int32_t frame,
+                                         const Rope3& r) {
+  constexpr int E = Elem<T>::PER_CHUNK;
+  Chunk<T> out;
+#pragma unroll
+  for (int pp = 0; pp < E / 2; ++pp) {
+    const float2 c = rope3_cs(r, D, d0 / 2 + pp, row, col, frame);
+    const float x0 = Elem<T>::load(in.v[2 * pp]);
+    const float x1 = Elem<T>::load(in.v[2 * pp + 1]);
+    out.v[2 * pp] = Elem<T>::store(x0 * c.x - x1 * c.y);
+    out.v[2 * pp + 1] = Elem<T>::store(x0 * c.y + x1 * c.x);
+  }
+  return out;
+}
+
 }  // namespace mf

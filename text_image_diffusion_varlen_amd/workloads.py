@@ -30,6 +30,8 @@ __all__ = [
     "make_workload",
     "make_segments",
     "make_custom",
+    "EDIT_CONFIGS",
+    "make_edit",
     "CfgBatch",
     "CFG_CONFIGS",
     "make_cfg_batch",
@@ -72,6 +74,8 @@ class Workload:
     k: np.ndarray = field(repr=False)
     v: np.ndarray = field(repr=False)
     seed: int = 0
+    frames: np.ndarray | None = None  # int32 [n]: images per editing sample (None: one image each)
+    rope_split: tuple | None = None   # (row, col, frame) channels of the frame-aware RoPE
 
     @property
     def n_seg(self) -> int:
@@ -285,3 +289,43 @@ def make_cfg_config(config: str, seed: int | None = None, layout="interleaved") 
     seed = c["seed"] if seed is None else seed
     return make_cfg_batch(c["grids"], None, c["uncond_text"], layout, c["channels"], c["dtype"], seed,
                           name=config)
+
+
+# Editing batches (tech report, NR-MMDiT editing paragraph): each sample is its
+# instruction, then the source image latents, then the target latents, all on
+# one grid; `frames` counts the images. The frame-aware RoPE split gives the
+# row, column and frame blocks of a 128-channel head 48, 48 and 32 channels
+# (the pages do not fix it; this is the proportion of the multimodal rotary
+# layout of the Qwen-VL encoders Mage-Flow builds on), 24/24/16 for 64.
+EDIT_SPLIT = {128: (48, 48, 32), 64: (24, 24, 16)}
+EDIT_CONFIGS = {
+    # One 1024x1024 edit: a 256-token instruction, a source and a target 64x64 grid.
+    "edit1024": dict(grids=[(64, 64)], texts=[256], frames=[2], heads=24, head_dim=128, dtype="bf16", seed=8),
+    # Three edits of mixed aspect, one or two source images, instructions of 77-256 tokens.
+    "edit_mixed": dict(grids=[(32, 128), (64, 64), (48, 84)], texts="draw", frames=[2, 3, 2], heads=24,
+                       head_dim=128, dtype="bf16", seed=9),
+}
+
+
+def make_edit(config=None, grids=None, texts=None, frames=None, heads=None, head_dim=None, dtype=None, seed=None,
+              split=None, scale=1.0, name="edit") -> Workload:
+    """An editing batch: a named config of EDIT_CONFIGS, or explicit segments.
+    Draw order: prompt lengths (when drawn), then q, k, v as for make_workload."""
+    if config is not None:
+        c = EDIT_CONFIGS[config]
+        grids, texts, frames = c["grids"], c["texts"], c["frames"]
+        heads = c["heads"] if heads is None else heads
+        head_dim = c["head_dim"] if head_dim is None else head_dim
+        dtype = c["dtype"] if dtype is None else dtype
+        seed = c["seed"] if seed is None else seed
+        name = config
+    rng = np.random.default_rng(0 if seed is None else seed)
+    if isinstance(texts, str):
+        texts = rng.integers(77, 257, size=len(grids)).tolist()
+    grid_hw = np.asarray(grids, dtype=np.int32).reshape(-1, 2)
+    text_len = np.asarray(texts, dtype=np.int32).reshape(-1)
+    fr = np.asarray(frames, dtype=np.int32).reshape(-1)
+    n_tokens = int(text_len.astype(np.int64).sum() + (fr.astype(np.int64) * grid_hw[:, 0] * grid_hw[:, 1]).sum())
+    q, k, v = _draw_qkv(rng, n_tokens, heads, head_dim, dtype, scale)
+    split = EDIT_SPLIT[head_dim] if split is None else tuple(split)
+    return Workload(name, grid_hw, text_len, heads, head_dim, dtype, q, k, v, 0 if seed is None else seed, fr, split)
