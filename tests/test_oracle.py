@@ -618,3 +618,53 @@ def test_attention_3d_backward_finite_differences():
     np.testing.assert_allclose(dq, _numeric_grad(lambda x: loss(x, k, v), q), atol=1e-7)
     np.testing.assert_allclose(dk, _numeric_grad(lambda x: loss(q, x, v), k), atol=1e-7)
     np.testing.assert_allclose(dv, _numeric_grad(lambda x: loss(q, k, x), v), atol=1e-7)
+
+
+# ---------------------------------------------------------------- RMSNorm + packed QKV
+
+from oracle import projection  # noqa: E402
+
+
+def test_rmsnorm_closed_forms():
+    rng = np.random.default_rng(70)
+    x = rng.standard_normal((6, 32))
+    h = projection.rmsnorm(x, np.ones(32), eps=0.0)
+    np.testing.assert_allclose(np.mean(h * h, axis=-1), 1.0, atol=1e-14)   # unit RMS
+    np.testing.assert_allclose(projection.rmsnorm(7.5 * x, np.ones(32), eps=0.0), h, atol=1e-13)  # scale-free
+    ms = np.mean(x * x, axis=-1)
+    he = projection.rmsnorm(x, np.ones(32), eps=0.25)
+    np.testing.assert_allclose(np.mean(he * he, axis=-1), ms / (ms + 0.25), atol=1e-14)
+    g = rng.standard_normal(32)
+    np.testing.assert_allclose(projection.rmsnorm(x, g, eps=0.0), h * g, atol=1e-14)
+    # a constant row c: sqrt(c^2) = |c|, so the row becomes sign(c) * gamma
+    np.testing.assert_allclose(projection.rmsnorm(np.full((1, 4), -3.0), [1, 2, 3, 4], eps=0.0), [[-1, -2, -3, -4]])
+
+
+def test_rmsnorm_qkv_brute_force_and_routing():
+    grid, text, heads, d = [[2, 2], [1, 3]], [3, 1], 2, 4
+    C, hd = 8, heads * d
+    T = 3 + 4 + 1 + 3
+    rng = np.random.default_rng(71)
+    x = rng.standard_normal((T, C))
+    wt, wi = rng.standard_normal((3 * hd, C)), rng.standard_normal((3 * hd, C))
+    gt, gi = rng.standard_normal(C), rng.standard_normal(C)
+    q, k, v = projection.rmsnorm_qkv(x, wt, wi, gt, gi, grid, text, heads, d)
+    is_text = [True] * 3 + [False] * 4 + [True] + [False] * 3
+    for t in range(T):
+        w, g = (wt, gt) if is_text[t] else (wi, gi)
+        r = math.sqrt(sum(float(a) ** 2 for a in x[t]) / C + 1e-6)
+        hrow = [float(x[t, c]) / r * float(g[c]) for c in range(C)]
+        for which, out in enumerate((q, k, v)):
+            for h in range(heads):
+                for j in range(d):
+                    n = which * hd + h * d + j
+                    ref = sum(hrow[c] * float(w[n, c]) for c in range(C))
+                    assert abs(out[t, h, j] - ref) < 1e-12
+    # zero visual weights: visual rows vanish, text rows do not
+    q0, _, _ = projection.rmsnorm_qkv(x, wt, np.zeros_like(wi), gt, gi, grid, text, heads, d)
+    assert not q0[~np.array(is_text)].any() and q0[np.array(is_text)].any()
+
+
+def test_text_mask_editing_samples():
+    m = projection.text_mask([[1, 2], [2, 1]], [2, 0], [3, 2])
+    assert m.tolist() == [True, True] + [False] * 6 + [False] * 4
