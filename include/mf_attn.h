@@ -245,6 +245,50 @@ int mf_rope_2d(const void* x_in, void* x_out, const int32_t* pos, int64_t total_
                int32_t heads, int32_t head_dim, int32_t dtype, float theta, hipStream_t stream);
 
 /*
+ * Modality-specific RMSNorm + packed QKV projection, the prologue that feeds
+ * the joint attention. Sources: Mage-Flow tech report, NR-MMDiT section
+ * (separate normalization and projection layers for the text and the visual
+ * stream of every MMDiT block); mageflow.net architecture page, section 7
+ * (fused RMSNorm, packed linear projections). Readings: RMSNorm over the
+ * hidden channels with a gain per modality, no modulation, no bias; prompt
+ * tokens are "text", every other token "visual".
+ *
+ * mf_qkv_fold_weights folds the gains into the weights once per weight update:
+ *   w_txt, w_img    device bf16 [3 * heads * head_dim][hidden], a linear
+ *                   layer's weight (rows: q, then k, then v, head-major)
+ *   gamma_txt, gamma_img  device float [hidden]
+ *   w_out           device bf16 [2][3 * heads * head_dim][hidden]:
+ *                   w_out[m][n][c] = bf16(gamma_m[c] * w_m[n][c]), m = 0 text
+ * hidden a multiple of 64; heads * head_dim a multiple of 256.
+ */
+int mf_qkv_fold_weights(const void* w_txt, const void* w_img, const float* gamma_txt, const float* gamma_img,
+                        int32_t hidden, int32_t heads, int32_t head_dim, void* w_out, hipStream_t stream);
+
+/*
+ * mf_qkv_rmsnorm: for every token t of modality m,
+ *   [q | k | v][t] = (x[t] / sqrt(mean(x[t]^2) + eps)) (w_folded[m])^T
+ * (fp32 statistics and accumulation, bf16 results).
+ *   x           device bf16 [total_tokens][hidden], packed like the attention input
+ *   w_folded    device bf16 from mf_qkv_fold_weights
+ *   cu_seqlens, grid_hw, text_len  as for mf_attn_packed; frames (device int32
+ *               [n_seg], NULL = one image per sample) as for mf_attn_packed_3d
+ *   q, k, v     device bf16 [total_tokens][heads][head_dim], the attention's inputs
+ * The metadata is checked on the device; on a mismatch nothing is written and
+ * mf_get_device_error() reports MF_ERR_METADATA. Uses a library-owned
+ * per-device workspace (row lists and 1/rms per token, 12 bytes per token),
+ * same stream-order rule as mf_attn_packed.
+ */
+int mf_qkv_rmsnorm(const void* x, const void* w_folded, const int32_t* cu_seqlens, const int32_t* grid_hw,
+                   const int32_t* text_len, const int32_t* frames, int32_t n_seg, int64_t total_tokens, int32_t hidden,
+                   int32_t heads, int32_t head_dim, float eps, void* q, void* k, void* v, hipStream_t stream);
+
+/* mf_qkv_rmsnorm recording three hipEvent_t: before, after the statistics, after the projection. */
+int mf_qkv_rmsnorm_profiled(const void* x, const void* w_folded, const int32_t* cu_seqlens, const int32_t* grid_hw,
+                            const int32_t* text_len, const int32_t* frames, int32_t n_seg, int64_t total_tokens,
+                            int32_t hidden, int32_t heads, int32_t head_dim, float eps, void* q, void* k, void* v,
+                            hipEvent_t const* events, hipStream_t stream);
+
+/*
  * Guided rectified-flow Euler step over a packed classifier-free-guidance batch.
  * Sources: Mage-Flow tech report, NR-MMDiT section (the conditional and the
  * unconditional branch are packed together and evaluated in one forward pass);

@@ -57,6 +57,9 @@ def _declare(lib):
         "mf_build_metadata": ([I32, P, P, P, P, P, I64, P], ctypes.c_int),
         "mf_rope_2d": ([P, P, P, I64, I32, I32, I32, F, P], ctypes.c_int),
         "mf_rf_cfg_euler_step": ([P, P, P, P, P, I32, I64, P, P, I32, I64, I32, I32, F, F, P], ctypes.c_int),
+        "mf_qkv_fold_weights": ([P, P, P, P, I32, I32, I32, P, P], ctypes.c_int),
+        "mf_qkv_rmsnorm": ([P] * 6 + [I32, I64, I32, I32, I32, F, P, P, P, P], ctypes.c_int),
+        "mf_qkv_rmsnorm_profiled": ([P] * 6 + [I32, I64, I32, I32, I32, F, P, P, P, P, P], ctypes.c_int),
         "mf_get_device_error": ([P], ctypes.c_int),
         "mf_get_workspace_error": ([P, P], ctypes.c_int),
     }
@@ -355,6 +358,57 @@ def rf_cfg_euler_step(z, v, cu_seqlens, grid_hw, text_len, cond_seg, uncond_seg,
                                       z.shape[0], z.shape[1], _DTYPES[v.dtype], float(guidance), float(dt),
                                       _stream(stream)))
     return z
+
+
+def qkv_fold_weights(w_txt, w_img, gamma_txt, gamma_img, heads: int, head_dim: int, out=None, stream=None):
+    """Gains folded into the packed QKV weights (mf_qkv_fold_weights): [2, 3HD, hidden] bf16."""
+    for name, t in (("w_txt", w_txt), ("w_img", w_img)):
+        _need(t, name, torch.bfloat16, 2)
+    for name, t in (("gamma_txt", gamma_txt), ("gamma_img", gamma_img)):
+        _need(t, name, torch.float32, 1)
+    n_out, hidden = w_txt.shape
+    if w_img.shape != w_txt.shape or n_out != 3 * heads * head_dim or gamma_txt.shape[0] != hidden \
+            or gamma_img.shape[0] != hidden:
+        raise ValueError("weights must be [3*heads*head_dim, hidden] and gains [hidden]")
+    if out is None:
+        out = torch.empty((2, n_out, hidden), dtype=torch.bfloat16, device=w_txt.device)
+    _need(out, "out", torch.bfloat16, 3)
+    _check(lib().mf_qkv_fold_weights(_ptr(w_txt), _ptr(w_img), _ptr(gamma_txt), _ptr(gamma_img), hidden, heads,
+                                     head_dim, _ptr(out), _stream(stream)))
+    return out
+
+
+def qkv_rmsnorm(x, w_folded, cu_seqlens, grid_hw, text_len, heads: int, head_dim: int, frames=None, eps: float = 1e-6,
+                out=None, events=None, stream=None):
+    """Modality-specific RMSNorm + packed QKV projection (mf_qkv_rmsnorm). Returns (q, k, v) [T, H, d]."""
+    _need(x, "x", torch.bfloat16, 2)
+    _need(w_folded, "w_folded", torch.bfloat16, 3)
+    _need(cu_seqlens, "cu_seqlens", torch.int32, 1)
+    _need(grid_hw, "grid_hw", torch.int32, 2)
+    _need(text_len, "text_len", torch.int32, 1)
+    T, hidden = x.shape
+    n = grid_hw.shape[0]
+    if w_folded.shape != (2, 3 * heads * head_dim, hidden):
+        raise ValueError("w_folded must be [2, 3*heads*head_dim, hidden]")
+    if frames is not None:
+        _need(frames, "frames", torch.int32, 1)
+    if out is None:
+        out = tuple(torch.empty((T, heads, head_dim), dtype=torch.bfloat16, device=x.device) for _ in range(3))
+    for name, t in zip("qkv", out):
+        _need(t, name, torch.bfloat16, 3)
+        if t.shape != (T, heads, head_dim):
+            raise ValueError(f"{name} must be [T, heads, head_dim]")
+    q, k, v = out
+    fr = _ptr(frames) if frames is not None else None
+    if events is None:
+        _check(lib().mf_qkv_rmsnorm(_ptr(x), _ptr(w_folded), _ptr(cu_seqlens), _ptr(grid_hw), _ptr(text_len), fr, n, T,
+                                    hidden, heads, head_dim, float(eps), _ptr(q), _ptr(k), _ptr(v), _stream(stream)))
+    else:
+        arr = (ctypes.c_void_p * 3)(*events)
+        _check(lib().mf_qkv_rmsnorm_profiled(_ptr(x), _ptr(w_folded), _ptr(cu_seqlens), _ptr(grid_hw),
+                                             _ptr(text_len), fr, n, T, hidden, heads, head_dim, float(eps), _ptr(q),
+                                             _ptr(k), _ptr(v), ctypes.cast(arr, ctypes.c_void_p), _stream(stream)))
+    return q, k, v
 
 
 def get_device_error(stream=None) -> int:

@@ -45,6 +45,12 @@ hipError_t launch_attn_bwd(const void* q, const void* k, const void* v, const vo
                            const float2* cs, const Rope3* r3, char* ws, const BwdLayout& l, void* dq, void* dk,
                            void* dv, int64_t tokens, int32_t heads, int32_t head_dim, float scale, hipStream_t s,
                            hipEvent_t const* ev);
+hipError_t launch_qkv_fold(const void* w_txt, const void* w_img, const float* g_txt, const float* g_img,
+                           int32_t hidden, int32_t out_features, void* out, hipStream_t s);
+hipError_t launch_qkv(const void* x, const void* w, const int32_t* cu, const int32_t* grid_hw, const int32_t* text_len,
+                      const int32_t* frames, int32_t n_seg, int64_t tokens, int32_t hidden, int32_t hd, float eps,
+                      char* ws, void* q, void* k, void* v, hipStream_t s, hipEvent_t const* ev);
+size_t qkv_workspace_bytes(int64_t tokens, int32_t n_seg);
 hipError_t launch_cfg_euler(float* z, const void* v, const int32_t* cu, const int32_t* grid_hw,
                             const int32_t* text_len, int32_t n_seg, int64_t total_tokens,
                             const int32_t* cond_seg, const int32_t* uncond_seg, int32_t n_img,
@@ -77,6 +83,8 @@ struct DeviceState {
   size_t ws_bytes = 0;
   char* bws = nullptr;        // library workspace of mf_attn_packed_bwd
   size_t bws_bytes = 0;
+  char* qws = nullptr;        // library workspace of mf_qkv_rmsnorm
+  size_t qws_bytes = 0;
   // (head_dim, theta bits, row channels, column channels) -> cos/sin table;
   // row channels -1 marks the 2D table
   std::map<std::tuple<int, uint32_t, int, int>, float2*> tables;
@@ -590,6 +598,74 @@ int mf_rope_3d(const void* x_in, void* x_out, const int32_t* pos, int64_t total_
   return rope_impl(x_in, x_out, pos, split, total_tokens, heads, head_dim, dtype, theta, stream);
 }
 
+int mf_qkv_fold_weights(const void* w_txt, const void* w_img, const float* gamma_txt, const float* gamma_img,
+                        int32_t hidden, int32_t heads, int32_t head_dim, void* w_out, hipStream_t stream) {
+  if (!w_txt || !w_img || !gamma_txt || !gamma_img || !w_out) return fail(MF_ERR_INVALID_ARG, "null pointer argument");
+  if (hidden < 64 || hidden > 65536 || hidden % 64)
+    return fail(MF_ERR_UNSUPPORTED, "hidden=%d (need a multiple of 64 in [64, 65536])", hidden);
+  if (heads < 1 || head_dim < 1 || int64_t(heads) * head_dim % 256 || int64_t(heads) * head_dim > 65536)
+    return fail(MF_ERR_UNSUPPORTED, "heads * head_dim = %lld (need a multiple of 256, at most 65536)",
+                (long long)(int64_t(heads) * head_dim));
+  const int32_t out_features = 3 * heads * head_dim;
+  const size_t wb = size_t(out_features) * hidden * 2;
+  if (overlaps(w_out, 2 * wb, w_txt, wb) || overlaps(w_out, 2 * wb, w_img, wb))
+    return fail(MF_ERR_INVALID_ARG, "w_out overlaps an input weight");
+  if ((reinterpret_cast<uintptr_t>(w_txt) | reinterpret_cast<uintptr_t>(w_img) | reinterpret_cast<uintptr_t>(w_out)) & 15)
+    return fail(MF_ERR_INVALID_ARG, "weights must be 16-byte aligned");
+  const hipError_t e = mf::launch_qkv_fold(w_txt, w_img, gamma_txt, gamma_img, hidden, out_features, w_out, stream);
+  return e == hipSuccess ? MF_OK : hip_fail(e, "qkv_fold_kernel launch");
+}
+
+int mf_qkv_rmsnorm_profiled(const void* x, const void* w_folded, const int32_t* cu_seqlens, const int32_t* grid_hw,
+                            const int32_t* text_len, const int32_t* frames, int32_t n_seg, int64_t total_tokens,
+                            int32_t hidden, int32_t heads, int32_t head_dim, float eps, void* q, void* k, void* v,
+                            hipEvent_t const* events, hipStream_t stream) {
+  if (!x || !w_folded || !cu_seqlens || !grid_hw || !text_len || !q || !k || !v)
+    return fail(MF_ERR_INVALID_ARG, "null pointer argument");
+  if (n_seg < 1 || n_seg > MF_MAX_SEGMENTS)
+    return fail(MF_ERR_INVALID_ARG, "n_seg=%d outside [1, %d]", n_seg, MF_MAX_SEGMENTS);
+  if (total_tokens < 1 || total_tokens >= (int64_t(1) << 31))
+    return fail(MF_ERR_INVALID_ARG, "total_tokens=%lld outside [1, 2^31)", (long long)total_tokens);
+  if (hidden < 64 || hidden > 65536 || hidden % 64)
+    return fail(MF_ERR_UNSUPPORTED, "hidden=%d (need a multiple of 64 in [64, 65536])", hidden);
+  if (heads < 1 || head_dim < 1 || int64_t(heads) * head_dim % 256 || int64_t(heads) * head_dim > 65536)
+    return fail(MF_ERR_UNSUPPORTED, "heads * head_dim = %lld (need a multiple of 256, at most 65536)",
+                (long long)(int64_t(heads) * head_dim));
+  if (!(eps >= 0.f) || !std::isfinite(eps)) return fail(MF_ERR_INVALID_ARG, "eps must be finite and >= 0");
+  const int32_t hd = heads * head_dim;
+  const size_t xb = size_t(total_tokens) * hidden * 2, ob = size_t(total_tokens) * hd * 2,
+               wb = size_t(6) * hd * hidden * 2;
+  void* outs[3] = {q, k, v};
+  for (int i = 0; i < 3; ++i) {
+    if (overlaps(outs[i], ob, x, xb) || overlaps(outs[i], ob, w_folded, wb))
+      return fail(MF_ERR_INVALID_ARG, "q, k or v overlaps x or the weights");
+    for (int j = i + 1; j < 3; ++j)
+      if (overlaps(outs[i], ob, outs[j], ob)) return fail(MF_ERR_INVALID_ARG, "q, k, v overlap");
+  }
+  const uintptr_t mis = reinterpret_cast<uintptr_t>(x) | reinterpret_cast<uintptr_t>(w_folded) |
+                        reinterpret_cast<uintptr_t>(q) | reinterpret_cast<uintptr_t>(k) | reinterpret_cast<uintptr_t>(v);
+  if (mis & 15) return fail(MF_ERR_INVALID_ARG, "x, weights, q, k, v must be 16-byte aligned");
+  int dev, rc;
+  if ((rc = current_device(&dev))) return rc;
+  std::lock_guard<std::mutex> lock(g_mu);
+  DeviceState& st = g_dev[dev];
+  if ((rc = ensure_buffer(st.qws, st.qws_bytes, mf::qkv_workspace_bytes(total_tokens, n_seg)))) return rc;
+  hipError_t e;
+  if (events && (e = hipEventRecord(events[0], stream)) != hipSuccess) return hip_fail(e, "hipEventRecord");
+  e = mf::launch_qkv(x, w_folded, cu_seqlens, grid_hw, text_len, frames, n_seg, total_tokens, hidden, hd, eps, st.qws,
+                     q, k, v, stream, events ? events + 1 : nullptr);
+  if (e != hipSuccess) return hip_fail(e, "qkv kernels launch");
+  if (events && (e = hipEventRecord(events[2], stream)) != hipSuccess) return hip_fail(e, "hipEventRecord");
+  return MF_OK;
+}
+
+int mf_qkv_rmsnorm(const void* x, const void* w_folded, const int32_t* cu_seqlens, const int32_t* grid_hw,
+                   const int32_t* text_len, const int32_t* frames, int32_t n_seg, int64_t total_tokens, int32_t hidden,
+                   int32_t heads, int32_t head_dim, float eps, void* q, void* k, void* v, hipStream_t stream) {
+  return mf_qkv_rmsnorm_profiled(x, w_folded, cu_seqlens, grid_hw, text_len, frames, n_seg, total_tokens, hidden,
+                                 heads, head_dim, eps, q, k, v, nullptr, stream);
+}
+
 int mf_rf_cfg_euler_step(float* z, const void* v, const int32_t* cu_seqlens, const int32_t* grid_hw,
                          const int32_t* text_len, int32_t n_seg, int64_t total_tokens,
                          const int32_t* cond_seg, const int32_t* uncond_seg, int32_t n_img,
@@ -649,6 +725,12 @@ int mf_get_device_error(hipStream_t stream) {
       return hip_fail(e, "hipMemcpy(status)");
     if (v && (e = hipMemset(st.status, 0, 4)) != hipSuccess) return hip_fail(e, "hipMemset(status)");
     flags |= v;
+  }
+  if (st.qws) {
+    int32_t qf = 0;
+    if ((e = hipMemcpy(&qf, st.qws, 4, hipMemcpyDeviceToHost)) != hipSuccess)
+      return hip_fail(e, "hipMemcpy(projection workspace header)");
+    flags |= qf;
   }
   for (char* w : {st.ws, st.bws}) {
     if (!w) continue;

@@ -31,6 +31,7 @@ __all__ = [
     "make_segments",
     "make_custom",
     "EDIT_CONFIGS",
+    "make_qkv_inputs",
     "make_edit",
     "CfgBatch",
     "CFG_CONFIGS",
@@ -329,3 +330,22 @@ def make_edit(config=None, grids=None, texts=None, frames=None, heads=None, head
     q, k, v = _draw_qkv(rng, n_tokens, heads, head_dim, dtype, scale)
     split = EDIT_SPLIT[head_dim] if split is None else tuple(split)
     return Workload(name, grid_hw, text_len, heads, head_dim, dtype, q, k, v, 0 if seed is None else seed, fr, split)
+
+
+def make_qkv_inputs(grid_hw, text_len, hidden: int, heads: int, head_dim: int, frames=None, seed: int = 0):
+    """Hidden states and synthetic modality-specific weights for the RMSNorm +
+    packed QKV projection: x ~ N(0, 1) [T, hidden] (bf16 values), W_txt, W_img ~
+    N(0, 1/hidden) [3 heads head_dim, hidden] (bf16 values), gains 1 + 0.1 N(0, 1)
+    (float32). Draw order: x, W_txt, W_img, gamma_txt, gamma_img."""
+    g = np.asarray(grid_hw, dtype=np.int64).reshape(-1, 2)
+    t = np.asarray(text_len, dtype=np.int64).reshape(-1)
+    f = np.ones_like(t) if frames is None else np.asarray(frames, dtype=np.int64).reshape(-1)
+    T = int((t + f * g[:, 0] * g[:, 1]).sum())
+    rng = np.random.default_rng(seed)
+    rnd = lambda shape, s: bf16_bits_to_f32(f32_to_bf16_bits(rng.standard_normal(shape, dtype=np.float32) * s))  # noqa: E731
+    x = rnd((T, hidden), 1.0)
+    w_txt = rnd((3 * heads * head_dim, hidden), 1.0 / np.sqrt(hidden))
+    w_img = rnd((3 * heads * head_dim, hidden), 1.0 / np.sqrt(hidden))
+    g_txt = (1.0 + 0.1 * rng.standard_normal(hidden)).astype(np.float32)
+    g_img = (1.0 + 0.1 * rng.standard_normal(hidden)).astype(np.float32)
+    return x, w_txt, w_img, g_txt, g_img
