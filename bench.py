@@ -262,6 +262,59 @@ def backward_bench(w, q, k, v, cu, grid, text, steps: int, warmup: int, frames=N
     }
 
 
+def qkv_bench(w, grid, text, cu, steps: int, warmup: int, frames=None):
+    """Modality-specific RMSNorm + packed QKV projection feeding the same batch:
+    hidden = heads * head_dim (3072 for 24 x 128), synthetic weights. TFLOP/s
+    count 2 * T * hidden * 3 * heads * head_dim. For context, torch.matmul
+    (hipBLASLt) of one [T, hidden] x [hidden, 3 heads head_dim] bf16 product of
+    the same size is timed too (no normalization, one weight for all tokens)."""
+    import torch
+    from text_image_diffusion_varlen_amd import binding, workloads
+
+    hidden = w.heads * w.head_dim
+    x, wt, wi, gt, gi = workloads.make_qkv_inputs(w.grid_hw, w.text_len, hidden, w.heads, w.head_dim, w.frames,
+                                                  seed=11)
+    bf = lambda a: torch.from_numpy(a).to(torch.bfloat16).cuda()  # noqa: E731
+    xd = bf(x)
+    wf = binding.qkv_fold_weights(bf(wt), bf(wi), torch.from_numpy(gt).cuda(), torch.from_numpy(gi).cuda(),
+                                  w.heads, w.head_dim)
+    out = tuple(torch.empty((w.tokens, w.heads, w.head_dim), dtype=torch.bfloat16, device="cuda") for _ in range(3))
+    for _ in range(warmup):
+        binding.qkv_rmsnorm(xd, wf, cu, grid, text, w.heads, w.head_dim, frames=frames, out=out)
+    torch.cuda.synchronize()
+    ev = HipEvents(3 * steps)
+    for st in range(steps):
+        binding.qkv_rmsnorm(xd, wf, cu, grid, text, w.heads, w.head_dim, frames=frames, out=out,
+                            events=ev.ev[3 * st:3 * st + 3])
+    torch.cuda.synchronize()
+    if binding.get_device_error() != binding.MF_OK:
+        raise RuntimeError(binding.last_error())
+    stats = sum(ev.elapsed_ms(3 * st, 3 * st + 1) for st in range(steps)) / steps
+    gemm = sum(ev.elapsed_ms(3 * st + 1, 3 * st + 2) for st in range(steps)) / steps
+    ev.close()
+    flops = 2.0 * w.tokens * hidden * 3 * w.heads * w.head_dim
+    wplain = bf(wt).t().contiguous()
+    y = torch.matmul(xd, wplain)
+    start, stop = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    start.record()
+    for _ in range(steps):
+        torch.matmul(xd, wplain, out=y)
+    stop.record()
+    torch.cuda.synchronize()
+    mm = start.elapsed_time(stop) / steps
+    return {
+        "tflops": round(flops / ((stats + gemm) / 1e3) / 1e12, 1),
+        "us_per_call": round((stats + gemm) * 1e3, 2),
+        "stages_us": {"route_rms": round(stats * 1e3, 2), "gemm": round(gemm * 1e3, 2)},
+        "gemm_tflops": round(flops / (gemm / 1e3) / 1e12, 1),
+        "gemm_frac_mfma_peak": round(flops / (gemm / 1e3) / PEAK["bf16"], 4),
+        "flop_per_call": flops,
+        "hidden": hidden,
+        "torch_matmul_same_size_tflops": round(flops / (mm / 1e3) / 1e12, 1),
+    }
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -273,6 +326,7 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-sampler", action="store_true", help="skip the packed CFG Euler-step measurement")
     ap.add_argument("--no-backward", action="store_true", help="skip the packed backward measurement")
+    ap.add_argument("--no-qkv", action="store_true", help="skip the RMSNorm + QKV projection measurement")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="only run a plain device copy of 1 GiB (HBM-counter calibration for profiling)")
     args = ap.parse_args()
@@ -405,6 +459,8 @@ def main():
     if w.dtype == "bf16" and not args.no_backward:
         result["backward"] = backward_bench(w, q, k, v, cu, grid, text, args.steps, args.warmup,
                                             frames if edit else None)
+    if w.dtype == "bf16" and not args.no_qkv:
+        result["qkv_rmsnorm"] = qkv_bench(w, grid, text, cu, args.steps, args.warmup, frames if edit else None)
     if not args.no_sampler:
         result["cfg_euler_step"] = sampler_bench(args.steps, args.warmup)
     if not args.no_cpu_baseline:

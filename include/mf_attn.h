@@ -257,8 +257,12 @@ int mf_rope_2d(const void* x_in, void* x_out, const int32_t* pos, int64_t total_
  *   w_txt, w_img    device bf16 [3 * heads * head_dim][hidden], a linear
  *                   layer's weight (rows: q, then k, then v, head-major)
  *   gamma_txt, gamma_img  device float [hidden]
- *   w_out           device bf16 [2][3 * heads * head_dim][hidden]:
- *                   w_out[m][n][c] = bf16(gamma_m[c] * w_m[n][c]), m = 0 text
+ *   w_out           device bf16, 2 * 3 * heads * head_dim * hidden elements
+ *                   holding W'_m[n][c] = bf16(gamma_m[c] * w_m[n][c]) (m = 0
+ *                   text, 1 visual) in the projection's tiled order: stacked
+ *                   row R = m * 3HD + n, 8-channel chunk g = c / 8, stored as
+ *                   16-byte chunk ((R / 256) * (hidden / 64) + g / 8) * 2048
+ *                   + (g % 8) * 256 + R % 256
  * hidden a multiple of 64; heads * head_dim a multiple of 256.
  */
 int mf_qkv_fold_weights(const void* w_txt, const void* w_img, const float* gamma_txt, const float* gamma_img,
@@ -275,8 +279,8 @@ int mf_qkv_fold_weights(const void* w_txt, const void* w_img, const float* gamma
  *   q, k, v     device bf16 [total_tokens][heads][head_dim], the attention's inputs
  * The metadata is checked on the device; on a mismatch nothing is written and
  * mf_get_device_error() reports MF_ERR_METADATA. Uses a library-owned
- * per-device workspace (row lists and 1/rms per token, 12 bytes per token),
- * same stream-order rule as mf_attn_packed.
+ * per-device workspace (row lists, 1/rms and a tiled copy of x, about
+ * 12 + 2 * hidden bytes per token), same stream-order rule as mf_attn_packed.
  */
 int mf_qkv_rmsnorm(const void* x, const void* w_folded, const int32_t* cu_seqlens, const int32_t* grid_hw,
                    const int32_t* text_len, const int32_t* frames, int32_t n_seg, int64_t total_tokens, int32_t hidden,

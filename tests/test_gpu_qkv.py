@@ -3,7 +3,8 @@
 
 Outputs are ~N(0, 1) bf16 values, so the bf16 bar of the attention applies:
 max abs <= 2e-2, mean abs <= 2e-3. The folded weights are compared bit for bit
-with bf16(gamma * W) formed in float32 on the host.
+with bf16(gamma * W) formed in float32 on the host and put in the tiled order
+the header documents.
 """
 import numpy as np
 import pytest
@@ -40,12 +41,25 @@ def _check(grid, text, hidden, heads, d, frames=None, seed=0):
     return wf, (wt, wi, gt, gi)
 
 
+def _tiled(a):
+    """Chunk order of the projection's tiled weights: stacked row R, 8-channel chunk
+    g -> 16-byte chunk ((R // 256) * (C // 64) + g // 8) * 2048 + (g % 8) * 256 + R % 256."""
+    R, C = a.shape
+    chunks = a.reshape(R, C // 8, 8)
+    out = np.empty_like(chunks.reshape(-1, 8))
+    r = np.arange(R)[:, None]
+    g = np.arange(C // 8)[None, :]
+    idx = ((r // 256) * (C // 64) + g // 8) * 2048 + (g % 8) * 256 + r % 256
+    out[idx.reshape(-1)] = chunks.reshape(-1, 8)
+    return out.reshape(-1)
+
+
 def test_fold_weights_bitwise():
     wf, (wt, wi, gt, gi) = _check([[3, 5]], [7], 128, 2, 128, seed=1)
-    for m, (w, g) in enumerate(((wt, gt), (wi, gi))):
-        ref = workloads.f32_to_bf16_bits((w * g[None, :]).astype(np.float32))
-        got = wf[m].cpu().view(torch.int16).numpy().view(np.uint16)
-        assert np.array_equal(got, ref)
+    ref = np.concatenate([workloads.f32_to_bf16_bits((w * g[None, :]).astype(np.float32))
+                          for w, g in ((wt, gt), (wi, gi))])
+    got = wf.cpu().view(torch.int16).numpy().view(np.uint16).reshape(-1)
+    assert np.array_equal(got, _tiled(ref))
 
 
 @pytest.mark.parametrize("grid,text,frames", [

@@ -13,17 +13,20 @@
 // Three kernels:
 //   qkv_route_kernel  (one workgroup) checks the metadata and counts each
 //                     sample's prompt and visual tokens (prefix sums).
-//   qkv_rms_kernel    one wave per token: writes the token into its
-//                     modality's row list and 1 / r_t.
-//   qkv_gemm_kernel   per modality a GEMM over its row list: workgroup tile
-//                     256 output features x 256 tokens, 8 waves of 128 x 64,
+//   qkv_rms_kernel    per 64 rows of one modality: the rows' tokens, 1 / r_t,
+//                     the row lists, and the rows copied into the tiled
+//                     activation buffer X~ (text rows, then visual rows).
+//   qkv_gemm_kernel   per modality a GEMM over its rows: workgroup tile 256
+//                     output features x 256 tokens, 8 waves of 128 x 64,
 //                     v_mfma_f32_32x32x16_bf16 with D = W' X^T (lane = token),
 //                     K staged 64 channels at a time in LDS by direct-to-LDS
-//                     copies (the token rows are gathered through the row list
-//                     by the copy itself), double-buffered; the epilogue scales
-//                     by 1 / r_t and writes q, k, v rows directly.
-// gamma is folded into the weight beforehand (qkv_fold_kernel:
-// W' = W diag(gamma), bf16), so the normalized activations are never stored.
+//                     copies, double-buffered; the epilogue scales by 1 / r_t
+//                     and writes q, k, v rows directly.
+// Both GEMM operands are stored tiled: for every 256-row x 64-channel tile,
+// 2048 16-byte chunks, chunk c (channels 8c .. 8c+7) of row r at c * 256 + r.
+// A stage is then one contiguous 32 KB copy per operand, and the LDS image
+// gives conflict-free MFMA operand reads at immediate offsets. gamma is folded
+// into the weight beforehand (qkv_fold_kernel: W' = W diag(gamma), bf16, tiled).
 #include <algorithm>
 
 #include "mf_common.h"
@@ -47,20 +50,35 @@ struct QkvHeader {
 };
 static_assert(sizeof(QkvHeader) == 256, "one 256-byte block");
 
-// Workspace: [header][tp n+1][vp n+1][idx_txt T][idx_img T][inv_r T], 256-byte aligned sections.
+// Workspace: [header][tp n+1][vp n+1][idx_txt T][idx_img T][ssq T x G][X~], 256-byte
+// aligned sections. ssq holds each token's sum of squares in G partial sums
+// (one per group of RMS_STAGES channel stages). X~ holds the text rows from
+// tile 0 and the visual rows from the first tile after them: at most
+// ceil(T / 256) + 1 tiles of 256 x hidden.
+constexpr int RMS_STAGES = 8;  // 64-channel stages per statistics workgroup
+__host__ __device__ inline int32_t rms_groups(int32_t hidden) {
+  return int32_t(ceil_div(hidden / QKV_KS, RMS_STAGES));
+}
 struct QkvLayout {
-  int64_t off_tp, off_vp, off_txt, off_img, off_inv, total;
+  int64_t off_tp, off_vp, off_txt, off_img, off_inv, off_x, total;
 };
-__host__ __device__ inline QkvLayout qkv_layout(int64_t tokens, int32_t n_seg) {
+__host__ __device__ inline QkvLayout qkv_layout(int64_t tokens, int32_t n_seg, int32_t hidden) {
   QkvLayout l;
   int64_t o = 256;
   l.off_tp = o;  o += round_up(int64_t(n_seg + 1) * 4, 256);
   l.off_vp = o;  o += round_up(int64_t(n_seg + 1) * 4, 256);
   l.off_txt = o; o += round_up(tokens * 4, 256);
   l.off_img = o; o += round_up(tokens * 4, 256);
-  l.off_inv = o; o += round_up(tokens * 4, 256);
+  l.off_inv = o; o += round_up(tokens * rms_groups(hidden) * 4, 256);
+  l.off_x = o;   o += (ceil_div(tokens, QKV_TT) + 1) * QKV_TT * int64_t(hidden) * 2;
   l.total = o;
   return l;
+}
+
+// Chunk index of (row, 8-channel chunk cg) in a tiled operand with `stages`
+// 64-channel stages per 256-row tile.
+__host__ __device__ inline int64_t tiled_chunk(int64_t row, int64_t cg, int64_t stages) {
+  return ((row / QKV_TT) * stages + cg / 8) * QKV_CH + (cg % 8) * QKV_TT + row % QKV_TT;
 }
 
 // Prompt / visual token counts of every sample, their exclusive prefix sums
@@ -117,39 +135,84 @@ qkv_route_kernel(const int32_t* __restrict__ cu, const int32_t* __restrict__ gri
   }
 }
 
-// One wave per token: its place in its modality's row list and 1 / r_t.
+// One workgroup per (64 consecutive rows of one modality (text rows, then
+// visual rows), group of RMS_STAGES channel stages): finds each row's token,
+// copies its part of the rows into X~ one 64-channel stage at a time through
+// LDS (row-contiguous reads, tile-contiguous writes), and writes the rows'
+// partial sums of squares; the first group also writes the row lists. The
+// partial sums are added in group order by the GEMM epilogue (deterministic).
+constexpr int RMS_ROWS = 64;
 __global__ void __launch_bounds__(256)
 qkv_rms_kernel(const uint16_t* __restrict__ x, const int32_t* __restrict__ cu, const int32_t* __restrict__ text_len,
                int32_t n, int64_t tokens, int32_t hidden, float eps, char* __restrict__ ws, QkvLayout l) {
   const QkvHeader* hdr = reinterpret_cast<const QkvHeader*>(ws);
   if (hdr->flag != FLAG_OK) return;
-  const int64_t tok = int64_t(blockIdx.x) * 4 + (threadIdx.x >> 6);
-  const int lane = threadIdx.x & 63;
-  if (tok >= tokens) return;
-  const u32x4* row = reinterpret_cast<const u32x4*>(x + tok * hidden);
-  float ss = 0.f;
-  for (int c = lane; c < hidden / 8; c += 64) {
-    const u32x4 r = row[c];
-#pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      const float a = __uint_as_float(r[e] << 16), b = __uint_as_float(r[e] & 0xFFFF0000u);
-      ss = __builtin_fmaf(a, a, __builtin_fmaf(b, b, ss));
-    }
+  const int32_t n_txt = hdr->n_txt, n_img = hdr->n_img;
+  const int txt_blocks = (n_txt + RMS_ROWS - 1) / RMS_ROWS;
+  const int32_t groups = rms_groups(hidden);
+  const int grp = int(blockIdx.x % unsigned(groups));
+  int blk = int(blockIdx.x / unsigned(groups));
+  const bool is_text = blk < txt_blocks;
+  if (!is_text) {
+    blk -= txt_blocks;
+    if (blk * RMS_ROWS >= n_img) return;
   }
+  const int32_t count = is_text ? n_txt : n_img;
+  const int32_t* pre = reinterpret_cast<const int32_t*>(ws + (is_text ? l.off_tp : l.off_vp));
+  const int32_t r0 = blk * RMS_ROWS;
+  const int64_t t0 = is_text ? r0 : round_up(n_txt, QKV_TT) + r0;  // X~ row of this block's first row
+  const int t = threadIdx.x;
+  __shared__ int32_t tok_of[RMS_ROWS];
+  __shared__ float ssq[RMS_ROWS];
+  __shared__ u32x4 stage[8 * RMS_ROWS];  // chunk c of row r at c * 64 + r
+  if (t < RMS_ROWS) {
+    const int32_t rank = min(r0 + t, count - 1);
+    const int32_t i = upper_segment(pre, n, rank);  // pre[] is non-decreasing, pre[0] = 0
+    tok_of[t] = cu[i] + (is_text ? 0 : text_len[i]) + (rank - pre[i]);
+  }
+  __syncthreads();
+  const int64_t stages = hidden / QKV_KS;
+  u32x4* xt = reinterpret_cast<u32x4*>(ws + l.off_x);
+  float ss[2] = {0.f, 0.f};
+  const int64_t s_end = min(stages, int64_t(grp + 1) * RMS_STAGES);
+  for (int64_t s = int64_t(grp) * RMS_STAGES; s < s_end; ++s) {
 #pragma unroll
-  for (int o = 32; o >= 1; o >>= 1) ss += __shfl_xor(ss, o, 64);
-  if (lane == 0) {
-    const int32_t i = upper_segment(cu, n, tok);
-    const int32_t u = int32_t(tok - cu[i]);
-    const int32_t* tp = reinterpret_cast<const int32_t*>(ws + l.off_tp);
-    const int32_t* vp = reinterpret_cast<const int32_t*>(ws + l.off_vp);
-    if (u < text_len[i]) reinterpret_cast<int32_t*>(ws + l.off_txt)[tp[i] + u] = int32_t(tok);
-    else reinterpret_cast<int32_t*>(ws + l.off_img)[vp[i] + u - text_len[i]] = int32_t(tok);
-    reinterpret_cast<float*>(ws + l.off_inv)[tok] = 1.0f / sqrtf(ss / float(hidden) + eps);
+    for (int j = 0; j < 2; ++j) {  // 512 chunks: 8 per row, 8 consecutive threads per row
+      const int q = t + 256 * j, r = q >> 3, c = q & 7;
+      const u32x4 v = reinterpret_cast<const u32x4*>(x + int64_t(tok_of[r]) * hidden)[8 * s + c];
+      stage[c * RMS_ROWS + r] = v;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const float a = __uint_as_float(v[e] << 16), b = __uint_as_float(v[e] & 0xFFFF0000u);
+        ss[j] = __builtin_fmaf(a, a, __builtin_fmaf(b, b, ss[j]));
+      }
+    }
+    __syncthreads();
+#pragma unroll
+    for (int j = 0; j < 2; ++j) {
+      const int q = t + 256 * j, c = q / RMS_ROWS, r = q % RMS_ROWS;
+      const int64_t row = t0 + r;
+      xt[((row / QKV_TT) * stages + s) * QKV_CH + c * QKV_TT + row % QKV_TT] = stage[c * RMS_ROWS + r];
+    }
+    __syncthreads();
+  }
+  // Rows t/8 and t/8 + 32: sum over the 8 threads of each row.
+#pragma unroll
+  for (int j = 0; j < 2; ++j) {
+#pragma unroll
+    for (int o = 4; o >= 1; o >>= 1) ss[j] += __shfl_xor(ss[j], o, 64);
+    if ((t & 7) == 0) ssq[(t >> 3) + 32 * j] = ss[j];
+  }
+  __syncthreads();
+  if (t < RMS_ROWS && r0 + t < count) {
+    const int32_t tok = tok_of[t];
+    if (grp == 0) reinterpret_cast<int32_t*>(ws + (is_text ? l.off_txt : l.off_img))[r0 + t] = tok;
+    reinterpret_cast<float*>(ws + l.off_inv)[int64_t(tok) * groups + grp] = ssq[t];
   }
 }
 
-// W'_m[n][c] = bf16(gamma_m[c] * W_m[n][c]) for both modalities.
+// W'_m[n][c] = bf16(gamma_m[c] * W_m[n][c]) for both modalities, stored tiled
+// (rows n of modality m at row m * out_features + n).
 __global__ void __launch_bounds__(256)
 qkv_fold_kernel(const uint16_t* __restrict__ w_txt, const uint16_t* __restrict__ w_img,
                 const float* __restrict__ g_txt, const float* __restrict__ g_img, int64_t per_modality,
@@ -161,6 +224,7 @@ qkv_fold_kernel(const uint16_t* __restrict__ w_txt, const uint16_t* __restrict__
   const int64_t local = img ? e0 - per_modality : e0;
   const uint16_t* src = (img ? w_img : w_txt) + local;
   const float* g = (img ? g_img : g_txt) + local % hidden;
+  const int64_t grow = e0 / hidden, cg = (e0 % hidden) / 8;  // row of the stacked [2 * out_features] weight
   const u32x4 r = *reinterpret_cast<const u32x4*>(src);
   u32x4 o;
 #pragma unroll
@@ -169,7 +233,7 @@ qkv_fold_kernel(const uint16_t* __restrict__ w_txt, const uint16_t* __restrict__
     const float b = __uint_as_float(r[e] & 0xFFFF0000u) * g[2 * e + 1];
     o[e] = pack_bf16x2(a, b);
   }
-  *reinterpret_cast<u32x4*>(out + e0) = o;
+  reinterpret_cast<u32x4*>(out)[tiled_chunk(grow, cg, hidden / QKV_KS)] = o;
 }
 
 struct QkvGemmArgs {
@@ -181,6 +245,7 @@ struct QkvGemmArgs {
   uint16_t* k;
   uint16_t* v;
   int32_t hidden;
+  float eps;
   int32_t hd;          // heads * head_dim
   int32_t n_tiles;     // 3 hd / QKV_NT
 };
@@ -206,29 +271,16 @@ __global__ void __launch_bounds__(QKV_THREADS, 2) qkv_gemm_kernel(QkvGemmArgs a)
   const int wave = tid >> 6, lane = tid & 63, hf = lane >> 5, l32 = lane & 31;
   const int wn = wave & 1, wt = wave >> 1;  // wave tile: 128 features x 64 tokens
 
-  // Copy pattern (both operands): wave w moves chunk w (channels 8w .. 8w+7 of
-  // the stage) of all 256 rows, one 64-row block per instruction; LDS is
-  // chunk-major (chunk c of row r at c * 256 + r).
-  const int64_t K = a.hidden;
-  const uint16_t* wsrc[4];
-  const uint16_t* xsrc[4];
-#pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const int r = 64 * i + lane;
-    wsrc[i] = a.w + (int64_t(m) * 3 * a.hd + int64_t(nt) * QKV_NT + r) * K + 8 * wave;
-    const int32_t tok = rows[min(row0 + r, count - 1)];  // rows past the list repeat its last token (not stored)
-    xsrc[i] = a.x + int64_t(tok) * K + 8 * wave;
-  }
+  // Both operands are tiled: a stage of one operand is 2048 contiguous chunks,
+  // copied verbatim (chunk c of row r lands at c * 256 + r).
+  const int64_t stages_k = a.hidden / QKV_KS;
+  const int64_t xtile = m ? round_up(n_txt, QKV_TT) / QKV_TT + tt : tt;  // tile row of X~
+  const u32x4* wsrc = reinterpret_cast<const u32x4*>(a.w) + (int64_t(m) * a.n_tiles + nt) * stages_k * QKV_CH;
+  const u32x4* xsrc = reinterpret_cast<const u32x4*>(a.ws + a.l.off_x) + xtile * stages_k * QKV_CH;
   __shared__ u32x4 lds[2][2 * QKV_CH];  // [stage][A (features) | B (tokens)]
   auto load_stage = [&](int s, u32x4* dst) {
-    const int64_t k0 = int64_t(s) * QKV_KS;
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      __builtin_amdgcn_global_load_lds(reinterpret_cast<const u32x4*>(wsrc[i] + k0),
-                                       (lds_ptr_t)(dst + wave * QKV_NT + 64 * i), 16, 0, 0);
-      __builtin_amdgcn_global_load_lds(reinterpret_cast<const u32x4*>(xsrc[i] + k0),
-                                       (lds_ptr_t)(dst + QKV_CH + wave * QKV_NT + 64 * i), 16, 0, 0);
-    }
+    copy_to_lds<QKV_CH, QKV_THREADS / 64>(wsrc + int64_t(s) * QKV_CH, dst, wave, lane);
+    copy_to_lds<QKV_CH, QKV_THREADS / 64>(xsrc + int64_t(s) * QKV_CH, dst + QKV_CH, wave, lane);
   };
 
   f32x16 acc[4][2];
@@ -258,13 +310,16 @@ __global__ void __launch_bounds__(QKV_THREADS, 2) qkv_gemm_kernel(QkvGemmArgs a)
   }
 
   // Epilogue: lane = token, entry e of block nb = feature 32nb + 8(e/4) + 4hf + e%4.
-  const float* inv = reinterpret_cast<const float*>(a.ws + a.l.off_inv);
+  const float* ssq = reinterpret_cast<const float*>(a.ws + a.l.off_inv);
+  const int32_t groups = rms_groups(a.hidden);
 #pragma unroll
   for (int tb = 0; tb < 2; ++tb) {
     const int32_t row = row0 + wt * 64 + tb * 32 + l32;
     if (row >= count) continue;
     const int32_t tok = rows[row];
-    const float sc = inv[tok];
+    float ss = 0.f;
+    for (int g = 0; g < groups; ++g) ss += ssq[int64_t(tok) * groups + g];
+    const float sc = 1.0f / sqrtf(ss / float(a.hidden) + a.eps);
 #pragma unroll
     for (int nb = 0; nb < 4; ++nb) {
 #pragma unroll
@@ -281,7 +336,9 @@ __global__ void __launch_bounds__(QKV_THREADS, 2) qkv_gemm_kernel(QkvGemmArgs a)
   }
 }
 
-size_t qkv_workspace_bytes(int64_t tokens, int32_t n_seg) { return size_t(qkv_layout(tokens, n_seg).total); }
+size_t qkv_workspace_bytes(int64_t tokens, int32_t n_seg, int32_t hidden) {
+  return size_t(qkv_layout(tokens, n_seg, hidden).total);
+}
 
 hipError_t launch_qkv_fold(const void* w_txt, const void* w_img, const float* g_txt, const float* g_img,
                            int32_t hidden, int32_t out_features, void* out, hipStream_t s) {
@@ -295,11 +352,13 @@ hipError_t launch_qkv_fold(const void* w_txt, const void* w_img, const float* g_
 hipError_t launch_qkv(const void* x, const void* w, const int32_t* cu, const int32_t* grid_hw, const int32_t* text_len,
                       const int32_t* frames, int32_t n_seg, int64_t tokens, int32_t hidden, int32_t hd, float eps,
                       char* ws, void* q, void* k, void* v, hipStream_t s, hipEvent_t const* ev) {
-  const QkvLayout l = qkv_layout(tokens, n_seg);
+  const QkvLayout l = qkv_layout(tokens, n_seg, hidden);
   hipError_t e;
   hipLaunchKernelGGL(qkv_route_kernel, dim3(1), dim3(ROUTE_THREADS), 0, s, cu, grid_hw, text_len, frames, n_seg,
                      tokens, ws, l);
-  hipLaunchKernelGGL(qkv_rms_kernel, dim3(unsigned(ceil_div(tokens, 4))), dim3(256), 0, s,
+  // Row blocks of both modalities together never exceed ceil(T / 64) + 1.
+  hipLaunchKernelGGL(qkv_rms_kernel, dim3(unsigned((ceil_div(tokens, RMS_ROWS) + 1) * rms_groups(hidden))), dim3(256),
+                     0, s,
                      static_cast<const uint16_t*>(x), cu, text_len, n_seg, tokens, hidden, eps, ws, l);
   if ((e = hipGetLastError()) != hipSuccess) return e;
   if (ev && (e = hipEventRecord(ev[0], s)) != hipSuccess) return e;
@@ -312,10 +371,11 @@ hipError_t launch_qkv(const void* x, const void* w, const int32_t* cu, const int
   a.k = static_cast<uint16_t*>(k);
   a.v = static_cast<uint16_t*>(v);
   a.hidden = hidden;
+  a.eps = eps;
   a.hd = hd;
   a.n_tiles = 3 * hd / QKV_NT;
   // Token tiles of both modalities together never exceed ceil(T / 256) + 1.
-  const int64_t tiles = (ceil_div(tokens, QKV_TT) + 1) * a.n_tiles;
+  const int64_t tiles = (ceil_div(tokens, QKV_TT) + 1) * a.n_tiles;  // text tiles + visual tiles
   hipLaunchKernelGGL(qkv_gemm_kernel, dim3(unsigned(tiles)), dim3(QKV_THREADS), 0, s, a);
   return hipGetLastError();
 }
