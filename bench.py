@@ -28,8 +28,8 @@ PEAK = {"bf16": 2.5e15, "f32": 157.3e12}  # dense MFMA bf16; fp32 vector ALU
 HBM_PEAK = 8.0e12
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "attn_fwd_bf16_1024sq_traffic.json")
 KERNEL_SOURCES = [
-    os.path.join(ROOT, "text_image_diffusion_varlen_amd", "csrc", "attn_fwd.hip"),
-    os.path.join(ROOT, "text_image_diffusion_varlen_amd", "csrc", "mf_common.h"),
+    os.path.join(ROOT, "text_image_diffusion_varlen_amd", "csrc", name)
+    for name in ("attn_fwd.hip", "mf_common.h", "mfma_util.h", "rope_math.h")
 ]
 DESCRIPTIONS = {
     "tiny": "one 256x256 image (16x16 grid) + 32 prompt tokens, L=288, 2 heads x 64, fp32",
