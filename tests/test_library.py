@@ -105,3 +105,31 @@ def test_cfg_step_rejects_bad_arguments_on_host():
     assert call(z=0x10004) == bad  # misaligned
     assert call(v=0x10000 + 64) == bad  # z overlaps v
     assert binding.last_error() != ""
+
+
+def test_backward_3d_and_projection_reject_bad_arguments_on_host():
+    lib = binding.lib()
+    P = ctypes.c_void_p
+    bad, uns = binding.MF_ERR_INVALID_ARG, binding.MF_ERR_UNSUPPORTED
+    a = [P(0x10000 * (i + 1)) for i in range(12)]
+    # backward: fp32 is unsupported, null d_out rejected
+    assert lib.mf_attn_packed_bwd(*a, 1, 64, 2, 64, 1, None) == uns
+    args = list(a)
+    args[4] = None
+    assert lib.mf_attn_packed_bwd(*args, 1, 64, 2, 64, 0, None) == bad
+    # 3D forward: split must be even, non-negative and sum to head_dim; frames required
+    f3 = [P(0x100000 * (i + 1)) for i in range(7)]
+    assert lib.mf_attn_packed_3d(*f3, 30, 30, 2, P(0x900000), None, 1, 64, 2, 64, 0, None) == bad
+    assert lib.mf_attn_packed_3d(*f3, 31, 31, 2, P(0x900000), None, 1, 64, 2, 64, 0, None) == bad
+    f3[6] = None
+    assert lib.mf_attn_packed_3d(*f3, 24, 24, 16, P(0x900000), None, 1, 64, 2, 64, 0, None) == bad
+    assert lib.mf_build_metadata_3d(1, P(1), P(2), None, P(3), P(4), P(5), 10, None) == bad
+    assert lib.mf_rope_3d(P(16), P(4096), P(64), 10, 1, 64, 0, 10000.0, 24, 24, 18, None) == bad
+    # projection: hidden must be a multiple of 64, heads * head_dim a multiple of 256
+    q = [P(0x1000000 * (i + 1)) for i in range(6)]
+    o = [P(0x9000000 + 0x1000000 * i) for i in range(3)]
+    assert lib.mf_qkv_rmsnorm(*q, 1, 10, 96, 2, 128, 1e-6, *o, None) == uns
+    assert lib.mf_qkv_rmsnorm(*q, 1, 10, 128, 3, 64, 1e-6, *o, None) == uns
+    assert lib.mf_qkv_rmsnorm(*q, 1, 10, 128, 2, 128, -1.0, *o, None) == bad
+    assert lib.mf_qkv_fold_weights(P(16), P(32), P(48), P(64), 96, 2, 128, P(4096), None) == uns
+    assert binding.last_error() != ""
