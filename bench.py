@@ -21,6 +21,8 @@ import os
 import sys
 import time
 
+import numpy as np
+
 ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
@@ -406,11 +408,24 @@ def main():
             binding.attn_packed_profiled(q, k, v, cu, grid, text, ev.ev[4 * s : 4 * s + 4], out=out)
         torch.cuda.synchronize()
         stage = {"meta": 0.0, "rope_pack": 0.0, "attn": 0.0}
+        attn_each = []
         for s in range(args.steps):
             b = 4 * s
             stage["meta"] += ev.elapsed_ms(b, b + 1) / args.steps
             stage["rope_pack"] += ev.elapsed_ms(b + 1, b + 2) / args.steps
-            stage["attn"] += ev.elapsed_ms(b + 2, b + 3) / args.steps
+            attn_each.append(ev.elapsed_ms(b + 2, b + 3))
+        stage["attn"] = sum(attn_each) / args.steps
+        # The same calls with the 256 MB MALL flushed before each (a 512 MB
+        # buffer written in between): the RoPE prologue then reads k and v from HBM.
+        flush = torch.empty(512 << 20, dtype=torch.uint8, device="cuda")
+        pack_cold = []
+        for s in range(args.steps):
+            flush.fill_(s & 255)
+            binding.attn_packed_profiled(q, k, v, cu, grid, text, ev.ev[4 * s : 4 * s + 4], out=out)
+        torch.cuda.synchronize()
+        for s in range(args.steps):
+            pack_cold.append(ev.elapsed_ms(4 * s + 1, 4 * s + 2))
+        del flush
         ev.close()
 
     attn_s = stage["attn"] / 1e3
@@ -443,7 +458,9 @@ def main():
         "pct_mfma_peak": round(100.0 * flops / (ms / 1e3) / PEAK[w.dtype], 2),
         "tokens_per_s": round(w.tokens / (ms / 1e3), 1),
         "stages_ms": {k2: round(v2, 4) for k2, v2 in stage.items()},
+        "attn_ms_p10_p50_p90": [round(float(x), 4) for x in np.percentile(attn_each, [10, 50, 90])] if not edit else None,
         "rope_pack_gbps": round(rope_bytes / (stage["rope_pack"] / 1e3) / 1e9, 1) if not edit else None,
+        "rope_pack_gbps_cold_mall": round(rope_bytes / (float(np.median(pack_cold)) / 1e3) / 1e9, 1) if not edit else None,
         "roofline": {
             "kernel": f"attn_fwd_{w.dtype}_kernel<{w.head_dim}, {'true' if edit else 'false'}>"
                       + (" (whole step: no per-kernel events on the frame-aware path)" if edit else ""),
