@@ -7,6 +7,15 @@
  * where a function says it synchronizes. Functions return an mf_status; on a
  * negative status nothing was enqueued and mf_last_error() holds a message.
  *
+ * HIP graph capture: the first call of an entry point on a device may
+ * allocate (library workspace, status word) and upload the RoPE tables with
+ * synchronous copies. After one eager call with the same or larger sizes, the
+ * enqueuing calls launch kernels only (no host synchronization, allocation or
+ * memset) and can be captured into a graph and replayed. A later call that
+ * needs a larger library workspace reallocates it, which invalidates graphs
+ * that captured the old one; mf_attn_packed_ws with a caller-owned workspace
+ * avoids that.
+ *
  * Operation (sources, by page and section):
  *  - Mage-Flow tech report, NR-MMDiT section: text and image tokens of one
  *    sample are concatenated and processed by joint self-attention; samples
