@@ -23,8 +23,10 @@ def test_library_loads_and_exports_header_symbols():
 def test_workspace_bytes():
     import torch
     wb = binding.workspace_bytes
-    assert wb(4352, 24, 128, torch.bfloat16, 1) > 3 * 4352 * 24 * 128 * 2
-    assert wb(4352, 24, 128, torch.float32, 1) > wb(4352, 24, 128, torch.bfloat16, 1)
+    tensor = 4352 * 24 * 128
+    # bf16: K~ and V~^T (queries are rotated in the kernel); fp32: Q~, K~ and V
+    assert 2 * tensor * 2 < wb(4352, 24, 128, torch.bfloat16, 1) < 3 * tensor * 2
+    assert wb(4352, 24, 128, torch.float32, 1) > 3 * tensor * 4
     lib = binding.lib()
     assert lib.mf_workspace_bytes(100, 2, 96, 0, 1) == 0  # unsupported head_dim
     assert lib.mf_workspace_bytes(100, 2, 64, 7, 1) == 0  # unknown dtype

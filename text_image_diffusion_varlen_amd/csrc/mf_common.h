@@ -67,7 +67,7 @@ __host__ __device__ inline WsLayout ws_layout(int64_t tokens, int32_t heads, int
   l.off_tiles = o; o += round_up(l.n_tiles * 8, 256);
   l.rows = padded_rows(tokens, n_seg);
   const int64_t buf = round_up(int64_t(heads) * l.rows * head_dim * elem_bytes, 256);
-  l.off_q = o; o += buf;
+  l.off_q = o; o += elem_bytes == 4 ? buf : 0;  // rotated queries: fp32 path only (bf16 rotates them in the kernel)
   l.off_k = o; o += buf;
   l.off_v = o; o += buf;
   l.total = o;

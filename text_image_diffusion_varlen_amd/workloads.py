@@ -297,7 +297,8 @@ def make_cfg_config(config: str, seed: int | None = None, layout="interleaved") 
 # one grid; `frames` counts the images. The frame-aware RoPE split gives the
 # row, column and frame blocks of a 128-channel head 48, 48 and 32 channels
 # (the pages do not fix it; this is the proportion of the multimodal rotary
-# layout of the Qwen-VL encoders Mage-Flow builds on), 24/24/16 for 64.
+# layout of the vision-language text encoder the tech report names), 24/24/16
+# for 64.
 EDIT_SPLIT = {128: (48, 48, 32), 64: (24, 24, 16)}
 EDIT_CONFIGS = {
     # One 1024x1024 edit: a 256-token instruction, a source and a target 64x64 grid.
