@@ -105,7 +105,10 @@ int ensure_status(DeviceState& st) {
   hipError_t e = hipMalloc(&p, 256);
   if (e != hipSuccess) return fail(MF_ERR_OOM, "status buffer: %s", hipGetErrorString(e));
   e = hipMemset(p, 0, 256);
-  if (e != hipSuccess) return hip_fail(e, "hipMemset(status)");
+  if (e != hipSuccess) {
+    (void)hipFree(p);
+    return hip_fail(e, "hipMemset(status)");
+  }
   st.status = static_cast<int32_t*>(p);
   return MF_OK;
 }
