@@ -83,6 +83,33 @@ def test_attention_edge_cases(name, dtype, d):
     _full_check(w)
 
 
+@pytest.mark.parametrize("heads", [1, 7, 40])
+@pytest.mark.parametrize("d", [64, 128])
+def test_attention_head_counts(heads, d):
+    """Head counts that are not multiples of the XCD count, one head and many:
+    the workgroup id splits into (tile, head) differently for each."""
+    w = workloads.make_custom([[9, 14], [1, 70], [12, 12]], [40, 0, 77], heads=heads, head_dim=d, dtype="bf16",
+                              seed=heads + d, name=f"heads{heads}")
+    _full_check(w)
+
+
+def test_attention_largest_grid_sampled():
+    """The largest supported sample: a 512 x 512 grid (positions up to 511 on
+    both axes, 4100 key tiles) after a 256-token prompt, plus a small sample
+    after it; checked on seeded rows including the grid's corners."""
+    w = workloads.make_custom([[512, 512], [3, 4]], [256, 5], heads=2, head_dim=128, dtype="bf16", seed=12,
+                              name="grid512")
+    print(f"attention grid512 T={w.tokens}", flush=True)
+    got = run_attention(w)
+    t0 = 256  # first image token of the big sample
+    corners = [t0, t0 + 511, t0 + 511 * 512, t0 + 512 * 512 - 1]
+    rows = np.unique(np.concatenate([_sample_rows(w, 96, seed=13), corners]))
+    g = to_f64(got[torch.from_numpy(rows).cuda()])
+    exp = attention.joint_attention_rows(w.q, w.k, w.v, w.grid_hw, w.text_len, rows)
+    check_close(g, exp, w.dtype)
+    assert torch.isfinite(got.float()).all()
+
+
 def test_one_token_returns_v():
     w = workloads.make_custom([[1, 1], [1, 1]], [0, 0], heads=2, head_dim=128, dtype="bf16", seed=1)
     got = run_attention(w)
