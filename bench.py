@@ -32,7 +32,7 @@ TRAFFIC_FILE = os.path.join(ROOT, "profiles", "attn_fwd_bf16_1024sq_traffic.json
 KERNEL_SOURCES = [
     os.path.join(ROOT, "text_image_diffusion_varlen_amd", "csrc", name)
     for name in ("attn_fwd.hip", "mf_common.h", "mfma_util.h", "rope_math.h")
-]
+] + [os.path.join(ROOT, "text_image_diffusion_varlen_amd", "build.py")]  # compile flags
 DESCRIPTIONS = {
     "tiny": "one 256x256 image (16x16 grid) + 32 prompt tokens, L=288, 2 heads x 64, fp32",
     "1024sq": "one 1024x1024 image (64x64 grid) + 256 prompt tokens, L=4352, 24 heads x 128, bf16",

@@ -23,6 +23,10 @@ ARCH = "gfx950"
 DEVICE_FLAGS = ["-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops"]
 COMMON = ["-O3", "-std=c++17", "-fPIC", f"--offload-arch={ARCH}", "-Wall",
           "-I", os.path.join(ROOT, "include"), "-I", CSRC]
+# Per-source flags. The forward attention kernel is scheduled with the
+# memory-clause strategy: measured 1.5-2.6% faster than the default on the
+# mixed and 65k-token batches (same code, same registers).
+EXTRA = {"attn_fwd.hip": ["-mllvm", "-amdgpu-sched-strategy=max-memory-clause"]}
 
 
 def hipcc() -> str:
@@ -38,7 +42,7 @@ def sources():
 
 def _compile(src: str) -> str:
     obj = os.path.join(BUILD, os.path.basename(src)[:-4] + ".o")
-    cmd = [hipcc(), *COMMON, *DEVICE_FLAGS, "-c", src, "-o", obj]
+    cmd = [hipcc(), *COMMON, *DEVICE_FLAGS, *EXTRA.get(os.path.basename(src), []), "-c", src, "-o", obj]
     r = subprocess.run(cmd, capture_output=True, text=True)
     # hipcc's host pass does not know the device feature flag; that warning is expected.
     noise = "is not a recognized feature for this target"
