@@ -185,6 +185,28 @@ def sampler_bench(steps: int, warmup: int):
     if binding.get_device_error() != binding.MF_OK:
         raise RuntimeError(binding.last_error())
     nbytes = b.image_tokens * b.channels * (4 + 4 + 2 + 2)
+    # Context: torch.add of two fp32 tensors of z's size into a third moves the
+    # same bytes (reads 2 x 4 B, writes 4 B per element), timed the same way.
+    del sets, g
+    n = b.image_tokens * b.channels
+    adds = [tuple(torch.empty(n, dtype=torch.float32, device="cuda").normal_() for _ in range(3))
+            for _ in range(n_sets)]
+    for x, y, o in adds:
+        torch.add(x, y, out=o)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        for x, y, o in adds:
+            torch.add(x, y, out=o)
+    g.replay()
+    torch.cuda.synchronize()
+    start.record()
+    for _ in range(reps):
+        g.replay()
+    stop.record()
+    torch.cuda.synchronize()
+    add_sec = start.elapsed_time(stop) / 1e3 / (reps * n_sets)
+    del adds, g
     return {
         "workload": "cfg1024: 8 images of 64x64 latent tokens x 128 channels, conditional + empty-prompt "
                     "unconditional samples interleaved, bf16 velocities, fp32 latents",
@@ -192,6 +214,7 @@ def sampler_bench(steps: int, warmup: int):
         "us_per_step_eager": round(eager * 1e6, 2),
         "gbps": round(nbytes / sec / 1e9, 1),
         "frac_hbm": round(nbytes / sec / HBM_PEAK, 4),
+        "torch_add_same_bytes_us": round(add_sec * 1e6, 2),
         "algorithmic_bytes": nbytes,
         "buffer_sets": n_sets,
     }
