@@ -96,6 +96,13 @@ const char* mf_last_error(void);
  * freed at process exit); calls on one device are serialized by the caller's
  * stream order only, so concurrent calls on different streams of one device
  * must use mf_attn_packed_ws with separate workspaces.
+ * Results are deterministic (no atomics). For bf16, when the last round of
+ * (256-query tile, head) units would fill the device poorly and its units are
+ * long, those units are split over key ranges and a second kernel merges the
+ * pieces in a fixed order; this happens only for batches whose mean sample
+ * length is at least 8129 tokens, and it changes the rounding of the split
+ * units (not the result beyond it). MF_ATTN_SPLIT=0 in the environment (read
+ * at the first call on a device) turns the split off.
  */
 int mf_attn_packed(const void* q, const void* k, const void* v, const int32_t* cu_seqlens,
                    const int32_t* grid_hw, const int32_t* text_len, void* out, int32_t n_seg,

@@ -24,9 +24,11 @@ def test_workspace_bytes():
     import torch
     wb = binding.workspace_bytes
     tensor = 4352 * 24 * 128
-    # bf16: K~ and V~^T (queries are rotated in the kernel); fp32: Q~, K~ and V
-    assert 2 * tensor * 2 < wb(4352, 24, 128, torch.bfloat16, 1) < 3 * tensor * 2
-    assert wb(4352, 24, 128, torch.float32, 1) > 3 * tensor * 4
+    # bf16: K~ and V~^T (queries are rotated in the kernel) and 512 partial-result
+    # slots of 256 rows x (128 + 2) floats; fp32: Q~, K~ and V, no partials
+    partials = 512 * 256 * 130 * 4
+    assert 2 * tensor * 2 + partials < wb(4352, 24, 128, torch.bfloat16, 1) < 3 * tensor * 2 + partials
+    assert 3 * tensor * 4 < wb(4352, 24, 128, torch.float32, 1) < 4 * tensor * 4
     lib = binding.lib()
     assert lib.mf_workspace_bytes(100, 2, 96, 0, 1) == 0  # unsupported head_dim
     assert lib.mf_workspace_bytes(100, 2, 64, 7, 1) == 0  # unknown dtype

@@ -36,9 +36,9 @@ hipError_t launch_rope_pack(const void* q, const void* k, const void* v, const i
 hipError_t launch_rope(const void* x, void* y, const int32_t* pos, int64_t tokens, int32_t heads,
                        int32_t head_dim, bool bf16, const float2* cs, const Rope3* r3, int32_t* status,
                        hipStream_t s);
-hipError_t launch_attn_fwd(const char* ws, const WsLayout& l, const void* q, const int32_t* grid_hw,
+hipError_t launch_attn_fwd(char* ws, const WsLayout& l, const void* q, const int32_t* grid_hw,
                            const int32_t* text_len, const float2* cs, const Rope3* r3, void* out, float* lse,
-                           int64_t tokens, int32_t heads, int32_t head_dim, bool bf16, float scale,
+                           int64_t tokens, int32_t heads, int32_t head_dim, bool bf16, float scale, int32_t ncu,
                            hipStream_t s);
 hipError_t launch_attn_bwd(const void* q, const void* k, const void* v, const void* o, const void* dout,
                            const float* lse, const int32_t* grid_hw, const int32_t* text_len,
@@ -85,6 +85,7 @@ struct DeviceState {
   size_t bws_bytes = 0;
   char* qws = nullptr;        // library workspace of mf_qkv_rmsnorm
   size_t qws_bytes = 0;
+  int32_t ncu = -1;           // compute units for the forward's split plan (0: splitting off); -1 unknown
   // (head_dim, theta bits, row channels, column channels) -> cos/sin table;
   // row channels -1 marks the 2D table
   std::map<std::tuple<int, uint32_t, int, int>, float2*> tables;
@@ -96,6 +97,21 @@ std::map<int, DeviceState> g_dev;
 int current_device(int* dev) {
   const hipError_t e = hipGetDevice(dev);
   return e == hipSuccess ? MF_OK : hip_fail(e, "hipGetDevice");
+}
+
+// Compute units of the device, for the forward's split of a partly filled
+// last round (MF_ATTN_SPLIT=0 in the environment turns the split off).
+// Caller holds g_mu.
+int ensure_cus(DeviceState& st, int dev, int32_t* ncu) {
+  if (st.ncu < 0) {
+    int v = 0;
+    const hipError_t e = hipDeviceGetAttribute(&v, hipDeviceAttributeMultiprocessorCount, dev);
+    if (e != hipSuccess) return hip_fail(e, "hipDeviceGetAttribute(multiprocessor count)");
+    const char* off = std::getenv("MF_ATTN_SPLIT");
+    st.ncu = off && off[0] == '0' ? 0 : v;
+  }
+  *ncu = st.ncu;
+  return MF_OK;
 }
 
 // Caller holds g_mu.
@@ -260,7 +276,7 @@ int check_attn_args(const void* q, const void* k, const void* v, const int32_t* 
 
 int run_attn(const void* q, const void* k, const void* v, const int32_t* cu, const int32_t* grid_hw,
              const int32_t* text_len, void* out, int32_t n_seg, int64_t tokens, int32_t heads,
-             int32_t head_dim, int32_t dtype, char* ws, const float2* cs, hipStream_t s,
+             int32_t head_dim, int32_t dtype, char* ws, const float2* cs, int32_t ncu, hipStream_t s,
              hipEvent_t const* ev = nullptr, float* lse = nullptr, const int32_t* frames = nullptr,
              const mf::Rope3* r3 = nullptr) {
   const bool bf16 = dtype == MF_BF16;
@@ -274,7 +290,8 @@ int run_attn(const void* q, const void* k, const void* v, const int32_t* cu, con
   if (e != hipSuccess) return hip_fail(e, "rope_pack_kernel launch");
   if (ev && (e = hipEventRecord(ev[2], s)) != hipSuccess) return hip_fail(e, "hipEventRecord");
   e = mf::launch_attn_fwd(ws, l, q, grid_hw, text_len, cs, r3, out, lse, tokens, heads, head_dim, bf16,
-                          float(1.0 / std::sqrt(double(head_dim))), s);
+                          float(1.0 / std::sqrt(double(head_dim))),
+                          mf::split_possible(tokens, n_seg) ? ncu : 0, s);
   if (e != hipSuccess) return hip_fail(e, "attn_fwd launch");
   if (ev && (e = hipEventRecord(ev[3], s)) != hipSuccess) return hip_fail(e, "hipEventRecord");
   return MF_OK;
@@ -310,10 +327,12 @@ int mf_attn_packed_profiled(const void* q, const void* k, const void* v, const i
   std::lock_guard<std::mutex> lock(g_mu);
   DeviceState& st = g_dev[dev];
   const float2* cs = nullptr;
+  int32_t ncu = 0;
   if ((rc = ensure_table(st, head_dim, MF_ROPE_THETA, &cs))) return rc;
+  if ((rc = ensure_cus(st, dev, &ncu))) return rc;
   if ((rc = ensure_workspace(st, need))) return rc;
   return run_attn(q, k, v, cu_seqlens, grid_hw, text_len, out, n_seg, total_tokens, heads, head_dim,
-                  dtype, st.ws, cs, stream, events);
+                  dtype, st.ws, cs, ncu, stream, events);
 }
 
 int mf_attn_packed(const void* q, const void* k, const void* v, const int32_t* cu_seqlens,
@@ -344,12 +363,14 @@ int mf_attn_packed_ws(const void* q, const void* k, const void* v, const int32_t
   int dev;
   if ((rc = current_device(&dev))) return rc;
   const float2* cs = nullptr;
+  int32_t ncu = 0;
   {
     std::lock_guard<std::mutex> lock(g_mu);
     if ((rc = ensure_table(g_dev[dev], head_dim, MF_ROPE_THETA, &cs))) return rc;
+    if ((rc = ensure_cus(g_dev[dev], dev, &ncu))) return rc;
   }
   return run_attn(q, k, v, cu_seqlens, grid_hw, text_len, out, n_seg, total_tokens, heads, head_dim,
-                  dtype, static_cast<char*>(workspace), cs, stream);
+                  dtype, static_cast<char*>(workspace), cs, ncu, stream);
 }
 
 }  // extern "C"
@@ -390,9 +411,11 @@ int attn_impl(const void* q, const void* k, const void* v, const int32_t* cu_seq
   } else if ((rc = ensure_table(st, head_dim, MF_ROPE_THETA, &cs))) {
     return rc;
   }
+  int32_t ncu = 0;
+  if ((rc = ensure_cus(st, dev, &ncu))) return rc;
   if ((rc = ensure_workspace(st, need))) return rc;
   return run_attn(q, k, v, cu_seqlens, grid_hw, text_len, out, n_seg, total_tokens, heads, head_dim, dtype,
-                  st.ws, cs, stream, nullptr, lse, frames, split ? &r3 : nullptr);
+                  st.ws, cs, ncu, stream, nullptr, lse, frames, split ? &r3 : nullptr);
 }
 
 int bwd_impl(const void* q, const void* k, const void* v, const void* out, const void* d_out, const float* lse,

@@ -48,11 +48,21 @@ struct AttnArgs {
   const void* vw;
   void* out;
   float* lse;        // optional [heads][tokens] natural-log row sum-exp of the scaled scores
+  float* part;       // partial results of split units (bf16 path), PART_SLOTS slots
+  int32_t ncu;       // compute units for the split plan (0: never split)
   int64_t tokens;
   int32_t heads;
   int64_t rows;      // padded rows per head in the workspace
   float c_log2;      // softmax scale * log2(e)
 };
+
+// The split plan of this call (same in every workgroup of every kernel):
+// units = tiles x heads, the shortest unit is the last tile's.
+__device__ inline SplitPlan call_plan(const AttnArgs& a, const WsHeader* hdr) {
+  const int2 last = reinterpret_cast<const int2*>(a.ws + a.off_tiles)[hdr->n_tiles - 1];
+  const int32_t Ls = reinterpret_cast<const int32_t*>(a.ws + a.off_len)[last.x];
+  return split_plan(int64_t(hdr->n_tiles) * a.heads, a.ncu, (Ls + KTILE - 1) / KTILE);
+}
 
 // Copies one chunk-major tile (CHUNKS 16-byte chunks) from the workspace into
 // LDS with direct-to-LDS loads spread over the workgroup's waves.
@@ -174,14 +184,31 @@ __global__ void __launch_bounds__(ATTN_THREADS, 2) attn_fwd_bf16_kernel(AttnArgs
 
   const WsHeader* hdr = reinterpret_cast<const WsHeader*>(a.ws);
   const int32_t heads = a.heads;
-  const int h = int(blockIdx.x % unsigned(heads));
-  const int tile = int(blockIdx.x / unsigned(heads));
-  if (hdr->flag != FLAG_OK || tile >= hdr->n_tiles) return;
+  if (hdr->flag != FLAG_OK) return;
+  // Unit (query tile, head) of this workgroup: a whole unit, or piece `part`
+  // of a unit of the split last round (its key tiles [kt0, kt1)).
+  const SplitPlan plan = call_plan(a, hdr);
+  int unit = int(blockIdx.x), part = -1;
+  if (unit >= plan.n_full) {
+    const int piece = unit - plan.n_full;
+    if (piece >= plan.n_tail * plan.parts) return;
+    unit = plan.n_full + piece / plan.parts;
+    part = piece % plan.parts;
+  }
+  const int h = unit % heads;
+  const int tile = unit / heads;
   const int2 td = reinterpret_cast<const int2*>(a.ws + a.off_tiles)[tile];
   const int32_t seg = td.x, qs = td.y;
   const int32_t L = reinterpret_cast<const int32_t*>(a.ws + a.off_len)[seg];
   const int32_t pb = reinterpret_cast<const int32_t*>(a.ws + a.off_pcu)[seg];
   const int32_t cb = reinterpret_cast<const int32_t*>(a.ws + a.off_cu)[seg];
+  const int nkt_all = (L + KTILE - 1) / KTILE;
+  int kt0 = 0, kt1 = nkt_all;
+  if (part >= 0) {
+    kt0 = part * nkt_all / plan.parts;
+    kt1 = (part + 1) * nkt_all / plan.parts;
+    if (kt0 == kt1) return;  // empty piece of a short unit: the merge skips it
+  }
 
   const int tid = threadIdx.x;
   const int wave = tid >> 6, lane = tid & 63, hf = lane >> 5, l32 = lane & 31;
@@ -215,9 +242,12 @@ __global__ void __launch_bounds__(ATTN_THREADS, 2) attn_fwd_bf16_kernel(AttnArgs
 
   // Two LDS buffers, each one K~ tile and one V~^T tile (chunk-major, verbatim copies).
   __shared__ u32x4 kA[CHUNKS], vA[CHUNKS], kB[CHUNKS], vB[CHUNKS];
-  const u32x4* kg = reinterpret_cast<const u32x4*>(static_cast<const uint16_t*>(a.kw) + head_row0 * D);
-  const u32x4* vg = reinterpret_cast<const u32x4*>(static_cast<const uint16_t*>(a.vw) + head_row0 * D);
-  const int nkt = (L + KTILE - 1) / KTILE;
+  // Key tiles [kt0, kt1) of the sample; the sample's last tile carries the key mask.
+  const u32x4* kg = reinterpret_cast<const u32x4*>(static_cast<const uint16_t*>(a.kw) + head_row0 * D) + kt0 * CHUNKS;
+  const u32x4* vg = reinterpret_cast<const u32x4*>(static_cast<const uint16_t*>(a.vw) + head_row0 * D) + kt0 * CHUNKS;
+  const int nkt = kt1 - kt0;
+  const int key0 = KTILE * kt0;
+  const bool mask_last = kt1 == nkt_all;
 
   const float c = a.c_log2;
   float m = -INFINITY;  // reference row max (log2 units)
@@ -235,26 +265,46 @@ __global__ void __launch_bounds__(ATTN_THREADS, 2) attn_fwd_bf16_kernel(AttnArgs
   for (; j + 2 < nkt; j += 2) {
     tile_to_lds<CHUNKS>(kg + (j + 1) * CHUNKS, kB, wave, lane);
     tile_to_lds<CHUNKS>(vg + (j + 1) * CHUNKS, vB, wave, lane);
-    attend_tile<D, false>(kA, vA, qreg, acc, m, lsum, c, KTILE * j, L, hf, l32);
+    attend_tile<D, false>(kA, vA, qreg, acc, m, lsum, c, key0 + KTILE * j, L, hf, l32);
     wait_tile_and_sync();
     tile_to_lds<CHUNKS>(kg + (j + 2) * CHUNKS, kA, wave, lane);
     tile_to_lds<CHUNKS>(vg + (j + 2) * CHUNKS, vA, wave, lane);
-    attend_tile<D, false>(kB, vB, qreg, acc, m, lsum, c, KTILE * (j + 1), L, hf, l32);
+    attend_tile<D, false>(kB, vB, qreg, acc, m, lsum, c, key0 + KTILE * (j + 1), L, hf, l32);
     wait_tile_and_sync();
   }
   if (j + 1 < nkt) {
     tile_to_lds<CHUNKS>(kg + (j + 1) * CHUNKS, kB, wave, lane);
     tile_to_lds<CHUNKS>(vg + (j + 1) * CHUNKS, vB, wave, lane);
-    attend_tile<D, false>(kA, vA, qreg, acc, m, lsum, c, KTILE * j, L, hf, l32);
+    attend_tile<D, false>(kA, vA, qreg, acc, m, lsum, c, key0 + KTILE * j, L, hf, l32);
     wait_tile_and_sync();
-    attend_tile<D, true>(kB, vB, qreg, acc, m, lsum, c, KTILE * (j + 1), L, hf, l32);
+    if (mask_last) attend_tile<D, true>(kB, vB, qreg, acc, m, lsum, c, key0 + KTILE * (j + 1), L, hf, l32);
+    else attend_tile<D, false>(kB, vB, qreg, acc, m, lsum, c, key0 + KTILE * (j + 1), L, hf, l32);
   } else {
-    attend_tile<D, true>(kA, vA, qreg, acc, m, lsum, c, KTILE * j, L, hf, l32);
+    if (mask_last) attend_tile<D, true>(kA, vA, qreg, acc, m, lsum, c, key0 + KTILE * j, L, hf, l32);
+    else attend_tile<D, false>(kA, vA, qreg, acc, m, lsum, c, key0 + KTILE * j, L, hf, l32);
   }
 
   // Epilogue: O = acc / l. Accumulator entry e of block b holds channel
   // 32*b + 8*(e/4) + 4*hf + e%4 of query l32.
   lsum = halves_sum(lsum);
+  if (part >= 0) {
+    // Piece of a split unit: unnormalized accumulator, reference max and row
+    // sum into its slot, for the merge kernel.
+    const int r = 32 * wave + l32;
+    float* slot = a.part + int64_t(blockIdx.x - plan.n_full) * QTILE * (D + 2);
+#pragma unroll
+    for (int b = 0; b < DBLK; ++b) {
+#pragma unroll
+      for (int g = 0; g < 4; ++g)
+        *reinterpret_cast<float4*>(slot + int64_t(r) * D + 32 * b + 8 * g + 4 * hf) =
+            make_float4(acc[b][4 * g], acc[b][4 * g + 1], acc[b][4 * g + 2], acc[b][4 * g + 3]);
+    }
+    if (hf == 0) {
+      slot[QTILE * D + r] = m;
+      slot[QTILE * D + QTILE + r] = lsum;
+    }
+    return;
+  }
   const float inv = 1.f / lsum;
   const int32_t qrel = qs + 32 * wave + l32;
   // log-sum-exp in natural-log units: p = 2^(s c - m) / lsum, so
@@ -272,6 +322,80 @@ __global__ void __launch_bounds__(ATTN_THREADS, 2) attn_fwd_bf16_kernel(AttnArgs
         *reinterpret_cast<uint2*>(orow + 32 * b + 8 * g + 4 * hf) = v2;
       }
     }
+  }
+}
+
+// Merge of the pieces of split units. Piece i of a unit holds, per query row,
+// an accumulator and a row sum taken relative to its own reference max m_i;
+// with M = max_i m_i and w_i = 2^(m_i - M) the row is
+//   O = sum_i w_i acc_i / sum_i w_i l_i,   log-sum-exp = (M + log2 sum_i w_i l_i) ln 2,
+// summed in piece order (deterministic). Each workgroup takes 64 rows of one
+// split unit, each wave 16 rows: lanes 0-15 form the weights of one row each,
+// then all lanes stream the rows' accumulators (D/64 channels per lane) with
+// the weights broadcast from those lanes, every row's loads issued together.
+constexpr int MERGE_ROWS = 64;  // rows per merge workgroup
+template <int D>
+__global__ void __launch_bounds__(256) attn_merge_kernel(AttnArgs a) {
+  const WsHeader* hdr = reinterpret_cast<const WsHeader*>(a.ws);
+  if (hdr->flag != FLAG_OK) return;
+  const int32_t heads = a.heads;
+  const SplitPlan plan = call_plan(a, hdr);
+  constexpr int BLOCKS = QTILE / MERGE_ROWS;
+  const int u = int(blockIdx.x) / BLOCKS;
+  if (u >= plan.n_tail) return;
+  const int unit = plan.n_full + u;
+  const int h = unit % heads, tile = unit / heads;
+  const int2 td = reinterpret_cast<const int2*>(a.ws + a.off_tiles)[tile];
+  const int32_t seg = td.x, qs = td.y;
+  const int32_t L = reinterpret_cast<const int32_t*>(a.ws + a.off_len)[seg];
+  const int32_t cb = reinterpret_cast<const int32_t*>(a.ws + a.off_cu)[seg];
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int r0 = MERGE_ROWS * (int(blockIdx.x) % BLOCKS) + 16 * wave;  // this wave's first row
+  if (qs + r0 >= L) return;
+  const int nkt = (L + KTILE - 1) / KTILE;
+  const int S = plan.parts;  // 2 to 4
+  constexpr int CPL = D / 64;
+  constexpr int64_t SLOT = int64_t(QTILE) * (D + 2);
+  const float* slot0 = a.part + int64_t(u) * S * SLOT;
+  // Weights of row r0 + lane (lanes 0-15); an empty piece (never written) weighs 0.
+  float wgt[4] = {0.f, 0.f, 0.f, 0.f}, inv = 0.f;
+  if (lane < 16) {
+    const int r = r0 + lane;
+    float mp[4], lp[4];
+    float M = -INFINITY;
+#pragma unroll
+    for (int p = 0; p < 4; ++p) {
+      const bool live = p < S && (p + 1) * nkt / S != p * nkt / S;
+      mp[p] = live ? slot0[p * SLOT + QTILE * D + r] : -INFINITY;
+      lp[p] = live ? slot0[p * SLOT + QTILE * D + QTILE + r] : 0.f;
+      M = fmaxf(M, mp[p]);
+    }
+    float lsum = 0.f;
+#pragma unroll
+    for (int p = 0; p < 4; ++p) {
+      wgt[p] = lp[p] > 0.f ? __builtin_amdgcn_exp2f(mp[p] - M) : 0.f;
+      lsum += wgt[p] * lp[p];
+    }
+    inv = 1.f / lsum;
+    if (a.lse && qs + r < L) a.lse[int64_t(h) * a.tokens + cb + qs + r] = (M + log2f(lsum)) * 0.6931471805599453f;
+  }
+#pragma unroll 4
+  for (int rr = 0; rr < 16; ++rr) {
+    const int r = r0 + rr;
+    if (qs + r >= L) break;  // same for the whole wave
+    float o[CPL] = {};
+#pragma unroll
+    for (int p = 0; p < 4; ++p) {
+      const float w = __shfl(wgt[p], rr);
+      if (w != 0.f) {
+#pragma unroll
+        for (int e = 0; e < CPL; ++e) o[e] += w * slot0[p * SLOT + int64_t(r) * D + CPL * lane + e];
+      }
+    }
+    const float ir = __shfl(inv, rr);
+    uint16_t* orow = static_cast<uint16_t*>(a.out) + (int64_t(cb + qs + r) * heads + h) * D + CPL * lane;
+    if constexpr (CPL == 2) *reinterpret_cast<uint32_t*>(orow) = pack_bf16x2(o[0] * ir, o[1] * ir);
+    else orow[0] = uint16_t(pack_bf16x2(o[0] * ir, 0.f) & 0xFFFFu);
   }
 }
 
@@ -351,9 +475,9 @@ __global__ void __launch_bounds__(ATTN_THREADS) attn_fwd_f32_kernel(AttnArgs a) 
   }
 }
 
-hipError_t launch_attn_fwd(const char* ws, const WsLayout& l, const void* q, const int32_t* grid_hw,
+hipError_t launch_attn_fwd(char* ws, const WsLayout& l, const void* q, const int32_t* grid_hw,
                            const int32_t* text_len, const float2* cs, const Rope3* r3, void* out, float* lse,
-                           int64_t tokens, int32_t heads, int32_t head_dim, bool bf16, float scale,
+                           int64_t tokens, int32_t heads, int32_t head_dim, bool bf16, float scale, int32_t ncu,
                            hipStream_t s) {
   AttnArgs a;
   a.ws = ws;
@@ -371,11 +495,15 @@ hipError_t launch_attn_fwd(const char* ws, const WsLayout& l, const void* q, con
   a.vw = ws + l.off_v;
   a.out = out;
   a.lse = lse;
+  a.part = reinterpret_cast<float*>(ws + l.off_part);
+  a.ncu = bf16 ? ncu : 0;  // the fp32 path never splits
   a.tokens = tokens;
   a.heads = heads;
   a.rows = l.rows;
   a.c_log2 = scale * 1.4426950408889634f;
-  const dim3 grid(unsigned(l.n_tiles * heads));
+  // Whole units, then up to PART_SLOTS pieces of split units; workgroups past
+  // the plan return at once.
+  const dim3 grid(unsigned(l.n_tiles * heads + (a.ncu > 0 ? PART_SLOTS : 0)));
   if (bf16) {
     if (r3) {
       if (head_dim == 128) hipLaunchKernelGGL((attn_fwd_bf16_kernel<128, true>), grid, dim3(ATTN_THREADS), 0, s, a);
@@ -387,6 +515,14 @@ hipError_t launch_attn_fwd(const char* ws, const WsLayout& l, const void* q, con
   } else {
     if (head_dim == 128) hipLaunchKernelGGL(attn_fwd_f32_kernel<128>, grid, dim3(ATTN_THREADS), 0, s, a);
     else hipLaunchKernelGGL(attn_fwd_f32_kernel<64>, grid, dim3(ATTN_THREADS), 0, s, a);
+  }
+  if (a.ncu > 0) {
+    // Split units: at most PART_SLOTS / 2 (two or more pieces each).
+    const hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    const dim3 mgrid(unsigned(PART_SLOTS / 2 * (QTILE / MERGE_ROWS)));
+    if (head_dim == 128) hipLaunchKernelGGL(attn_merge_kernel<128>, mgrid, dim3(256), 0, s, a);
+    else hipLaunchKernelGGL(attn_merge_kernel<64>, mgrid, dim3(256), 0, s, a);
   }
   return hipGetLastError();
 }

@@ -39,7 +39,55 @@ __host__ __device__ inline int64_t max_tiles(int64_t tokens, int32_t n_seg) {
   return ceil_div(tokens, QTILE) + n_seg;
 }
 
-// Workspace: [header 256 B][len n][cu n+1][pcu n+1][tiles 2*max_tiles][Q~][K~][V~]
+// Split of the last partial round of (query tile, head) units over key ranges.
+// With U units on ncu CUs (one workgroup per CU), the last U mod ncu units
+// would run as a partly filled round as long as a whole unit. Cut into s key
+// ranges (2 to 4), they take ceil(s * tail / ncu) / s of that time, plus a
+// fixed cost per piece (its query load, first tile and partial write) and a
+// merge kernel that combines the partial results; on a 1024x1024 batch that
+// overhead measured about 60 us, some 35 key tiles of work, and erased the
+// saving. So the tail is split only when that saves at least
+// SPLIT_MIN_SAVED key tiles of its shortest unit (nkt_short key tiles; units
+// are dispatched longest first, so the last unit is the shortest).
+// Units are numbered in dispatch order: [0, n_full) whole, then n_tail units
+// of `parts` pieces each. Every kernel derives the same plan from
+// (U, ncu, nkt_short), so nothing is stored.
+constexpr int PART_SLOTS = 512;      // partial-result slots in the workspace (pieces per call)
+constexpr int SPLIT_MIN_SAVED = 96;  // key tiles a split must save on the tail's shortest unit
+// A split needs a shortest unit of at least 4/3 * SPLIT_MIN_SAVED key tiles
+// (4 parts in one round), i.e. a shortest sample of more than
+// (4/3 * SPLIT_MIN_SAVED - 1) * KTILE tokens; the shortest sample is never
+// longer than the mean, so a batch with tokens / n_seg below that cannot split
+// and the host then skips the merge launch (and tells the kernel not to split).
+constexpr int64_t SPLIT_MIN_MEAN_LEN = (int64_t(SPLIT_MIN_SAVED) * 4 / 3 - 1) * KTILE + 1;
+__host__ __device__ inline bool split_possible(int64_t tokens, int32_t n_seg) {
+  return tokens >= int64_t(n_seg) * SPLIT_MIN_MEAN_LEN;
+}
+struct SplitPlan {
+  int32_t n_full, n_tail, parts;
+};
+__host__ __device__ inline SplitPlan split_plan(int64_t units, int32_t ncu, int64_t nkt_short) {
+  SplitPlan p{int32_t(units), 0, 1};
+  if (ncu <= 0 || units <= ncu) return p;
+  const int64_t tail = units % ncu;
+  if (tail == 0) return p;
+  // Time of the tail in whole-unit times: ceil(s * tail / ncu) / s for s parts.
+  int64_t best_r = 1, best_s = 1;  // rounds of pieces, parts (ratio best_r / best_s)
+  for (int64_t s = 2; s <= 4 && s * tail <= PART_SLOTS; ++s) {
+    const int64_t r = (s * tail + ncu - 1) / ncu;
+    if (r * best_s < best_r * s) {
+      best_r = r;
+      best_s = s;
+    }
+  }
+  if (best_s == 1 || nkt_short * (best_s - best_r) < SPLIT_MIN_SAVED * best_s) return p;
+  p.n_full = int32_t(units - tail);
+  p.n_tail = int32_t(tail);
+  p.parts = int32_t(best_s);
+  return p;
+}
+
+// Workspace: [header 256 B][len n][cu n+1][pcu n+1][tiles 2*max_tiles][Q~][K~][V~][partials]
 // with every section 256-byte aligned. Q~, K~, V~ are [heads][rows][head_dim].
 struct WsHeader {
   int32_t flag;          // FLAG_* of the last metadata check
@@ -51,7 +99,7 @@ struct WsHeader {
 static_assert(sizeof(WsHeader) == 256, "header is one 256-byte block");
 
 struct WsLayout {
-  int64_t off_len, off_cu, off_pcu, off_tiles, off_q, off_k, off_v, total;
+  int64_t off_len, off_cu, off_pcu, off_tiles, off_q, off_k, off_v, off_part, total;
   int64_t rows;     // padded rows per head
   int64_t n_tiles;  // capacity of the tile table
 };
@@ -70,6 +118,9 @@ __host__ __device__ inline WsLayout ws_layout(int64_t tokens, int32_t heads, int
   l.off_q = o; o += elem_bytes == 4 ? buf : 0;  // rotated queries: fp32 path only (bf16 rotates them in the kernel)
   l.off_k = o; o += buf;
   l.off_v = o; o += buf;
+  // bf16 path: PART_SLOTS partial results of split units, each QTILE rows of
+  // head_dim fp32 accumulators followed by QTILE reference maxima and QTILE row sums.
+  l.off_part = o; o += elem_bytes == 2 ? int64_t(PART_SLOTS) * QTILE * (head_dim + 2) * 4 : 0;
   l.total = o;
   return l;
 }
