@@ -165,7 +165,13 @@ int mf_attn_packed_lse(const void* q, const void* k, const void* v, const int32_
  * metadata is checked on the device as for the forward: on a mismatch nothing
  * is written and mf_get_device_error() reports MF_ERR_METADATA. Uses a second
  * library-owned per-device workspace (mf_bwd_workspace_bytes), with the same
- * stream-order rule as mf_attn_packed. Deterministic: no atomics.
+ * stream-order rule as mf_attn_packed. Deterministic: no atomics. When the
+ * last round of (128-key block, head) units of the dK/dV kernel would fill the
+ * device poorly and its units are long, those units are split over query
+ * ranges and the pieces' fp32 partial sums are added in a fixed order; this
+ * happens only for batches whose mean sample length is at least 1985 tokens,
+ * changes the rounding of dk and dv in the split units, and is turned off by
+ * MF_ATTN_SPLIT=0 like the forward's split.
  */
 int mf_attn_packed_bwd(const void* q, const void* k, const void* v, const void* out, const void* d_out,
                        const float* lse, const int32_t* cu_seqlens, const int32_t* grid_hw,

@@ -1,12 +1,13 @@
-"""GPU parity of the split last round of the forward.
+"""GPU parity of the split last round (forward and the backward's dK/dV kernel).
 
-When the last round of (query tile, head) units fills less of the GPU than a
-split would recover, those units are cut into key ranges whose partial results
-a merge kernel combines (long samples, more units than compute units). These
-batches are built so that the plan splits (the shapes and head counts below
-give a short last round of long units on a 256-CU MI355X); outputs and the row
-log-sum-exp (also formed by the merge) are checked against the fp64 oracle with
-the bars of the whole-unit path, and repeated calls must agree bit for bit.
+When the last round of work units fills less of the GPU than a split would
+recover, those units are cut into pieces whose partial results a merge kernel
+combines: forward units (query tile, head) over key ranges, dK/dV units
+(128-key block, head) over query ranges. These batches are built so that the
+plans split (the shapes and head counts below give a short last round of long
+units on a 256-CU MI355X); outputs, the row log-sum-exp (formed by the forward
+merge) and the gradients are checked against the fp64 oracle with the bars of
+the whole-unit paths, and repeated calls must agree bit for bit.
 """
 import numpy as np
 import pytest
@@ -68,3 +69,58 @@ def test_split_round_edit():
     check_close(to_f64(out), ref, "bf16")
     lse_ref = attention.joint_attention_3d_lse(w.q, w.k, w.grid_hw, w.text_len, w.frames, w.rope_split)
     assert np.abs(lse.double().cpu().numpy() - lse_ref).max() <= LSE_TOL
+
+
+# Backward: the dK/dV kernel's units are (128-key block, head); a 4352-token
+# sample with 8 heads gives 272 units, the last 16 split 4 ways over query ranges.
+BWD_SPLIT = {
+    "bwd_1024_d128": ([[64, 64]], [256], 8, 128),
+    "bwd_1024_d64": ([[64, 64]], [256], 8, 64),
+    "bwd_edit": None,  # a 2-image edit of 40 x 52 after a 70-token prompt, 8 heads (frame-aware path)
+}
+GRAD_TOL = (2e-2, 1e-2)  # relative to the reference's own max / mean magnitude, as in the backward tests
+GRAD_FLOOR = 1e-5
+
+
+def _check_grad(name, got, ref):
+    err = np.abs(got - ref)
+    assert np.isfinite(got).all(), f"{name}: non-finite"
+    assert err.max() <= GRAD_TOL[0] * np.abs(ref).max() + GRAD_FLOOR, name
+    assert err.mean() <= GRAD_TOL[1] * np.abs(ref).mean() + GRAD_FLOOR, name
+
+
+@pytest.mark.parametrize("name", sorted(BWD_SPLIT))
+def test_split_round_backward(name):
+    if name == "bwd_edit":
+        w = workloads.make_edit(grids=[[40, 52]], texts=[70], frames=[2], heads=8, head_dim=128, dtype="bf16",
+                                seed=21, name=name)
+    else:
+        grids, texts, heads, d = BWD_SPLIT[name]
+        w = workloads.make_custom(grids, texts, heads=heads, head_dim=d, dtype="bf16", seed=20, name=name)
+    print(f"split {name} T={w.tokens} H={w.heads} d={w.head_dim}", flush=True)
+    rng = np.random.default_rng(22)
+    do = workloads.bf16_bits_to_f32(workloads.f32_to_bf16_bits(rng.standard_normal(w.q.shape, dtype=np.float32)))
+    q, k, v, grid, text = device_inputs(w)
+    dot = torch.from_numpy(do).to(torch.bfloat16).cuda()
+    if w.frames is None:
+        cu, _, _ = binding.build_metadata(grid, text, w.tokens)
+        out, lse = binding.attn_packed_lse(q, k, v, cu, grid, text)
+        run = lambda: binding.attn_packed_bwd(q, k, v, out, dot, lse, cu, grid, text)  # noqa: E731
+        ref = attention.joint_attention_backward(w.q, w.k, w.v, do, w.grid_hw, w.text_len)
+    else:
+        frames = torch.from_numpy(w.frames).cuda()
+        cu, _, _ = binding.build_metadata_3d(grid, text, frames, w.tokens)
+        out, lse = binding.attn_packed_3d(q, k, v, cu, grid, text, frames, w.rope_split, lse=True)
+        run = lambda: binding.attn_packed_3d_bwd(q, k, v, out, dot, lse, cu, grid, text, frames,  # noqa: E731
+                                                 w.rope_split)
+        ref = attention.joint_attention_3d_backward(w.q, w.k, w.v, do, w.grid_hw, w.text_len, w.frames,
+                                                    w.rope_split)
+    grads = run()
+    torch.cuda.synchronize()
+    assert binding.get_device_error() == binding.MF_OK, binding.last_error()
+    for nm, g, r in zip(("dq", "dk", "dv"), grads, ref):
+        _check_grad(nm, to_f64(g), r)
+    again = run()
+    torch.cuda.synchronize()
+    for nm, g, g2 in zip(("dq", "dk", "dv"), grads, again):
+        assert torch.equal(g, g2), f"{nm}: repeated calls differ"

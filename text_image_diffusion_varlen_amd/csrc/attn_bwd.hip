@@ -42,6 +42,7 @@ constexpr float LOG2E = 1.4426950408889634f;
 constexpr int KV_WAVES = 8;                 // waves of bwd_kv_kernel
 constexpr int KV_GROUPS = KV_WAVES / 2;     // 32-key groups: one dV wave and one dK wave each
 constexpr int KV_KEYS = 32 * KV_GROUPS;     // keys per bwd_kv workgroup
+static_assert(KV_KEYS == BWD_KV_KEYS, "partial slots of the workspace hold KV_KEYS keys");
 constexpr int KV_SPLIT = QTILE / KV_KEYS;   // key blocks per entry of the tile table
 constexpr int Q_WAVES = QTILE / 32;         // waves of bwd_q_kernel, 32 queries each
 static_assert(QTILE % KV_KEYS == 0, "whole key blocks per entry of the tile table");
@@ -70,6 +71,9 @@ struct BwdArgs {
   uint16_t* dq;
   uint16_t* dk;
   uint16_t* dv;
+  float* part;       // partial dV, dK of split dK/dV units, PART_SLOTS slots
+  int32_t ncu;       // compute units for the split plan (0: never split)
+  int64_t dq_units;  // workgroups of the dQ kernel's own grid (tile capacity x heads)
   int32_t heads;
   int64_t rows;      // padded rows per head
   int64_t tokens;
@@ -340,20 +344,48 @@ __device__ inline uint2 unrotate4(const float (&x)[4], int ch0, const TokPos& p,
   return o;
 }
 
+// Split of the dK/dV kernel's poorly filled last round (the plan of the
+// forward, over units = KV_SPLIT x tiles x heads key blocks, pieces over query
+// ranges): the same in every workgroup of both kernels. The last tile is the
+// shortest sample's.
+__device__ inline SplitPlan kv_plan(const BwdArgs& a, const WsHeader* hdr) {
+  const int2 last = reinterpret_cast<const int2*>(a.ws + a.off_tiles)[hdr->n_tiles - 1];
+  const int32_t Ls = reinterpret_cast<const int32_t*>(a.ws + a.off_len)[last.x];
+  return split_plan(int64_t(KV_SPLIT) * hdr->n_tiles * a.heads, a.ncu, (Ls + KTILE - 1) / KTILE,
+                    SPLIT_MIN_SAVED_BWD);
+}
+
 template <int D, bool R3>
 __global__ void __launch_bounds__(64 * KV_WAVES, 2) bwd_kv_kernel(BwdArgs a) {
   constexpr int CH = BwdTile<D>::CH, KSTEPS = BwdTile<D>::KSTEPS, DBLK = BwdTile<D>::DBLK;
   constexpr int SET = 4 * CH + 2 * KTILE / 4;  // chunks of one LDS tile set (4 tiles + stats)
   const WsHeader* hdr = reinterpret_cast<const WsHeader*>(a.ws);
   const int32_t heads = a.heads;
-  const int h = int(blockIdx.x % unsigned(heads));
-  const int rest = int(blockIdx.x / unsigned(heads));
+  if (hdr->flag != FLAG_OK) return;
+  // Unit (key block, head) of this workgroup: a whole unit, or piece `part`
+  // of a unit of the split last round (its query tiles [qt0, qt1)).
+  const SplitPlan plan = kv_plan(a, hdr);
+  int unit = int(blockIdx.x), part = -1;
+  if (unit >= plan.n_full) {
+    const int piece = unit - plan.n_full;
+    if (piece >= plan.n_tail * plan.parts) return;
+    unit = plan.n_full + piece / plan.parts;
+    part = piece % plan.parts;
+  }
+  const int h = unit % heads;
+  const int rest = unit / heads;
   const int tile = rest / KV_SPLIT;
-  if (hdr->flag != FLAG_OK || tile >= hdr->n_tiles) return;
   const int2 td = reinterpret_cast<const int2*>(a.ws + a.off_tiles)[tile];
   const int32_t seg = td.x, k0 = td.y + KV_KEYS * (rest % KV_SPLIT);
   const int32_t L = reinterpret_cast<const int32_t*>(a.ws + a.off_len)[seg];
   if (k0 >= L) return;
+  const int nqt_all = (L + KTILE - 1) / KTILE;
+  int qt0 = 0, qt1 = nqt_all;
+  if (part >= 0) {
+    qt0 = part * nqt_all / plan.parts;
+    qt1 = (part + 1) * nqt_all / plan.parts;
+    if (qt0 == qt1) return;  // empty piece: the merge skips it
+  }
   const int32_t pb = reinterpret_cast<const int32_t*>(a.ws + a.off_pcu)[seg];
   const int32_t cb = reinterpret_cast<const int32_t*>(a.ws + a.off_cu)[seg];
   const int tid = threadIdx.x;
@@ -402,14 +434,14 @@ __global__ void __launch_bounds__(64 * KV_WAVES, 2) bwd_kv_kernel(BwdArgs a) {
   f32x16 acc[DBLK];
 #pragma unroll
   for (int b = 0; b < DBLK; ++b) acc[b] = f32x16{};
-  const int nqt = (L + KTILE - 1) / KTILE;
-  load_set(0, sets);
+  const int nqt = qt1 - qt0;
+  load_set(qt0, sets);
   wait_vm_and_sync();
   u32x4 pk[4];     // dV waves: this step's P (bf16), as the B operand of its four k-steps
   f32x16 dp[2];    // dK waves: this step's dP, two 32-query halves
-  for (int j = 0; j < nqt; ++j) {
-    const u32x4* cur = sets + (j & 1) * SET;
-    if (j + 1 < nqt) load_set(j + 1, sets + ((j + 1) & 1) * SET);
+  for (int jj = 0; jj < nqt; ++jj) {
+    const u32x4* cur = sets + (jj & 1) * SET;
+    if (jj + 1 < nqt) load_set(qt0 + jj + 1, sets + ((jj + 1) & 1) * SET);
     if (dv_wave) kv_phase1_dv<D>(cur, pl, kreg, pk, a.c_log2, hf, l32, lane);
     else kv_phase1_dk<D>(cur, vreg, dp, hf, l32);
     __syncthreads();  // P of this step is in pl
@@ -419,6 +451,20 @@ __global__ void __launch_bounds__(64 * KV_WAVES, 2) bwd_kv_kernel(BwdArgs a) {
   }
 
   // Epilogue: entry e of block b is channel 32b + 8(e/4) + 4hf + e%4 of this lane's key.
+  if (part >= 0) {
+    // Piece of a split unit: fp32 dV (dV waves) or dK before the inverse
+    // rotation (dK waves) of this lane's key into the piece's slot.
+    float* slot = a.part + int64_t(blockIdx.x - plan.n_full) * 2 * KV_KEYS * D + (dv_wave ? 0 : KV_KEYS * D) +
+                  int64_t(32 * group + l32) * D;
+#pragma unroll
+    for (int b = 0; b < DBLK; ++b) {
+#pragma unroll
+      for (int g = 0; g < 4; ++g)
+        *reinterpret_cast<float4*>(slot + 32 * b + 8 * g + 4 * hf) =
+            make_float4(acc[b][4 * g], acc[b][4 * g + 1], acc[b][4 * g + 2], acc[b][4 * g + 3]);
+    }
+    return;
+  }
   if (key < L) {
     const TokPos pos = token_pos<R3>(key, seg, a);
     const int64_t off = (int64_t(cb + key) * heads + h) * D;
@@ -438,6 +484,54 @@ __global__ void __launch_bounds__(64 * KV_WAVES, 2) bwd_kv_kernel(BwdArgs a) {
         }
       }
     }
+  }
+}
+
+// Merge of the pieces of split dK/dV unit u of the tail: per key and 4
+// channels, the pieces' dV and dK sums in piece order (deterministic), then the
+// epilogue of the whole-unit path (dV to bf16; dK inverse-rotated, scaled, to
+// bf16). Run by extra workgroups of the dQ kernel, which is launched after the
+// dK/dV kernel has finished, so every piece is complete; they take CUs that
+// the dQ kernel's own last round leaves idle, and no launch is added.
+template <int D, bool R3>
+__device__ inline void kv_merge_unit(const BwdArgs& a, int u, int tid, int nthreads) {
+  const WsHeader* hdr = reinterpret_cast<const WsHeader*>(a.ws);
+  if (hdr->flag != FLAG_OK) return;
+  const int32_t heads = a.heads;
+  const SplitPlan plan = kv_plan(a, hdr);
+  if (u >= plan.n_tail) return;
+  const int unit = plan.n_full + u;
+  const int h = unit % heads;
+  const int rest = unit / heads;
+  const int tile = rest / KV_SPLIT;
+  const int2 td = reinterpret_cast<const int2*>(a.ws + a.off_tiles)[tile];
+  const int32_t seg = td.x, k0 = td.y + KV_KEYS * (rest % KV_SPLIT);
+  const int32_t L = reinterpret_cast<const int32_t*>(a.ws + a.off_len)[seg];
+  if (k0 >= L) return;
+  const int32_t cb = reinterpret_cast<const int32_t*>(a.ws + a.off_cu)[seg];
+  const int nqt = (L + KTILE - 1) / KTILE;
+  const int S = plan.parts;
+  constexpr int64_t SLOT = int64_t(2) * KV_KEYS * D;
+  const float* base = a.part + int64_t(u) * S * SLOT;
+  for (int item = tid; item < KV_KEYS * D / 4; item += nthreads) {
+    const int key = item / (D / 4), ch0 = 4 * (item % (D / 4));
+    if (k0 + key >= L) break;  // items are key-major: the rest lie past the sample too
+    float4 sv = make_float4(0.f, 0.f, 0.f, 0.f), sk = sv;
+    for (int p = 0; p < S; ++p) {
+      if ((p + 1) * nqt / S == p * nqt / S) continue;  // empty piece (never written)
+      const float* sl = base + p * SLOT + int64_t(key) * D + ch0;
+      const float4 x = *reinterpret_cast<const float4*>(sl);
+      const float4 y = *reinterpret_cast<const float4*>(sl + KV_KEYS * D);
+      sv.x += x.x; sv.y += x.y; sv.z += x.z; sv.w += x.w;
+      sk.x += y.x; sk.y += y.y; sk.z += y.z; sk.w += y.w;
+    }
+    const int64_t off = (int64_t(cb + k0 + key) * heads + h) * D + ch0;
+    uint2 o;
+    o.x = pack_bf16x2(sv.x, sv.y);
+    o.y = pack_bf16x2(sv.z, sv.w);
+    *reinterpret_cast<uint2*>(a.dv + off) = o;
+    const float xk[4] = {sk.x, sk.y, sk.z, sk.w};
+    *reinterpret_cast<uint2*>(a.dk + off) = unrotate4<D, R3>(xk, ch0, token_pos<R3>(k0 + key, seg, a), a.scale, a);
   }
 }
 
@@ -491,6 +585,10 @@ template <int D, bool R3>
 __global__ void __launch_bounds__(64 * Q_WAVES, 2) bwd_q_kernel(BwdArgs a) {
   constexpr int CH = BwdTile<D>::CH, KSTEPS = BwdTile<D>::KSTEPS, DBLK = BwdTile<D>::DBLK;
   constexpr int SET = 3 * CH;
+  if (int64_t(blockIdx.x) >= a.dq_units) {  // workgroups past the dQ grid merge split dK/dV units
+    kv_merge_unit<D, R3>(a, int(int64_t(blockIdx.x) - a.dq_units), int(threadIdx.x), 64 * Q_WAVES);
+    return;
+  }
   const WsHeader* hdr = reinterpret_cast<const WsHeader*>(a.ws);
   const int32_t heads = a.heads;
   const int h = int(blockIdx.x % unsigned(heads));
@@ -574,19 +672,25 @@ static hipError_t launch_bwd_t(const BwdArgs& a, const BwdLayout& l, hipStream_t
                      s, a);
   if ((e = hipGetLastError()) != hipSuccess) return e;
   if (ev && (e = hipEventRecord(ev[0], s)) != hipSuccess) return e;
-  hipLaunchKernelGGL((bwd_kv_kernel<D, R3>), dim3(unsigned(KV_SPLIT * l.m.n_tiles * a.heads)), dim3(64 * KV_WAVES),
-                     0, s, a);
+  // Whole units, then up to PART_SLOTS pieces of split units (workgroups past
+  // the plan return at once).
+  hipLaunchKernelGGL((bwd_kv_kernel<D, R3>),
+                     dim3(unsigned(KV_SPLIT * l.m.n_tiles * a.heads + (a.ncu > 0 ? PART_SLOTS : 0))),
+                     dim3(64 * KV_WAVES), 0, s, a);
   if ((e = hipGetLastError()) != hipSuccess) return e;
   if (ev && (e = hipEventRecord(ev[1], s)) != hipSuccess) return e;
-  hipLaunchKernelGGL((bwd_q_kernel<D, R3>), dim3(unsigned(l.m.n_tiles * a.heads)), dim3(64 * Q_WAVES), 0, s, a);
+  // The dQ grid, then (when the dK/dV kernel may have split) one workgroup per
+  // possible split dK/dV unit to merge it.
+  hipLaunchKernelGGL((bwd_q_kernel<D, R3>), dim3(unsigned(a.dq_units + (a.ncu > 0 ? PART_SLOTS / 2 : 0))),
+                     dim3(64 * Q_WAVES), 0, s, a);
   return hipGetLastError();
 }
 
 hipError_t launch_attn_bwd(const void* q, const void* k, const void* v, const void* o, const void* dout,
                            const float* lse, const int32_t* grid_hw, const int32_t* text_len,
                            const float2* cs, const Rope3* r3, char* ws, const BwdLayout& l, void* dq, void* dk,
-                           void* dv, int64_t tokens, int32_t heads, int32_t head_dim, float scale, hipStream_t s,
-                           hipEvent_t const* ev) {
+                           void* dv, int64_t tokens, int32_t heads, int32_t head_dim, float scale, int32_t ncu,
+                           hipStream_t s, hipEvent_t const* ev) {
   BwdArgs a;
   a.ws = ws;
   a.off_len = l.m.off_len;
@@ -619,6 +723,9 @@ hipError_t launch_attn_bwd(const void* q, const void* k, const void* v, const vo
   a.tokens = tokens;
   a.c_log2 = scale * LOG2E;
   a.scale = scale;
+  a.part = reinterpret_cast<float*>(ws + l.off_part);
+  a.ncu = ncu;
+  a.dq_units = l.m.n_tiles * heads;
   if (r3) return head_dim == 128 ? launch_bwd_t<128, true>(a, l, s, ev) : launch_bwd_t<64, true>(a, l, s, ev);
   return head_dim == 128 ? launch_bwd_t<128, false>(a, l, s, ev) : launch_bwd_t<64, false>(a, l, s, ev);
 }

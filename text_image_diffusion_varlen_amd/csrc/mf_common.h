@@ -60,13 +60,20 @@ constexpr int SPLIT_MIN_SAVED = 96;  // key tiles a split must save on the tail'
 // longer than the mean, so a batch with tokens / n_seg below that cannot split
 // and the host then skips the merge launch (and tells the kernel not to split).
 constexpr int64_t SPLIT_MIN_MEAN_LEN = (int64_t(SPLIT_MIN_SAVED) * 4 / 3 - 1) * KTILE + 1;
-__host__ __device__ inline bool split_possible(int64_t tokens, int32_t n_seg) {
-  return tokens >= int64_t(n_seg) * SPLIT_MIN_MEAN_LEN;
+__host__ __device__ inline bool split_possible(int64_t tokens, int32_t n_seg,
+                                               int64_t min_saved = SPLIT_MIN_SAVED) {
+  return tokens >= int64_t(n_seg) * ((min_saved * 4 / 3 - 1) * KTILE + 1);
 }
+// The backward's dK/dV kernel splits its last round over query ranges (64-row
+// steps, each ~2.4 us of a workgroup against ~1.8 us per forward key tile,
+// and a lighter merge: no rescale), so a smaller saving pays.
+constexpr int SPLIT_MIN_SAVED_BWD = 24;
+constexpr int BWD_KV_KEYS = 128;  // keys per dK/dV workgroup (4 groups of a dV and a dK wave)
 struct SplitPlan {
   int32_t n_full, n_tail, parts;
 };
-__host__ __device__ inline SplitPlan split_plan(int64_t units, int32_t ncu, int64_t nkt_short) {
+__host__ __device__ inline SplitPlan split_plan(int64_t units, int32_t ncu, int64_t nkt_short,
+                                               int64_t min_saved = SPLIT_MIN_SAVED) {
   SplitPlan p{int32_t(units), 0, 1};
   if (ncu <= 0 || units <= ncu) return p;
   const int64_t tail = units % ncu;
@@ -80,7 +87,7 @@ __host__ __device__ inline SplitPlan split_plan(int64_t units, int32_t ncu, int6
       best_s = s;
     }
   }
-  if (best_s == 1 || nkt_short * (best_s - best_r) < SPLIT_MIN_SAVED * best_s) return p;
+  if (best_s == 1 || nkt_short * (best_s - best_r) < min_saved * best_s) return p;
   p.n_full = int32_t(units - tail);
   p.n_tail = int32_t(tail);
   p.parts = int32_t(best_s);
@@ -135,8 +142,8 @@ __host__ __device__ inline WsLayout ws_layout(int64_t tokens, int32_t heads, int
 //   st  f32 [heads][rows / KTILE][2 * KTILE]: per tile, log2-domain LSE of
 //       the KTILE rows (+inf on padding rows), then D = rowsum(dO * O).
 struct BwdLayout {
-  WsLayout m;  // metadata sections (its off_q / off_k / off_v / total are not used)
-  int64_t off_qc, off_qt, off_oc, off_ot, off_kc, off_kt, off_vc, off_st, total;
+  WsLayout m;  // metadata sections (its off_q / off_k / off_v / off_part / total are not used)
+  int64_t off_qc, off_qt, off_oc, off_ot, off_kc, off_kt, off_vc, off_st, off_part, total;
 };
 
 __host__ __device__ inline BwdLayout bwd_layout(int64_t tokens, int32_t heads, int32_t head_dim,
@@ -153,6 +160,8 @@ __host__ __device__ inline BwdLayout bwd_layout(int64_t tokens, int32_t heads, i
   b.off_kt = o; o += buf;
   b.off_vc = o; o += buf;
   b.off_st = o; o += round_up(int64_t(heads) * b.m.rows * 2 * 4, 256);
+  // PART_SLOTS partial dV, dK of split dK/dV units: [dV | dK][BWD_KV_KEYS keys][head_dim] fp32 each.
+  b.off_part = o; o += int64_t(PART_SLOTS) * 2 * BWD_KV_KEYS * head_dim * 4;
   b.total = o;
   return b;
 }
