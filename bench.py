@@ -98,11 +98,17 @@ def sample_lengths(w):
     return (w.text_len.astype("int64") + f * w.grid_hw[:, 0].astype("int64") * w.grid_hw[:, 1]).tolist()
 
 
-def cpu_baseline(w, budget_s: float):
+def cpu_baseline(w, budget_s: float, gpu_out=None, gpu_meta=None):
     """The fp64 oracle (as it stands) on host cores, over as many whole heads of the
-    same workload as fit in the time budget (at least one)."""
+    same workload as fit in the time budget (at least one).
+
+    After the timed loop, the oracle's outputs of those heads are compared with
+    the GPU output of the same workload (`gpu_out`, [T][H][d] on the host) and
+    the library's metadata (`gpu_meta` = (cu_seqlens, positions) on the host)
+    with the oracle's packing: max / mean abs error, whether they are within
+    the parity bars, and whether the metadata is bit-exact."""
     import numpy as np
-    from oracle import attention
+    from oracle import attention, packing
 
     try:
         from threadpoolctl import threadpool_info
@@ -113,24 +119,41 @@ def cpu_baseline(w, budget_s: float):
     per_head = 4.0 * sum(L * L for L in lengths) * w.head_dim
     t0 = time.perf_counter()
     heads = 0
+    outs = []
     while heads < w.heads:
         h = slice(heads, heads + 1)
         if w.frames is None:
-            attention.joint_attention(w.q[:, h], w.k[:, h], w.v[:, h], w.grid_hw, w.text_len)
+            o = attention.joint_attention(w.q[:, h], w.k[:, h], w.v[:, h], w.grid_hw, w.text_len)
         else:
-            attention.joint_attention_3d(w.q[:, h], w.k[:, h], w.v[:, h], w.grid_hw, w.text_len, w.frames,
-                                         w.rope_split)
+            o = attention.joint_attention_3d(w.q[:, h], w.k[:, h], w.v[:, h], w.grid_hw, w.text_len, w.frames,
+                                             w.rope_split)
+        outs.append(o)
         heads += 1
         if time.perf_counter() - t0 > budget_s:
             break
     dt = time.perf_counter() - t0
-    return {
+    res = {
         "value": per_head * heads / dt / 1e12,
         "unit": "TFLOP/s",
         "cores": threads,
         "kind": "oracle",
         "sample": f"{heads} of {w.heads} heads of the same workload (all rows, fp64 numpy), {dt:.1f} s",
     }
+    if gpu_out is not None:
+        err = np.abs(gpu_out[:, :heads].astype(np.float64) - np.concatenate(outs, axis=1))
+        bars = (2e-2, 2e-3) if w.dtype == "bf16" else (1e-5, 1e-5)
+        res["max_abs_err_vs_gpu"] = float(err.max())
+        res["mean_abs_err_vs_gpu"] = float(err.mean())
+        res["within_parity_bars"] = bool(err.max() <= bars[0] and err.mean() <= bars[1])
+    if gpu_meta is not None:
+        cu, pos = gpu_meta
+        if w.frames is None:
+            ref_pos, _ = packing.token_positions(w.grid_hw, w.text_len)
+        else:
+            ref_pos, _ = packing.token_positions_3d(w.grid_hw, w.text_len, w.frames)
+        ref_cu = packing.cu_seqlens(w.grid_hw, w.text_len, w.frames)
+        res["metadata_bit_exact"] = bool(np.array_equal(cu, ref_cu) and np.array_equal(pos, ref_pos))
+    return res
 
 
 def sampler_bench(steps: int, warmup: int):
@@ -386,9 +409,9 @@ def main():
     text = torch.from_numpy(w.text_len).cuda()
     if edit:
         frames = torch.from_numpy(w.frames).cuda()
-        cu, _, _ = binding.build_metadata_3d(grid, text, frames, w.tokens)
+        cu, pos, _ = binding.build_metadata_3d(grid, text, frames, w.tokens)
     else:
-        cu, _, _ = binding.build_metadata(grid, text, w.tokens)
+        cu, pos, _ = binding.build_metadata(grid, text, w.tokens)
     out = torch.empty_like(q)
     torch.cuda.synchronize()
     if binding.get_device_error() != binding.MF_OK:
@@ -451,6 +474,14 @@ def main():
         del flush
         ev.close()
 
+    # The forward output and metadata of this workload, for the oracle comparison
+    # in the CPU baseline (the last call above ran the same inputs).
+    gpu_out = gpu_meta = None
+    if not args.no_cpu_baseline:
+        torch.cuda.synchronize()
+        gpu_out = out.float().cpu().numpy()
+        gpu_meta = (cu.cpu().numpy(), pos.cpu().numpy())
+
     attn_s = stage["attn"] / 1e3
     achieved = flops / attn_s
     # prologue: bf16 reads k, v and writes K~, V~ (queries are rotated inside the attention kernel);
@@ -504,7 +535,7 @@ def main():
     if not args.no_sampler:
         result["cfg_euler_step"] = sampler_bench(args.steps, args.warmup)
     if not args.no_cpu_baseline:
-        result["cpu_baseline"] = cpu_baseline(w, args.cpu_budget)
+        result["cpu_baseline"] = cpu_baseline(w, args.cpu_budget, gpu_out=gpu_out, gpu_meta=gpu_meta)
     print(json.dumps(result), flush=True)
 
 
