@@ -49,7 +49,7 @@ hipError_t launch_qkv_fold(const void* w_txt, const void* w_img, const float* g_
                            int32_t hidden, int32_t out_features, void* out, hipStream_t s);
 hipError_t launch_qkv(const void* x, const void* w, const int32_t* cu, const int32_t* grid_hw, const int32_t* text_len,
                       const int32_t* frames, int32_t n_seg, int64_t tokens, int32_t hidden, int32_t hd, float eps,
-                      char* ws, void* q, void* k, void* v, hipStream_t s, hipEvent_t const* ev);
+                      char* ws, void* q, void* k, void* v, int32_t ncu, hipStream_t s, hipEvent_t const* ev);
 size_t qkv_workspace_bytes(int64_t tokens, int32_t n_seg, int32_t hidden);
 hipError_t launch_cfg_euler(float* z, const void* v, const int32_t* cu, const int32_t* grid_hw,
                             const int32_t* text_len, int32_t n_seg, int64_t total_tokens,
@@ -679,10 +679,12 @@ int mf_qkv_rmsnorm_profiled(const void* x, const void* w_folded, const int32_t* 
   std::lock_guard<std::mutex> lock(g_mu);
   DeviceState& st = g_dev[dev];
   if ((rc = ensure_buffer(st.qws, st.qws_bytes, mf::qkv_workspace_bytes(total_tokens, n_seg, hidden)))) return rc;
+  int32_t ncu = 0;
+  if ((rc = ensure_cus(st, dev, &ncu))) return rc;
   hipError_t e;
   if (events && (e = hipEventRecord(events[0], stream)) != hipSuccess) return hip_fail(e, "hipEventRecord");
   e = mf::launch_qkv(x, w_folded, cu_seqlens, grid_hw, text_len, frames, n_seg, total_tokens, hidden, hd, eps, st.qws,
-                     q, k, v, stream, events ? events + 1 : nullptr);
+                     q, k, v, ncu, stream, events ? events + 1 : nullptr);
   if (e != hipSuccess) return hip_fail(e, "qkv kernels launch");
   if (events && (e = hipEventRecord(events[2], stream)) != hipSuccess) return hip_fail(e, "hipEventRecord");
   return MF_OK;

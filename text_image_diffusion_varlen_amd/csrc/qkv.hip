@@ -248,13 +248,21 @@ struct QkvGemmArgs {
   float eps;
   int32_t hd;          // heads * head_dim
   int32_t n_tiles;     // 3 hd / QKV_NT
+  int32_t ncu;         // compute units for the halved last round (0: never halve)
 };
 
-__global__ void __launch_bounds__(QKV_THREADS, 2) qkv_gemm_kernel(QkvGemmArgs a) {
-  const QkvHeader* hdr = reinterpret_cast<const QkvHeader*>(a.ws);
-  if (hdr->flag != FLAG_OK) return;
-  const int nt = int(blockIdx.x % unsigned(a.n_tiles));
-  int tt = int(blockIdx.x / unsigned(a.n_tiles));
+// One GEMM unit (256 output features x 256 tokens of one modality) or, with
+// NB = 2, one 128-feature half of it starting at feature fbase of the tile:
+// every wave owns NB * 32 features x 64 tokens. Both halves copy the whole
+// stages (the tiled layout keeps a stage contiguous) and read their features.
+// Per output element the products are summed in the same stage and k-step
+// order in both forms, so a half unit's outputs equal the whole unit's bit
+// for bit.
+template <int NB>
+__device__ inline void qkv_gemm_unit(const QkvGemmArgs& a, const QkvHeader* hdr, int unit, int fbase,
+                                     u32x4 (*lds)[2 * QKV_CH]) {
+  const int nt = unit % a.n_tiles;
+  int tt = unit / a.n_tiles;
   const int32_t n_txt = hdr->n_txt, n_img = hdr->n_img;
   const int txt_tiles = (n_txt + QKV_TT - 1) / QKV_TT;
   int m = 0;
@@ -263,13 +271,13 @@ __global__ void __launch_bounds__(QKV_THREADS, 2) qkv_gemm_kernel(QkvGemmArgs a)
     tt -= txt_tiles;
     m = 1;
     count = n_img;
-    if (tt * QKV_TT >= n_img) return;
   }
   const int32_t* rows = reinterpret_cast<const int32_t*>(a.ws + (m ? a.l.off_img : a.l.off_txt));
   const int32_t row0 = tt * QKV_TT;
   const int tid = threadIdx.x;
   const int wave = tid >> 6, lane = tid & 63, hf = lane >> 5, l32 = lane & 31;
-  const int wn = wave & 1, wt = wave >> 1;  // wave tile: 128 features x 64 tokens
+  const int wt = wave >> 1;                     // 64-token quarter
+  const int fw = fbase + (wave & 1) * NB * 32;  // this wave's first feature in the tile
 
   // Both operands are tiled: a stage of one operand is 2048 contiguous chunks,
   // copied verbatim (chunk c of row r lands at c * 256 + r).
@@ -277,22 +285,21 @@ __global__ void __launch_bounds__(QKV_THREADS, 2) qkv_gemm_kernel(QkvGemmArgs a)
   const int64_t xtile = m ? round_up(n_txt, QKV_TT) / QKV_TT + tt : tt;  // tile row of X~
   const u32x4* wsrc = reinterpret_cast<const u32x4*>(a.w) + (int64_t(m) * a.n_tiles + nt) * stages_k * QKV_CH;
   const u32x4* xsrc = reinterpret_cast<const u32x4*>(a.ws + a.l.off_x) + xtile * stages_k * QKV_CH;
-  __shared__ u32x4 lds[2][2 * QKV_CH];  // [stage][A (features) | B (tokens)]
   auto load_stage = [&](int s, u32x4* dst) {
     copy_to_lds<QKV_CH, QKV_THREADS / 64>(wsrc + int64_t(s) * QKV_CH, dst, wave, lane);
     copy_to_lds<QKV_CH, QKV_THREADS / 64>(xsrc + int64_t(s) * QKV_CH, dst + QKV_CH, wave, lane);
   };
 
-  f32x16 acc[4][2];
+  f32x16 acc[NB][2];
 #pragma unroll
-  for (int nb = 0; nb < 4; ++nb) acc[nb][0] = acc[nb][1] = f32x16{};
+  for (int nb = 0; nb < NB; ++nb) acc[nb][0] = acc[nb][1] = f32x16{};
   const int stages = a.hidden / QKV_KS;
   load_stage(0, lds[0]);
   wait_vm_and_sync();
   for (int s = 0; s < stages; ++s) {
     const u32x4* cur = lds[s & 1];
     if (s + 1 < stages) load_stage(s + 1, lds[(s + 1) & 1]);
-    const u32x4* al = cur + hf * QKV_NT + wn * 128 + l32;
+    const u32x4* al = cur + hf * QKV_NT + fw + l32;
     const u32x4* bl = cur + QKV_CH + hf * QKV_NT + wt * 64 + l32;
 #pragma unroll
     for (int ks = 0; ks < QKV_KS / 16; ++ks) {
@@ -300,7 +307,7 @@ __global__ void __launch_bounds__(QKV_THREADS, 2) qkv_gemm_kernel(QkvGemmArgs a)
 #pragma unroll
       for (int tb = 0; tb < 2; ++tb) bo[tb] = as_bf16x8(bl[2 * QKV_NT * ks + 32 * tb]);
 #pragma unroll
-      for (int nb = 0; nb < 4; ++nb) {
+      for (int nb = 0; nb < NB; ++nb) {
         const bf16x8 ao = as_bf16x8(al[2 * QKV_NT * ks + 32 * nb]);
         acc[nb][0] = mfma32(ao, bo[0], acc[nb][0]);
         acc[nb][1] = mfma32(ao, bo[1], acc[nb][1]);
@@ -309,7 +316,7 @@ __global__ void __launch_bounds__(QKV_THREADS, 2) qkv_gemm_kernel(QkvGemmArgs a)
     wait_vm_and_sync();
   }
 
-  // Epilogue: lane = token, entry e of block nb = feature 32nb + 8(e/4) + 4hf + e%4.
+  // Epilogue: lane = token, entry e of block nb = feature fw + 32nb + 8(e/4) + 4hf + e%4.
   const float* ssq = reinterpret_cast<const float*>(a.ws + a.l.off_inv);
   const int32_t groups = rms_groups(a.hidden);
 #pragma unroll
@@ -321,10 +328,10 @@ __global__ void __launch_bounds__(QKV_THREADS, 2) qkv_gemm_kernel(QkvGemmArgs a)
     for (int g = 0; g < groups; ++g) ss += ssq[int64_t(tok) * groups + g];
     const float sc = 1.0f / sqrtf(ss / float(a.hidden) + a.eps);
 #pragma unroll
-    for (int nb = 0; nb < 4; ++nb) {
+    for (int nb = 0; nb < NB; ++nb) {
 #pragma unroll
       for (int g = 0; g < 4; ++g) {
-        const int n = nt * QKV_NT + wn * 128 + nb * 32 + 8 * g + 4 * hf;
+        const int n = nt * QKV_NT + fw + nb * 32 + 8 * g + 4 * hf;
         const int which = n / a.hd, rem = n - which * a.hd;
         uint16_t* dst = (which == 0 ? a.q : which == 1 ? a.k : a.v) + int64_t(tok) * a.hd + rem;
         uint2 o;
@@ -333,6 +340,27 @@ __global__ void __launch_bounds__(QKV_THREADS, 2) qkv_gemm_kernel(QkvGemmArgs a)
         *reinterpret_cast<uint2*>(dst) = o;
       }
     }
+  }
+}
+
+// Units = feature tiles x (text + visual token tiles), one workgroup per unit
+// (one per CU: 128 KB of LDS). When the last round of units would occupy at
+// most half of the a.ncu compute units, its units run as two 128-feature
+// halves each, so that round takes about half as long. a.ncu = 0: never.
+__global__ void __launch_bounds__(QKV_THREADS, 2) qkv_gemm_kernel(QkvGemmArgs a) {
+  const QkvHeader* hdr = reinterpret_cast<const QkvHeader*>(a.ws);
+  if (hdr->flag != FLAG_OK) return;
+  const int32_t units = ((hdr->n_txt + QKV_TT - 1) / QKV_TT + (hdr->n_img + QKV_TT - 1) / QKV_TT) * a.n_tiles;
+  const int32_t tail = a.ncu > 0 ? units % a.ncu : 0;
+  const bool halve = tail > 0 && 2 * tail <= a.ncu;
+  const int32_t n_full = halve ? units - tail : units;
+  __shared__ u32x4 lds[2][2 * QKV_CH];  // [stage][A (features) | B (tokens)]
+  const int b = int(blockIdx.x);
+  if (b < n_full) {
+    qkv_gemm_unit<4>(a, hdr, b, 0, lds);
+  } else if (halve && b < n_full + 2 * tail) {
+    const int piece = b - n_full;
+    qkv_gemm_unit<2>(a, hdr, n_full + piece / 2, (piece % 2) * (QKV_NT / 2), lds);
   }
 }
 
@@ -351,7 +379,7 @@ hipError_t launch_qkv_fold(const void* w_txt, const void* w_img, const float* g_
 
 hipError_t launch_qkv(const void* x, const void* w, const int32_t* cu, const int32_t* grid_hw, const int32_t* text_len,
                       const int32_t* frames, int32_t n_seg, int64_t tokens, int32_t hidden, int32_t hd, float eps,
-                      char* ws, void* q, void* k, void* v, hipStream_t s, hipEvent_t const* ev) {
+                      char* ws, void* q, void* k, void* v, int32_t ncu, hipStream_t s, hipEvent_t const* ev) {
   const QkvLayout l = qkv_layout(tokens, n_seg, hidden);
   hipError_t e;
   hipLaunchKernelGGL(qkv_route_kernel, dim3(1), dim3(ROUTE_THREADS), 0, s, cu, grid_hw, text_len, frames, n_seg,
@@ -374,9 +402,17 @@ hipError_t launch_qkv(const void* x, const void* w, const int32_t* cu, const int
   a.eps = eps;
   a.hd = hd;
   a.n_tiles = 3 * hd / QKV_NT;
-  // Token tiles of both modalities together never exceed ceil(T / 256) + 1.
-  const int64_t tiles = (ceil_div(tokens, QKV_TT) + 1) * a.n_tiles;  // text tiles + visual tiles
-  hipLaunchKernelGGL(qkv_gemm_kernel, dim3(unsigned(tiles)), dim3(QKV_THREADS), 0, s, a);
+  a.ncu = ncu;
+  // Text tiles + visual tiles is ceil(T / 256) or ceil(T / 256) + 1 (the split
+  // of T between the modalities is known on the device only); a halved last
+  // round adds its tail count of workgroups.
+  const int64_t lo = ceil_div(tokens, QKV_TT) * a.n_tiles, hi = lo + a.n_tiles;
+  auto extra = [&](int64_t units) {
+    const int64_t tail = ncu > 0 ? units % ncu : 0;
+    return tail > 0 && 2 * tail <= ncu ? tail : 0;
+  };
+  hipLaunchKernelGGL(qkv_gemm_kernel, dim3(unsigned(hi + std::max(extra(lo), extra(hi)))), dim3(QKV_THREADS), 0, s,
+                     a);
   return hipGetLastError();
 }
 
