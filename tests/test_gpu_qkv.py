@@ -111,3 +111,30 @@ def test_qkv_rejects_unsupported_shapes():
     with pytest.raises(binding.MFError) as e:
         binding.qkv_rmsnorm(x, w, cu, g, t, 2, 128)
     assert e.value.code == binding.MF_ERR_UNSUPPORTED
+
+
+def test_halved_last_round_matches_whole_units(tmp_path):
+    """The 1024^2 sample at 24 x 128 (hidden 3072) has 612 GEMM units; on a
+    256-CU device the last 100 run as 128-feature halves. A child process with
+    MF_ATTN_SPLIT=0 runs every unit whole; q, k, v must agree bit for bit
+    (each output element is summed in the same order either way)."""
+    import os
+    import subprocess
+    import sys
+
+    args = ([[64, 64]], [256], 3072, 24, 128)
+    _, _, got = _run(*args, seed=6)
+    here = os.path.dirname(os.path.abspath(__file__))
+    out = tmp_path / "whole.pt"
+    child = (
+        "import sys, torch\n"
+        f"sys.path[:0] = [{here!r}, {os.path.dirname(here)!r}]\n"
+        "import test_gpu_qkv as t\n"
+        f"_, _, o = t._run(*{args!r}, seed=6)\n"
+        f"torch.save([x.cpu() for x in o], {str(out)!r})\n"
+    )
+    print("qkv halved vs whole: child process with MF_ATTN_SPLIT=0", flush=True)
+    subprocess.run([sys.executable, "-c", child], env=dict(os.environ, MF_ATTN_SPLIT="0"), check=True, timeout=300)
+    ref = torch.load(out, weights_only=True)
+    for name, a, b in zip("qkv", got, ref):
+        assert torch.equal(a.cpu(), b), f"{name} differs between halved and whole units"
