@@ -303,6 +303,9 @@ int mf_qkv_fold_weights(const void* w_txt, const void* w_img, const float* gamma
  * mf_get_device_error() reports MF_ERR_METADATA. Uses a library-owned
  * per-device workspace (row lists, 1/rms and a tiled copy of x, about
  * 12 + 2 * hidden bytes per token), same stream-order rule as mf_attn_packed.
+ * Deterministic (no atomics); the work schedule (a poorly filled last round
+ * of GEMM tiles runs as half tiles, off with MF_ATTN_SPLIT=0) never changes
+ * the summation order, so results do not depend on it.
  */
 int mf_qkv_rmsnorm(const void* x, const void* w_folded, const int32_t* cu_seqlens, const int32_t* grid_hw,
                    const int32_t* text_len, const int32_t* frames, int32_t n_seg, int64_t total_tokens, int32_t hidden,
