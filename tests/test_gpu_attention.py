@@ -71,6 +71,10 @@ EDGE = {
              np.random.default_rng(32).integers(0, 20, size=40).tolist()),
     # long prompt, tiny image
     "long_prompt": ([[2, 2]], [300]),
+    # the maximum number of samples (4096), each a few tokens: one query tile and
+    # one key tile per sample, 4096 tile-table entries
+    "max_samples": (np.random.default_rng(33).integers(1, 4, size=(4096, 2)).tolist(),
+                    np.random.default_rng(34).integers(0, 4, size=4096).tolist()),
 }
 
 

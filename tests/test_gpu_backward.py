@@ -11,8 +11,9 @@ the forward's bf16 output in D = rowsum(dO * O); those roundings stay well
 inside 1% of the gradient's scale. LSE: the forward normalizes by the row sum
 of the bf16-rounded P it multiplies into V (so that O is exactly that
 weighted mean), and bf16's unit roundoff is 2^-8, so the stored LSE can
-differ from the exact one by up to ln(1 + 2^-8) = 3.9e-3 plus fp32 rounding:
-max abs <= 4e-3.
+differ from the exact one by up to ln(1 + 2^-8) = 3.9e-3; the bf16 rounding of
+the rotated operands adds a score shift that long rows average away but rows
+of a few keys do not (the per-row bar of gpu_common.check_lse).
 """
 import numpy as np
 import pytest
@@ -21,12 +22,11 @@ import torch
 from oracle import attention
 from text_image_diffusion_varlen_amd import binding, workloads
 
-from gpu_common import device_inputs, to_f64
+from gpu_common import check_lse, device_inputs, to_f64
 
 pytestmark = pytest.mark.gpu
 GRAD_TOL = (2e-2, 1e-2)  # (max, mean) relative to the reference's own max / mean magnitude
 GRAD_FLOOR = 1e-5
-LSE_TOL = 4e-3
 
 
 def _d_out(w, seed=9):
@@ -60,9 +60,8 @@ def _full_check(w):
     do = _d_out(w)
     out, lse, dq, dk, dv = _run(w, do)
     ref_lse = attention.joint_attention_lse(w.q, w.k, w.grid_hw, w.text_len)
-    lerr = np.abs(lse.cpu().numpy().astype(np.float64) - ref_lse).max()
+    lerr = check_lse(lse.cpu().numpy(), ref_lse, w)
     print(f"  lse: max err {lerr:.3e}")
-    assert lerr <= LSE_TOL
     rq, rk, rv = attention.joint_attention_backward(w.q, w.k, w.v, do, w.grid_hw, w.text_len)
     for name, g, r in (("dq", dq, rq), ("dk", dk, rk), ("dv", dv, rv)):
         _check_grad(name, to_f64(g), r)
@@ -76,6 +75,8 @@ EDGE = {
              np.random.default_rng(32).integers(0, 20, size=40).tolist()),
     "long_prompt": ([[2, 2]], [300]),
     "key_blocks": ([[9, 29], [16, 16], [1, 200]], [20, 0, 57]),  # 281, 256, 257 tokens: 128-key block edges
+    "max_samples": (np.random.default_rng(33).integers(1, 4, size=(4096, 2)).tolist(),  # 4096 samples
+                    np.random.default_rng(34).integers(0, 4, size=4096).tolist()),
 }
 
 

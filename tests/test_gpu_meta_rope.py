@@ -44,6 +44,9 @@ def test_metadata_edge_cases_bit_exact():
     for _ in range(4):
         n = int(rng.integers(1, 300))
         cases.append((rng.integers(1, 40, size=(n, 2)).tolist(), rng.integers(0, 80, size=n).tolist()))
+    # 64 / 65 samples (the one-wave path and the workgroup path) and the maximum, 4096
+    for n in (64, 65, 4096):
+        cases.append((rng.integers(1, 4, size=(n, 2)).tolist(), rng.integers(0, 4, size=n).tolist()))
     for grid, text in cases:
         _meta_case(grid, text)
 
