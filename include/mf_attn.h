@@ -169,9 +169,11 @@ int mf_attn_packed_lse(const void* q, const void* k, const void* v, const int32_
  * last round of (128-key block, head) units of the dK/dV kernel would fill the
  * device poorly and its units are long, those units are split over query
  * ranges and the pieces' fp32 partial sums are added in a fixed order; this
- * happens only for batches whose mean sample length is at least 1985 tokens,
- * changes the rounding of dk and dv in the split units, and is turned off by
- * MF_ATTN_SPLIT=0 like the forward's split.
+ * happens only for batches whose mean sample length is at least 1985 tokens
+ * and changes the rounding of dk and dv in the split units. The dQ kernel's
+ * (256-query tile, head) units split the same way over key ranges, for
+ * batches whose mean sample length is at least 8129 tokens (rounding of dq in
+ * the split units). MF_ATTN_SPLIT=0 turns both off, like the forward's split.
  */
 int mf_attn_packed_bwd(const void* q, const void* k, const void* v, const void* out, const void* d_out,
                        const float* lse, const int32_t* cu_seqlens, const int32_t* grid_hw,

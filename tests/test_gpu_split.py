@@ -1,9 +1,9 @@
-"""GPU parity of the split last round (forward and the backward's dK/dV kernel).
+"""GPU parity of the split last round (forward, and the backward's dK/dV and dQ kernels).
 
 When the last round of work units fills less of the GPU than a split would
 recover, those units are cut into pieces whose partial results a merge kernel
-combines: forward units (query tile, head) over key ranges, dK/dV units
-(128-key block, head) over query ranges. These batches are built so that the
+combines: forward and dQ units (query tile, head) over key ranges, dK/dV
+units (128-key block, head) over query ranges. These batches are built so that the
 plans split (the shapes and head counts below give a short last round of long
 units on a 256-CU MI355X); outputs, the row log-sum-exp (formed by the forward
 merge) and the gradients are checked against the fp64 oracle with the bars of
@@ -72,10 +72,17 @@ def test_split_round_edit():
 
 # Backward: the dK/dV kernel's units are (128-key block, head); a 4352-token
 # sample with 8 heads gives 272 units, the last 16 split 4 ways over query ranges.
+# The dQ kernel's units are (256-query tile, head) and split over key ranges
+# when the mean sample length reaches the forward's threshold: a 9000-token
+# sample with 2 heads gives 72 dQ units, all in a partly filled round, split 3
+# ways (and 144 dK/dV units, also split).
 BWD_SPLIT = {
     "bwd_1024_d128": ([[64, 64]], [256], 8, 128),
     "bwd_1024_d64": ([[64, 64]], [256], 8, 64),
     "bwd_edit": None,  # a 2-image edit of 40 x 52 after a 70-token prompt, 8 heads (frame-aware path)
+    "bwd_long_d128": ([[88, 100]], [200], 2, 128),
+    "bwd_long_d64": ([[88, 100]], [200], 2, 64),
+    "bwd_edit_long": None,  # a 3-image edit of 48 x 64 after a 100-token prompt, 2 heads (dQ split, frame-aware)
 }
 GRAD_TOL = (2e-2, 1e-2)  # relative to the reference's own max / mean magnitude, as in the backward tests
 GRAD_FLOOR = 1e-5
@@ -93,6 +100,9 @@ def test_split_round_backward(name):
     if name == "bwd_edit":
         w = workloads.make_edit(grids=[[40, 52]], texts=[70], frames=[2], heads=8, head_dim=128, dtype="bf16",
                                 seed=21, name=name)
+    elif name == "bwd_edit_long":
+        w = workloads.make_edit(grids=[[48, 64]], texts=[100], frames=[3], heads=2, head_dim=128, dtype="bf16",
+                                seed=23, split=workloads.EDIT_SPLIT[128], name=name)
     else:
         grids, texts, heads, d = BWD_SPLIT[name]
         w = workloads.make_custom(grids, texts, heads=heads, head_dim=d, dtype="bf16", seed=20, name=name)

@@ -34,11 +34,12 @@ def test_workspace_bytes():
     assert lib.mf_workspace_bytes(100, 2, 64, 7, 1) == 0  # unknown dtype
     assert lib.mf_workspace_bytes(0, 2, 64, 0, 1) == 0
     assert lib.mf_workspace_bytes(100, 2, 64, 0, 5000) == 0
-    # backward: seven bf16 operand buffers, the row statistics and 512 slots of
-    # 128 keys x d fp32 partial dV and dK for the split last round
+    # backward: seven bf16 operand buffers, the row statistics, 512 slots of
+    # 128 keys x d fp32 partial dV and dK and 512 slots of 256 rows x d fp32
+    # partial dQ for the split last rounds
     for d in (64, 128):
         t = 4352 * 24 * d * 2
-        slots = 512 * 2 * 128 * d * 4
+        slots = 512 * 2 * 128 * d * 4 + 512 * 256 * d * 4
         assert 7 * t + slots < lib.mf_bwd_workspace_bytes(4352, 24, d, 1) < 8 * t + slots
     assert lib.mf_bwd_workspace_bytes(4352, 24, 96, 1) == 0
     assert lib.mf_bwd_workspace_bytes(0, 24, 128, 1) == 0

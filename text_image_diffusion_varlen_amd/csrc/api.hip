@@ -44,7 +44,7 @@ hipError_t launch_attn_bwd(const void* q, const void* k, const void* v, const vo
                            const float* lse, const int32_t* grid_hw, const int32_t* text_len,
                            const float2* cs, const Rope3* r3, char* ws, const BwdLayout& l, void* dq, void* dk,
                            void* dv, int64_t tokens, int32_t heads, int32_t head_dim, float scale, int32_t ncu,
-                           hipStream_t s, hipEvent_t const* ev);
+                           int32_t ncu_q, hipStream_t s, hipEvent_t const* ev);
 hipError_t launch_qkv_fold(const void* w_txt, const void* w_img, const float* g_txt, const float* g_img,
                            int32_t hidden, int32_t out_features, void* out, hipStream_t s);
 hipError_t launch_qkv(const void* x, const void* w, const int32_t* cu, const int32_t* grid_hw, const int32_t* text_len,
@@ -466,6 +466,8 @@ int bwd_impl(const void* q, const void* k, const void* v, const void* out, const
   if ((rc = ensure_buffer(st.bws, st.bws_bytes, size_t(l.total)))) return rc;
   int32_t ncu = 0;
   if ((rc = ensure_cus(st, dev, &ncu))) return rc;
+  // dQ units split with the forward's threshold, dK/dV units with the backward's.
+  const int32_t ncu_q = mf::split_possible(total_tokens, n_seg) ? ncu : 0;
   if (!mf::split_possible(total_tokens, n_seg, mf::SPLIT_MIN_SAVED_BWD)) ncu = 0;
   hipError_t e;
   if (events && (e = hipEventRecord(events[0], stream)) != hipSuccess) return hip_fail(e, "hipEventRecord");
@@ -473,7 +475,7 @@ int bwd_impl(const void* q, const void* k, const void* v, const void* out, const
   if (e != hipSuccess) return hip_fail(e, "meta_kernel launch");
   e = mf::launch_attn_bwd(q, k, v, out, d_out, lse, grid_hw, text_len, cs, split ? &r3 : nullptr, st.bws, l, dq,
                           dk, dv, total_tokens, heads, head_dim, float(1.0 / std::sqrt(double(head_dim))), ncu,
-                          stream, events ? events + 1 : nullptr);
+                          ncu_q, stream, events ? events + 1 : nullptr);
   if (e != hipSuccess) return hip_fail(e, "backward kernels launch");
   if (events && (e = hipEventRecord(events[3], stream)) != hipSuccess) return hip_fail(e, "hipEventRecord");
   return MF_OK;

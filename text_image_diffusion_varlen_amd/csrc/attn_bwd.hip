@@ -72,8 +72,10 @@ struct BwdArgs {
   uint16_t* dk;
   uint16_t* dv;
   float* part;       // partial dV, dK of split dK/dV units, PART_SLOTS slots
-  int32_t ncu;       // compute units for the split plan (0: never split)
-  int64_t dq_units;  // workgroups of the dQ kernel's own grid (tile capacity x heads)
+  float* qpart;      // partial dQ of split dQ units, PART_SLOTS slots
+  int32_t ncu;       // compute units for the dK/dV split plan (0: never split)
+  int32_t ncu_q;     // compute units for the dQ split plan (0: never split)
+  int64_t dq_units;  // workgroups of the dQ kernel's own grid (units and pieces); dK/dV merges follow
   int32_t heads;
   int64_t rows;      // padded rows per head
   int64_t tokens;
@@ -355,6 +357,15 @@ __device__ inline SplitPlan kv_plan(const BwdArgs& a, const WsHeader* hdr) {
                     SPLIT_MIN_SAVED_BWD);
 }
 
+// The dQ kernel's plan: units = (256-query tile, head), split over key ranges
+// when the last round fills the device poorly, with the forward's threshold
+// (SPLIT_MIN_SAVED key tiles of the shortest unit).
+__device__ inline SplitPlan q_plan(const BwdArgs& a, const WsHeader* hdr) {
+  const int2 last = reinterpret_cast<const int2*>(a.ws + a.off_tiles)[hdr->n_tiles - 1];
+  const int32_t Ls = reinterpret_cast<const int32_t*>(a.ws + a.off_len)[last.x];
+  return split_plan(int64_t(hdr->n_tiles) * a.heads, a.ncu_q, (Ls + KTILE - 1) / KTILE);
+}
+
 template <int D, bool R3>
 __global__ void __launch_bounds__(64 * KV_WAVES, 2) bwd_kv_kernel(BwdArgs a) {
   constexpr int CH = BwdTile<D>::CH, KSTEPS = BwdTile<D>::KSTEPS, DBLK = BwdTile<D>::DBLK;
@@ -591,14 +602,31 @@ __global__ void __launch_bounds__(64 * Q_WAVES, 2) bwd_q_kernel(BwdArgs a) {
   }
   const WsHeader* hdr = reinterpret_cast<const WsHeader*>(a.ws);
   const int32_t heads = a.heads;
-  const int h = int(blockIdx.x % unsigned(heads));
-  const int tile = int(blockIdx.x / unsigned(heads));
-  if (hdr->flag != FLAG_OK || tile >= hdr->n_tiles) return;
+  if (hdr->flag != FLAG_OK) return;
+  // A whole unit, or piece `part` of a unit of the split last round (its key
+  // tiles [kt0, kt1)); workgroups past the plan return at once.
+  const SplitPlan plan = q_plan(a, hdr);
+  int unit = int(blockIdx.x), part = -1;
+  if (unit >= plan.n_full) {
+    const int piece = unit - plan.n_full;
+    if (piece >= plan.n_tail * plan.parts) return;
+    unit = plan.n_full + piece / plan.parts;
+    part = piece % plan.parts;
+  }
+  const int h = unit % heads;
+  const int tile = unit / heads;
   const int2 td = reinterpret_cast<const int2*>(a.ws + a.off_tiles)[tile];
   const int32_t seg = td.x, qs = td.y;
   const int32_t L = reinterpret_cast<const int32_t*>(a.ws + a.off_len)[seg];
   const int32_t pb = reinterpret_cast<const int32_t*>(a.ws + a.off_pcu)[seg];
   const int32_t cb = reinterpret_cast<const int32_t*>(a.ws + a.off_cu)[seg];
+  const int nkt_all = (L + KTILE - 1) / KTILE;
+  int kt0 = 0, kt1 = nkt_all;
+  if (part >= 0) {
+    kt0 = part * nkt_all / plan.parts;
+    kt1 = (part + 1) * nkt_all / plan.parts;
+    if (kt0 == kt1) return;  // empty piece of a short unit: the merge skips it
+  }
   const int tid = threadIdx.x;
   const int wave = tid >> 6, lane = tid & 63, hf = lane >> 5, l32 = lane & 31;
   const int64_t tile0 = (int64_t(h) * a.rows + pb) / KTILE;
@@ -637,17 +665,35 @@ __global__ void __launch_bounds__(64 * Q_WAVES, 2) bwd_q_kernel(BwdArgs a) {
   f32x16 acc[DBLK];
 #pragma unroll
   for (int b = 0; b < DBLK; ++b) acc[b] = f32x16{};
-  const int nkt = (L + KTILE - 1) / KTILE;
-  load_set(0, sets);
+  const int nkt = kt1 - kt0;
+  load_set(kt0, sets);
   wait_vm_and_sync();
-  for (int j = 0; j + 1 < nkt; ++j) {
-    load_set(j + 1, sets + ((j + 1) & 1) * SET);
-    q_step<D, false>(sets + (j & 1) * SET, qreg, oreg, acc, a.c_log2, lse2, dsum, KTILE * j, L, hf, l32);
+  for (int jj = 0; jj + 1 < nkt; ++jj) {
+    load_set(kt0 + jj + 1, sets + ((jj + 1) & 1) * SET);
+    q_step<D, false>(sets + (jj & 1) * SET, qreg, oreg, acc, a.c_log2, lse2, dsum, KTILE * (kt0 + jj), L, hf, l32);
     wait_vm_and_sync();
   }
-  q_step<D, true>(sets + ((nkt - 1) & 1) * SET, qreg, oreg, acc, a.c_log2, lse2, dsum, KTILE * (nkt - 1), L,
-                  hf, l32);
+  // The sample's last key tile carries the key mask.
+  if (kt1 == nkt_all)
+    q_step<D, true>(sets + ((nkt - 1) & 1) * SET, qreg, oreg, acc, a.c_log2, lse2, dsum, KTILE * (kt1 - 1), L,
+                    hf, l32);
+  else
+    q_step<D, false>(sets + ((nkt - 1) & 1) * SET, qreg, oreg, acc, a.c_log2, lse2, dsum, KTILE * (kt1 - 1), L,
+                     hf, l32);
 
+  if (part >= 0) {
+    // Piece of a split unit: the fp32 partial dQ (before the inverse rotation)
+    // of its 256 rows into its slot, for bwd_q_merge_kernel.
+    float* slot = a.qpart + int64_t(blockIdx.x - plan.n_full) * QTILE * D + int64_t(32 * wave + l32) * D;
+#pragma unroll
+    for (int b = 0; b < DBLK; ++b) {
+#pragma unroll
+      for (int g = 0; g < 4; ++g)
+        *reinterpret_cast<float4*>(slot + 32 * b + 8 * g + 4 * hf) =
+            make_float4(acc[b][4 * g], acc[b][4 * g + 1], acc[b][4 * g + 2], acc[b][4 * g + 3]);
+    }
+    return;
+  }
   if (qrel < L) {
     const TokPos pos = token_pos<R3>(qrel, seg, a);
     const int64_t off = (int64_t(cb + qrel) * heads + h) * D;
@@ -660,6 +706,46 @@ __global__ void __launch_bounds__(64 * Q_WAVES, 2) bwd_q_kernel(BwdArgs a) {
         *reinterpret_cast<uint2*>(a.dq + off + ch) = unrotate4<D, R3>(x, ch, pos, a.scale, a);
       }
     }
+  }
+}
+
+// Merge of split dQ units: one workgroup per split unit; each row's channel
+// quad is summed over the unit's non-empty pieces in piece order, then turned
+// back (inverse rotation), scaled and rounded like a whole unit's epilogue.
+template <int D, bool R3>
+__global__ void __launch_bounds__(256) bwd_q_merge_kernel(BwdArgs a) {
+  const WsHeader* hdr = reinterpret_cast<const WsHeader*>(a.ws);
+  if (hdr->flag != FLAG_OK) return;
+  const SplitPlan plan = q_plan(a, hdr);
+  const int u = int(blockIdx.x);
+  if (u >= plan.n_tail) return;
+  const int32_t heads = a.heads;
+  const int unit = plan.n_full + u;
+  const int h = unit % heads;
+  const int tile = unit / heads;
+  const int2 td = reinterpret_cast<const int2*>(a.ws + a.off_tiles)[tile];
+  const int32_t seg = td.x, qs = td.y;
+  const int32_t L = reinterpret_cast<const int32_t*>(a.ws + a.off_len)[seg];
+  const int32_t cb = reinterpret_cast<const int32_t*>(a.ws + a.off_cu)[seg];
+  const int nkt_all = (L + KTILE - 1) / KTILE;
+  constexpr int QUADS = D / 4;  // channel quads per row
+  const float* base = a.qpart + int64_t(u) * plan.parts * QTILE * D;
+  for (int item = int(threadIdx.x); item < QTILE * QUADS; item += 256) {
+    const int row = item / QUADS, c4 = item % QUADS;
+    const int32_t qrel = qs + row;
+    if (qrel >= L) continue;
+    float4 sum = make_float4(0.f, 0.f, 0.f, 0.f);
+    for (int p = 0; p < plan.parts; ++p) {
+      if (p * nkt_all / plan.parts == (p + 1) * nkt_all / plan.parts) continue;  // empty piece
+      const float4 x = *reinterpret_cast<const float4*>(base + int64_t(p) * QTILE * D + int64_t(row) * D + 4 * c4);
+      sum.x += x.x;
+      sum.y += x.y;
+      sum.z += x.z;
+      sum.w += x.w;
+    }
+    const float xs[4] = {sum.x, sum.y, sum.z, sum.w};
+    *reinterpret_cast<uint2*>(a.dq + (int64_t(cb + qrel) * heads + h) * D + 4 * c4) =
+        unrotate4<D, R3>(xs, 4 * c4, token_pos<R3>(qrel, seg, a), a.scale, a);
   }
 }
 
@@ -679,10 +765,13 @@ static hipError_t launch_bwd_t(const BwdArgs& a, const BwdLayout& l, hipStream_t
                      dim3(64 * KV_WAVES), 0, s, a);
   if ((e = hipGetLastError()) != hipSuccess) return e;
   if (ev && (e = hipEventRecord(ev[1], s)) != hipSuccess) return e;
-  // The dQ grid, then (when the dK/dV kernel may have split) one workgroup per
-  // possible split dK/dV unit to merge it.
+  // The dQ grid (whole units, then up to PART_SLOTS pieces of split units),
+  // then (when the dK/dV kernel may have split) one workgroup per possible
+  // split dK/dV unit to merge it; then the merge of split dQ units.
   hipLaunchKernelGGL((bwd_q_kernel<D, R3>), dim3(unsigned(a.dq_units + (a.ncu > 0 ? PART_SLOTS / 2 : 0))),
                      dim3(64 * Q_WAVES), 0, s, a);
+  if ((e = hipGetLastError()) != hipSuccess) return e;
+  if (a.ncu_q > 0) hipLaunchKernelGGL((bwd_q_merge_kernel<D, R3>), dim3(PART_SLOTS / 2), dim3(256), 0, s, a);
   return hipGetLastError();
 }
 
@@ -690,7 +779,7 @@ hipError_t launch_attn_bwd(const void* q, const void* k, const void* v, const vo
                            const float* lse, const int32_t* grid_hw, const int32_t* text_len,
                            const float2* cs, const Rope3* r3, char* ws, const BwdLayout& l, void* dq, void* dk,
                            void* dv, int64_t tokens, int32_t heads, int32_t head_dim, float scale, int32_t ncu,
-                           hipStream_t s, hipEvent_t const* ev) {
+                           int32_t ncu_q, hipStream_t s, hipEvent_t const* ev) {
   BwdArgs a;
   a.ws = ws;
   a.off_len = l.m.off_len;
@@ -724,8 +813,10 @@ hipError_t launch_attn_bwd(const void* q, const void* k, const void* v, const vo
   a.c_log2 = scale * LOG2E;
   a.scale = scale;
   a.part = reinterpret_cast<float*>(ws + l.off_part);
+  a.qpart = reinterpret_cast<float*>(ws + l.off_qpart);
   a.ncu = ncu;
-  a.dq_units = l.m.n_tiles * heads;
+  a.ncu_q = ncu_q;
+  a.dq_units = l.m.n_tiles * heads + (ncu_q > 0 ? PART_SLOTS : 0);
   if (r3) return head_dim == 128 ? launch_bwd_t<128, true>(a, l, s, ev) : launch_bwd_t<64, true>(a, l, s, ev);
   return head_dim == 128 ? launch_bwd_t<128, false>(a, l, s, ev) : launch_bwd_t<64, false>(a, l, s, ev);
 }

@@ -143,7 +143,7 @@ __host__ __device__ inline WsLayout ws_layout(int64_t tokens, int32_t heads, int
 //       the KTILE rows (+inf on padding rows), then D = rowsum(dO * O).
 struct BwdLayout {
   WsLayout m;  // metadata sections (its off_q / off_k / off_v / off_part / total are not used)
-  int64_t off_qc, off_qt, off_oc, off_ot, off_kc, off_kt, off_vc, off_st, off_part, total;
+  int64_t off_qc, off_qt, off_oc, off_ot, off_kc, off_kt, off_vc, off_st, off_part, off_qpart, total;
 };
 
 __host__ __device__ inline BwdLayout bwd_layout(int64_t tokens, int32_t heads, int32_t head_dim,
@@ -162,6 +162,8 @@ __host__ __device__ inline BwdLayout bwd_layout(int64_t tokens, int32_t heads, i
   b.off_st = o; o += round_up(int64_t(heads) * b.m.rows * 2 * 4, 256);
   // PART_SLOTS partial dV, dK of split dK/dV units: [dV | dK][BWD_KV_KEYS keys][head_dim] fp32 each.
   b.off_part = o; o += int64_t(PART_SLOTS) * 2 * BWD_KV_KEYS * head_dim * 4;
+  // PART_SLOTS partial dQ of split dQ units: [QTILE rows][head_dim] fp32 each.
+  b.off_qpart = o; o += int64_t(PART_SLOTS) * QTILE * head_dim * 4;
   b.total = o;
   return b;
 }
