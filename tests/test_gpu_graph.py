@@ -1,7 +1,8 @@
 """HIP-graph capture of the stream-ordered entry points.
 
-The packed forward, the packed backward, the guided Euler step and the
-RMSNorm + QKV projection prologue are each captured once (after an eager call
+The packed forward, the packed backward, the guided Euler step, the
+RMSNorm + QKV projection prologue, and a forward + backward whose kernels all
+split their last round, are each captured once (after an eager call
 has sized the library's workspaces and uploaded its RoPE table), then replayed
 several times with new values written into the captured input buffers, with
 eager library calls, other device work and host synchronizations between the
@@ -132,4 +133,39 @@ def test_qkv_prologue_graph_replays_match_eager():
         torch.cuda.synchronize()
         assert binding.get_device_error() == binding.MF_OK, binding.last_error()
         for name, a, b in zip("qkv", out_g, out_e):
+            assert torch.equal(a, b), f"replay {rep}: {name} differs from the eager call"
+
+
+def test_split_paths_graph_replays_match_eager():
+    """A 9000-token sample with 2 heads: the forward, dK/dV and dQ kernels all
+    split their last round (pieces, partial slots, merges). The forward with
+    LSE and the backward are captured together and replayed against eager calls."""
+    w = workloads.make_custom([[88, 100]], [200], heads=2, head_dim=128, dtype="bf16", seed=19, name="split_graph")
+    q, k, v, grid, text = device_inputs(w)
+    cu, _, _ = binding.build_metadata(grid, text, w.tokens)
+    print(f"graph split paths T={w.tokens}", flush=True)
+    d_out = torch.randn(q.shape, generator=torch.Generator(device="cuda").manual_seed(12), device="cuda",
+                        dtype=torch.float32).to(q.dtype)
+    lse_e, lse_g = (torch.empty((w.heads, w.tokens), dtype=torch.float32, device="cuda") for _ in range(2))
+    out_e, out_g = torch.empty_like(q), torch.empty_like(q)
+    grads_e = tuple(torch.empty_like(q) for _ in range(3))
+    grads_g = tuple(torch.empty_like(q) for _ in range(3))
+
+    def step(qq, out, lse, grads):
+        binding.attn_packed_lse(qq, k, v, cu, grid, text, out=out, lse=lse)
+        binding.attn_packed_bwd(qq, k, v, out, d_out, lse, cu, grid, text, grads=grads)
+
+    step(q, out_e, lse_e, grads_e)  # sizes both workspaces
+    torch.cuda.synchronize()
+    qg = q.clone()
+    g = _capture(lambda: step(qg, out_g, lse_g, grads_g))
+    for rep in range(3):
+        _new_inputs((qg,), (q,), rep)
+        g.replay()
+        torch.cuda.synchronize()
+        step(qg, out_e, lse_e, grads_e)
+        torch.cuda.synchronize()
+        assert binding.get_device_error() == binding.MF_OK, binding.last_error()
+        assert torch.equal(out_g, out_e) and torch.equal(lse_g, lse_e), f"replay {rep}: forward differs"
+        for name, a, b in zip(("dq", "dk", "dv"), grads_g, grads_e):
             assert torch.equal(a, b), f"replay {rep}: {name} differs from the eager call"
