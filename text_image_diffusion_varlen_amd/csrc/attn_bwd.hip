@@ -12,7 +12,7 @@
 // P is recomputed from the forward's saved row log-sum-exp (natural log,
 // [heads][tokens]); no score matrix is stored.
 //
-// Three kernels:
+// Kernels:
 //   bwd_pack_kernel  one workgroup per (KTILE padded rows, head): rotates q and
 //                    k, and writes Q~, dO, K~, V chunk-major, Q~^T, dO^T, K~^T
 //                    in MFMA order (as the forward's V~^T) and per-row
@@ -29,9 +29,16 @@
 //                    the sample's 64-key tiles:
 //                      S^T = K~ Q~^T, dP^T = V dO^T (lane = query),
 //                      dQ^T += K~^T dX^T.
+// When the last round of either kernel's units would fill the device poorly
+// and the units are long, those units run as pieces (dK/dV over query ranges,
+// dQ over key ranges) that write fp32 partial sums to slots of the workspace;
+// extra workgroups of bwd_q_kernel merge the dK/dV pieces and
+// bwd_q_merge_kernel the dQ pieces, adding them in piece order before the
+// usual epilogue (the plans are derived identically on the device from the
+// tile table, nothing is stored).
 // Every product runs on v_mfma_f32_32x32x16_bf16 with fp32 accumulation; P
-// and dX are rounded to bf16 (RNE) as MFMA operands. Nothing is accumulated
-// across workgroups, so results are deterministic.
+// and dX are rounded to bf16 (RNE) as MFMA operands. No atomics and a fixed
+// summation order everywhere, so results are deterministic.
 #include "mf_common.h"
 #include "mfma_util.h"
 #include "rope_math.h"
