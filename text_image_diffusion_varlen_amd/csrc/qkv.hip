@@ -21,7 +21,9 @@
 //                     v_mfma_f32_32x32x16_bf16 with D = W' X^T (lane = token),
 //                     K staged 64 channels at a time in LDS by direct-to-LDS
 //                     copies, double-buffered; the epilogue scales by 1 / r_t
-//                     and writes q, k, v rows directly.
+//                     and writes q, k, v rows directly. A last round that
+//                     would fill at most half the CUs runs as 128-feature
+//                     halves of its tiles (same summation order).
 // Both GEMM operands are stored tiled: for every 256-row x 64-channel tile,
 // 2048 16-byte chunks, chunk c (channels 8c .. 8c+7) of row r at c * 256 + r.
 // A stage is then one contiguous 32 KB copy per operand, and the LDS image
