@@ -146,3 +146,40 @@ def test_backward_3d_and_projection_reject_bad_arguments_on_host():
     assert lib.mf_qkv_rmsnorm(*q, 1, 10, 128, 2, 128, -1.0, *o, None) == bad
     assert lib.mf_qkv_fold_weights(P(16), P(32), P(48), P(64), 96, 2, 128, P(4096), None) == uns
     assert binding.last_error() != ""
+
+
+def test_header_is_c99_and_the_library_links_from_c():
+    """The boundary is a C ABI: a C99 program that includes only mf_attn.h (and
+    the HIP runtime API header it names) compiles without warnings, links
+    against the built library and runs its host-side calls without a GPU."""
+    import os
+    import shutil
+
+    gcc = shutil.which("gcc")
+    if gcc is None:
+        pytest.skip("gcc not available")
+    root = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+    out = os.path.join(root, "_build", "c_abi")  # build folder, kept out of the repository
+    os.makedirs(out, exist_ok=True)
+    src = os.path.join(out, "main.c")
+    with open(src, "w") as f:
+        f.write(
+            "#include <stdio.h>\n"
+            "#include \"mf_attn.h\"\n"
+            "int main(void) {\n"
+            "  size_t ws = mf_workspace_bytes(4352, 24, 128, MF_BF16, 1);\n"
+            "  int bad = mf_attn_packed(NULL, NULL, NULL, NULL, NULL, NULL, NULL, 1, 64, 2, 64, MF_BF16, NULL);\n"
+            "  printf(\"%d %zu %d %d\\n\", mf_version(), ws, bad, mf_last_error()[0] != 0);\n"
+            "  return 0;\n"
+            "}\n")
+    lib_dir = os.path.dirname(binding.LIB_PATH)
+    exe = os.path.join(out, "main")
+    r = subprocess.run([gcc, "-std=c99", "-Wall", "-Wextra", "-Werror", "-D__HIP_PLATFORM_AMD__",
+                        "-I", os.path.join(root, "include"), "-I", "/opt/rocm/include", src, "-L", lib_dir,
+                        "-lmfattn", f"-Wl,-rpath,{lib_dir}", "-o", exe], capture_output=True, text=True)
+    assert r.returncode == 0, r.stderr
+    run = subprocess.run([exe], capture_output=True, text=True, timeout=60)
+    assert run.returncode == 0, run.stderr
+    version, ws, bad, has_msg = run.stdout.split()
+    assert int(version) == 100 and int(ws) == binding.lib().mf_workspace_bytes(4352, 24, 128, 0, 1)
+    assert int(bad) == binding.MF_ERR_INVALID_ARG and has_msg == "1"
