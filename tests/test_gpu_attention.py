@@ -198,6 +198,36 @@ def test_workspace_variant_matches():
     assert e.value.code == binding.MF_ERR_INVALID_ARG
 
 
+def test_concurrent_streams_with_separate_workspaces():
+    """Two batches on two side streams at once, each with its own workspace
+    (the documented rule for concurrent calls on one device): every result
+    equals an eager call on the default stream bit for bit, and each
+    workspace reports its own status."""
+    wa = workloads.make_workload("mixed", seed=22)
+    wb = workloads.make_custom([[64, 64]], [256], heads=4, head_dim=128, dtype="bf16", seed=41, name="b")
+    print(f"two streams: T={wa.tokens} and T={wb.tokens}", flush=True)
+    ins = []
+    for w in (wa, wb):
+        q, k, v, grid, text = device_inputs(w)
+        cu, _, _ = binding.build_metadata(grid, text, w.tokens)
+        ref = binding.attn_packed(q, k, v, cu, grid, text)
+        ws = torch.empty(binding.workspace_bytes(w.tokens, w.heads, w.head_dim, torch.bfloat16, w.n_seg),
+                         dtype=torch.uint8, device="cuda")
+        ins.append((q, k, v, cu, grid, text, ref, ws, torch.empty_like(q)))
+    torch.cuda.synchronize()
+    streams = [torch.cuda.Stream(), torch.cuda.Stream()]
+    for s in streams:
+        s.wait_stream(torch.cuda.current_stream())
+    for _ in range(5):
+        for s, (q, k, v, cu, grid, text, _, ws, out) in zip(streams, ins):
+            with torch.cuda.stream(s):
+                binding.attn_packed_ws(q, k, v, cu, grid, text, ws, out=out, stream=s)
+    torch.cuda.synchronize()
+    for s, (*_, ref, ws, out) in zip(streams, ins):
+        assert binding.get_workspace_error(ws, s) == binding.MF_OK
+        assert torch.equal(out, ref)
+
+
 def test_metadata_mismatch_writes_nothing():
     w = workloads.make_custom([[4, 4], [3, 5]], [2, 1], heads=2, head_dim=128, dtype="bf16", seed=2)
     q, k, v, grid, text = device_inputs(w)
