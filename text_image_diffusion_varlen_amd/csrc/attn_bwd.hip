@@ -459,9 +459,12 @@ __global__ void __launch_bounds__(64 * KV_WAVES, 2) bwd_kv_kernel(BwdArgs a) {
   f32x16 dp[2];    // dK waves: this step's dP, two 32-query halves
   for (int jj = 0; jj < nqt; ++jj) {
     const u32x4* cur = sets + (jj & 1) * SET;
-    if (jj + 1 < nqt) load_set(qt0 + jj + 1, sets + ((jj + 1) & 1) * SET);
     if (dv_wave) kv_phase1_dv<D>(cur, pl, kreg, pk, a.c_log2, hf, l32, lane);
     else kv_phase1_dk<D>(cur, vreg, dp, hf, l32);
+    // The next step's tiles go to the other set (last read in the previous
+    // step). Issued after this step's first phase, not before it, so that
+    // the 64 copy instructions do not hold back the start of the MFMAs.
+    if (jj + 1 < nqt) load_set(qt0 + jj + 1, sets + ((jj + 1) & 1) * SET);
     __syncthreads();  // P of this step is in pl
     if (dv_wave) kv_phase2_dv<D>(cur, pk, acc, hf, l32);
     else kv_phase2_dk<D>(cur, pl, dp, acc, hf, l32, lane);
