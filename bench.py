@@ -380,8 +380,8 @@ def main():
     args = ap.parse_args()
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
-        print("bench.py measures one GPU only: this build has no multi-GPU path "
-              "(samples would shard by segment across GPUs; see the design notes).", file=sys.stderr)
+        print("bench.py measures one GPU only: the library has no multi-GPU path "
+              "(a packed batch would shard by whole samples, one process per GPU).", file=sys.stderr)
         sys.exit(2)
 
     import torch
