@@ -23,7 +23,9 @@
 //                     copies, double-buffered; the epilogue scales by 1 / r_t
 //                     and writes q, k, v rows directly. A last round that
 //                     would fill at most half the CUs runs as 128-feature
-//                     halves of its tiles (same summation order).
+//                     halves of its tiles (same summation order). Workgroups
+//                     are mapped to tiles so that those running together on
+//                     one XCD (one L2) share operand tiles.
 // Both GEMM operands are stored tiled: for every 256-row x 64-channel tile,
 // 2048 16-byte chunks, chunk c (channels 8c .. 8c+7) of row r at c * 256 + r.
 // A stage is then one contiguous 32 KB copy per operand, and the LDS image
@@ -41,6 +43,7 @@ constexpr int QKV_NT = 256;                       // output features per workgro
 constexpr int QKV_TT = 256;                       // tokens per workgroup
 constexpr int QKV_KS = 64;                        // hidden channels per LDS stage
 constexpr int QKV_CH = QKV_NT * QKV_KS / 8;       // 16-byte chunks per operand tile
+constexpr int QKV_GROUP_TT = 4;                   // token tiles per group of the XCD-aware order
 static_assert(QKV_TT == QKV_NT, "A and B tiles share one copy pattern");
 constexpr int ROUTE_THREADS = 1024;
 
@@ -345,6 +348,27 @@ __device__ inline void qkv_gemm_unit(const QkvGemmArgs& a, const QkvHeader* hdr,
   }
 }
 
+// XCD-aware order of the units. Workgroups are dispatched to the 8 XCDs
+// round-robin by index, and each XCD has its own L2, so the ~32 workgroups
+// one XCD runs together should share operand tiles. Positions are laid out
+// in groups of QKV_GROUP_TT token tiles, feature tile major inside a group,
+// so 32 consecutive positions cover 8 feature tiles x 4 token tiles (12
+// distinct 32 KB operand tiles per stage instead of ~17 in index order), and
+// inside every whole group of 256 workgroups the 32 of one XCD take 32
+// consecutive positions. Both maps are bijections, so every unit is computed
+// exactly once and the outputs do not depend on the order.
+__device__ inline int unit_at(int pos, int n_tiles, int token_tiles) {
+  const int gsz = QKV_GROUP_TT * n_tiles;
+  const int g = pos / gsz, r = pos % gsz;
+  const int gs = min(QKV_GROUP_TT, token_tiles - g * QKV_GROUP_TT);  // token tiles in this group
+  return (g * QKV_GROUP_TT + r % gs) * n_tiles + r / gs;
+}
+__device__ inline int xcd_position(int b, int n_whole) {
+  const int g0 = b & ~255;
+  if (g0 + 256 > n_whole) return b;
+  return g0 + 32 * (b & 7) + ((b & 255) >> 3);
+}
+
 // Units = feature tiles x (text + visual token tiles), one workgroup per unit
 // (one per CU: 128 KB of LDS). When the last round of units would occupy at
 // most half of the a.ncu compute units, its units run as two 128-feature
@@ -358,11 +382,12 @@ __global__ void __launch_bounds__(QKV_THREADS, 2) qkv_gemm_kernel(QkvGemmArgs a)
   const int32_t n_full = halve ? units - tail : units;
   __shared__ u32x4 lds[2][2 * QKV_CH];  // [stage][A (features) | B (tokens)]
   const int b = int(blockIdx.x);
+  const int token_tiles = units / a.n_tiles;
   if (b < n_full) {
-    qkv_gemm_unit<4>(a, hdr, b, 0, lds);
+    qkv_gemm_unit<4>(a, hdr, unit_at(xcd_position(b, n_full), a.n_tiles, token_tiles), 0, lds);
   } else if (halve && b < n_full + 2 * tail) {
     const int piece = b - n_full;
-    qkv_gemm_unit<2>(a, hdr, n_full + piece / 2, (piece % 2) * (QKV_NT / 2), lds);
+    qkv_gemm_unit<2>(a, hdr, unit_at(n_full + piece / 2, a.n_tiles, token_tiles), (piece % 2) * (QKV_NT / 2), lds);
   }
 }
 
