@@ -623,11 +623,17 @@ __global__ void __launch_bounds__(64 * Q_WAVES, 2) bwd_q_kernel(BwdArgs a) {
     unit = plan.n_full + piece / plan.parts;
     part = piece % plan.parts;
   }
-  const int h = unit % heads;
-  const int tile = unit / heads;
-  const int2 td = reinterpret_cast<const int2*>(a.ws + a.off_tiles)[tile];
-  const int32_t seg = td.x, qs = td.y;
+  int tile = unit / heads;
+  int2 td = reinterpret_cast<const int2*>(a.ws + a.off_tiles)[tile];
+  const int32_t seg = td.x;
   const int32_t L = reinterpret_cast<const int32_t*>(a.ws + a.off_len)[seg];
+  if (part < 0) {
+    unit = xcd_unit(unit, heads, tile, td.y, L, plan.n_full);
+    tile = unit / heads;
+    td = reinterpret_cast<const int2*>(a.ws + a.off_tiles)[tile];
+  }
+  const int h = unit % heads;
+  const int32_t qs = td.y;
   const int32_t pb = reinterpret_cast<const int32_t*>(a.ws + a.off_pcu)[seg];
   const int32_t cb = reinterpret_cast<const int32_t*>(a.ws + a.off_cu)[seg];
   const int nkt_all = (L + KTILE - 1) / KTILE;

@@ -64,27 +64,6 @@ __device__ inline SplitPlan call_plan(const AttnArgs& a, const WsHeader* hdr) {
   return split_plan(int64_t(hdr->n_tiles) * a.heads, a.ncu, (Ls + KTILE - 1) / KTILE);
 }
 
-// XCD-aware order of the whole units. Workgroups go to the 8 XCDs
-// round-robin by index, so with heads a multiple of 8 the units of one sample
-// that land on XCD x are those of 3 (generally heads / 8) heads, every query
-// tile of each. In tile-major order each XCD runs all of those heads in every
-// round of the grid and streams their K~ and V~^T tiles once per round; here
-// they are reordered head-major (all tiles of one head, then the next), so
-// the workgroups sharing a head's key tiles run together and each head is
-// streamed about once. The permutation stays inside one sample's units on one
-// XCD (equal work, longest-first order between samples kept) and is applied
-// only to samples whose units are all whole (not split); results do not
-// depend on it.
-__device__ inline int xcd_unit(int unit, int heads, int tile, int qs, int32_t L, int n_full) {
-  if (heads % 8 != 0) return unit;
-  const int n_s = (L + QTILE - 1) / QTILE;        // query tiles of the sample
-  const int u0 = (tile - qs / QTILE) * heads;      // its first unit
-  if (u0 + n_s * heads > n_full) return unit;
-  const int p = unit - u0;
-  const int c = p & 7, k = p >> 3;                 // run of XCD (u0 + c) % 8, position k in it
-  return u0 + (k % n_s) * heads + c + 8 * (k / n_s);
-}
-
 // Copies one chunk-major tile (CHUNKS 16-byte chunks) from the workspace into
 // LDS with direct-to-LDS loads spread over the workgroup's waves.
 template <int CHUNKS>

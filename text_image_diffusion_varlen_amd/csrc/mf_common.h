@@ -94,6 +94,27 @@ __host__ __device__ inline SplitPlan split_plan(int64_t units, int32_t ncu, int6
   return p;
 }
 
+// XCD-aware order of the whole (query tile, head) units of the forward and
+// dQ kernels. Workgroups go to the 8 XCDs round-robin by index, so with heads
+// a multiple of 8 the units of one sample that land on XCD x are those of
+// heads / 8 heads, every query tile of each. In tile-major order each XCD runs
+// all of those heads in every round of the grid and streams their key-side
+// tiles once per round; here they are reordered head-major (all tiles of one
+// head, then the next), so the workgroups sharing a head's key tiles run
+// together and each head is streamed about once. The permutation stays inside one sample's units on one
+// XCD (equal work, longest-first order between samples kept) and is applied
+// only to samples whose units are all whole (not split); results do not
+// depend on it.
+__device__ inline int xcd_unit(int unit, int heads, int tile, int qs, int32_t L, int n_full) {
+  if (heads % 8 != 0) return unit;
+  const int n_s = (L + QTILE - 1) / QTILE;        // query tiles of the sample
+  const int u0 = (tile - qs / QTILE) * heads;      // its first unit
+  if (u0 + n_s * heads > n_full) return unit;
+  const int p = unit - u0;
+  const int c = p & 7, k = p >> 3;                 // run of XCD (u0 + c) % 8, position k in it
+  return u0 + (k % n_s) * heads + c + 8 * (k / n_s);
+}
+
 // Workspace: [header 256 B][len n][cu n+1][pcu n+1][tiles 2*max_tiles][Q~][K~][V~][partials]
 // with every section 256-byte aligned. Q~, K~, V~ are [heads][rows][head_dim].
 struct WsHeader {
