@@ -101,15 +101,17 @@ __host__ __device__ inline SplitPlan split_plan(int64_t units, int32_t ncu, int6
 // all of those heads in every round of the grid and streams their key-side
 // tiles once per round; here they are reordered head-major (all tiles of one
 // head, then the next), so the workgroups sharing a head's key tiles run
-// together and each head is streamed about once. The permutation stays inside one sample's units on one
-// XCD (equal work, longest-first order between samples kept) and is applied
-// only to samples whose units are all whole (not split); results do not
-// depend on it.
+// together and each head is streamed about once. The permutation stays
+// inside one sample's units on one XCD (equal work, longest-first order
+// between samples kept), among its query tiles whose units are all whole (not
+// split); results do not depend on it.
 __device__ inline int xcd_unit(int unit, int heads, int tile, int qs, int32_t L, int n_full) {
   if (heads % 8 != 0) return unit;
-  const int n_s = (L + QTILE - 1) / QTILE;        // query tiles of the sample
-  const int u0 = (tile - qs / QTILE) * heads;      // its first unit
-  if (u0 + n_s * heads > n_full) return unit;
+  const int u0 = (tile - qs / QTILE) * heads;      // the sample's first unit
+  // its query tiles whose units are all whole (all of them unless the split
+  // last round cuts into the sample)
+  const int n_s = min((L + QTILE - 1) / QTILE, (n_full - u0) / heads);
+  if (unit >= u0 + n_s * heads) return unit;
   const int p = unit - u0;
   const int c = p & 7, k = p >> 3;                 // run of XCD (u0 + c) % 8, position k in it
   return u0 + (k % n_s) * heads + c + 8 * (k / n_s);
