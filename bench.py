@@ -98,61 +98,117 @@ def sample_lengths(w):
     return (w.text_len.astype("int64") + f * w.grid_hw[:, 0].astype("int64") * w.grid_hw[:, 1]).tolist()
 
 
-def cpu_baseline(w, budget_s: float, gpu_out=None, gpu_meta=None):
-    """The fp64 oracle (as it stands) on host cores, over as many whole heads of the
-    same workload as fit in the time budget (at least one).
+def _oracle_item(args):
+    """One (sample, head) work item of the CPU baseline: the fp64 oracle on that
+    sample's rows of that head alone (runs in a worker process)."""
+    q, k, v, grid_hw, text_len, frames, split = args
+    from oracle import attention
+    if frames is None:
+        return attention.joint_attention(q, k, v, grid_hw, text_len)
+    return attention.joint_attention_3d(q, k, v, grid_hw, text_len, frames, split)
 
-    After the timed loop, the oracle's outputs of those heads are compared with
+
+def _pool_worker_init():
+    # one BLAS thread per worker process: the pool, not BLAS, spreads the work
+    for var in ("OMP_NUM_THREADS", "OPENBLAS_NUM_THREADS", "MKL_NUM_THREADS", "BLIS_NUM_THREADS"):
+        os.environ[var] = "1"
+
+
+def cpu_baseline(w, budget_s: float, gpu_out=None, gpu_meta=None, max_workers: int = 16):
+    """The fp64 oracle (as it stands) on host cores: a process pool over
+    (sample, head) work items, one BLAS thread per worker, workers = the cores
+    this process may run on (at most `max_workers`, the host share of one GPU).
+    Heads are submitted whole (all samples of head 0, then head 1, ...) until
+    the time budget is spent; the heads finished by then are the sample.
+
+    After the timed region, the oracle's outputs of those heads are compared with
     the GPU output of the same workload (`gpu_out`, [T][H][d] on the host) and
     the library's metadata (`gpu_meta` = (cu_seqlens, positions) on the host)
     with the oracle's packing: max / mean abs error, whether they are within
     the parity bars, and whether the metadata is bit-exact."""
-    import numpy as np
-    from oracle import attention, packing
+    import concurrent.futures
+    import multiprocessing
 
-    try:
-        from threadpoolctl import threadpool_info
-        threads = max([int(i.get("num_threads", 1)) for i in threadpool_info() if i.get("user_api") == "blas"] or [1])
-    except Exception:  # threadpoolctl missing: report the affinity set
-        threads = len(os.sched_getaffinity(0))
+    import numpy as np
+    from oracle import packing
+
+    cores = min(len(os.sched_getaffinity(0)), max_workers)
     lengths = sample_lengths(w)
+    cu = np.concatenate([[0], np.cumsum(lengths)]).astype(np.int64)
     per_head = 4.0 * sum(L * L for L in lengths) * w.head_dim
-    t0 = time.perf_counter()
-    heads = 0
-    outs = []
-    while heads < w.heads:
-        h = slice(heads, heads + 1)
-        if w.frames is None:
-            o = attention.joint_attention(w.q[:, h], w.k[:, h], w.v[:, h], w.grid_hw, w.text_len)
-        else:
-            o = attention.joint_attention_3d(w.q[:, h], w.k[:, h], w.v[:, h], w.grid_hw, w.text_len, w.frames,
-                                             w.rope_split)
-        outs.append(o)
-        heads += 1
-        if time.perf_counter() - t0 > budget_s:
-            break
-    dt = time.perf_counter() - t0
+    frames = w.frames
+
+    def item(i, h):
+        a, b = int(cu[i]), int(cu[i + 1])
+        return (w.q[a:b, h:h + 1], w.k[a:b, h:h + 1], w.v[a:b, h:h + 1], w.grid_hw[i:i + 1], w.text_len[i:i + 1],
+                None if frames is None else frames[i:i + 1], w.rope_split)
+
+    # Children get one BLAS thread from the environment they start with.
+    saved = {var: os.environ.get(var) for var in ("OMP_NUM_THREADS", "OPENBLAS_NUM_THREADS", "MKL_NUM_THREADS",
+                                                  "BLIS_NUM_THREADS")}
+    _pool_worker_init()
+    ctx = multiprocessing.get_context("spawn")  # no fork of a process that holds the GPU
+    outs = np.zeros((w.tokens, w.heads, w.head_dim))
+    try:
+        with concurrent.futures.ProcessPoolExecutor(max_workers=cores, mp_context=ctx,
+                                                    initializer=_pool_worker_init) as ex:
+            # start-up of every worker (interpreter, numpy, oracle import) outside the timed region:
+            # a one-token sample per worker
+            one = (w.q[:1, :1], w.k[:1, :1], w.v[:1, :1], np.ones((1, 2), np.int32), np.zeros(1, np.int32),
+                   None if frames is None else np.ones(1, np.int32), w.rope_split)
+            list(ex.map(_oracle_item, [one] * (2 * cores)))
+            t0 = time.perf_counter()
+            pending = {}
+            done_heads = 0
+            next_head = 0
+            left = {}
+            # keep the pool busy with a little more than one head's items in flight
+            while done_heads < w.heads:
+                while next_head < w.heads and len(pending) < 2 * cores and time.perf_counter() - t0 <= budget_s:
+                    for i in range(w.n_seg):
+                        pending[ex.submit(_oracle_item, item(i, next_head))] = (i, next_head)
+                    left[next_head] = w.n_seg
+                    next_head += 1
+                if not pending:
+                    break
+                finished, _ = concurrent.futures.wait(pending, return_when=concurrent.futures.FIRST_COMPLETED)
+                for f in finished:
+                    i, h = pending.pop(f)
+                    outs[int(cu[i]):int(cu[i + 1]), h] = f.result()[:, 0]
+                    left[h] -= 1
+                while done_heads < next_head and left[done_heads] == 0:
+                    done_heads += 1
+            dt = time.perf_counter() - t0
+            heads = done_heads
+    finally:
+        for var, val in saved.items():
+            if val is None:
+                os.environ.pop(var, None)
+            else:
+                os.environ[var] = val
     res = {
         "value": per_head * heads / dt / 1e12,
         "unit": "TFLOP/s",
-        "cores": threads,
+        "cores": cores,
         "kind": "oracle",
-        "sample": f"{heads} of {w.heads} heads of the same workload (all rows, fp64 numpy), {dt:.1f} s",
+        "sample": f"{heads} of {w.heads} heads of the same workload (all rows, fp64 numpy, "
+                  f"{w.n_seg * heads} (sample, head) items over {cores} worker processes with one BLAS thread each),"
+                  f" {dt:.1f} s",
     }
-    if gpu_out is not None:
-        err = np.abs(gpu_out[:, :heads].astype(np.float64) - np.concatenate(outs, axis=1))
+    if gpu_out is not None and heads > 0:
+        err = np.abs(gpu_out[:, :heads].astype(np.float64) - outs[:, :heads])
         bars = (2e-2, 2e-3) if w.dtype == "bf16" else (1e-5, 1e-5)
         res["max_abs_err_vs_gpu"] = float(err.max())
         res["mean_abs_err_vs_gpu"] = float(err.mean())
         res["within_parity_bars"] = bool(err.max() <= bars[0] and err.mean() <= bars[1])
     if gpu_meta is not None:
-        cu, pos = gpu_meta
+        gcu, pos = gpu_meta
         if w.frames is None:
             ref_pos, _ = packing.token_positions(w.grid_hw, w.text_len)
         else:
             ref_pos, _ = packing.token_positions_3d(w.grid_hw, w.text_len, w.frames)
         ref_cu = packing.cu_seqlens(w.grid_hw, w.text_len, w.frames)
-        res["metadata_bit_exact"] = bool(np.array_equal(cu, ref_cu) and np.array_equal(pos, ref_pos))
+        res["metadata_bit_exact"] = bool(np.array_equal(gcu, ref_cu) and np.array_equal(pos, ref_pos))
     return res
 
 
@@ -363,6 +419,138 @@ def qkv_bench(w, grid, text, cu, steps: int, warmup: int, frames=None):
     }
 
 
+def forward_bench(config: str, seed, steps: int, warmup: int, keep_host: bool):
+    """Times the packed joint-attention forward on one workload.
+
+    One step = one library call (metadata, RoPE prologue, attention) on resident
+    inputs; K steps between two synchronizations, torch events on the stream the
+    library launches on. Then the same K calls with HIP events between the three
+    kernels (2D path) give per-kernel times, and K more with the 256 MB MALL
+    flushed before each give the prologue's cold-cache rate."""
+    import torch
+    from text_image_diffusion_varlen_amd import binding, workloads
+
+    edit = config in workloads.EDIT_CONFIGS
+    w = workloads.make_edit(config, seed=seed) if edit else workloads.make_workload(config, seed=seed)
+    dt = torch.bfloat16 if w.dtype == "bf16" else torch.float32
+    q, k, v = (torch.from_numpy(x).to(dt).cuda() for x in (w.q, w.k, w.v))
+    grid = torch.from_numpy(w.grid_hw).cuda()
+    text = torch.from_numpy(w.text_len).cuda()
+    frames = None
+    if edit:
+        frames = torch.from_numpy(w.frames).cuda()
+        cu, pos, _ = binding.build_metadata_3d(grid, text, frames, w.tokens)
+    else:
+        cu, pos, _ = binding.build_metadata(grid, text, w.tokens)
+    out = torch.empty_like(q)
+    torch.cuda.synchronize()
+    if binding.get_device_error() != binding.MF_OK:
+        raise RuntimeError(binding.last_error())
+
+    lengths = sample_lengths(w)
+    flops = 4.0 * sum(L * L for L in lengths) * w.head_dim * w.heads
+    elem = 2 if w.dtype == "bf16" else 4
+    qkvo_bytes = 4.0 * w.tokens * w.heads * w.head_dim * elem
+
+    if edit:
+        def step():
+            binding.attn_packed_3d(q, k, v, cu, grid, text, frames, w.rope_split, out=out)
+    else:
+        def step():
+            binding.attn_packed(q, k, v, cu, grid, text, out=out)
+    for _ in range(warmup):
+        step()
+    torch.cuda.synchronize()
+
+    # Timed region: K whole steps, torch events on the stream the library launches on.
+    start, stop = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    start.record()
+    for _ in range(steps):
+        step()
+    stop.record()
+    torch.cuda.synchronize()
+    ms = start.elapsed_time(stop) / steps
+    if binding.get_device_error() != binding.MF_OK:
+        raise RuntimeError(binding.last_error())
+
+    # Per-kernel durations: the same calls with HIP events between the three
+    # kernels (2D path; the frame-aware batches report the whole step).
+    attn_each = pack_cold = None
+    if edit:
+        stage = {"meta": 0.0, "rope_pack": 0.0, "attn": ms}
+    else:
+        ev = HipEvents(4 * steps)
+        for s in range(steps):
+            binding.attn_packed_profiled(q, k, v, cu, grid, text, ev.ev[4 * s : 4 * s + 4], out=out)
+        torch.cuda.synchronize()
+        stage = {"meta": 0.0, "rope_pack": 0.0, "attn": 0.0}
+        attn_each = []
+        for s in range(steps):
+            b = 4 * s
+            stage["meta"] += ev.elapsed_ms(b, b + 1) / steps
+            stage["rope_pack"] += ev.elapsed_ms(b + 1, b + 2) / steps
+            attn_each.append(ev.elapsed_ms(b + 2, b + 3))
+        stage["attn"] = sum(attn_each) / steps
+        # The same calls with the 256 MB MALL flushed before each (a 512 MB
+        # buffer written in between): the RoPE prologue then reads k and v from HBM.
+        flush = torch.empty(512 << 20, dtype=torch.uint8, device="cuda")
+        pack_cold = []
+        for s in range(steps):
+            flush.fill_(s & 255)
+            binding.attn_packed_profiled(q, k, v, cu, grid, text, ev.ev[4 * s : 4 * s + 4], out=out)
+        torch.cuda.synchronize()
+        for s in range(steps):
+            pack_cold.append(ev.elapsed_ms(4 * s + 1, 4 * s + 2))
+        del flush
+        ev.close()
+
+    # The forward output and metadata of this workload, for the oracle comparison
+    # in the CPU baseline (the last call above ran the same inputs).
+    gpu_out = gpu_meta = None
+    if keep_host:
+        torch.cuda.synchronize()
+        gpu_out = out.float().cpu().numpy()
+        gpu_meta = (cu.cpu().numpy(), pos.cpu().numpy())
+
+    achieved = flops / (stage["attn"] / 1e3)
+    # prologue: bf16 reads k, v and writes K~, V~ (queries are rotated inside the attention kernel);
+    # f32 also reads q and writes Q~
+    rope_bytes = (4.0 if w.dtype == "bf16" else 6.0) * w.tokens * w.heads * w.head_dim * elem
+    record = {
+        "value": round(flops / (ms / 1e3) / 1e12, 2),
+        "ms_per_step": round(ms, 4),
+        "config": {
+            "workload": f"{config}: {DESCRIPTIONS[config]}",
+            "tokens": w.tokens,
+            "samples": w.n_seg,
+            "heads": w.heads,
+            "head_dim": w.head_dim,
+            "seed": w.seed,
+            "flop_per_step": flops,
+        },
+        "pct_mfma_peak": round(100.0 * flops / (ms / 1e3) / PEAK[w.dtype], 2),
+        "tokens_per_s": round(w.tokens / (ms / 1e3), 1),
+        "stages_ms": {k2: round(v2, 4) for k2, v2 in stage.items()},
+        "attn_ms_p10_p50_p90": [round(float(x), 4) for x in np.percentile(attn_each, [10, 50, 90])] if not edit else None,
+        "rope_pack_gbps": round(rope_bytes / (stage["rope_pack"] / 1e3) / 1e9, 1) if not edit else None,
+        "rope_pack_gbps_cold_mall": round(rope_bytes / (float(np.median(pack_cold)) / 1e3) / 1e9, 1) if not edit else None,
+        "roofline": {
+            "kernel": f"attn_fwd_{w.dtype}_kernel<{w.head_dim}, {'true' if edit else 'false'}>"
+                      + (" (whole step: no per-kernel events on the frame-aware path)" if edit else ""),
+            "bound": "mfma" if w.dtype == "bf16" else "alu",
+            "achieved": round(achieved / 1e12, 2),
+            "peak": PEAK[w.dtype] / 1e12,
+            "unit": "TFLOP/s",
+            "frac": round(achieved / PEAK[w.dtype], 4),
+            "traffic": stored_traffic(config),
+            "algorithmic_bytes": qkvo_bytes,
+        },
+    }
+    return {"workload": w, "record": record, "q": q, "k": k, "v": v, "cu": cu, "grid": grid, "text": text,
+            "frames": frames, "gpu_out": gpu_out, "gpu_meta": gpu_meta}
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -375,6 +563,8 @@ def main():
     ap.add_argument("--no-sampler", action="store_true", help="skip the packed CFG Euler-step measurement")
     ap.add_argument("--no-backward", action="store_true", help="skip the packed backward measurement")
     ap.add_argument("--no-qkv", action="store_true", help="skip the RMSNorm + QKV projection measurement")
+    ap.add_argument("--no-mixed", action="store_true",
+                    help="with the default 1024sq workload, skip the second (mixed-aspect) forward record")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="only run a plain device copy of 1 GiB (HBM-counter calibration for profiling)")
     args = ap.parse_args()
@@ -401,132 +591,30 @@ def main():
         print(json.dumps({"calibrate_copy_bytes_read": n, "calibrate_copy_bytes_written": n,
                           "dispatches": max(args.steps, 1)}), flush=True)
         return
-    edit = args.config in workloads.EDIT_CONFIGS
-    w = workloads.make_edit(args.config, seed=args.seed) if edit else workloads.make_workload(args.config, seed=args.seed)
-    dt = torch.bfloat16 if w.dtype == "bf16" else torch.float32
-    q, k, v = (torch.from_numpy(x).to(dt).cuda() for x in (w.q, w.k, w.v))
-    grid = torch.from_numpy(w.grid_hw).cuda()
-    text = torch.from_numpy(w.text_len).cuda()
-    if edit:
-        frames = torch.from_numpy(w.frames).cuda()
-        cu, pos, _ = binding.build_metadata_3d(grid, text, frames, w.tokens)
-    else:
-        cu, pos, _ = binding.build_metadata(grid, text, w.tokens)
-    out = torch.empty_like(q)
-    torch.cuda.synchronize()
-    if binding.get_device_error() != binding.MF_OK:
-        raise RuntimeError(binding.last_error())
-
-    lengths = sample_lengths(w)
-    flops = 4.0 * sum(L * L for L in lengths) * w.head_dim * w.heads
-    elem = 2 if w.dtype == "bf16" else 4
-    qkvo_bytes = 4.0 * w.tokens * w.heads * w.head_dim * elem
-
-    if edit:
-        def step():
-            binding.attn_packed_3d(q, k, v, cu, grid, text, frames, w.rope_split, out=out)
-    else:
-        def step():
-            binding.attn_packed(q, k, v, cu, grid, text, out=out)
-    for _ in range(args.warmup):
-        step()
-    torch.cuda.synchronize()
-
-    # Timed region: K whole steps, torch events on the stream the library launches on.
-    start, stop = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    torch.cuda.synchronize()
-    start.record()
-    for _ in range(args.steps):
-        step()
-    stop.record()
-    torch.cuda.synchronize()
-    ms = start.elapsed_time(stop) / args.steps
-    if binding.get_device_error() != binding.MF_OK:
-        raise RuntimeError(binding.last_error())
-
-    # Per-kernel durations: the same calls with HIP events between the three
-    # kernels (2D path; the frame-aware batches report the whole step).
-    if edit:
-        stage = {"meta": 0.0, "rope_pack": 0.0, "attn": ms}
-    else:
-        ev = HipEvents(4 * args.steps)
-        for s in range(args.steps):
-            binding.attn_packed_profiled(q, k, v, cu, grid, text, ev.ev[4 * s : 4 * s + 4], out=out)
-        torch.cuda.synchronize()
-        stage = {"meta": 0.0, "rope_pack": 0.0, "attn": 0.0}
-        attn_each = []
-        for s in range(args.steps):
-            b = 4 * s
-            stage["meta"] += ev.elapsed_ms(b, b + 1) / args.steps
-            stage["rope_pack"] += ev.elapsed_ms(b + 1, b + 2) / args.steps
-            attn_each.append(ev.elapsed_ms(b + 2, b + 3))
-        stage["attn"] = sum(attn_each) / args.steps
-        # The same calls with the 256 MB MALL flushed before each (a 512 MB
-        # buffer written in between): the RoPE prologue then reads k and v from HBM.
-        flush = torch.empty(512 << 20, dtype=torch.uint8, device="cuda")
-        pack_cold = []
-        for s in range(args.steps):
-            flush.fill_(s & 255)
-            binding.attn_packed_profiled(q, k, v, cu, grid, text, ev.ev[4 * s : 4 * s + 4], out=out)
-        torch.cuda.synchronize()
-        for s in range(args.steps):
-            pack_cold.append(ev.elapsed_ms(4 * s + 1, 4 * s + 2))
-        del flush
-        ev.close()
-
-    # The forward output and metadata of this workload, for the oracle comparison
-    # in the CPU baseline (the last call above ran the same inputs).
-    gpu_out = gpu_meta = None
-    if not args.no_cpu_baseline:
-        torch.cuda.synchronize()
-        gpu_out = out.float().cpu().numpy()
-        gpu_meta = (cu.cpu().numpy(), pos.cpu().numpy())
-
-    attn_s = stage["attn"] / 1e3
-    achieved = flops / attn_s
-    # prologue: bf16 reads k, v and writes K~, V~ (queries are rotated inside the attention kernel);
-    # f32 also reads q and writes Q~
-    rope_bytes = (4.0 if w.dtype == "bf16" else 6.0) * w.tokens * w.heads * w.head_dim * elem
+    fwd = forward_bench(args.config, args.seed, args.steps, args.warmup, keep_host=not args.no_cpu_baseline)
+    w, result = fwd["workload"], fwd["record"]
     result = {
         "metric": "packed joint-attn TFLOP/s (bf16, 2D RoPE) + % of MFMA peak; tokens/s",
-        "value": round(flops / (ms / 1e3) / 1e12, 2),
+        "value": result["value"],
         "unit": "TFLOP/s",
         "n_gpus": 1,
         "steps": args.steps,
         "warmup": args.warmup,
-        "ms_per_step": round(ms, 4),
+        "ms_per_step": result["ms_per_step"],
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
         "dtype": w.dtype,
         "data": "synthetic",
-        "config": {
-            "workload": f"{args.config}: {DESCRIPTIONS[args.config]}",
-            "tokens": w.tokens,
-            "samples": w.n_seg,
-            "heads": w.heads,
-            "head_dim": w.head_dim,
-            "seed": w.seed,
-            "flop_per_step": flops,
-        },
-        "pct_mfma_peak": round(100.0 * flops / (ms / 1e3) / PEAK[w.dtype], 2),
-        "tokens_per_s": round(w.tokens / (ms / 1e3), 1),
-        "stages_ms": {k2: round(v2, 4) for k2, v2 in stage.items()},
-        "attn_ms_p10_p50_p90": [round(float(x), 4) for x in np.percentile(attn_each, [10, 50, 90])] if not edit else None,
-        "rope_pack_gbps": round(rope_bytes / (stage["rope_pack"] / 1e3) / 1e9, 1) if not edit else None,
-        "rope_pack_gbps_cold_mall": round(rope_bytes / (float(np.median(pack_cold)) / 1e3) / 1e9, 1) if not edit else None,
-        "roofline": {
-            "kernel": f"attn_fwd_{w.dtype}_kernel<{w.head_dim}, {'true' if edit else 'false'}>"
-                      + (" (whole step: no per-kernel events on the frame-aware path)" if edit else ""),
-            "bound": "mfma" if w.dtype == "bf16" else "alu",
-            "achieved": round(achieved / 1e12, 2),
-            "peak": PEAK[w.dtype] / 1e12,
-            "unit": "TFLOP/s",
-            "frac": round(achieved / PEAK[w.dtype], 4),
-            "traffic": stored_traffic(args.config),
-            "algorithmic_bytes": qkvo_bytes,
-        },
+        "config": result["config"],
+        **{k2: v2 for k2, v2 in result.items() if k2 not in ("value", "ms_per_step", "config")},
     }
+    if args.config == "1024sq" and not args.no_mixed:
+        # The second workload the throughput target names, timed the same way in the same run.
+        mixed = forward_bench("mixed", None, args.steps, args.warmup, keep_host=False)["record"]
+        result["mixed"] = mixed
+    q, k, v, cu, grid, text, frames = (fwd[x] for x in ("q", "k", "v", "cu", "grid", "text", "frames"))
+    edit = frames is not None
     if w.dtype == "bf16" and not args.no_backward:
         result["backward"] = backward_bench(w, q, k, v, cu, grid, text, args.steps, args.warmup,
                                             frames if edit else None)
@@ -535,7 +623,7 @@ def main():
     if not args.no_sampler:
         result["cfg_euler_step"] = sampler_bench(args.steps, args.warmup)
     if not args.no_cpu_baseline:
-        result["cpu_baseline"] = cpu_baseline(w, args.cpu_budget, gpu_out=gpu_out, gpu_meta=gpu_meta)
+        result["cpu_baseline"] = cpu_baseline(w, args.cpu_budget, gpu_out=fwd["gpu_out"], gpu_meta=fwd["gpu_meta"])
     print(json.dumps(result), flush=True)
 
 

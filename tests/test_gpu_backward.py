@@ -95,6 +95,43 @@ def test_backward_configs_two_heads(config):
     _full_check(workloads.make_custom(g, t, heads=2, head_dim=128, dtype="bf16", seed=12, name=config))
 
 
+def _head_subset(w, heads):
+    return workloads.Workload(f"{w.name}[heads {heads}]", w.grid_hw, w.text_len, len(heads), w.head_dim, w.dtype,
+                              w.q[:, heads], w.k[:, heads], w.v[:, heads], seed=w.seed)
+
+
+# (config, heads, compared heads): the real head counts run the XCD-aware dQ
+# order (heads a multiple of 8, at least 16) and, on 1024sq with 24 heads, the
+# dK/dV split plan (816 units on 256 CUs, the last 48 cut into 4 query ranges).
+ALL_HEADS = {
+    "1024sq_h24": ("1024sq", 24, [0, 7, 8, 23]),
+    "mixed_h24": ("mixed", 24, [0, 9, 16, 23]),
+    "1024sq_h16": ("1024sq", 16, [0, 9, 15]),
+}
+
+
+@pytest.mark.parametrize("name", sorted(ALL_HEADS))
+def test_backward_configs_all_heads(name):
+    """The 1024^2 and mixed batches at their real head count on the GPU; heads
+    are independent, so a few heads are compared with the oracle run on those
+    head slices alone (LSE, dq, dk, dv, every element of those heads)."""
+    config, heads, sel = ALL_HEADS[name]
+    g, t = workloads.make_segments(config)
+    w = workloads.make_custom(g, t, heads=heads, head_dim=128, dtype="bf16", seed=14, name=config)
+    print(f"backward {name} T={w.tokens} n={w.n_seg} H={heads} compared heads {sel}", flush=True)
+    do = _d_out(w)
+    out, lse, dq, dk, dv = _run(w, do)
+    ws = _head_subset(w, sel)
+    dos = do[:, sel]
+    lerr = check_lse(lse.cpu().numpy()[sel], attention.joint_attention_lse(ws.q, ws.k, ws.grid_hw, ws.text_len), ws)
+    print(f"  lse: max err {lerr:.3e}")
+    rq, rk, rv = attention.joint_attention_backward(ws.q, ws.k, ws.v, dos, ws.grid_hw, ws.text_len)
+    for gname, g, r in (("dq", dq, rq), ("dk", dk, rk), ("dv", dv, rv)):
+        _check_grad(gname, to_f64(g[:, sel]), r)
+    for gname, g in (("dq", dq), ("dk", dk), ("dv", dv)):
+        assert torch.isfinite(g.float()).all(), f"{gname}: non-finite"
+
+
 def test_forward_with_lse_matches_forward_bitwise():
     w = workloads.make_workload("mixed", seed=24)
     q, k, v, grid, text = device_inputs(w)

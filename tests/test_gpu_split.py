@@ -55,6 +55,29 @@ def test_split_round_2d(name):
     assert torch.equal(out, out2) and torch.equal(lse, lse2), "repeated calls differ"
 
 
+def test_split_round_16_heads_partly_split_sample():
+    """One 9000-token sample with 16 heads: 576 units, the last 64 split 4 ways.
+    Heads are a multiple of 8, so the whole units take the XCD-aware head-major
+    order; the sample's last 4 query tiles are split, so the order covers only
+    its first 32 tiles (the partly split branch of the unit permutation).
+    Output and LSE of six heads, every element, against the oracle on those
+    head slices (heads are independent)."""
+    sel = [0, 3, 7, 8, 12, 15]
+    w = workloads.make_custom([[88, 100]], [200], heads=16, head_dim=128, dtype="bf16", seed=19, name="h16")
+    print(f"split 16 heads T={w.tokens} compared heads {sel}", flush=True)
+    q, k, v, grid, text = device_inputs(w)
+    cu, _, _ = binding.build_metadata(grid, text, w.tokens)
+    out, lse = _forward(q, k, v, grid, text, cu)
+    ws = workloads.Workload("h16 subset", w.grid_hw, w.text_len, len(sel), w.head_dim, w.dtype,
+                            w.q[:, sel], w.k[:, sel], w.v[:, sel], seed=w.seed)
+    check_close(to_f64(out[:, sel]), attention.joint_attention(ws.q, ws.k, ws.v, ws.grid_hw, ws.text_len), "bf16")
+    lse_ref = attention.joint_attention_lse(ws.q, ws.k, ws.grid_hw, ws.text_len)
+    check_lse(lse.double().cpu().numpy()[sel], lse_ref, ws)
+    assert torch.isfinite(out.float()).all()
+    out2, lse2 = _forward(q, k, v, grid, text, cu)
+    assert torch.equal(out, out2) and torch.equal(lse, lse2), "repeated calls differ"
+
+
 def test_split_round_edit():
     # one edit of 3 images of 48 x 64 after a 100-token instruction, 8 heads: 296 units, 40 split
     w = workloads.make_edit(grids=[[48, 64]], texts=[100], frames=[3], heads=8, head_dim=128, dtype="bf16",
