@@ -3,8 +3,13 @@
 //   meta_kernel      metadata check, padded offsets, longest-first tile table
 //   rope_pack_kernel 2D RoPE on q, k into the padded workspace (+ V transpose)
 //   attn_fwd_*       per-sample flash-style attention
-// Nothing here synchronizes except mf_get_device_error / mf_get_workspace_error
-// and the first-use allocations of the library-owned state.
+// Nothing here synchronizes except mf_get_device_error / mf_get_workspace_error,
+// the first-use allocations of the library-owned state, and the debug mode
+// (MF_DEBUG=1 in the environment: every stage is followed by a stream
+// synchronization and a check of the launch, of device faults and of the
+// device flags, so a failure is reported by the call that caused it, naming
+// the stage). Every stage is bracketed by a roctx range ("mf <kernel>"), which
+// rocprofv3 --marker-trace records next to the kernels.
 #include <algorithm>
 #include <cmath>
 #include <cstdarg>
@@ -17,6 +22,8 @@
 #include <tuple>
 #include <utility>
 #include <vector>
+
+#include <rocprofiler-sdk-roctx/roctx.h>
 
 #include "mf_attn.h"
 #include "mf_common.h"
@@ -76,6 +83,45 @@ int fail(int code, const char* fmt, ...) {
 int hip_fail(hipError_t e, const char* what) {
   return fail(MF_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
 }
+
+// roctx range around the launches of one stage (host-side enqueue; the
+// profiler correlates it with the kernels it enqueues).
+struct Range {
+  explicit Range(const char* name) { roctxRangePushA(name); }
+  ~Range() { roctxRangePop(); }
+  Range(const Range&) = delete;
+  Range& operator=(const Range&) = delete;
+};
+
+bool debug_mode() {
+  static const bool on = [] {
+    const char* e = std::getenv("MF_DEBUG");
+    return e && e[0] == '1';
+  }();
+  return on;
+}
+
+// Debug mode only: waits for the stream, then reports a failed launch, a
+// device fault, or a set device flag (a workspace header's flag or the sticky
+// status word; `clear` resets a status word once reported) as the error of
+// this call. Outside debug mode it does nothing.
+int debug_stage(hipStream_t s, const char* stage, const int32_t* flag = nullptr, bool clear = false) {
+  if (!debug_mode()) return MF_OK;
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return fail(MF_ERR_HIP, "%s: launch: %s", stage, hipGetErrorString(e));
+  if ((e = hipStreamSynchronize(s)) != hipSuccess)
+    return fail(MF_ERR_HIP, "%s: hipStreamSynchronize: %s", stage, hipGetErrorString(e));
+  if (!flag) return MF_OK;
+  int32_t v = 0;
+  if ((e = hipMemcpy(&v, flag, 4, hipMemcpyDeviceToHost)) != hipSuccess)
+    return fail(MF_ERR_HIP, "%s: reading the device flag: %s", stage, hipGetErrorString(e));
+  if (v && clear && (e = hipMemset(const_cast<int32_t*>(flag), 0, 4)) != hipSuccess)
+    return fail(MF_ERR_HIP, "%s: clearing the device flag: %s", stage, hipGetErrorString(e));
+  if (v) return fail(MF_ERR_METADATA, "%s: device check failed (flags 0x%x)", stage, unsigned(v));
+  return MF_OK;
+}
+
+const int32_t* ws_flag(const char* ws) { return reinterpret_cast<const int32_t*>(ws); }  // WsHeader::flag
 
 struct DeviceState {
   int32_t* status = nullptr;  // sticky FLAG_* of the standalone metadata / RoPE / sampler calls
@@ -282,17 +328,30 @@ int run_attn(const void* q, const void* k, const void* v, const int32_t* cu, con
   const bool bf16 = dtype == MF_BF16;
   const mf::WsLayout l = mf::ws_layout(tokens, heads, head_dim, elem_bytes(dtype), n_seg);
   hipError_t e;
+  int rc;
   if (ev && (e = hipEventRecord(ev[0], s)) != hipSuccess) return hip_fail(e, "hipEventRecord");
-  e = mf::launch_meta(grid_hw, text_len, frames, cu, n_seg, tokens, ws, l, s);
+  {
+    Range r("mf meta_kernel");
+    e = mf::launch_meta(grid_hw, text_len, frames, cu, n_seg, tokens, ws, l, s);
+  }
   if (e != hipSuccess) return hip_fail(e, "meta_kernel launch");
+  if ((rc = debug_stage(s, "meta_kernel", ws_flag(ws)))) return rc;
   if (ev && (e = hipEventRecord(ev[1], s)) != hipSuccess) return hip_fail(e, "hipEventRecord");
-  e = mf::launch_rope_pack(q, k, v, grid_hw, text_len, ws, l, cs, r3, heads, head_dim, bf16, s);
+  {
+    Range r("mf rope_pack_kernel");
+    e = mf::launch_rope_pack(q, k, v, grid_hw, text_len, ws, l, cs, r3, heads, head_dim, bf16, s);
+  }
   if (e != hipSuccess) return hip_fail(e, "rope_pack_kernel launch");
+  if ((rc = debug_stage(s, "rope_pack_kernel"))) return rc;
   if (ev && (e = hipEventRecord(ev[2], s)) != hipSuccess) return hip_fail(e, "hipEventRecord");
-  e = mf::launch_attn_fwd(ws, l, q, grid_hw, text_len, cs, r3, out, lse, tokens, heads, head_dim, bf16,
-                          float(1.0 / std::sqrt(double(head_dim))),
-                          mf::split_possible(tokens, n_seg) ? ncu : 0, s);
+  {
+    Range r("mf attn_fwd");
+    e = mf::launch_attn_fwd(ws, l, q, grid_hw, text_len, cs, r3, out, lse, tokens, heads, head_dim, bf16,
+                            float(1.0 / std::sqrt(double(head_dim))),
+                            mf::split_possible(tokens, n_seg) ? ncu : 0, s);
+  }
   if (e != hipSuccess) return hip_fail(e, "attn_fwd launch");
+  if ((rc = debug_stage(s, "attn_fwd"))) return rc;
   if (ev && (e = hipEventRecord(ev[3], s)) != hipSuccess) return hip_fail(e, "hipEventRecord");
   return MF_OK;
 }
@@ -471,12 +530,20 @@ int bwd_impl(const void* q, const void* k, const void* v, const void* out, const
   if (!mf::split_possible(total_tokens, n_seg, mf::SPLIT_MIN_SAVED_BWD)) ncu = 0;
   hipError_t e;
   if (events && (e = hipEventRecord(events[0], stream)) != hipSuccess) return hip_fail(e, "hipEventRecord");
-  e = mf::launch_meta(grid_hw, text_len, frames, cu_seqlens, n_seg, total_tokens, st.bws, l.m, stream);
+  {
+    Range r("mf meta_kernel");
+    e = mf::launch_meta(grid_hw, text_len, frames, cu_seqlens, n_seg, total_tokens, st.bws, l.m, stream);
+  }
   if (e != hipSuccess) return hip_fail(e, "meta_kernel launch");
-  e = mf::launch_attn_bwd(q, k, v, out, d_out, lse, grid_hw, text_len, cs, split ? &r3 : nullptr, st.bws, l, dq,
-                          dk, dv, total_tokens, heads, head_dim, float(1.0 / std::sqrt(double(head_dim))), ncu,
-                          ncu_q, stream, events ? events + 1 : nullptr);
+  if ((rc = debug_stage(stream, "meta_kernel", ws_flag(st.bws)))) return rc;
+  {
+    Range r("mf attn_bwd");
+    e = mf::launch_attn_bwd(q, k, v, out, d_out, lse, grid_hw, text_len, cs, split ? &r3 : nullptr, st.bws, l, dq,
+                            dk, dv, total_tokens, heads, head_dim, float(1.0 / std::sqrt(double(head_dim))), ncu,
+                            ncu_q, stream, events ? events + 1 : nullptr);
+  }
   if (e != hipSuccess) return hip_fail(e, "backward kernels launch");
+  if ((rc = debug_stage(stream, "backward kernels"))) return rc;
   if (events && (e = hipEventRecord(events[3], stream)) != hipSuccess) return hip_fail(e, "hipEventRecord");
   return MF_OK;
 }
@@ -498,9 +565,14 @@ int metadata_impl(int32_t n_seg, const int32_t* grid_hw, const int32_t* text_len
     if ((rc = ensure_status(g_dev[dev]))) return rc;
     status = g_dev[dev].status;
   }
-  const hipError_t e = mf::launch_build_metadata(grid_hw, text_len, frames, n_seg, total_tokens, cu_seqlens_out,
-                                                 pos_out, seg_id_out, status, stream);
-  return e == hipSuccess ? MF_OK : hip_fail(e, "metadata kernels launch");
+  hipError_t e;
+  {
+    Range r("mf metadata");
+    e = mf::launch_build_metadata(grid_hw, text_len, frames, n_seg, total_tokens, cu_seqlens_out, pos_out,
+                                  seg_id_out, status, stream);
+  }
+  if (e != hipSuccess) return hip_fail(e, "metadata kernels launch");
+  return debug_stage(stream, "metadata kernels", status, true);
 }
 
 int rope_impl(const void* x_in, void* x_out, const int32_t* pos, const int32_t* split, int64_t total_tokens,
@@ -539,9 +611,14 @@ int rope_impl(const void* x_in, void* x_out, const int32_t* pos, const int32_t* 
     }
     status = st.status;
   }
-  const hipError_t e = mf::launch_rope(x_in, x_out, pos, total_tokens, heads, head_dim, dtype == MF_BF16, cs,
-                                       split ? &r3 : nullptr, status, stream);
-  return e == hipSuccess ? MF_OK : hip_fail(e, "rope_kernel launch");
+  hipError_t e;
+  {
+    Range r("mf rope_kernel");
+    e = mf::launch_rope(x_in, x_out, pos, total_tokens, heads, head_dim, dtype == MF_BF16, cs,
+                        split ? &r3 : nullptr, status, stream);
+  }
+  if (e != hipSuccess) return hip_fail(e, "rope_kernel launch");
+  return debug_stage(stream, "rope_kernel", status, true);
 }
 
 }  // namespace
@@ -685,9 +762,13 @@ int mf_qkv_rmsnorm_profiled(const void* x, const void* w_folded, const int32_t* 
   if ((rc = ensure_cus(st, dev, &ncu))) return rc;
   hipError_t e;
   if (events && (e = hipEventRecord(events[0], stream)) != hipSuccess) return hip_fail(e, "hipEventRecord");
-  e = mf::launch_qkv(x, w_folded, cu_seqlens, grid_hw, text_len, frames, n_seg, total_tokens, hidden, hd, eps, st.qws,
-                     q, k, v, ncu, stream, events ? events + 1 : nullptr);
+  {
+    Range r("mf qkv_rmsnorm");
+    e = mf::launch_qkv(x, w_folded, cu_seqlens, grid_hw, text_len, frames, n_seg, total_tokens, hidden, hd, eps,
+                       st.qws, q, k, v, ncu, stream, events ? events + 1 : nullptr);
+  }
   if (e != hipSuccess) return hip_fail(e, "qkv kernels launch");
+  if ((rc = debug_stage(stream, "qkv kernels", ws_flag(st.qws)))) return rc;
   if (events && (e = hipEventRecord(events[2], stream)) != hipSuccess) return hip_fail(e, "hipEventRecord");
   return MF_OK;
 }
@@ -738,10 +819,14 @@ int mf_rf_cfg_euler_step(float* z, const void* v, const int32_t* cu_seqlens, con
     if ((rc = ensure_status(st))) return rc;
     status = st.status;
   }
-  const hipError_t e = mf::launch_cfg_euler(z, v, cu_seqlens, grid_hw, text_len, n_seg, total_tokens, cond_seg,
-                                            uncond_seg, n_img, image_tokens, channels, dtype == MF_BF16,
-                                            guidance, dt, status, stream);
-  return e == hipSuccess ? MF_OK : hip_fail(e, "cfg_euler_kernel launch");
+  hipError_t e;
+  {
+    Range r("mf cfg_euler_kernel");
+    e = mf::launch_cfg_euler(z, v, cu_seqlens, grid_hw, text_len, n_seg, total_tokens, cond_seg, uncond_seg, n_img,
+                             image_tokens, channels, dtype == MF_BF16, guidance, dt, status, stream);
+  }
+  if (e != hipSuccess) return hip_fail(e, "cfg_euler_kernel launch");
+  return debug_stage(stream, "cfg_euler_kernel", status, true);
 }
 
 int mf_get_device_error(hipStream_t stream) {
