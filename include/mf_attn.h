@@ -135,6 +135,39 @@ int mf_attn_packed_ws(const void* q, const void* k, const void* v, const int32_t
                       void* workspace, size_t workspace_bytes, hipStream_t stream);
 
 /*
+ * Allocation-free forward, for callers that cannot allocate device memory:
+ * code under HIP graph capture, tight serving loops, harnesses that forbid
+ * hipMalloc. Same arguments, checks and results as mf_attn_packed, but the
+ * workspace is a fixed static device array of MF_NOALLOC_SCRATCH_BYTES bytes
+ * (each device the library runs on holds its own copy from the first call on
+ * it until the process ends), so no call allocates or frees anything.
+ *  - Limit: header and metadata plus the rotated-key and transposed-value
+ *    buffers (MF_F32: also the rotated queries) of heads x rows x head_dim
+ *    elements each must fit, rows = the sum over samples of L_i rounded up to
+ *    64, plus 192. bf16 with 24 heads x 128: about 21,600 packed tokens (the
+ *    1024x1024, 2048x2048 and mixed-aspect batches fit). Larger batches return
+ *    MF_ERR_UNSUPPORTED with the bytes they would need.
+ *  - Never splits a poorly filled last round (the split needs partial-result
+ *    slots), so results equal mf_attn_packed's bit for bit wherever that call
+ *    does not split either (mean sample length below 8129 tokens), and are
+ *    within rounding of them elsewhere.
+ *  - The first call on a device does a one-time synchronous setup: it looks
+ *    up the static arrays' device addresses and copies the RoPE cos/sin tables
+ *    into one of them (no allocation). Make one call before capturing.
+ *  - Every call on a device uses that device's one scratch array and leaves
+ *    its contents behind. Calls that overlap on one device (two streams,
+ *    concurrent graph replays) race on it and give wrong results; order them
+ *    on one stream.
+ * A metadata mismatch behaves as for mf_attn_packed (nothing written,
+ * reported by mf_get_device_error).
+ */
+#define MF_NOALLOC_SCRATCH_BYTES ((size_t)256 << 20)
+int mf_attn_packed_noalloc(const void* q, const void* k, const void* v, const int32_t* cu_seqlens,
+                           const int32_t* grid_hw, const int32_t* text_len, void* out, int32_t n_seg,
+                           int64_t total_tokens, int32_t heads, int32_t head_dim, int32_t dtype,
+                           hipStream_t stream);
+
+/*
  * Forward for training: mf_attn_packed that also stores each query row's
  * log-sum-exp of its scaled scores, the statistic the backward recomputes P
  * from (no score matrix is kept).
@@ -356,7 +389,10 @@ int mf_rf_cfg_euler_step(float* z, const void* v, const int32_t* cu_seqlens, con
 
 /*
  * Synchronizes `stream`, then returns MF_ERR_METADATA if the last enqueued
- * metadata check on this device's library workspace failed, else MF_OK.
+ * metadata check on any of this device's library workspaces (forward,
+ * backward, projection, the allocation-free forward's scratch) or the sticky
+ * flag of the standalone metadata, RoPE and sampler calls failed, else MF_OK.
+ * The sticky flag is cleared once reported.
  */
 int mf_get_device_error(hipStream_t stream);
 

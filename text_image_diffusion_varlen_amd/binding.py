@@ -46,6 +46,7 @@ def _declare(lib):
         "mf_attn_packed_profiled": ([P, P, P, P, P, P, P, I32, I64, I32, I32, I32, P, P], ctypes.c_int),
         "mf_workspace_bytes": ([I64, I32, I32, I32, I32], SZ),
         "mf_attn_packed_ws": ([P, P, P, P, P, P, P, I32, I64, I32, I32, I32, P, SZ, P], ctypes.c_int),
+        "mf_attn_packed_noalloc": ([P, P, P, P, P, P, P, I32, I64, I32, I32, I32, P], ctypes.c_int),
         "mf_attn_packed_lse": ([P, P, P, P, P, P, P, P, I32, I64, I32, I32, I32, P], ctypes.c_int),
         "mf_attn_packed_bwd": ([P] * 12 + [I32, I64, I32, I32, I32, P], ctypes.c_int),
         "mf_attn_packed_bwd_profiled": ([P] * 12 + [I32, I64, I32, I32, I32, P, P], ctypes.c_int),
@@ -171,6 +172,15 @@ def attn_packed_ws(q, k, v, cu_seqlens, grid_hw, text_len, workspace, out=None, 
     _check(lib().mf_attn_packed_ws(_ptr(q), _ptr(k), _ptr(v), _ptr(cu_seqlens), _ptr(grid_hw), _ptr(text_len),
                                    _ptr(out), n, T, H, D, _DTYPES[q.dtype], _ptr(workspace),
                                    workspace.numel(), _stream(stream)))
+    return out
+
+
+def attn_packed_noalloc(q, k, v, cu_seqlens, grid_hw, text_len, out, stream=None):
+    """mf_attn_packed_noalloc: the forward on the library's fixed static scratch.
+    `out` must be given (this call allocates nothing). Returns out."""
+    out, n, T, H, D = _attn_args(q, k, v, cu_seqlens, grid_hw, text_len, out)
+    _check(lib().mf_attn_packed_noalloc(_ptr(q), _ptr(k), _ptr(v), _ptr(cu_seqlens), _ptr(grid_hw),
+                                        _ptr(text_len), _ptr(out), n, T, H, D, _DTYPES[q.dtype], _stream(stream)))
     return out
 
 

@@ -132,6 +132,8 @@ struct DeviceState {
   char* qws = nullptr;        // library workspace of mf_qkv_rmsnorm
   size_t qws_bytes = 0;
   int32_t ncu = -1;           // compute units for the forward's split plan (0: splitting off); -1 unknown
+  char* scratch = nullptr;    // this device's copy of the static scratch array (mf_attn_packed_noalloc)
+  const float2* scratch_tables = nullptr;  // its copy of the static 2D cos/sin tables (d = 128, then d = 64)
   // (head_dim, theta bits, row channels, column channels) -> cos/sin table;
   // row channels -1 marks the 2D table
   std::map<std::tuple<int, uint32_t, int, int>, float2*> tables;
@@ -192,6 +194,20 @@ int upload_table(DeviceState& st, std::tuple<int, uint32_t, int, int> key, const
 
 // 2D cos/sin table [ROPE_PMAX][head_dim/4]: entry (p, j) = (cos, sin) of
 // p * theta^(-2j/(head_dim/2)), evaluated in double and rounded to float.
+std::vector<float2> table2d_host(int head_dim, float theta) {
+  const int nf = head_dim / 4;
+  std::vector<float2> host(size_t(mf::ROPE_PMAX) * nf);
+  for (int p = 0; p < mf::ROPE_PMAX; ++p) {
+    for (int j = 0; j < nf; ++j) {
+      const double w = std::pow(double(theta), -2.0 * j / (head_dim / 2));
+      const double ang = double(p) * w;
+      host[size_t(p) * nf + j] = make_float2(float(std::cos(ang)), float(std::sin(ang)));
+    }
+  }
+  return host;
+}
+
+// The 2D table of mf_attn_packed for this head_dim, created on first use.
 // Caller holds g_mu.
 int ensure_table(DeviceState& st, int head_dim, float theta, const float2** out) {
   uint32_t tb;
@@ -202,16 +218,7 @@ int ensure_table(DeviceState& st, int head_dim, float theta, const float2** out)
     *out = it->second;
     return MF_OK;
   }
-  const int nf = head_dim / 4;
-  std::vector<float2> host(size_t(mf::ROPE_PMAX) * nf);
-  for (int p = 0; p < mf::ROPE_PMAX; ++p) {
-    for (int j = 0; j < nf; ++j) {
-      const double w = std::pow(double(theta), -2.0 * j / (head_dim / 2));
-      const double ang = double(p) * w;
-      host[size_t(p) * nf + j] = make_float2(float(std::cos(ang)), float(std::sin(ang)));
-    }
-  }
-  return upload_table(st, key, host, out);
+  return upload_table(st, key, table2d_host(head_dim, theta), out);
 }
 
 // Frame-aware cos/sin table [ROPE_PMAX][head_dim/2] for the channel split
@@ -324,9 +331,10 @@ int run_attn(const void* q, const void* k, const void* v, const int32_t* cu, con
              const int32_t* text_len, void* out, int32_t n_seg, int64_t tokens, int32_t heads,
              int32_t head_dim, int32_t dtype, char* ws, const float2* cs, int32_t ncu, hipStream_t s,
              hipEvent_t const* ev = nullptr, float* lse = nullptr, const int32_t* frames = nullptr,
-             const mf::Rope3* r3 = nullptr) {
+             const mf::Rope3* r3 = nullptr, bool with_parts = true) {
   const bool bf16 = dtype == MF_BF16;
-  const mf::WsLayout l = mf::ws_layout(tokens, heads, head_dim, elem_bytes(dtype), n_seg);
+  const mf::WsLayout l = mf::ws_layout(tokens, heads, head_dim, elem_bytes(dtype), n_seg, with_parts);
+  if (!with_parts) ncu = 0;  // no partial-result slots: never split
   hipError_t e;
   int rc;
   if (ev && (e = hipEventRecord(ev[0], s)) != hipSuccess) return hip_fail(e, "hipEventRecord");
@@ -850,7 +858,7 @@ int mf_get_device_error(hipStream_t stream) {
       return hip_fail(e, "hipMemcpy(projection workspace header)");
     flags |= qf;
   }
-  for (char* w : {st.ws, st.bws}) {
+  for (char* w : {st.ws, st.bws, st.scratch}) {
     if (!w) continue;
     mf::WsHeader hdr;
     if ((e = hipMemcpy(&hdr, w, sizeof(hdr), hipMemcpyDeviceToHost)) != hipSuccess)
@@ -870,6 +878,79 @@ int mf_get_workspace_error(const void* workspace, hipStream_t stream) {
     return hip_fail(e, "hipMemcpy(workspace header)");
   if (hdr.flag) return fail(MF_ERR_METADATA, "device check failed (flags 0x%x)", unsigned(hdr.flag));
   return MF_OK;
+}
+
+}  // extern "C"
+
+// ---------------------------------------------------------------------------
+// Allocation-free forward for callers that cannot allocate device memory.
+// The workspace is a file-scope static device array (every device the library
+// runs on holds its own copy, allocated when this module is first used there
+// and kept until the process ends); so are the 2D cos/sin tables. Host code
+// never passes the arrays' names to a kernel (on the host they are stand-ins,
+// not device addresses): the device addresses come from hipGetSymbolAddress,
+// once per device, and only those are used.
+namespace {
+
+constexpr size_t NOALLOC_BYTES = size_t(MF_NOALLOC_SCRATCH_BYTES);
+constexpr int NOALLOC_TABLE_128 = mf::ROPE_PMAX * (128 / 4);  // float2 entries of the d = 128 table
+constexpr int NOALLOC_TABLE_64 = mf::ROPE_PMAX * (64 / 4);
+static __device__ __align__(256) char scratch[NOALLOC_BYTES];
+static __device__ __align__(256) float2 scratch_tables[NOALLOC_TABLE_128 + NOALLOC_TABLE_64];
+
+// First use on a device (caller holds g_mu, the device is current): the
+// arrays' device addresses, and the tables (the same host-computed values as
+// mf_attn_packed's) copied in. The scratch needs no clearing: every call's
+// metadata kernel rewrites the header, offsets and tile table, and the
+// prologue rewrites every row of the K~ / V~ (and Q~) buffers it uses before
+// the attention kernel reads them.
+int noalloc_setup(DeviceState& st) {
+  if (st.scratch) return MF_OK;
+  void* p = nullptr;
+  hipError_t e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+  if (e != hipSuccess) return hip_fail(e, "hipGetSymbolAddress(scratch)");
+  void* t = nullptr;
+  e = hipGetSymbolAddress(&t, HIP_SYMBOL(scratch_tables));
+  if (e != hipSuccess) return hip_fail(e, "hipGetSymbolAddress(scratch_tables)");
+  std::vector<float2> host = table2d_host(128, MF_ROPE_THETA);
+  const std::vector<float2> t64 = table2d_host(64, MF_ROPE_THETA);
+  host.insert(host.end(), t64.begin(), t64.end());
+  e = hipMemcpy(t, host.data(), host.size() * sizeof(float2), hipMemcpyHostToDevice);
+  if (e != hipSuccess) return hip_fail(e, "hipMemcpy(scratch tables)");
+  st.scratch_tables = static_cast<const float2*>(t);
+  st.scratch = static_cast<char*>(p);
+  return MF_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int mf_attn_packed_noalloc(const void* q, const void* k, const void* v, const int32_t* cu_seqlens,
+                           const int32_t* grid_hw, const int32_t* text_len, void* out, int32_t n_seg,
+                           int64_t total_tokens, int32_t heads, int32_t head_dim, int32_t dtype,
+                           hipStream_t stream) {
+  int rc = check_attn_args(q, k, v, cu_seqlens, grid_hw, text_len, out, n_seg, total_tokens, heads, head_dim,
+                           dtype);
+  if (rc) return rc;
+  const mf::WsLayout l = mf::ws_layout(total_tokens, heads, head_dim, elem_bytes(dtype), n_seg, false);
+  if (size_t(l.total) > NOALLOC_BYTES)
+    return fail(MF_ERR_UNSUPPORTED,
+                "mf_attn_packed_noalloc: these sizes need %lld bytes of scratch, the fixed maximum is %zu",
+                (long long)l.total, NOALLOC_BYTES);
+  int dev;
+  if ((rc = current_device(&dev))) return rc;
+  char* ws;
+  const float2* cs;
+  {
+    std::lock_guard<std::mutex> lock(g_mu);
+    DeviceState& st = g_dev[dev];
+    if ((rc = noalloc_setup(st))) return rc;
+    ws = st.scratch;
+    cs = st.scratch_tables + (head_dim == 128 ? 0 : NOALLOC_TABLE_128);
+  }
+  return run_attn(q, k, v, cu_seqlens, grid_hw, text_len, out, n_seg, total_tokens, heads, head_dim, dtype, ws, cs,
+                  0, stream, nullptr, nullptr, nullptr, nullptr, false);
 }
 
 }  // extern "C"

@@ -134,8 +134,10 @@ struct WsLayout {
   int64_t n_tiles;  // capacity of the tile table
 };
 
+// with_parts = false leaves out the partial-result slots of split units (the
+// caller then never lets the attention kernel split).
 __host__ __device__ inline WsLayout ws_layout(int64_t tokens, int32_t heads, int32_t head_dim,
-                                              int32_t elem_bytes, int32_t n_seg) {
+                                              int32_t elem_bytes, int32_t n_seg, bool with_parts = true) {
   WsLayout l;
   int64_t o = 256;
   l.off_len = o;   o += round_up(int64_t(n_seg) * 4, 256);
@@ -150,7 +152,7 @@ __host__ __device__ inline WsLayout ws_layout(int64_t tokens, int32_t heads, int
   l.off_v = o; o += buf;
   // bf16 path: PART_SLOTS partial results of split units, each QTILE rows of
   // head_dim fp32 accumulators followed by QTILE reference maxima and QTILE row sums.
-  l.off_part = o; o += elem_bytes == 2 ? int64_t(PART_SLOTS) * QTILE * (head_dim + 2) * 4 : 0;
+  l.off_part = o; o += elem_bytes == 2 && with_parts ? int64_t(PART_SLOTS) * QTILE * (head_dim + 2) * 4 : 0;
   l.total = o;
   return l;
 }
