@@ -17,6 +17,12 @@ Readings taken where the pages are silent:
 * positions are zero-based integers with no centring or rescaling;
 * prompt tokens carry position (0, 0).
 
+Joint layout (tech report, NR-MMDiT section): text and visual tokens go
+through their own modality-specific layers, and their per-token features are
+concatenated sample by sample for the joint attention; both streams are packed
+without padding. ``pack_joint`` builds the joint packed rows from the two
+packed streams and ``unpack_joint`` splits joint rows back into them.
+
 Editing samples (tech report, NR-MMDiT editing paragraph): the sequence is
 the condition tau, then the latents of the source image(s), then the noisy
 target latents, and every visual token has a 3D position (h, w, f) with f the
@@ -105,3 +111,48 @@ def token_positions_3d(grid_hw, text_len, frames):
         pos[a : a + n_img * h * w, 2] = p // (h * w)
         start += int(lengths[i])
     return pos, seg
+
+
+def pack_joint(text_stream, image_stream, grid_hw, text_len, frames=None):
+    """Joint packed rows from the two packed modality streams.
+
+    ``text_stream`` [sum T_i, ...] holds every sample's prompt rows back to back
+    and ``image_stream`` [sum f_i h_i w_i, ...] every sample's image rows (grid
+    row-major, images of an edit one after another). Sample i of the result is
+    its T_i prompt rows, then its f_i h_i w_i image rows, at cu_seqlens[i].
+    """
+    lengths = segment_lengths(grid_hw, text_len, frames)
+    t = np.asarray(text_len, dtype=np.int64).reshape(-1)
+    text_stream = np.asarray(text_stream)
+    image_stream = np.asarray(image_stream)
+    if text_stream.shape[0] != t.sum() or image_stream.shape[0] != (lengths - t).sum():
+        raise ValueError("stream lengths disagree with the metadata")
+    if text_stream.shape[1:] != image_stream.shape[1:]:
+        raise ValueError("the two streams must have the same row shape")
+    out = np.empty((int(lengths.sum()),) + text_stream.shape[1:], dtype=text_stream.dtype)
+    start = ts = im = 0
+    for i in range(lengths.shape[0]):
+        n_text, n_img = int(t[i]), int(lengths[i] - t[i])
+        out[start : start + n_text] = text_stream[ts : ts + n_text]
+        out[start + n_text : start + n_text + n_img] = image_stream[im : im + n_img]
+        start += n_text + n_img
+        ts += n_text
+        im += n_img
+    return out
+
+
+def unpack_joint(joint, grid_hw, text_len, frames=None):
+    """Inverse of ``pack_joint``: (text_stream, image_stream) from joint rows."""
+    lengths = segment_lengths(grid_hw, text_len, frames)
+    t = np.asarray(text_len, dtype=np.int64).reshape(-1)
+    joint = np.asarray(joint)
+    if joint.shape[0] != lengths.sum():
+        raise ValueError("joint length disagrees with the metadata")
+    text_rows, image_rows = [], []
+    start = 0
+    for i in range(lengths.shape[0]):
+        n_text = int(t[i])
+        text_rows.append(joint[start : start + n_text])
+        image_rows.append(joint[start + n_text : start + int(lengths[i])])
+        start += int(lengths[i])
+    return np.concatenate(text_rows, axis=0), np.concatenate(image_rows, axis=0)

@@ -25,6 +25,77 @@ def _golden(name):
 
 # ---------------------------------------------------------------- packing
 
+def test_joint_pack_hand_example():
+    """Labelled rows through the joint layout, worked by hand (tests/golden)."""
+    g = _golden("joint_pack_small.json")
+    ts = np.array(g["text_stream"]).reshape(-1, 1)
+    im = np.array(g["image_stream"]).reshape(-1, 1)
+    joint = packing.pack_joint(ts, im, g["grid_hw"], g["text_len"])
+    assert joint[:, 0].tolist() == g["joint"]
+    t2, i2 = packing.unpack_joint(np.array(g["joint"]).reshape(-1, 1), g["grid_hw"], g["text_len"])
+    assert t2[:, 0].tolist() == g["text_stream"] and i2[:, 0].tolist() == g["image_stream"]
+
+
+@pytest.mark.parametrize("seed", [0, 1, 2])
+def test_joint_pack_agrees_with_token_positions(seed):
+    """Every joint row comes from the stream its position says: rows at a
+    sample's prompt positions (u < T_i) from the text stream in order, and the
+    image row p of sample i (image stream order) at grid position (p // w, p % w)
+    of that sample. Rows are labelled with their stream index, so a swapped
+    text/image order, an off-by-one offset or a transposed grid fails."""
+    rng = np.random.default_rng(seed)
+    n = int(rng.integers(1, 9))
+    grid = rng.integers(1, 7, size=(n, 2))
+    text = rng.integers(0, 5, size=n)
+    n_text, n_img = int(text.sum()), int((grid[:, 0] * grid[:, 1]).sum())
+    ts = np.arange(n_text).reshape(-1, 1) + 10_000
+    im = np.arange(n_img).reshape(-1, 1) + 20_000
+    joint = packing.pack_joint(ts, im, grid, text)[:, 0]
+    pos, seg = packing.token_positions(grid, text)
+    cu = packing.cu_seqlens(grid, text)
+    t_seen = i_seen = 0
+    for i in range(n):
+        h, w = int(grid[i, 0]), int(grid[i, 1])
+        for u in range(int(cu[i + 1] - cu[i])):
+            r = int(cu[i]) + u
+            assert seg[r] == i
+            if u < text[i]:
+                assert joint[r] == 10_000 + t_seen
+                t_seen += 1
+            else:
+                p = joint[r] - 20_000
+                assert p == i_seen
+                local = p - int((grid[:i, 0] * grid[:i, 1]).sum())
+                assert (pos[r, 0], pos[r, 1]) == (local // w, local % w)
+                i_seen += 1
+    assert (t_seen, i_seen) == (n_text, n_img)
+
+
+@pytest.mark.parametrize("seed", [3, 4])
+def test_joint_pack_round_trip_and_permutation(seed):
+    """unpack(pack(x)) = x for 2D and editing (frames) samples; pack is a
+    permutation of the concatenated streams (every row once); an empty prompt
+    stream and an all-prompt-free batch work."""
+    rng = np.random.default_rng(seed)
+    n = int(rng.integers(1, 7))
+    grid = rng.integers(1, 6, size=(n, 2))
+    text = rng.integers(0, 4, size=n)
+    frames = rng.integers(1, 4, size=n)
+    for fr in (None, frames):
+        n_img = int(((1 if fr is None else fr) * grid[:, 0] * grid[:, 1]).sum())
+        ts = rng.standard_normal((int(text.sum()), 2, 3))
+        im = rng.standard_normal((n_img, 2, 3))
+        joint = packing.pack_joint(ts, im, grid, text, fr)
+        assert joint.shape[0] == packing.cu_seqlens(grid, text, fr)[-1]
+        t2, i2 = packing.unpack_joint(joint, grid, text, fr)
+        assert np.array_equal(t2, ts) and np.array_equal(i2, im)
+        rows = np.concatenate([ts, im]).reshape(-1, 6)
+        assert sorted(map(tuple, joint.reshape(-1, 6))) == sorted(map(tuple, rows))
+    zero = np.zeros(n, dtype=np.int64)
+    im = rng.standard_normal((int((grid[:, 0] * grid[:, 1]).sum()), 4))
+    assert np.array_equal(packing.pack_joint(np.zeros((0, 4)), im, grid, zero), im)
+
+
 def test_packing_hand_example():
     g = _golden("packing_small.json")
     cu = packing.cu_seqlens(g["grid_hw"], g["text_len"])
