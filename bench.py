@@ -74,6 +74,7 @@ class HipEvents:
         self.hip.hipEventCreate.argtypes = [ctypes.POINTER(ctypes.c_void_p)]
         self.hip.hipEventElapsedTime.argtypes = [ctypes.POINTER(ctypes.c_float), ctypes.c_void_p, ctypes.c_void_p]
         self.hip.hipEventDestroy.argtypes = [ctypes.c_void_p]
+        self.hip.hipEventRecord.argtypes = [ctypes.c_void_p, ctypes.c_void_p]
         self.ev = []
         for _ in range(n):
             e = ctypes.c_void_p()
@@ -366,6 +367,65 @@ def backward_bench(w, q, k, v, cu, grid, text, steps: int, warmup: int, frames=N
     }
 
 
+def pack_bench(w, cu, grid, text, steps: int, warmup: int, frames=None):
+    """Joint-layout pack of q, k, v (one launch, from the text and image streams)
+    and unpack of the attention output back to the two streams, on the same
+    batch. GB/s count the algorithmic bytes (every row read once and written
+    once); each call is timed by HIP events, back to back (warm) and with the
+    256 MB MALL flushed before it by writing a 512 MB buffer (cold)."""
+    import torch
+    from text_image_diffusion_varlen_amd import binding
+
+    Tt = int(w.text_len.sum())
+    shape = (w.heads, w.head_dim)
+    dt = torch.bfloat16 if w.dtype == "bf16" else torch.float32
+    gen = torch.Generator(device="cuda").manual_seed(3)
+    mk = lambda rows: torch.randn((rows,) + shape, generator=gen, device="cuda").to(dt)  # noqa: E731
+    ts = [mk(Tt) for _ in range(3)]
+    im = [mk(w.tokens - Tt) for _ in range(3)]
+    joint = [torch.empty((w.tokens,) + shape, dtype=dt, device="cuda") for _ in range(3)]
+    o_t, o_i = [mk(Tt)], [mk(w.tokens - Tt)]
+    elem = 2 if w.dtype == "bf16" else 4
+    row = w.heads * w.head_dim * elem
+    calls = {
+        "pack_qkv": (lambda: binding.pack_joint(ts, im, cu, grid, text, frames=frames, out=joint),
+                     2 * 3 * w.tokens * row),
+        "unpack_o": (lambda: binding.unpack_joint(joint[:1], Tt, cu, grid, text, frames=frames, out=(o_t, o_i)),
+                     2 * w.tokens * row),
+    }
+    ev = HipEvents(2 * steps)
+    flush = torch.empty(512 << 20, dtype=torch.uint8, device="cuda")
+    res = {}
+    for name, (fn, nbytes) in calls.items():
+        for _ in range(warmup):
+            fn()
+        times = {}
+        for mode in ("warm", "cold"):
+            torch.cuda.synchronize()
+            stream = torch.cuda.current_stream().cuda_stream
+            for st in range(steps):
+                if mode == "cold":
+                    flush.fill_(st & 255)
+                ev.hip.hipEventRecord(ev.ev[2 * st], stream)
+                fn()
+                ev.hip.hipEventRecord(ev.ev[2 * st + 1], stream)
+            torch.cuda.synchronize()
+            times[mode] = float(np.median([ev.elapsed_ms(2 * st, 2 * st + 1) for st in range(steps)]))
+        res[name] = {
+            "us": round(times["warm"] * 1e3, 2),
+            "gbps": round(nbytes / (times["warm"] / 1e3) / 1e9, 1),
+            "us_cold_mall": round(times["cold"] * 1e3, 2),
+            "gbps_cold_mall": round(nbytes / (times["cold"] / 1e3) / 1e9, 1),
+            "frac_hbm_cold_mall": round(nbytes / (times["cold"] / 1e3) / HBM_PEAK, 4),
+            "algorithmic_bytes": nbytes,
+        }
+    if binding.get_device_error() != binding.MF_OK:
+        raise RuntimeError(binding.last_error())
+    ev.close()
+    del flush
+    return res
+
+
 def qkv_bench(w, grid, text, cu, steps: int, warmup: int, frames=None):
     """Modality-specific RMSNorm + packed QKV projection feeding the same batch:
     hidden = heads * head_dim (3072 for 24 x 128), synthetic weights. TFLOP/s
@@ -563,6 +623,7 @@ def main():
     ap.add_argument("--no-sampler", action="store_true", help="skip the packed CFG Euler-step measurement")
     ap.add_argument("--no-backward", action="store_true", help="skip the packed backward measurement")
     ap.add_argument("--no-qkv", action="store_true", help="skip the RMSNorm + QKV projection measurement")
+    ap.add_argument("--no-pack", action="store_true", help="skip the joint-layout pack / unpack measurement")
     ap.add_argument("--no-mixed", action="store_true",
                     help="with the default 1024sq workload, skip the second (mixed-aspect) forward record")
     ap.add_argument("--calibrate-copy", action="store_true",
@@ -618,6 +679,8 @@ def main():
     if w.dtype == "bf16" and not args.no_backward:
         result["backward"] = backward_bench(w, q, k, v, cu, grid, text, args.steps, args.warmup,
                                             frames if edit else None)
+    if not args.no_pack:
+        result["joint_pack"] = pack_bench(w, cu, grid, text, args.steps, args.warmup, frames)
     if w.dtype == "bf16" and not args.no_qkv:
         result["qkv_rmsnorm"] = qkv_bench(w, grid, text, cu, args.steps, args.warmup, frames if edit else None)
     if not args.no_sampler:

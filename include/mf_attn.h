@@ -291,6 +291,40 @@ int mf_build_metadata(int32_t n_seg, const int32_t* grid_hw, const int32_t* text
                       int64_t total_tokens, hipStream_t stream);
 
 /*
+ * Joint-layout pack and unpack. Source: Mage-Flow tech report, NR-MMDiT
+ * section: text and visual tokens pass through modality-specific layers and
+ * are concatenated, sample by sample, for the joint attention; prompts and
+ * images are each packed without padding. The text stream holds every
+ * sample's prompt rows back to back (text_tokens = sum of text_len rows), the
+ * image stream every sample's image rows (grid row-major; the frames images
+ * of an edit one after another; total_tokens - text_tokens rows), and the
+ * joint tensor sample i's prompt rows then its image rows at cu_seqlens[i]:
+ *   joint[cu[i] + u] = u < T_i ? text[tcu[i] + u] : image[cu[i] - tcu[i] + u - T_i],
+ * tcu[i] = T_0 + ... + T_{i-1}. mf_unpack_joint is the inverse map (e.g. the
+ * attention output back to the two streams). Pure copies, bit-exact.
+ *   n_tensors   1 .. 4 tensors moved by one launch (e.g. q, k, v)
+ *   text, image, joint  host arrays of n_tensors device pointers; each tensor
+ *               [rows][heads][head_dim] contiguous, dtype, 16-byte aligned; a
+ *               stream with no rows may be NULL
+ *   cu_seqlens, grid_hw, text_len  device int32 as for mf_attn_packed;
+ *               frames device int32 [n_seg] or NULL (one image per sample)
+ * The outputs must not overlap each other, the inputs or the metadata. The
+ * metadata is checked on the device (cu_seqlens against the prefix sums of
+ * text_len + frames * h * w, sides in range, cu_seqlens[n_seg] ==
+ * total_tokens, the prompts adding up to text_tokens); on a mismatch nothing
+ * is written and mf_get_device_error() reports MF_ERR_METADATA. One kernel
+ * launch, no library workspace (only the device's status word).
+ */
+int mf_pack_joint(int32_t n_tensors, const void* const* text, const void* const* image, void* const* joint,
+                  const int32_t* cu_seqlens, const int32_t* grid_hw, const int32_t* text_len, const int32_t* frames,
+                  int32_t n_seg, int64_t total_tokens, int64_t text_tokens, int32_t heads, int32_t head_dim,
+                  int32_t dtype, hipStream_t stream);
+int mf_unpack_joint(int32_t n_tensors, const void* const* joint, void* const* text, void* const* image,
+                    const int32_t* cu_seqlens, const int32_t* grid_hw, const int32_t* text_len, const int32_t* frames,
+                    int32_t n_seg, int64_t total_tokens, int64_t text_tokens, int32_t heads, int32_t head_dim,
+                    int32_t dtype, hipStream_t stream);
+
+/*
  * 2D RoPE alone: x_out = R(pos) x_in, per token and head.
  *   x_in, x_out device [total_tokens][heads][head_dim], dtype (may be the same buffer)
  *   pos         device int32 [total_tokens][2], each in [0, 512)

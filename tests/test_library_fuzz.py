@@ -60,6 +60,19 @@ def _draw(rng, t, position):
     raise AssertionError(f"no generator for {t}")
 
 
+# Arguments that are host arrays of device pointers (position in the argument list).
+HOST_ARRAYS = {"mf_pack_joint": {1, 2, 3}, "mf_unpack_joint": {1, 2, 3}}
+
+
+def _host_array(rng, position):
+    """A host array of 4 device pointers: plausible (disjoint, aligned) entries,
+    each replaced with probability 0.15 by an edge address; or a null array."""
+    if rng.random() < 0.1:
+        return None
+    entries = [0x40000000 * (8 * position + i + 1) if rng.random() < 0.85 else _pointer(rng) for i in range(4)]
+    return (ctypes.c_void_p * 4)(*entries)
+
+
 def _functions():
     lib = binding.lib()
     return [(name, getattr(lib, name)) for name in binding.header_functions()]
@@ -70,7 +83,8 @@ def test_entry_point_returns_documented_codes(name):
     fn = dict(_functions())[name]
     rng = random.Random(zlib.crc32(name.encode()))
     for _ in range(600):
-        args = [_draw(rng, t, i) for i, t in enumerate(fn.argtypes)]
+        args = [_host_array(rng, i) if i in HOST_ARRAYS.get(name, ()) else _draw(rng, t, i)
+                for i, t in enumerate(fn.argtypes)]
         r = fn(*args)
         if fn.restype is ctypes.c_size_t:
             assert 0 <= r < (1 << 50), (name, args, r)

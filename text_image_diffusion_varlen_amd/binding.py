@@ -61,6 +61,8 @@ def _declare(lib):
         "mf_qkv_fold_weights": ([P, P, P, P, I32, I32, I32, P, P], ctypes.c_int),
         "mf_qkv_rmsnorm": ([P] * 6 + [I32, I64, I32, I32, I32, F, P, P, P, P], ctypes.c_int),
         "mf_qkv_rmsnorm_profiled": ([P] * 6 + [I32, I64, I32, I32, I32, F, P, P, P, P, P], ctypes.c_int),
+        "mf_pack_joint": ([I32, P, P, P, P, P, P, P, I32, I64, I64, I32, I32, I32, P], ctypes.c_int),
+        "mf_unpack_joint": ([I32, P, P, P, P, P, P, P, I32, I64, I64, I32, I32, I32, P], ctypes.c_int),
         "mf_get_device_error": ([P], ctypes.c_int),
         "mf_get_workspace_error": ([P, P], ctypes.c_int),
     }
@@ -419,6 +421,68 @@ def qkv_rmsnorm(x, w_folded, cu_seqlens, grid_hw, text_len, heads: int, head_dim
                                              _ptr(text_len), fr, n, T, hidden, heads, head_dim, float(eps), _ptr(q),
                                              _ptr(k), _ptr(v), ctypes.cast(arr, ctypes.c_void_p), _stream(stream)))
     return q, k, v
+
+
+def _ptr_array(ts):
+    return (ctypes.c_void_p * len(ts))(*[t.data_ptr() if t is not None and t.numel() > 0 else None for t in ts])
+
+
+def _stream_args(text, image, joint, grid_hw, text_len, cu_seqlens, frames):
+    n = len(joint)
+    if not 1 <= n <= 4 or len(text) != n or len(image) != n:
+        raise ValueError("1 to 4 tensors, the same number of text, image and joint tensors")
+    ref = joint[0]
+    _need(ref, "joint", ndim=3)
+    if ref.dtype not in _DTYPES:
+        raise ValueError("tensors must be bfloat16 or float32")
+    T, H, D = ref.shape
+    Tt = text[0].shape[0]
+    for name, group, rows in (("joint", joint, T), ("text", text, Tt), ("image", image, T - Tt)):
+        for t in group:
+            _need(t, name, ref.dtype, 3)
+            if t.shape != (rows, H, D):
+                raise ValueError(f"{name} tensors must be [{rows}, {H}, {D}]")
+    _need(cu_seqlens, "cu_seqlens", torch.int32, 1)
+    _need(grid_hw, "grid_hw", torch.int32, 2)
+    _need(text_len, "text_len", torch.int32, 1)
+    if frames is not None:
+        _need(frames, "frames", torch.int32, 1)
+    return grid_hw.shape[0], T, Tt, H, D, ref.dtype
+
+
+def pack_joint(text, image, cu_seqlens, grid_hw, text_len, frames=None, out=None, stream=None):
+    """Joint packed rows from the text and image streams (mf_pack_joint).
+
+    text: tensors [sum T_i, H, d]; image: tensors [T - sum T_i, H, d] (one per
+    tensor moved, up to 4, e.g. (q, k, v)). Returns the joint tensors [T, H, d]."""
+    text, image = list(text), list(image)
+    T = int(text[0].shape[0] + image[0].shape[0])
+    if out is None:
+        out = [torch.empty((T,) + tuple(text[0].shape[1:]), dtype=text[0].dtype, device=text[0].device)
+               for _ in text]
+    out = list(out)
+    n, T, Tt, H, D, dt = _stream_args(text, image, out, grid_hw, text_len, cu_seqlens, frames)
+    _check(lib().mf_pack_joint(len(out), _ptr_array(text), _ptr_array(image), _ptr_array(out), _ptr(cu_seqlens),
+                               _ptr(grid_hw), _ptr(text_len), _ptr(frames) if frames is not None else None, n, T, Tt,
+                               H, D, _DTYPES[dt], _stream(stream)))
+    return out
+
+
+def unpack_joint(joint, text_tokens: int, cu_seqlens, grid_hw, text_len, frames=None, out=None, stream=None):
+    """Text and image streams from joint rows (mf_unpack_joint). Returns (text list, image list)."""
+    joint = list(joint)
+    T = int(joint[0].shape[0])
+    if out is None:
+        mk = lambda rows: [torch.empty((rows,) + tuple(j.shape[1:]), dtype=j.dtype, device=j.device)  # noqa: E731
+                           for j in joint]
+        out = (mk(text_tokens), mk(T - text_tokens))
+    text, image = list(out[0]), list(out[1])
+    n, T, Tt, H, D, dt = _stream_args(text, image, joint, grid_hw, text_len, cu_seqlens, frames)
+    _check(lib().mf_unpack_joint(len(joint), _ptr_array(joint), _ptr_array(text), _ptr_array(image),
+                                 _ptr(cu_seqlens), _ptr(grid_hw), _ptr(text_len),
+                                 _ptr(frames) if frames is not None else None, n, T, Tt, H, D, _DTYPES[dt],
+                                 _stream(stream)))
+    return text, image
 
 
 def get_device_error(stream=None) -> int:

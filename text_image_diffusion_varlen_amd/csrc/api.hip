@@ -58,6 +58,10 @@ hipError_t launch_qkv(const void* x, const void* w, const int32_t* cu, const int
                       const int32_t* frames, int32_t n_seg, int64_t tokens, int32_t hidden, int32_t hd, float eps,
                       char* ws, void* q, void* k, void* v, int32_t ncu, hipStream_t s, hipEvent_t const* ev);
 size_t qkv_workspace_bytes(int64_t tokens, int32_t n_seg, int32_t hidden);
+hipError_t launch_pack(bool unpack, int32_t n_tensors, const void* const* src0, const void* const* src1,
+                       void* const* dst0, void* const* dst1, const int32_t* cu, const int32_t* grid_hw,
+                       const int32_t* text_len, const int32_t* frames, int32_t n_seg, int64_t tokens,
+                       int64_t text_tokens, int64_t row_bytes, int32_t ncu, int32_t* status, hipStream_t s);
 hipError_t launch_cfg_euler(float* z, const void* v, const int32_t* cu, const int32_t* grid_hw,
                             const int32_t* text_len, int32_t n_seg, int64_t total_tokens,
                             const int32_t* cond_seg, const int32_t* uncond_seg, int32_t n_img,
@@ -835,6 +839,110 @@ int mf_rf_cfg_euler_step(float* z, const void* v, const int32_t* cu_seqlens, con
   }
   if (e != hipSuccess) return hip_fail(e, "cfg_euler_kernel launch");
   return debug_stage(stream, "cfg_euler_kernel", status, true);
+}
+
+}  // extern "C"
+
+namespace {
+
+// Joint-layout pack (unpack == false: text/image streams -> joint rows) or
+// unpack (joint rows -> streams) of n_tensors tensors in one launch.
+int pack_impl(bool unpack, int32_t n_tensors, const void* const* a0, const void* const* a1, void* const* b0,
+              void* const* b1, const int32_t* cu_seqlens, const int32_t* grid_hw, const int32_t* text_len,
+              const int32_t* frames, int32_t n_seg, int64_t total_tokens, int64_t text_tokens, int32_t heads,
+              int32_t head_dim, int32_t dtype, hipStream_t stream) {
+  if (n_tensors < 1 || n_tensors > 4) return fail(MF_ERR_INVALID_ARG, "n_tensors=%d outside [1, 4]", n_tensors);
+  if (!a0 || !b0 || (unpack ? !b1 : !a1) || !cu_seqlens || !grid_hw || !text_len)
+    return fail(MF_ERR_INVALID_ARG, "null pointer argument");
+  if (n_seg < 1 || n_seg > MF_MAX_SEGMENTS)
+    return fail(MF_ERR_INVALID_ARG, "n_seg=%d outside [1, %d]", n_seg, MF_MAX_SEGMENTS);
+  if (total_tokens < 1 || total_tokens >= (int64_t(1) << 31))
+    return fail(MF_ERR_INVALID_ARG, "total_tokens=%lld outside [1, 2^31)", (long long)total_tokens);
+  if (text_tokens < 0 || text_tokens > total_tokens)
+    return fail(MF_ERR_INVALID_ARG, "text_tokens=%lld outside [0, total_tokens]", (long long)text_tokens);
+  if (heads < 1 || heads > 256) return fail(MF_ERR_INVALID_ARG, "heads=%d outside [1, 256]", heads);
+  if (head_dim != 64 && head_dim != 128)
+    return fail(MF_ERR_UNSUPPORTED, "head_dim=%d (supported: 64, 128)", head_dim);
+  const int eb = elem_bytes(dtype);
+  if (!eb) return fail(MF_ERR_UNSUPPORTED, "dtype=%d (supported: MF_BF16, MF_F32)", dtype);
+  const int64_t row = int64_t(heads) * head_dim * eb;
+  const int64_t image_tokens = total_tokens - text_tokens;
+  // The joint tensors and the two streams of every tensor, with their sizes.
+  const void* joint[4];
+  const void* txt[4];
+  const void* img[4];
+  for (int i = 0; i < n_tensors; ++i) {
+    joint[i] = unpack ? a0[i] : b0[i];
+    txt[i] = unpack ? b0[i] : a0[i];
+    img[i] = unpack ? b1[i] : a1[i];
+    if (!joint[i] || (text_tokens > 0 && !txt[i]) || (image_tokens > 0 && !img[i]))
+      return fail(MF_ERR_INVALID_ARG, "null tensor pointer (tensor %d)", i);
+    if ((reinterpret_cast<uintptr_t>(joint[i]) | reinterpret_cast<uintptr_t>(txt[i]) |
+         reinterpret_cast<uintptr_t>(img[i])) & 15)
+      return fail(MF_ERR_INVALID_ARG, "tensor %d is not 16-byte aligned", i);
+  }
+  // Destinations must not overlap each other, any source or the metadata.
+  std::vector<std::pair<const void*, size_t>> dst, src;
+  for (int i = 0; i < n_tensors; ++i) {
+    auto& d = unpack ? dst : src;
+    auto& j = unpack ? src : dst;
+    j.emplace_back(joint[i], size_t(total_tokens * row));
+    if (text_tokens > 0) d.emplace_back(txt[i], size_t(text_tokens * row));
+    if (image_tokens > 0) d.emplace_back(img[i], size_t(image_tokens * row));
+  }
+  src.emplace_back(cu_seqlens, size_t(n_seg + 1) * 4);
+  src.emplace_back(grid_hw, size_t(n_seg) * 8);
+  src.emplace_back(text_len, size_t(n_seg) * 4);
+  if (frames) src.emplace_back(frames, size_t(n_seg) * 4);
+  for (size_t i = 0; i < dst.size(); ++i) {
+    for (const auto& x : src)
+      if (overlaps(dst[i].first, dst[i].second, x.first, x.second))
+        return fail(MF_ERR_INVALID_ARG, "an output overlaps an input or the metadata");
+    for (size_t j = i + 1; j < dst.size(); ++j)
+      if (overlaps(dst[i].first, dst[i].second, dst[j].first, dst[j].second))
+        return fail(MF_ERR_INVALID_ARG, "outputs overlap");
+  }
+  int dev, rc;
+  if ((rc = current_device(&dev))) return rc;
+  int32_t* status;
+  int32_t ncu = 0;
+  {
+    std::lock_guard<std::mutex> lock(g_mu);
+    DeviceState& st = g_dev[dev];
+    if ((rc = ensure_status(st))) return rc;
+    if ((rc = ensure_cus(st, dev, &ncu))) return rc;
+    status = st.status;
+  }
+  hipError_t e;
+  {
+    Range r(unpack ? "mf unpack_joint" : "mf pack_joint");
+    e = mf::launch_pack(unpack, n_tensors, a0, a1, b0, b1, cu_seqlens, grid_hw, text_len, frames, n_seg,
+                        total_tokens, text_tokens, row, ncu, status, stream);
+  }
+  if (e != hipSuccess) return hip_fail(e, "pack_kernel launch");
+  return debug_stage(stream, unpack ? "unpack_joint" : "pack_joint", status, true);
+}
+
+}  // namespace
+
+extern "C" {
+
+int mf_pack_joint(int32_t n_tensors, const void* const* text, const void* const* image, void* const* joint,
+                  const int32_t* cu_seqlens, const int32_t* grid_hw, const int32_t* text_len, const int32_t* frames,
+                  int32_t n_seg, int64_t total_tokens, int64_t text_tokens, int32_t heads, int32_t head_dim,
+                  int32_t dtype, hipStream_t stream) {
+  if (!text || !image || !joint) return fail(MF_ERR_INVALID_ARG, "null pointer argument");
+  return pack_impl(false, n_tensors, text, image, joint, nullptr, cu_seqlens, grid_hw, text_len, frames, n_seg,
+                   total_tokens, text_tokens, heads, head_dim, dtype, stream);
+}
+
+int mf_unpack_joint(int32_t n_tensors, const void* const* joint, void* const* text, void* const* image,
+                    const int32_t* cu_seqlens, const int32_t* grid_hw, const int32_t* text_len, const int32_t* frames,
+                    int32_t n_seg, int64_t total_tokens, int64_t text_tokens, int32_t heads, int32_t head_dim,
+                    int32_t dtype, hipStream_t stream) {
+  if (!text || !image || !joint) return fail(MF_ERR_INVALID_ARG, "null pointer argument");
+  return pack_impl(true, n_tensors, joint, nullptr, text, image, cu_seqlens, grid_hw, text_len, frames, n_seg,
+                   total_tokens, text_tokens, heads, head_dim, dtype, stream);
 }
 
 int mf_get_device_error(hipStream_t stream) {
