@@ -30,7 +30,14 @@ constexpr int PACK_THREADS = 256;
 constexpr int PACK_WAVES = PACK_THREADS / 64;
 constexpr int PACK_MAX_TENSORS = 4;
 constexpr int PACK_PER_THREAD = MAX_SEGMENTS / PACK_THREADS;  // 16
-constexpr int PACK_CHUNKS = 8;  // 16-byte chunks per lane in flight: a row moves in pieces of 8 KB
+#ifndef MF_PACK_ROWS
+#define MF_PACK_ROWS 2
+#endif
+#ifndef MF_PACK_WG_PER_CU
+#define MF_PACK_WG_PER_CU 4
+#endif
+constexpr int PACK_CHUNKS = 8 * MF_PACK_ROWS;  // 16-byte chunks per lane in flight
+constexpr int PACK_ROWS = MF_PACK_ROWS;        // rows per wave and step when they fit in PACK_CHUNKS
 
 struct PackArgs {
   const char* src[PACK_MAX_TENSORS][2];  // pack: (text, image) stream of each tensor; unpack: (joint, -)
@@ -47,22 +54,26 @@ struct PackArgs {
   int32_t row_chunks;   // 16-byte chunks per row
 };
 
-struct PackShared {
-  int32_t cu[MAX_SEGMENTS + 1];
-  int32_t tcu[MAX_SEGMENTS + 1];
-  int32_t text[MAX_SEGMENTS];
-  int32_t part[PACK_THREADS];
-  int32_t bad;
-};
+// LDS image of the metadata, sized to the batch (dynamic shared memory):
+// part[PACK_THREADS], bad, cu[n + 1], tcu[n + 1], text[n].
+__host__ __device__ inline size_t pack_lds_bytes(int32_t n) { return size_t(PACK_THREADS + 1 + 3 * n + 2) * 4; }
+
+// Keeps the compiler from sinking the loads above it down to their stores
+// (which would leave one load in flight per wave).
+__device__ inline void loads_before_stores() { __builtin_amdgcn_sched_barrier(0); }
+
+typedef uint32_t chunk_t __attribute__((ext_vector_type(4)));  // one 16-byte chunk, held in 4 VGPRs
 
 // Copies one row of c16 16-byte chunks in pieces of 64 * PACK_CHUNKS chunks;
 // in a piece lane l moves chunks l, l + 64, ..., all loads before the stores.
-__device__ inline void copy_row(const uint4* __restrict__ s, uint4* __restrict__ d, int c16, int lane) {
+// Loads are unconditional (a lane past the row's end re-reads its last chunk)
+// so that they issue back to back; only the stores are masked.
+__device__ inline void copy_row(const chunk_t* __restrict__ s, chunk_t* __restrict__ d, int c16, int lane) {
   for (int base = 0; base < c16; base += 64 * PACK_CHUNKS) {
-    uint4 v[PACK_CHUNKS];
+    chunk_t v[PACK_CHUNKS];
 #pragma unroll
-    for (int i = 0; i < PACK_CHUNKS; ++i)
-      if (base + lane + 64 * i < c16) v[i] = s[base + lane + 64 * i];
+    for (int i = 0; i < PACK_CHUNKS; ++i) v[i] = s[min(base + lane + 64 * i, c16 - 1)];
+    loads_before_stores();
 #pragma unroll
     for (int i = 0; i < PACK_CHUNKS; ++i)
       if (base + lane + 64 * i < c16) d[base + lane + 64 * i] = v[i];
@@ -71,9 +82,17 @@ __device__ inline void copy_row(const uint4* __restrict__ s, uint4* __restrict__
 
 template <bool UNPACK>
 __global__ void __launch_bounds__(PACK_THREADS) pack_kernel(PackArgs a) {
-  __shared__ PackShared sh;
+  extern __shared__ int32_t lds[];
   const int t = threadIdx.x;
   const int32_t n = a.n_seg;
+  struct {
+    int32_t* part;
+    int32_t& bad;
+    int32_t* cu;
+    int32_t* tcu;
+    int32_t* text;
+  } sh{lds, lds[PACK_THREADS], lds + PACK_THREADS + 1, lds + PACK_THREADS + 1 + (n + 1),
+       lds + PACK_THREADS + 1 + 2 * (n + 1)};
   if (t == 0) sh.bad = 0;
   __syncthreads();
   // Metadata: lengths checked against cu_seqlens; prompt lengths scanned.
@@ -125,7 +144,8 @@ __global__ void __launch_bounds__(PACK_THREADS) pack_kernel(PackArgs a) {
   const int64_t rows = a.tokens * a.n_tensors;
   const int c16 = a.row_chunks;
   const int64_t row_bytes = int64_t(c16) * 16;
-  for (int64_t x = int64_t(blockIdx.x) * PACK_WAVES + wave; x < rows; x += int64_t(gridDim.x) * PACK_WAVES) {
+  // Source and destination of joint row x (tensor-major over all tensors).
+  auto row_ptrs = [&](int64_t x, const chunk_t*& src, chunk_t*& dst) {
     const int tensor = int(x / a.tokens);
     const int32_t r = int32_t(x - int64_t(tensor) * a.tokens);
     int32_t lo = 0, hi = n;  // sample: largest i with cu[i] <= r
@@ -136,16 +156,45 @@ __global__ void __launch_bounds__(PACK_THREADS) pack_kernel(PackArgs a) {
     const int32_t u = r - sh.cu[lo];
     const bool is_text = u < sh.text[lo];
     const int64_t srow = is_text ? int64_t(sh.tcu[lo]) + u : int64_t(sh.cu[lo]) - sh.tcu[lo] + (u - sh.text[lo]);
-    const char* src;
-    char* dst;
     if constexpr (UNPACK) {
-      src = a.src[tensor][0] + int64_t(r) * row_bytes;
-      dst = a.dst[tensor][is_text ? 0 : 1] + srow * row_bytes;
+      src = reinterpret_cast<const chunk_t*>(a.src[tensor][0] + int64_t(r) * row_bytes);
+      dst = reinterpret_cast<chunk_t*>(a.dst[tensor][is_text ? 0 : 1] + srow * row_bytes);
     } else {
-      src = a.src[tensor][is_text ? 0 : 1] + srow * row_bytes;
-      dst = a.dst[tensor][0] + int64_t(r) * row_bytes;
+      src = reinterpret_cast<const chunk_t*>(a.src[tensor][is_text ? 0 : 1] + srow * row_bytes);
+      dst = reinterpret_cast<chunk_t*>(a.dst[tensor][0] + int64_t(r) * row_bytes);
     }
-    copy_row(reinterpret_cast<const uint4*>(src), reinterpret_cast<uint4*>(dst), c16, lane);
+  };
+  // Each wave moves PACK_ROWS consecutive rows per step (their loads all in
+  // flight together when a row is at most 64 * PACK_CHUNKS / PACK_ROWS chunks).
+  const int64_t step = int64_t(gridDim.x) * PACK_WAVES * PACK_ROWS;
+  for (int64_t x0 = (int64_t(blockIdx.x) * PACK_WAVES + wave) * PACK_ROWS; x0 < rows; x0 += step) {
+    if (c16 * PACK_ROWS <= 64 * PACK_CHUNKS) {
+      constexpr int PER_ROW = PACK_CHUNKS / PACK_ROWS;
+      const chunk_t* src[PACK_ROWS];
+      chunk_t* dst[PACK_ROWS];
+      chunk_t v[PACK_ROWS][PER_ROW];
+#pragma unroll
+      for (int k = 0; k < PACK_ROWS; ++k) {
+        // rows past the end re-read the last row (their stores are masked)
+        row_ptrs(min(x0 + k, rows - 1), src[k], dst[k]);
+#pragma unroll
+        for (int i = 0; i < PER_ROW; ++i) v[k][i] = src[k][min(lane + 64 * i, c16 - 1)];
+      }
+      loads_before_stores();
+#pragma unroll
+      for (int k = 0; k < PACK_ROWS; ++k) {
+#pragma unroll
+        for (int i = 0; i < PER_ROW; ++i)
+          if (x0 + k < rows && lane + 64 * i < c16) dst[k][lane + 64 * i] = v[k][i];
+      }
+    } else {
+      for (int k = 0; k < PACK_ROWS && x0 + k < rows; ++k) {
+        const chunk_t* src;
+        chunk_t* dst;
+        row_ptrs(x0 + k, src, dst);
+        copy_row(src, dst, c16, lane);
+      }
+    }
   }
 }
 
@@ -171,12 +220,14 @@ hipError_t launch_pack(bool unpack, int32_t n_tensors, const void* const* src0, 
   a.tokens = tokens;
   a.text_tokens = text_tokens;
   a.row_chunks = int32_t(row_bytes / 16);
-  // Enough workgroups to keep every CU streaming, no more than one per 4 rows.
-  const int64_t want = ceil_div(tokens * n_tensors, PACK_WAVES);
-  const int64_t cap = int64_t(ncu > 0 ? ncu : 256) * 8;
+  // Persistent grid: a few workgroups per CU, each checking the metadata once
+  // and then streaming rows; no more workgroups than row pairs per wave.
+  const int64_t want = ceil_div(tokens * n_tensors, PACK_WAVES * PACK_ROWS);
+  const int64_t cap = MF_PACK_WG_PER_CU > 0 ? int64_t(ncu > 0 ? ncu : 256) * MF_PACK_WG_PER_CU : want;
   const dim3 grid(unsigned(want < cap ? want : cap));
-  if (unpack) hipLaunchKernelGGL(pack_kernel<true>, grid, dim3(PACK_THREADS), 0, s, a);
-  else hipLaunchKernelGGL(pack_kernel<false>, grid, dim3(PACK_THREADS), 0, s, a);
+  const size_t lds = pack_lds_bytes(n_seg);
+  if (unpack) hipLaunchKernelGGL(pack_kernel<true>, grid, dim3(PACK_THREADS), lds, s, a);
+  else hipLaunchKernelGGL(pack_kernel<false>, grid, dim3(PACK_THREADS), lds, s, a);
   return hipGetLastError();
 }
 
