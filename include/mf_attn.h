@@ -42,7 +42,8 @@
  *
  * Tensor layout: q, k, v and out are contiguous [T][heads][head_dim] with
  * elements of the given dtype (MF_BF16: bfloat16 bit patterns; MF_F32:
- * float). Metadata arrays are contiguous int32 in device memory.
+ * float), except in mf_attn_packed_strided, which takes strided descriptors.
+ * Metadata arrays are contiguous int32 in device memory.
  * Supported: head_dim in {64, 128}; 1 <= heads <= 256; 1 <= n_seg <= 4096;
  * 1 <= h, w <= 512; 0 <= text_len; T < 2^31 (and every buffer < 2^31 elements
  * per head).
@@ -73,6 +74,22 @@ typedef enum { MF_BF16 = 0, MF_F32 = 1 } mf_dtype;
 #define MF_MAX_SEGMENTS 4096
 #define MF_MAX_GRID_SIDE 512
 #define MF_ROPE_THETA 10000.0f
+
+/*
+ * Strided tensor descriptor (host struct, owned by the caller, read during
+ * the call only). Element (token t, head h, channel c) of the tensor is at
+ * data + (t * stride_token + h * stride_head + c) elements; channels are
+ * contiguous. dtype is MF_BF16 or MF_F32.
+ */
+typedef struct {
+  void* data;
+  int32_t dtype;
+  int32_t tokens;
+  int32_t heads;
+  int32_t head_dim;
+  int64_t stride_token;
+  int64_t stride_head;
+} mf_tensor;
 
 /* Library version as major*10000 + minor*100 + patch. */
 int mf_version(void);
@@ -133,6 +150,25 @@ int mf_attn_packed_ws(const void* q, const void* k, const void* v, const int32_t
                       const int32_t* grid_hw, const int32_t* text_len, void* out, int32_t n_seg,
                       int64_t total_tokens, int32_t heads, int32_t head_dim, int32_t dtype,
                       void* workspace, size_t workspace_bytes, hipStream_t stream);
+
+/*
+ * mf_attn_packed on strided tensors, e.g. views of one fused [T][3][heads][d]
+ * projection output (stride_token 3 * heads * d) or of a head-major
+ * [heads][T][d] buffer, without a copy. Same operation, metadata checks,
+ * workspace and results as mf_attn_packed (bit for bit on the same values).
+ *   q, k, v, out  descriptors with equal dtype, tokens, heads and head_dim;
+ *                 data 16-byte aligned; both strides at least head_dim and
+ *                 multiples of 16 bytes; q, k and v may overlap each other
+ *   out           must be one-to-one (stride_head >= head_dim and
+ *                 stride_token >= (heads - 1) * stride_head + head_dim, or
+ *                 the head-major analogue), and its span must not overlap
+ *                 the spans of q, k, v or the metadata
+ * The forward only: mf_attn_packed_lse, the backward and the frame-aware
+ * variants take contiguous tensors.
+ */
+int mf_attn_packed_strided(const mf_tensor* q, const mf_tensor* k, const mf_tensor* v, const int32_t* cu_seqlens,
+                           const int32_t* grid_hw, const int32_t* text_len, int32_t n_seg, const mf_tensor* out,
+                           hipStream_t stream);
 
 /*
  * Allocation-free forward, for callers that cannot allocate device memory:

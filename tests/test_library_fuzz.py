@@ -62,6 +62,22 @@ def _draw(rng, t, position):
 
 # Arguments that are host arrays of device pointers (position in the argument list).
 HOST_ARRAYS = {"mf_pack_joint": {1, 2, 3}, "mf_unpack_joint": {1, 2, 3}}
+# Arguments that are host pointers to mf_tensor descriptors.
+DESCRIPTORS = {"mf_attn_packed_strided": {0, 1, 2, 7}}
+STRIDES = [0, 1, 8, 64, 128, 3072, 9216, 2**31, -8, 2**40]
+
+
+def _descriptor(rng, position):
+    """A host mf_tensor: plausible fields (a contiguous bf16 4352 x 24 x 128
+    tensor at a disjoint fake address), each replaced with probability 0.15 by
+    an edge value; or a null descriptor."""
+    if rng.random() < 0.1:
+        return None
+    pick = lambda plausible, edge: plausible if rng.random() < 0.85 else rng.choice(edge)  # noqa: E731
+    d = binding.MfTensor(pick(0x40000000 * (position + 1), [None, 0x100004, 0x100000]),
+                         pick(0, I32), pick(4352, I32), pick(24, I32), pick(128, I32),
+                         pick(24 * 128, STRIDES), pick(128, STRIDES))
+    return ctypes.pointer(d)
 
 
 def _host_array(rng, position):
@@ -83,7 +99,8 @@ def test_entry_point_returns_documented_codes(name):
     fn = dict(_functions())[name]
     rng = random.Random(zlib.crc32(name.encode()))
     for _ in range(600):
-        args = [_host_array(rng, i) if i in HOST_ARRAYS.get(name, ()) else _draw(rng, t, i)
+        args = [_host_array(rng, i) if i in HOST_ARRAYS.get(name, ()) else
+                _descriptor(rng, i) if i in DESCRIPTORS.get(name, ()) else _draw(rng, t, i)
                 for i, t in enumerate(fn.argtypes)]
         r = fn(*args)
         if fn.restype is ctypes.c_size_t:

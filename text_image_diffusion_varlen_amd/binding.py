@@ -37,6 +37,13 @@ class MFError(RuntimeError):
         self.code = code
 
 
+class MfTensor(ctypes.Structure):
+    """mf_tensor: strided tensor descriptor of the C ABI."""
+    _fields_ = [("data", ctypes.c_void_p), ("dtype", ctypes.c_int32), ("tokens", ctypes.c_int32),
+                ("heads", ctypes.c_int32), ("head_dim", ctypes.c_int32), ("stride_token", ctypes.c_int64),
+                ("stride_head", ctypes.c_int64)]
+
+
 def _declare(lib):
     P, I32, I64, SZ, F = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64, ctypes.c_size_t, ctypes.c_float
     sig = {
@@ -47,6 +54,7 @@ def _declare(lib):
         "mf_workspace_bytes": ([I64, I32, I32, I32, I32], SZ),
         "mf_attn_packed_ws": ([P, P, P, P, P, P, P, I32, I64, I32, I32, I32, P, SZ, P], ctypes.c_int),
         "mf_attn_packed_noalloc": ([P, P, P, P, P, P, P, I32, I64, I32, I32, I32, P], ctypes.c_int),
+        "mf_attn_packed_strided": ([P, P, P, P, P, P, I32, P, P], ctypes.c_int),
         "mf_attn_packed_lse": ([P, P, P, P, P, P, P, P, I32, I64, I32, I32, I32, P], ctypes.c_int),
         "mf_attn_packed_bwd": ([P] * 12 + [I32, I64, I32, I32, I32, P], ctypes.c_int),
         "mf_attn_packed_bwd_profiled": ([P] * 12 + [I32, I64, I32, I32, I32, P, P], ctypes.c_int),
@@ -183,6 +191,31 @@ def attn_packed_noalloc(q, k, v, cu_seqlens, grid_hw, text_len, out, stream=None
     out, n, T, H, D = _attn_args(q, k, v, cu_seqlens, grid_hw, text_len, out)
     _check(lib().mf_attn_packed_noalloc(_ptr(q), _ptr(k), _ptr(v), _ptr(cu_seqlens), _ptr(grid_hw),
                                         _ptr(text_len), _ptr(out), n, T, H, D, _DTYPES[q.dtype], _stream(stream)))
+    return out
+
+
+def _descriptor(t, name):
+    """mf_tensor of a [tokens, heads, head_dim] view whose channels are contiguous."""
+    if not isinstance(t, torch.Tensor) or not t.is_cuda or t.dim() != 3:
+        raise ValueError(f"{name} must be a 3-dim device tensor")
+    if t.dtype not in _DTYPES:
+        raise ValueError(f"{name} must be bfloat16 or float32")
+    if t.stride(2) != 1:
+        raise ValueError(f"{name} must have contiguous channels")
+    T, H, D = t.shape
+    return MfTensor(t.data_ptr(), _DTYPES[t.dtype], T, H, D, t.stride(0), t.stride(1))
+
+
+def attn_packed_strided(q, k, v, cu_seqlens, grid_hw, text_len, out, stream=None):
+    """mf_attn_packed_strided: the forward on strided [T, H, d] views (channels
+    contiguous), e.g. slices of one fused QKV buffer. Returns out."""
+    _need(cu_seqlens, "cu_seqlens", torch.int32, 1)
+    _need(grid_hw, "grid_hw", torch.int32, 2)
+    _need(text_len, "text_len", torch.int32, 1)
+    d = [_descriptor(t, name) for t, name in ((q, "q"), (k, "k"), (v, "v"), (out, "out"))]
+    ptr = lambda x: ctypes.cast(ctypes.pointer(x), ctypes.c_void_p)  # noqa: E731
+    _check(lib().mf_attn_packed_strided(ptr(d[0]), ptr(d[1]), ptr(d[2]), _ptr(cu_seqlens), _ptr(grid_hw),
+                                        _ptr(text_len), grid_hw.shape[0], ptr(d[3]), _stream(stream)))
     return out
 
 

@@ -38,15 +38,20 @@ hipError_t launch_build_metadata(const int32_t* grid_hw, const int32_t* text_len
                                  int32_t* status, hipStream_t s);
 hipError_t launch_rope_pack(const void* q, const void* k, const void* v, const int32_t* grid_hw,
                             const int32_t* text_len, const char* ws, const WsLayout& l,
-                            const float2* cs, const Rope3* r3, int32_t heads, int32_t head_dim, bool bf16,
+                            const float2* cs, const Rope3* r3, int32_t heads, int32_t head_dim, const Strides& st,
                             hipStream_t s);
+hipError_t launch_prologue_bf16(const void* k, int64_t k_st, int64_t k_sh, const void* v, int64_t v_st, int64_t v_sh,
+                                const int32_t* grid_hw, const int32_t* text_len, const int32_t* frames,
+                                const int32_t* cu_in, int32_t n_seg, int64_t tokens, char* ws, const WsLayout& l,
+                                const float2* cs, const Rope3* r3, int32_t heads, int32_t head_dim, bool fused,
+                                hipStream_t s);
 hipError_t launch_rope(const void* x, void* y, const int32_t* pos, int64_t tokens, int32_t heads,
                        int32_t head_dim, bool bf16, const float2* cs, const Rope3* r3, int32_t* status,
                        hipStream_t s);
 hipError_t launch_attn_fwd(char* ws, const WsLayout& l, const void* q, const int32_t* grid_hw,
                            const int32_t* text_len, const float2* cs, const Rope3* r3, void* out, float* lse,
                            int64_t tokens, int32_t heads, int32_t head_dim, bool bf16, float scale, int32_t ncu,
-                           hipStream_t s);
+                           const Strides& st, hipStream_t s);
 hipError_t launch_attn_bwd(const void* q, const void* k, const void* v, const void* o, const void* dout,
                            const float* lse, const int32_t* grid_hw, const int32_t* text_len,
                            const float2* cs, const Rope3* r3, char* ws, const BwdLayout& l, void* dq, void* dk,
@@ -300,11 +305,12 @@ bool overlaps(const void* a, size_t na, const void* b, size_t nb) {
   return x < y + nb && y < x + na;
 }
 
-// Scalar checks shared by the attention entry points.
-int check_attn_args(const void* q, const void* k, const void* v, const int32_t* cu,
-                    const int32_t* grid_hw, const int32_t* text_len, const void* out,
-                    int32_t n_seg, int64_t tokens, int32_t heads, int32_t head_dim,
-                    int32_t dtype) {
+// Checks of the attention entry points that do not depend on the tensors'
+// layout: null pointers, sizes, dtype.
+int check_attn_scalars(const void* q, const void* k, const void* v, const int32_t* cu,
+                       const int32_t* grid_hw, const int32_t* text_len, const void* out,
+                       int32_t n_seg, int64_t tokens, int32_t heads, int32_t head_dim,
+                       int32_t dtype) {
   if (!q || !k || !v || !cu || !grid_hw || !text_len || !out)
     return fail(MF_ERR_INVALID_ARG, "null pointer argument");
   if (n_seg < 1 || n_seg > MF_MAX_SEGMENTS)
@@ -319,7 +325,17 @@ int check_attn_args(const void* q, const void* k, const void* v, const int32_t* 
   const mf::WsLayout l = mf::ws_layout(tokens, heads, head_dim, eb, n_seg);
   if (int64_t(heads) * l.rows * head_dim >= (int64_t(1) << 40) || l.n_tiles * heads >= (int64_t(1) << 31))
     return fail(MF_ERR_UNSUPPORTED, "problem too large");
-  const size_t tb = size_t(tokens) * heads * head_dim * eb;
+  return MF_OK;
+}
+
+// All checks of the attention entry points on contiguous [T][heads][d] tensors.
+int check_attn_args(const void* q, const void* k, const void* v, const int32_t* cu,
+                    const int32_t* grid_hw, const int32_t* text_len, const void* out,
+                    int32_t n_seg, int64_t tokens, int32_t heads, int32_t head_dim,
+                    int32_t dtype) {
+  const int rc = check_attn_scalars(q, k, v, cu, grid_hw, text_len, out, n_seg, tokens, heads, head_dim, dtype);
+  if (rc) return rc;
+  const size_t tb = size_t(tokens) * heads * head_dim * elem_bytes(dtype);
   if (overlaps(out, tb, q, tb) || overlaps(out, tb, k, tb) || overlaps(out, tb, v, tb))
     return fail(MF_ERR_INVALID_ARG, "out overlaps q, k or v");
   if (overlaps(out, tb, cu, size_t(n_seg + 1) * 4) || overlaps(out, tb, grid_hw, size_t(n_seg) * 8) ||
@@ -335,32 +351,44 @@ int run_attn(const void* q, const void* k, const void* v, const int32_t* cu, con
              const int32_t* text_len, void* out, int32_t n_seg, int64_t tokens, int32_t heads,
              int32_t head_dim, int32_t dtype, char* ws, const float2* cs, int32_t ncu, hipStream_t s,
              hipEvent_t const* ev = nullptr, float* lse = nullptr, const int32_t* frames = nullptr,
-             const mf::Rope3* r3 = nullptr, bool with_parts = true) {
+             const mf::Rope3* r3 = nullptr, bool with_parts = true, const mf::Strides* strides = nullptr) {
   const bool bf16 = dtype == MF_BF16;
+  const mf::Strides st = strides ? *strides : mf::contiguous_strides(heads, head_dim);
   const mf::WsLayout l = mf::ws_layout(tokens, heads, head_dim, elem_bytes(dtype), n_seg, with_parts);
   if (!with_parts) ncu = 0;  // no partial-result slots: never split
   hipError_t e;
   int rc;
+  // bf16 batches of at most 64 samples: the prologue derives the metadata
+  // itself (one launch less); otherwise the metadata kernel runs first.
+  const bool fused = bf16 && n_seg <= 64;
   if (ev && (e = hipEventRecord(ev[0], s)) != hipSuccess) return hip_fail(e, "hipEventRecord");
-  {
-    Range r("mf meta_kernel");
-    e = mf::launch_meta(grid_hw, text_len, frames, cu, n_seg, tokens, ws, l, s);
+  if (!fused) {
+    {
+      Range r("mf meta_kernel");
+      e = mf::launch_meta(grid_hw, text_len, frames, cu, n_seg, tokens, ws, l, s);
+    }
+    if (e != hipSuccess) return hip_fail(e, "meta_kernel launch");
+    if ((rc = debug_stage(s, "meta_kernel", ws_flag(ws)))) return rc;
   }
-  if (e != hipSuccess) return hip_fail(e, "meta_kernel launch");
-  if ((rc = debug_stage(s, "meta_kernel", ws_flag(ws)))) return rc;
   if (ev && (e = hipEventRecord(ev[1], s)) != hipSuccess) return hip_fail(e, "hipEventRecord");
   {
-    Range r("mf rope_pack_kernel");
-    e = mf::launch_rope_pack(q, k, v, grid_hw, text_len, ws, l, cs, r3, heads, head_dim, bf16, s);
+    Range r("mf rope prologue");
+    if (bf16) {
+      e = mf::launch_prologue_bf16(k, st.k_st, st.k_sh, v, st.v_st, st.v_sh, grid_hw, text_len, frames, cu, n_seg,
+                                   tokens, ws, l, cs, r3, heads, head_dim, fused, s);
+    } else {
+      e = mf::launch_rope_pack(q, k, v, grid_hw, text_len, ws, l, cs, r3, heads, head_dim, st, s);
+    }
   }
-  if (e != hipSuccess) return hip_fail(e, "rope_pack_kernel launch");
-  if ((rc = debug_stage(s, "rope_pack_kernel"))) return rc;
+  if (e != hipSuccess) return hip_fail(e, "rope prologue launch");
+  if ((rc = debug_stage(s, fused ? "metadata + rope prologue" : "rope prologue", fused ? ws_flag(ws) : nullptr)))
+    return rc;
   if (ev && (e = hipEventRecord(ev[2], s)) != hipSuccess) return hip_fail(e, "hipEventRecord");
   {
     Range r("mf attn_fwd");
     e = mf::launch_attn_fwd(ws, l, q, grid_hw, text_len, cs, r3, out, lse, tokens, heads, head_dim, bf16,
                             float(1.0 / std::sqrt(double(head_dim))),
-                            mf::split_possible(tokens, n_seg) ? ncu : 0, s);
+                            mf::split_possible(tokens, n_seg) ? ncu : 0, st, s);
   }
   if (e != hipSuccess) return hip_fail(e, "attn_fwd launch");
   if ((rc = debug_stage(s, "attn_fwd"))) return rc;
@@ -986,6 +1014,86 @@ int mf_get_workspace_error(const void* workspace, hipStream_t stream) {
     return hip_fail(e, "hipMemcpy(workspace header)");
   if (hdr.flag) return fail(MF_ERR_METADATA, "device check failed (flags 0x%x)", unsigned(hdr.flag));
   return MF_OK;
+}
+
+}  // extern "C"
+
+namespace {
+
+// Byte span [first, last) touched by a strided tensor.
+std::pair<uintptr_t, uintptr_t> tensor_span(const mf_tensor& t, int eb) {
+  const uintptr_t a = reinterpret_cast<uintptr_t>(t.data);
+  const int64_t last = (int64_t(t.tokens) - 1) * t.stride_token + (int64_t(t.heads) - 1) * t.stride_head + t.head_dim;
+  return {a, a + uintptr_t(last) * eb};
+}
+
+bool spans_overlap(std::pair<uintptr_t, uintptr_t> x, std::pair<uintptr_t, uintptr_t> y) {
+  return x.first < y.second && y.first < x.second;
+}
+
+}  // namespace
+
+extern "C" {
+
+int mf_attn_packed_strided(const mf_tensor* q, const mf_tensor* k, const mf_tensor* v, const int32_t* cu_seqlens,
+                           const int32_t* grid_hw, const int32_t* text_len, int32_t n_seg, const mf_tensor* out,
+                           hipStream_t stream) {
+  if (!q || !k || !v || !out) return fail(MF_ERR_INVALID_ARG, "null tensor descriptor");
+  const mf_tensor* ts[4] = {q, k, v, out};
+  for (const mf_tensor* t : ts) {
+    if (t->dtype != q->dtype || t->tokens != q->tokens || t->heads != q->heads || t->head_dim != q->head_dim)
+      return fail(MF_ERR_INVALID_ARG, "q, k, v and out must agree on dtype, tokens, heads and head_dim");
+  }
+  const int64_t T = q->tokens;
+  const int32_t H = q->heads, D = q->head_dim;
+  int rc = check_attn_scalars(q->data, k->data, v->data, cu_seqlens, grid_hw, text_len, out->data, n_seg, T, H, D,
+                              q->dtype);
+  if (rc) return rc;
+  const int eb = elem_bytes(q->dtype);
+  const int64_t align = 16 / eb;  // elements per 16-byte chunk
+  for (const mf_tensor* t : ts) {
+    if (t->stride_token < D || t->stride_head < D || t->stride_token % align || t->stride_head % align)
+      return fail(MF_ERR_INVALID_ARG,
+                  "strides (%lld, %lld) must be at least head_dim=%d and multiples of %lld elements",
+                  (long long)t->stride_token, (long long)t->stride_head, D, (long long)align);
+    if (reinterpret_cast<uintptr_t>(t->data) & 15) return fail(MF_ERR_INVALID_ARG, "tensors must be 16-byte aligned");
+  }
+  for (const mf_tensor* t : ts) {
+    // extent below 2^60 elements (no overflow in the span arithmetic below)
+    const int64_t lim = int64_t(1) << 60;
+    if (t->stride_token > lim / T || t->stride_head > lim / H)
+      return fail(MF_ERR_INVALID_ARG, "strides (%lld, %lld) too large", (long long)t->stride_token,
+                  (long long)t->stride_head);
+  }
+  // out must be one-to-one: rows of a token (or of a head) must not interleave.
+  const int64_t ost = out->stride_token, osh = out->stride_head;
+  const bool token_major = osh >= D && ost >= (int64_t(H) - 1) * osh + D;
+  const bool head_major = ost >= D && osh >= (T - 1) * ost + D;
+  if (!token_major && !head_major)
+    return fail(MF_ERR_INVALID_ARG, "out strides (%lld, %lld) let rows overlap", (long long)ost, (long long)osh);
+  const auto os = tensor_span(*out, eb);
+  for (const mf_tensor* t : {q, k, v})
+    if (spans_overlap(os, tensor_span(*t, eb))) return fail(MF_ERR_INVALID_ARG, "out overlaps q, k or v");
+  const std::pair<uintptr_t, uintptr_t> meta[3] = {
+      {reinterpret_cast<uintptr_t>(cu_seqlens), reinterpret_cast<uintptr_t>(cu_seqlens) + size_t(n_seg + 1) * 4},
+      {reinterpret_cast<uintptr_t>(grid_hw), reinterpret_cast<uintptr_t>(grid_hw) + size_t(n_seg) * 8},
+      {reinterpret_cast<uintptr_t>(text_len), reinterpret_cast<uintptr_t>(text_len) + size_t(n_seg) * 4}};
+  for (const auto& m : meta)
+    if (spans_overlap(os, m)) return fail(MF_ERR_INVALID_ARG, "out overlaps the metadata");
+  const mf::Strides st{q->stride_token, q->stride_head, k->stride_token, k->stride_head,
+                       v->stride_token, v->stride_head, ost, osh};
+  int dev;
+  if ((rc = current_device(&dev))) return rc;
+  const size_t need = mf_workspace_bytes(T, H, D, q->dtype, n_seg);
+  std::lock_guard<std::mutex> lock(g_mu);
+  DeviceState& ds = g_dev[dev];
+  const float2* cs = nullptr;
+  int32_t ncu = 0;
+  if ((rc = ensure_table(ds, D, MF_ROPE_THETA, &cs))) return rc;
+  if ((rc = ensure_cus(ds, dev, &ncu))) return rc;
+  if ((rc = ensure_workspace(ds, need))) return rc;
+  return run_attn(q->data, k->data, v->data, cu_seqlens, grid_hw, text_len, out->data, n_seg, T, H, D, q->dtype,
+                  ds.ws, cs, ncu, stream, nullptr, nullptr, nullptr, nullptr, true, &st);
 }
 
 }  // extern "C"

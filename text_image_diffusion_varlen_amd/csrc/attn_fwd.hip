@@ -38,7 +38,9 @@ namespace mf {
 struct AttnArgs {
   const char* ws;
   int64_t off_len, off_cu, off_pcu, off_tiles;
-  const void* q;            // caller's queries [T][heads][d] (bf16 kernel rotates them on load)
+  const void* q;            // caller's queries (bf16 kernel rotates them on load)
+  int64_t q_st, q_sh;       // their element strides (token, head)
+  int64_t o_st, o_sh;       // element strides of out
   const int32_t* grid_hw;   // caller's (h, w) per sample
   const int32_t* text_len;  // caller's prompt length per sample
   const float2* cs;         // cos/sin table [ROPE_PMAX][d/4]
@@ -230,7 +232,7 @@ __global__ void __launch_bounds__(ATTN_THREADS, 2) attn_fwd_bf16_kernel(AttnArgs
     int32_t row, col, frame = 0;
     if constexpr (R3) token_position3(u, a.text_len[seg], a.grid_hw[2 * seg], a.grid_hw[2 * seg + 1], row, col, frame);
     else token_position(u, a.text_len[seg], a.grid_hw[2 * seg + 1], row, col);
-    const uint16_t* qrow = static_cast<const uint16_t*>(a.q) + (int64_t(cb + u) * heads + h) * D + 8 * hf;
+    const uint16_t* qrow = static_cast<const uint16_t*>(a.q) + int64_t(cb + u) * a.q_st + int64_t(h) * a.q_sh + 8 * hf;
 #pragma unroll
     for (int ks = 0; ks < KSTEPS; ++ks) {
       const Chunk<uint16_t> raw = *reinterpret_cast<const Chunk<uint16_t>*>(qrow + 16 * ks);
@@ -317,7 +319,7 @@ __global__ void __launch_bounds__(ATTN_THREADS, 2) attn_fwd_bf16_kernel(AttnArgs
   // ln sum_k e^(s_k * scale) = (m + log2 lsum) * ln 2.
   if (a.lse && qrel < L && hf == 0) a.lse[int64_t(h) * a.tokens + cb + qrel] = (m + log2f(lsum)) * 0.6931471805599453f;
   if (qrel < L) {
-    uint16_t* orow = static_cast<uint16_t*>(a.out) + (int64_t(cb + qrel) * heads + h) * D;
+    uint16_t* orow = static_cast<uint16_t*>(a.out) + int64_t(cb + qrel) * a.o_st + int64_t(h) * a.o_sh;
 #pragma unroll
     for (int b = 0; b < DBLK; ++b) {
 #pragma unroll
@@ -399,7 +401,7 @@ __global__ void __launch_bounds__(256) attn_merge_kernel(AttnArgs a) {
       }
     }
     const float ir = __shfl(inv, rr);
-    uint16_t* orow = static_cast<uint16_t*>(a.out) + (int64_t(cb + qs + r) * heads + h) * D + CPL * lane;
+    uint16_t* orow = static_cast<uint16_t*>(a.out) + int64_t(cb + qs + r) * a.o_st + int64_t(h) * a.o_sh + CPL * lane;
     if constexpr (CPL == 2) *reinterpret_cast<uint32_t*>(orow) = pack_bf16x2(o[0] * ir, o[1] * ir);
     else orow[0] = uint16_t(pack_bf16x2(o[0] * ir, 0.f) & 0xFFFFu);
   }
@@ -474,7 +476,7 @@ __global__ void __launch_bounds__(ATTN_THREADS) attn_fwd_f32_kernel(AttnArgs a) 
   const int32_t qrel = qs + 32 * wave + l32;
   if (a.lse && qrel < L && hf == 0) a.lse[int64_t(h) * a.tokens + cb + qrel] = (m + log2f(lsum)) * 0.6931471805599453f;
   if (qrel < L) {
-    float* orow = static_cast<float*>(a.out) + (int64_t(cb + qrel) * heads + h) * D + HD * hf;
+    float* orow = static_cast<float*>(a.out) + int64_t(cb + qrel) * a.o_st + int64_t(h) * a.o_sh + HD * hf;
     const float inv = 1.f / lsum;
 #pragma unroll
     for (int i = 0; i < HD; ++i) orow[i] = acc[i] * inv;
@@ -484,10 +486,14 @@ __global__ void __launch_bounds__(ATTN_THREADS) attn_fwd_f32_kernel(AttnArgs a) 
 hipError_t launch_attn_fwd(char* ws, const WsLayout& l, const void* q, const int32_t* grid_hw,
                            const int32_t* text_len, const float2* cs, const Rope3* r3, void* out, float* lse,
                            int64_t tokens, int32_t heads, int32_t head_dim, bool bf16, float scale, int32_t ncu,
-                           hipStream_t s) {
+                           const Strides& st, hipStream_t s) {
   AttnArgs a;
   a.ws = ws;
   a.q = q;
+  a.q_st = st.q_st;
+  a.q_sh = st.q_sh;
+  a.o_st = st.o_st;
+  a.o_sh = st.o_sh;
   a.grid_hw = grid_hw;
   a.text_len = text_len;
   a.cs = cs;

@@ -117,6 +117,16 @@ __device__ inline int xcd_unit(int unit, int heads, int tile, int qs, int32_t L,
   return u0 + (k % n_s) * heads + c + 8 * (k / n_s);
 }
 
+// Element strides of the caller's q, k, v and out: token t, head h, channel c
+// of a tensor sits at t * st + h * sh + c (channels contiguous).
+struct Strides {
+  int64_t q_st, q_sh, k_st, k_sh, v_st, v_sh, o_st, o_sh;
+};
+__host__ __device__ inline Strides contiguous_strides(int32_t heads, int32_t head_dim) {
+  const int64_t st = int64_t(heads) * head_dim, sh = head_dim;
+  return Strides{st, sh, st, sh, st, sh, st, sh};
+}
+
 // Workspace: [header 256 B][len n][cu n+1][pcu n+1][tiles 2*max_tiles][Q~][K~][V~][partials]
 // with every section 256-byte aligned. Q~, K~, V~ are [heads][rows][head_dim].
 struct WsHeader {

@@ -15,9 +15,10 @@
 // frame-aware variant: (row, col, frame) positions, three channel blocks
 // (rope_math.h, Rope3).
 //
-// rope_pack_kernel is the prologue of the attention path. One workgroup per
-// (KTILE-row tile of the padded layout, head). It rotates the keys (and, for
-// f32, the queries) of every token of the tile and writes into the workspace:
+// The prologue of the attention path (prologue_bf16_kernel, and
+// rope_pack_kernel for fp32) runs one workgroup per (KTILE-row tile of the
+// padded layout, head). It rotates the keys (and, for fp32, the queries) of
+// every token of the tile and writes into the workspace:
 //   Q~  f32 only: [head][row][d] row-major (the bf16 attention kernel rotates
 //       its query rows itself while loading them)
 //   K~  bf16: each KTILE x d tile stored chunk-major: 16-byte chunk c (channels
@@ -33,10 +34,182 @@
 // from a per-lane base.
 // Rows that belong to no token (padding up to KTILE, and the slack after the
 // last sample) are written as zeros.
+#include "meta_small.h"
 #include "mf_common.h"
 #include "rope_math.h"
 
 namespace mf {
+
+// ---------------------------------------------------------------------------
+// bf16 prologue. One workgroup per (KTILE-row tile of the padded layout,
+// head), the head index fastest. Rows are read whole (16 lanes x 16 B per
+// row), keys rotated in fp32, and both tiles staged through LDS: K~ leaves
+// chunk-major, V transposed in the score MFMA's key order. Inputs are read
+// with element strides (token, head).
+//
+// FUSED (batches of at most 64 samples): every wave derives the batch's
+// offsets itself (one lane per sample, wave scans), and workgroup 0 also
+// writes the metadata sections of the workspace for the attention kernel, so
+// no separate metadata launch precedes the prologue. Otherwise the metadata
+// kernel has run and its sections are read.
+struct PrologueArgs {
+  const uint16_t* k;
+  const uint16_t* v;
+  int64_t k_st, k_sh, v_st, v_sh;  // element strides between tokens / heads
+  const int32_t* grid_hw;
+  const int32_t* text_len;
+  const int32_t* frames;  // editing samples (R3), else null
+  const int32_t* cu_in;   // caller's cu_seqlens (FUSED)
+  int32_t n_seg;
+  int64_t tokens;
+  char* ws;
+  int64_t off_len, off_cu, off_pcu, off_tiles;
+  uint16_t* kw;
+  uint16_t* vw;
+  const float2* cs;
+  Rope3 r3;
+  int32_t heads;
+  int64_t rows;
+};
+
+// Sample covering padded row r0 of this call: first token u0 of the tile in
+// the sample, its length, prompt length, grid and first packed token index.
+struct TileSample {
+  int32_t u0, L, tl, gh, w;
+  int64_t tok0;
+};
+
+template <bool R3>
+__device__ inline bool fused_tile_sample(const PrologueArgs& a, int64_t r0, TileSample& ts) {
+  const int lane = threadIdx.x & 63;
+  const int32_t n = a.n_seg;
+  const bool mine = lane < n;
+  bool ok = true;
+  int32_t L = 0, h = 1, w = 1, tl = 0;
+  if (mine) {
+    L = sample_length(a.grid_hw, a.text_len, R3 ? a.frames : nullptr, lane, ok);
+    h = a.grid_hw[2 * lane];
+    w = a.grid_hw[2 * lane + 1];
+    tl = a.text_len[lane];
+  }
+  const int64_t incl = wave_inclusive_scan(L);
+  const int64_t total = __shfl(incl, 63);
+  const int64_t excl = incl - L;
+  if (mine && int64_t(a.cu_in[lane]) != excl) ok = false;
+  if (lane == 0 && (int64_t(a.cu_in[n]) != total || total != a.tokens || total >= (int64_t(1) << 31))) ok = false;
+  if (__any(!ok)) return false;
+  const int64_t padded = mine ? round_up(L, KTILE) : 0;
+  const int64_t pincl = wave_inclusive_scan(padded);
+  const int64_t pexcl = pincl - padded;
+  const int64_t ptotal = __shfl(pincl, 63);
+  ts = TileSample{0, 0, 0, 1, 1, 0};
+  if (r0 < ptotal) {
+    const uint64_t before = __ballot(mine && pexcl <= r0);
+    const int s = int(__popcll(before)) - 1;  // padded offsets strictly increase
+    ts.u0 = int32_t(r0 - __shfl(pexcl, s));
+    ts.L = __shfl(L, s);
+    ts.tl = __shfl(tl, s);
+    ts.gh = __shfl(h, s);
+    ts.w = __shfl(w, s);
+    ts.tok0 = __shfl(excl, s) + ts.u0;
+  }
+  return true;
+}
+
+template <bool R3>
+__device__ inline void ws_tile_sample(const PrologueArgs& a, int64_t r0, TileSample& ts) {
+  const WsHeader* hdr = reinterpret_cast<const WsHeader*>(a.ws);
+  const int32_t* len = reinterpret_cast<const int32_t*>(a.ws + a.off_len);
+  const int32_t* cu = reinterpret_cast<const int32_t*>(a.ws + a.off_cu);
+  const int32_t* pcu = reinterpret_cast<const int32_t*>(a.ws + a.off_pcu);
+  ts = TileSample{0, 0, 0, 1, 1, 0};
+  if (r0 < hdr->padded_total) {
+    const int32_t s = upper_segment(pcu, hdr->n_seg, r0);
+    ts.u0 = int32_t(r0 - pcu[s]);
+    ts.L = len[s];
+    ts.tok0 = int64_t(cu[s]) + ts.u0;
+    ts.tl = a.text_len[s];
+    ts.gh = a.grid_hw[2 * s];
+    ts.w = a.grid_hw[2 * s + 1];
+  }
+}
+
+template <int D, bool R3, bool FUSED>
+__global__ void __launch_bounds__(256) prologue_bf16_kernel(PrologueArgs a) {
+  constexpr int CPR = D / 8;          // 16-byte chunks per row
+  constexpr int CPT = KTILE * CPR;    // chunks per tile
+  constexpr int KS = KTILE + 1;       // LDS stride (chunks) between channel chunks: no bank conflicts
+  constexpr int VS = D + 2;           // padded LDS row (elements): consecutive keys in different banks
+  __shared__ Chunk<uint16_t> ks[CPR * KS];
+  __shared__ uint16_t vs[KTILE * VS];
+  const int t = threadIdx.x;
+  const int h = int(blockIdx.x % unsigned(a.heads));
+  const int64_t tile = int64_t(blockIdx.x / unsigned(a.heads));
+  const int64_t r0 = tile * KTILE;
+  TileSample ts;
+  if constexpr (FUSED) {
+    if (blockIdx.x == 0 && t < 64) {
+      meta_small(a.grid_hw, a.text_len, R3 ? a.frames : nullptr, a.cu_in, a.n_seg, a.tokens,
+                 reinterpret_cast<WsHeader*>(a.ws), reinterpret_cast<int32_t*>(a.ws + a.off_len),
+                 reinterpret_cast<int32_t*>(a.ws + a.off_cu), reinterpret_cast<int32_t*>(a.ws + a.off_pcu),
+                 reinterpret_cast<int2*>(a.ws + a.off_tiles));
+    }
+    if (!fused_tile_sample<R3>(a, r0, ts)) return;  // same verdict in every wave
+  } else {
+    if (reinterpret_cast<const WsHeader*>(a.ws)->flag != FLAG_OK) return;
+    ws_tile_sample<R3>(a, r0, ts);
+  }
+  const int64_t tile_off = (int64_t(h) * a.rows + r0) * D;
+  const int64_t tok_base = ts.tok0 - ts.u0;  // packed index of the sample's first token
+  // Every thread loads, for chunks f = t, t + 256, ...: the K chunk (rotated
+  // here) and the V chunk of row f / CPR, both into LDS.
+  for (int f = t; f < CPT; f += 256) {
+    const int rr = f / CPR, cc = f % CPR;
+    const int32_t u = ts.u0 + rr;
+    Chunk<uint16_t> ko, vi;
+    if (u < ts.L) {
+      const Chunk<uint16_t> x =
+          *reinterpret_cast<const Chunk<uint16_t>*>(a.k + (tok_base + u) * a.k_st + int64_t(h) * a.k_sh + cc * 8);
+      vi = *reinterpret_cast<const Chunk<uint16_t>*>(a.v + (tok_base + u) * a.v_st + int64_t(h) * a.v_sh + cc * 8);
+      if constexpr (R3) {
+        int32_t row, col, frame;
+        token_position3(u, ts.tl, ts.gh, ts.w, row, col, frame);
+        ko = rotate_chunk3<uint16_t, D>(x, cc * 8, row, col, frame, a.r3);
+      } else {
+        int32_t row, col;
+        token_position(u, ts.tl, ts.w, row, col);
+        ko = rotate_chunk<uint16_t, D>(x, cc * 8, row, col, a.cs);
+      }
+    } else {
+#pragma unroll
+      for (int e = 0; e < 8; ++e) ko.v[e] = vi.v[e] = 0;
+    }
+    ks[cc * KS + rr] = ko;
+    uint32_t* dst = reinterpret_cast<uint32_t*>(vs + rr * VS + cc * 8);
+    const uint32_t* sv = reinterpret_cast<const uint32_t*>(vi.v);
+#pragma unroll
+    for (int e = 0; e < 4; ++e) dst[e] = sv[e];
+  }
+  __syncthreads();
+  // K~ chunk f2 = cc * KTILE + rr (chunk-major).
+  for (int f2 = t; f2 < CPT; f2 += 256) {
+    const int cc = f2 / KTILE, rr = f2 % KTILE;
+    *reinterpret_cast<Chunk<uint16_t>*>(a.kw + tile_off + int64_t(f2) * 8) = ks[cc * KS + rr];
+  }
+  // V~^T chunk f2 = g * D + c: channel c, keys b..b+3 and b+8..b+11 of the
+  // tile (b = 16 (g / 2) + 4 (g % 2): the score MFMA's accumulator order).
+  for (int f2 = t; f2 < D * (KTILE / 8); f2 += 256) {
+    const int g = f2 / D, c = f2 % D;
+    const int b = 16 * (g >> 1) + 4 * (g & 1);
+    Chunk<uint16_t> o;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      o.v[e] = vs[(b + e) * VS + c];
+      o.v[4 + e] = vs[(b + 8 + e) * VS + c];
+    }
+    *reinterpret_cast<Chunk<uint16_t>*>(a.vw + tile_off + int64_t(f2) * 8) = o;
+  }
+}
 
 // R3: editing samples with frame-aware (row, col, frame) RoPE (r3), else 2D (cs).
 template <typename T, int D, bool R3>
@@ -45,7 +218,7 @@ rope_pack_kernel(const T* __restrict__ q, const T* __restrict__ k, const T* __re
                  const int32_t* __restrict__ grid_hw, const int32_t* __restrict__ text_len,
                  const char* __restrict__ ws, int64_t off_len, int64_t off_cu, int64_t off_pcu,
                  T* __restrict__ qw, T* __restrict__ kw, T* __restrict__ vw,
-                 const float2* __restrict__ cs, Rope3 r3, int32_t heads, int64_t rows) {
+                 const float2* __restrict__ cs, Rope3 r3, int32_t heads, int64_t rows, Strides st) {
   constexpr int E = Elem<T>::PER_CHUNK;
   constexpr int CPR = D / E;             // chunks per row
   constexpr int CPT = KTILE * CPR;       // chunks per tile
@@ -82,86 +255,34 @@ rope_pack_kernel(const T* __restrict__ q, const T* __restrict__ k, const T* __re
     }
   };
   const int64_t tile_off = (int64_t(h) * rows + r0) * D;
-  const int64_t src_stride = int64_t(heads) * D;  // elements between consecutive tokens
 
-  if constexpr (sizeof(T) == 4) {
-    // f32: Q~ and K~ rotated, row-major.
-    for (int f = threadIdx.x; f < CPT; f += 256) {
-      const int rr = f / CPR, cc = f % CPR;
-      const int32_t u = u0 + rr;
-      Chunk<T> qo, ko;
-      if (u < L) {
-        const int64_t src = (tok0 + rr) * src_stride + int64_t(h) * D + cc * E;
-        qo = rotate(*reinterpret_cast<const Chunk<T>*>(q + src), cc, u);
-        ko = rotate(*reinterpret_cast<const Chunk<T>*>(k + src), cc, u);
-      } else {
+  // Q~ and K~ rotated, row-major.
+  for (int f = threadIdx.x; f < CPT; f += 256) {
+    const int rr = f / CPR, cc = f % CPR;
+    const int32_t u = u0 + rr;
+    Chunk<T> qo, ko;
+    if (u < L) {
+      qo = rotate(*reinterpret_cast<const Chunk<T>*>(q + (tok0 + rr) * st.q_st + int64_t(h) * st.q_sh + cc * E), cc, u);
+      ko = rotate(*reinterpret_cast<const Chunk<T>*>(k + (tok0 + rr) * st.k_st + int64_t(h) * st.k_sh + cc * E), cc, u);
+    } else {
 #pragma unroll
-        for (int e = 0; e < E; ++e) qo.v[e] = ko.v[e] = T(0);
-      }
-      *reinterpret_cast<Chunk<T>*>(qw + tile_off + int64_t(f) * E) = qo;
-      *reinterpret_cast<Chunk<T>*>(kw + tile_off + int64_t(f) * E) = ko;
+      for (int e = 0; e < E; ++e) qo.v[e] = ko.v[e] = T(0);
     }
+    *reinterpret_cast<Chunk<T>*>(qw + tile_off + int64_t(f) * E) = qo;
+    *reinterpret_cast<Chunk<T>*>(kw + tile_off + int64_t(f) * E) = ko;
   }
 
-  if constexpr (sizeof(T) == 4) {
-    // f32: V copied row-major into the padded layout.
-    for (int f = threadIdx.x; f < CPT; f += 256) {
-      const int rr = f / CPR, cc = f % CPR;
-      Chunk<T> vo;
-      if (u0 + rr < L) {
-        vo = *reinterpret_cast<const Chunk<T>*>(v + (tok0 + rr) * src_stride + int64_t(h) * D + cc * E);
-      } else {
+  // f32: V copied row-major into the padded layout.
+  for (int f = threadIdx.x; f < CPT; f += 256) {
+    const int rr = f / CPR, cc = f % CPR;
+    Chunk<T> vo;
+    if (u0 + rr < L) {
+      vo = *reinterpret_cast<const Chunk<T>*>(v + (tok0 + rr) * st.v_st + int64_t(h) * st.v_sh + cc * E);
+    } else {
 #pragma unroll
-        for (int e = 0; e < E; ++e) vo.v[e] = T(0);
-      }
-      *reinterpret_cast<Chunk<T>*>(vw + tile_off + int64_t(f) * E) = vo;
+      for (int e = 0; e < E; ++e) vo.v[e] = T(0);
     }
-  } else {
-    // bf16 (queries are rotated by the attention kernel itself): the K tile is
-    // rotated and staged through LDS, then written chunk-major; the V tile goes
-    // through LDS and is written transposed ([d][KTILE]) in MFMA key order.
-    // Loads read whole rows (16 lanes x 16 B), stores write consecutive chunks.
-    constexpr int KS = KTILE + 1;  // LDS stride (chunks) between channel chunks: no bank conflicts
-    constexpr int VS = D + 2;      // padded LDS row (elements): consecutive keys fall in different banks
-    __shared__ Chunk<T> ks[CPR * KS];
-    __shared__ uint16_t vs[KTILE * VS];
-    for (int f = threadIdx.x; f < CPT; f += 256) {
-      const int rr = f / CPR, cc = f % CPR;
-      const int32_t u = u0 + rr;
-      Chunk<T> ko, vi;
-      if (u < L) {
-        const int64_t src = (tok0 + rr) * src_stride + int64_t(h) * D + cc * E;
-        ko = rotate(*reinterpret_cast<const Chunk<T>*>(k + src), cc, u);
-        vi = *reinterpret_cast<const Chunk<T>*>(v + src);
-      } else {
-#pragma unroll
-        for (int e = 0; e < E; ++e) ko.v[e] = vi.v[e] = T(0);
-      }
-      ks[cc * KS + rr] = ko;
-      uint32_t* dst = reinterpret_cast<uint32_t*>(vs + rr * VS + cc * E);
-      const uint32_t* sv = reinterpret_cast<const uint32_t*>(vi.v);
-#pragma unroll
-      for (int e = 0; e < E / 2; ++e) dst[e] = sv[e];
-    }
-    __syncthreads();
-    // K~ chunk f2 = cc * KTILE + rr (chunk-major).
-    for (int f2 = threadIdx.x; f2 < CPT; f2 += 256) {
-      const int cc = f2 / KTILE, rr = f2 % KTILE;
-      *reinterpret_cast<Chunk<T>*>(kw + tile_off + int64_t(f2) * E) = ks[cc * KS + rr];
-    }
-    __syncthreads();
-    // Output chunk f2 = g * D + c: channel c, keys of chunk g of the 64-key row.
-    for (int f2 = threadIdx.x; f2 < D * (KTILE / 8); f2 += 256) {
-      const int g = f2 / D, c = f2 % D;
-      const int base = 16 * (g >> 1) + 4 * (g & 1);
-      Chunk<T> o;
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        o.v[e] = vs[(base + e) * VS + c];
-        o.v[4 + e] = vs[(base + 8 + e) * VS + c];
-      }
-      *reinterpret_cast<Chunk<T>*>(vw + tile_off + int64_t(f2) * 8) = o;
-    }
+    *reinterpret_cast<Chunk<T>*>(vw + tile_off + int64_t(f) * E) = vo;
   }
 }
 
@@ -197,37 +318,79 @@ template <typename T, int D, bool R3>
 static hipError_t launch_rope_pack_t(const void* q, const void* k, const void* v,
                                      const int32_t* grid_hw, const int32_t* text_len,
                                      const char* ws, const WsLayout& l, const float2* cs, Rope3 r3,
-                                     int32_t heads, hipStream_t s) {
+                                     int32_t heads, const Strides& st, hipStream_t s) {
   char* w = const_cast<char*>(ws);
   dim3 grid(unsigned(l.rows / KTILE), unsigned(heads));
   hipLaunchKernelGGL((rope_pack_kernel<T, D, R3>), grid, dim3(256), 0, s,
                      static_cast<const T*>(q), static_cast<const T*>(k), static_cast<const T*>(v),
                      grid_hw, text_len, ws, l.off_len, l.off_cu, l.off_pcu,
                      reinterpret_cast<T*>(w + l.off_q), reinterpret_cast<T*>(w + l.off_k),
-                     reinterpret_cast<T*>(w + l.off_v), cs, r3, heads, l.rows);
+                     reinterpret_cast<T*>(w + l.off_v), cs, r3, heads, l.rows, st);
   return hipGetLastError();
 }
 
 template <typename T, bool R3>
 static hipError_t launch_rope_pack_d(const void* q, const void* k, const void* v, const int32_t* grid_hw,
                                      const int32_t* text_len, const char* ws, const WsLayout& l,
-                                     const float2* cs, Rope3 r3, int32_t heads, int32_t head_dim, hipStream_t s) {
-  return head_dim == 128 ? launch_rope_pack_t<T, 128, R3>(q, k, v, grid_hw, text_len, ws, l, cs, r3, heads, s)
-                         : launch_rope_pack_t<T, 64, R3>(q, k, v, grid_hw, text_len, ws, l, cs, r3, heads, s);
+                                     const float2* cs, Rope3 r3, int32_t heads, int32_t head_dim,
+                                     const Strides& st, hipStream_t s) {
+  return head_dim == 128 ? launch_rope_pack_t<T, 128, R3>(q, k, v, grid_hw, text_len, ws, l, cs, r3, heads, st, s)
+                         : launch_rope_pack_t<T, 64, R3>(q, k, v, grid_hw, text_len, ws, l, cs, r3, heads, st, s);
 }
 
-// r3 == nullptr: 2D RoPE with the table cs; else frame-aware RoPE.
+// bf16 prologue: fused with the metadata derivation (n_seg <= 64) or after
+// meta_kernel. k, v with element strides (token, head).
+hipError_t launch_prologue_bf16(const void* k, int64_t k_st, int64_t k_sh, const void* v, int64_t v_st, int64_t v_sh,
+                                const int32_t* grid_hw, const int32_t* text_len, const int32_t* frames,
+                                const int32_t* cu_in, int32_t n_seg, int64_t tokens, char* ws, const WsLayout& l,
+                                const float2* cs, const Rope3* r3, int32_t heads, int32_t head_dim, bool fused,
+                                hipStream_t s) {
+  PrologueArgs a;
+  a.k = static_cast<const uint16_t*>(k);
+  a.v = static_cast<const uint16_t*>(v);
+  a.k_st = k_st;
+  a.k_sh = k_sh;
+  a.v_st = v_st;
+  a.v_sh = v_sh;
+  a.grid_hw = grid_hw;
+  a.text_len = text_len;
+  a.frames = frames;
+  a.cu_in = cu_in;
+  a.n_seg = n_seg;
+  a.tokens = tokens;
+  a.ws = ws;
+  a.off_len = l.off_len;
+  a.off_cu = l.off_cu;
+  a.off_pcu = l.off_pcu;
+  a.off_tiles = l.off_tiles;
+  a.kw = reinterpret_cast<uint16_t*>(ws + l.off_k);
+  a.vw = reinterpret_cast<uint16_t*>(ws + l.off_v);
+  a.cs = cs;
+  a.r3 = r3 ? *r3 : Rope3{nullptr, 0, 0};
+  a.heads = heads;
+  a.rows = l.rows;
+  const dim3 grid(unsigned(l.rows / KTILE * heads));
+#define MF_PROLOGUE(D, R3, F) hipLaunchKernelGGL((prologue_bf16_kernel<D, R3, F>), grid, dim3(256), 0, s, a)
+  if (head_dim == 128) {
+    if (r3) { if (fused) MF_PROLOGUE(128, true, true); else MF_PROLOGUE(128, true, false); }
+    else { if (fused) MF_PROLOGUE(128, false, true); else MF_PROLOGUE(128, false, false); }
+  } else {
+    if (r3) { if (fused) MF_PROLOGUE(64, true, true); else MF_PROLOGUE(64, true, false); }
+    else { if (fused) MF_PROLOGUE(64, false, true); else MF_PROLOGUE(64, false, false); }
+  }
+#undef MF_PROLOGUE
+  return hipGetLastError();
+}
+
+// f32 prologue (after meta_kernel). r3 == nullptr: 2D RoPE with the table cs;
+// else frame-aware RoPE.
 hipError_t launch_rope_pack(const void* q, const void* k, const void* v, const int32_t* grid_hw,
                             const int32_t* text_len, const char* ws, const WsLayout& l,
-                            const float2* cs, const Rope3* r3, int32_t heads, int32_t head_dim, bool bf16,
+                            const float2* cs, const Rope3* r3, int32_t heads, int32_t head_dim, const Strides& st,
                             hipStream_t s) {
   const Rope3 r = r3 ? *r3 : Rope3{nullptr, 0, 0};
-  if (bf16) {
-    return r3 ? launch_rope_pack_d<uint16_t, true>(q, k, v, grid_hw, text_len, ws, l, cs, r, heads, head_dim, s)
-              : launch_rope_pack_d<uint16_t, false>(q, k, v, grid_hw, text_len, ws, l, cs, r, heads, head_dim, s);
-  }
-  return r3 ? launch_rope_pack_d<float, true>(q, k, v, grid_hw, text_len, ws, l, cs, r, heads, head_dim, s)
-            : launch_rope_pack_d<float, false>(q, k, v, grid_hw, text_len, ws, l, cs, r, heads, head_dim, s);
+  return r3 ? launch_rope_pack_d<float, true>(q, k, v, grid_hw, text_len, ws, l, cs, r, heads, head_dim, st, s)
+            : launch_rope_pack_d<float, false>(q, k, v, grid_hw, text_len, ws, l, cs, r, heads, head_dim, st, s);
 }
 
 template <typename T, int D, bool R3>

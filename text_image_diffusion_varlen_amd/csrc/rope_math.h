@@ -23,6 +23,14 @@ template <> struct Elem<float> {
 
 template <typename T> struct alignas(16) Chunk { T v[16 / sizeof(T)]; };
 
+// One channel pair turned by the angle with cosine c and sine s:
+// (x0, x1) -> (x0 c - x1 s, x0 s + x1 c). The fused multiply-adds are written
+// out so that every kernel that rotates (prologue, query load, standalone
+// RoPE, 2D and frame-aware tables) rounds identically.
+__device__ inline float2 rotate_pair(float x0, float x1, float c, float s) {
+  return make_float2(__builtin_fmaf(x0, c, -(x1 * s)), __builtin_fmaf(x0, s, x1 * c));
+}
+
 // Rotates one 16-byte chunk (channels d0 .. d0+E-1, E even) of a row at (row, col).
 template <typename T, int D>
 __device__ inline Chunk<T> rotate_chunk(const Chunk<T>& in, int d0, int32_t row, int32_t col,
@@ -38,8 +46,9 @@ __device__ inline Chunk<T> rotate_chunk(const Chunk<T>& in, int d0, int32_t row,
     const float2 r = cs[p * (D / 4) + j];
     const float x0 = Elem<T>::load(in.v[2 * pp]);
     const float x1 = Elem<T>::load(in.v[2 * pp + 1]);
-    out.v[2 * pp] = Elem<T>::store(x0 * r.x - x1 * r.y);
-    out.v[2 * pp + 1] = Elem<T>::store(x0 * r.y + x1 * r.x);
+    const float2 y = rotate_pair(x0, x1, r.x, r.y);
+    out.v[2 * pp] = Elem<T>::store(y.x);
+    out.v[2 * pp + 1] = Elem<T>::store(y.y);
   }
   return out;
 }
@@ -70,8 +79,9 @@ __device__ inline Chunk<T> rotate_chunk3(const Chunk<T>& in, int d0, int32_t row
     const float2 c = rope3_cs(r, D, d0 / 2 + pp, row, col, frame);
     const float x0 = Elem<T>::load(in.v[2 * pp]);
     const float x1 = Elem<T>::load(in.v[2 * pp + 1]);
-    out.v[2 * pp] = Elem<T>::store(x0 * c.x - x1 * c.y);
-    out.v[2 * pp + 1] = Elem<T>::store(x0 * c.y + x1 * c.x);
+    const float2 y = rotate_pair(x0, x1, c.x, c.y);
+    out.v[2 * pp] = Elem<T>::store(y.x);
+    out.v[2 * pp + 1] = Elem<T>::store(y.y);
   }
   return out;
 }
