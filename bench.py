@@ -28,7 +28,7 @@ sys.path.insert(0, ROOT)
 
 PEAK = {"bf16": 2.5e15, "f32": 157.3e12}  # dense MFMA bf16; fp32 vector ALU
 HBM_PEAK = 8.0e12
-TRAFFIC_FILE = os.path.join(ROOT, "profiles", "attn_fwd_bf16_1024sq_traffic.json")
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "attn_fwd_bf16_{config}_traffic.json")
 KERNEL_SOURCES = [
     os.path.join(ROOT, "text_image_diffusion_varlen_amd", "csrc", name)
     for name in ("attn_fwd.hip", "mf_common.h", "mfma_util.h", "rope_math.h")
@@ -57,9 +57,10 @@ def kernel_sha() -> str:
 def stored_traffic(config: str):
     """Measured HBM bytes per launch of the attention kernel, if the counters were
     taken on the current kernel source for this workload; else None."""
-    if config != "1024sq" or not os.path.exists(TRAFFIC_FILE):
+    path = TRAFFIC_FILE.format(config=config)
+    if not os.path.exists(path):
         return None
-    with open(TRAFFIC_FILE) as f:
+    with open(path) as f:
         rec = json.load(f)
     if rec.get("source_sha256") != kernel_sha():
         return None
