@@ -575,6 +575,10 @@ def forward_bench(config: str, seed, steps: int, warmup: int, keep_host: bool):
         gpu_meta = (cu.cpu().numpy(), pos.cpu().numpy())
 
     achieved = flops / (stage["attn"] / 1e3)
+    # bf16 batches of at most 64 samples have no separate metadata kernel (its
+    # stage is only the gap between two events)
+    meta_kernel = w.dtype != "bf16" or w.n_seg > 64
+    b2b_ms = ms - stage["rope_pack"] - (stage["meta"] if meta_kernel else 0.0)
     # prologue: bf16 reads k, v and writes K~, V~ (queries are rotated inside the attention kernel);
     # f32 also reads q and writes Q~
     rope_bytes = (4.0 if w.dtype == "bf16" else 6.0) * w.tokens * w.heads * w.head_dim * elem
@@ -594,6 +598,11 @@ def forward_bench(config: str, seed, steps: int, warmup: int, keep_host: bool):
         "tokens_per_s": round(w.tokens / (ms / 1e3), 1),
         "stages_ms": {k2: round(v2, 4) for k2, v2 in stage.items()},
         "attn_ms_p10_p50_p90": [round(float(x), 4) for x in np.percentile(attn_each, [10, 50, 90])] if not edit else None,
+        # The attention kernel inside the back-to-back timed steps (no events between
+        # launches): step time minus the prologue's event-timed share. Back-to-back
+        # launches run slower than the event-bracketed ones that `roofline` uses.
+        "attn_ms_back_to_back_est": round(b2b_ms, 4) if not edit else None,
+        "frac_back_to_back_est": round(flops / (b2b_ms / 1e3) / PEAK[w.dtype], 4) if not edit else None,
         "rope_pack_gbps": round(rope_bytes / (stage["rope_pack"] / 1e3) / 1e9, 1) if not edit else None,
         "rope_pack_gbps_cold_mall": round(rope_bytes / (float(np.median(pack_cold)) / 1e3) / 1e9, 1) if not edit else None,
         "roofline": {
