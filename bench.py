@@ -621,6 +621,32 @@ def forward_bench(config: str, seed, steps: int, warmup: int, keep_host: bool):
             "frames": frames, "gpu_out": gpu_out, "gpu_meta": gpu_meta}
 
 
+def gemm_context(steps: int = 20):
+    """For context: the dense bf16 rate a large library GEMM (torch.matmul,
+    hipBLASLt, 8192^3, random N(0,1) operands) reaches on this device in this
+    run, i.e. the practical MFMA ceiling the attention kernel is compared with."""
+    import torch
+
+    n = 8192
+    gen = torch.Generator(device="cuda").manual_seed(1)
+    a = torch.randn((n, n), generator=gen, device="cuda").to(torch.bfloat16)
+    b = torch.randn((n, n), generator=gen, device="cuda").to(torch.bfloat16)
+    c = torch.empty((n, n), dtype=torch.bfloat16, device="cuda")
+    for _ in range(3):
+        torch.matmul(a, b, out=c)
+    start, stop = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    start.record()
+    for _ in range(steps):
+        torch.matmul(a, b, out=c)
+    stop.record()
+    torch.cuda.synchronize()
+    ms = start.elapsed_time(stop) / steps
+    tf = 2.0 * n ** 3 / (ms / 1e3) / 1e12
+    del a, b, c
+    return {"torch_matmul_bf16_8192cube_tflops": round(tf, 1), "frac_of_peak": round(tf * 1e12 / PEAK["bf16"], 4)}
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -689,6 +715,8 @@ def main():
     if w.dtype == "bf16" and not args.no_backward:
         result["backward"] = backward_bench(w, q, k, v, cu, grid, text, args.steps, args.warmup,
                                             frames if edit else None)
+    if w.dtype == "bf16":
+        result["gemm_context"] = gemm_context()
     if not args.no_pack:
         result["joint_pack"] = pack_bench(w, cu, grid, text, args.steps, args.warmup, frames)
     if w.dtype == "bf16" and not args.no_qkv:

@@ -32,8 +32,10 @@
 // there, the 16 lanes that read one MFMA operand row block touch 16
 // consecutive chunks (no bank conflicts) and every read is a fixed offset
 // from a per-lane base.
-// Rows that belong to no token (padding up to KTILE, and the slack after the
-// last sample) are written as zeros.
+// Rows that belong to no token are written as zeros: the padding up to KTILE
+// of every sample, and for fp32 also the slack after the last sample (read by
+// the last query tile's Q~ rows; the bf16 prologue skips the slack, which no
+// bf16 kernel reads).
 #include "meta_small.h"
 #include "mf_common.h"
 #include "rope_math.h"
@@ -159,6 +161,9 @@ __global__ void __launch_bounds__(256) prologue_bf16_kernel(PrologueArgs a) {
     if (reinterpret_cast<const WsHeader*>(a.ws)->flag != FLAG_OK) return;
     ws_tile_sample<R3>(a, r0, ts);
   }
+  // Tiles past the last sample (the slack rows) are never read by the bf16
+  // attention kernel, which visits only its sample's own key tiles.
+  if (ts.L == 0) return;
   const int64_t tile_off = (int64_t(h) * a.rows + r0) * D;
   const int64_t tok_base = ts.tok0 - ts.u0;  // packed index of the sample's first token
   // Every thread loads, for chunks f = t, t + 256, ...: the K chunk (rotated

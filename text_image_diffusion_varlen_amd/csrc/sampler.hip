@@ -72,22 +72,12 @@ cfg_euler_kernel(float* __restrict__ z, const T* __restrict__ v, const int32_t* 
   __shared__ int32_t wbad[CFG_THREADS / 64];
   const int t = threadIdx.x;
 
-  // Chunk i is channels [8 (i % groups), +8) of z token i / groups. The z loads
-  // of the first pass depend on nothing but the chunk index, so they are issued
-  // before the table is built and their latency overlaps it.
+  // Chunk i is channels [8 (i % groups), +8) of z token i / groups.
   const uint32_t groups = uint32_t(channels) >> 3;
   const uint32_t work = uint32_t(image_tokens) * groups;  // < 2^31, checked on the host
   const uint32_t stride = gridDim.x * CFG_THREADS;
   uint32_t base = blockIdx.x * CFG_THREADS + t;
   float zz[CFG_UNROLL][8];
-#pragma unroll
-  for (int u = 0; u < CFG_UNROLL; ++u) {
-    const uint32_t i = base + u * stride;
-    if (i < work) {
-      const uint32_t tk = i / groups;
-      load8(z + int64_t(tk) * channels + (i - tk * groups) * 8, zz[u]);
-    }
-  }
 
   // Thread t checks and sizes the contiguous run of images [b0, b1). Every map
   // entry is loaded in one round (indices clamped into range, checks applied
@@ -110,6 +100,18 @@ cfg_euler_kernel(float* __restrict__ z, const T* __restrict__ v, const int32_t* 
     urow[b] = us >= 0 ? ua + ut : ca + ct;
     zoff[b] = hw;  // image size for now; replaced by its offset below
     local += hw;   // <= 4096 images of <= 512 x 512 tokens: fits int32
+  }
+  // The z loads of the first pass depend on nothing but the chunk index: they
+  // are issued after this thread's map loads (so that those, which the table
+  // waits for, are not queued behind them) and before the table is built,
+  // whose latency they overlap.
+#pragma unroll
+  for (int u = 0; u < CFG_UNROLL; ++u) {
+    const uint32_t i = base + u * stride;
+    if (i < work) {
+      const uint32_t tk = i / groups;
+      load8(z + int64_t(tk) * channels + (i - tk * groups) * 8, zz[u]);
+    }
   }
   // Block-wide exclusive scan of `local`: shuffles inside each wave, then the
   // four wave totals through LDS.
