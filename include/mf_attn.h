@@ -462,7 +462,9 @@ int mf_rf_cfg_euler_step(float* z, const void* v, const int32_t* cu_seqlens, con
  * metadata check on any of this device's library workspaces (forward,
  * backward, projection, the allocation-free forward's scratch) or the sticky
  * flag of the standalone metadata, RoPE and sampler calls failed, else MF_OK.
- * The sticky flag is cleared once reported.
+ * Each failure is reported once: the sticky flag is cleared and a failed
+ * workspace check is marked as reported (the next call on that workspace
+ * checks afresh), so a later call that fails nothing returns MF_OK.
  */
 int mf_get_device_error(hipStream_t stream);
 

@@ -988,18 +988,18 @@ int mf_get_device_error(hipStream_t stream) {
     if (v && (e = hipMemset(st.status, 0, 4)) != hipSuccess) return hip_fail(e, "hipMemset(status)");
     flags |= v;
   }
-  if (st.qws) {
-    int32_t qf = 0;
-    if ((e = hipMemcpy(&qf, st.qws, 4, hipMemcpyDeviceToHost)) != hipSuccess)
-      return hip_fail(e, "hipMemcpy(projection workspace header)");
-    flags |= qf;
-  }
-  for (char* w : {st.ws, st.bws, st.scratch}) {
+  // Workspace headers (their flag is the first field): a failed check is
+  // marked as reported; the next call on that workspace rewrites the header.
+  for (char* w : {st.qws, st.ws, st.bws, st.scratch}) {
     if (!w) continue;
-    mf::WsHeader hdr;
-    if ((e = hipMemcpy(&hdr, w, sizeof(hdr), hipMemcpyDeviceToHost)) != hipSuccess)
+    int32_t f = 0;
+    if ((e = hipMemcpy(&f, w, sizeof(f), hipMemcpyDeviceToHost)) != hipSuccess)
       return hip_fail(e, "hipMemcpy(workspace header)");
-    flags |= hdr.flag;
+    if (f == mf::FLAG_OK || f == mf::FLAG_REPORTED) continue;
+    flags |= f;
+    const int32_t reported = mf::FLAG_REPORTED;
+    if ((e = hipMemcpy(w, &reported, sizeof(reported), hipMemcpyHostToDevice)) != hipSuccess)
+      return hip_fail(e, "hipMemcpy(workspace header)");
   }
   if (flags) return fail(MF_ERR_METADATA, "device check failed (flags 0x%x)", unsigned(flags));
   return MF_OK;

@@ -23,7 +23,9 @@ constexpr int ATTN_THREADS = 64 * ATTN_WAVES;
 constexpr int ROPE_PMAX = 512;
 constexpr int MAX_SEGMENTS = 4096;
 
-enum : int32_t { FLAG_OK = 0, FLAG_METADATA = 1, FLAG_POSITION = 2 };
+// FLAG_REPORTED marks a failed check that mf_get_device_error has already
+// returned: still not FLAG_OK (no kernel uses that header), not reported again.
+enum : int32_t { FLAG_OK = 0, FLAG_METADATA = 1, FLAG_POSITION = 2, FLAG_REPORTED = 4 };
 
 __host__ __device__ inline int64_t round_up(int64_t x, int64_t m) { return (x + m - 1) / m * m; }
 __host__ __device__ inline int64_t ceil_div(int64_t x, int64_t m) { return (x + m - 1) / m; }
