@@ -166,34 +166,64 @@ __global__ void __launch_bounds__(256) prologue_bf16_kernel(PrologueArgs a) {
   if (ts.L == 0) return;
   const int64_t tile_off = (int64_t(h) * a.rows + r0) * D;
   const int64_t tok_base = ts.tok0 - ts.u0;  // packed index of the sample's first token
-  // Every thread loads, for chunks f = t, t + 256, ...: the K chunk (rotated
-  // here) and the V chunk of row f / CPR, both into LDS.
-  for (int f = t; f < CPT; f += 256) {
-    const int rr = f / CPR, cc = f % CPR;
+  // Every thread handles chunks f = t + 256 i of the tile (row f / CPR, channel
+  // chunk f % CPR): its K and V chunks and (2D) the four (cos, sin) entries of
+  // the K chunk are all loaded before any is used (native vector registers;
+  // rows past the sample re-read its last token and are zeroed), then K is
+  // rotated and both go to LDS.
+  constexpr int PER = CPT / 256;
+  typedef uint32_t u32x4v __attribute__((ext_vector_type(4)));
+  typedef float f32x4 __attribute__((ext_vector_type(4)));
+  u32x4v kr[PER], vr[PER];
+  f32x4 tab[R3 ? 1 : PER][2];
+#pragma unroll
+  for (int i = 0; i < PER; ++i) {
+    const int f = t + 256 * i, rr = f / CPR, cc = f % CPR;
+    const int32_t u = min(ts.u0 + rr, ts.L - 1);
+    const int64_t row = tok_base + u;
+    kr[i] = *reinterpret_cast<const u32x4v*>(a.k + row * a.k_st + int64_t(h) * a.k_sh + cc * 8);
+    vr[i] = *reinterpret_cast<const u32x4v*>(a.v + row * a.v_st + int64_t(h) * a.v_sh + cc * 8);
+    if constexpr (!R3) {
+      int32_t prow, pcol;
+      token_position(u, ts.tl, ts.w, prow, pcol);
+      const bool first_half = cc < CPR / 2;
+      const f32x4* e = reinterpret_cast<const f32x4*>(a.cs + (first_half ? prow : pcol) * (D / 4) +
+                                                      4 * (first_half ? cc : cc - CPR / 2));
+      tab[i][0] = e[0];
+      tab[i][1] = e[1];
+    }
+  }
+  __builtin_amdgcn_sched_barrier(0);  // every load above in flight before the first use
+#pragma unroll
+  for (int i = 0; i < PER; ++i) {
+    const int f = t + 256 * i, rr = f / CPR, cc = f % CPR;
     const int32_t u = ts.u0 + rr;
-    Chunk<uint16_t> ko, vi;
+    Chunk<uint16_t> ko;
+    u32x4v vo = vr[i];
     if (u < ts.L) {
-      const Chunk<uint16_t> x =
-          *reinterpret_cast<const Chunk<uint16_t>*>(a.k + (tok_base + u) * a.k_st + int64_t(h) * a.k_sh + cc * 8);
-      vi = *reinterpret_cast<const Chunk<uint16_t>*>(a.v + (tok_base + u) * a.v_st + int64_t(h) * a.v_sh + cc * 8);
+      const Chunk<uint16_t> x = __builtin_bit_cast(Chunk<uint16_t>, kr[i]);
       if constexpr (R3) {
         int32_t row, col, frame;
         token_position3(u, ts.tl, ts.gh, ts.w, row, col, frame);
         ko = rotate_chunk3<uint16_t, D>(x, cc * 8, row, col, frame, a.r3);
       } else {
-        int32_t row, col;
-        token_position(u, ts.tl, ts.w, row, col);
-        ko = rotate_chunk<uint16_t, D>(x, cc * 8, row, col, a.cs);
+#pragma unroll
+        for (int pp = 0; pp < 4; ++pp) {
+          const float c = tab[i][pp >> 1][2 * (pp & 1)], sn = tab[i][pp >> 1][2 * (pp & 1) + 1];
+          const float2 y = rotate_pair(bf16_to_f32(x.v[2 * pp]), bf16_to_f32(x.v[2 * pp + 1]), c, sn);
+          ko.v[2 * pp] = f32_to_bf16_rne(y.x);
+          ko.v[2 * pp + 1] = f32_to_bf16_rne(y.y);
+        }
       }
     } else {
 #pragma unroll
-      for (int e = 0; e < 8; ++e) ko.v[e] = vi.v[e] = 0;
+      for (int e = 0; e < 8; ++e) ko.v[e] = 0;
+      vo = u32x4v{0, 0, 0, 0};
     }
     ks[cc * KS + rr] = ko;
     uint32_t* dst = reinterpret_cast<uint32_t*>(vs + rr * VS + cc * 8);
-    const uint32_t* sv = reinterpret_cast<const uint32_t*>(vi.v);
 #pragma unroll
-    for (int e = 0; e < 4; ++e) dst[e] = sv[e];
+    for (int e = 0; e < 4; ++e) dst[e] = vo[e];
   }
   __syncthreads();
   // K~ chunk f2 = cc * KTILE + rr (chunk-major).
