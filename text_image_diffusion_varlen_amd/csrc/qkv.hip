@@ -18,7 +18,7 @@
 //                     activation buffer X~ (text rows, then visual rows).
 //   qkv_gemm_kernel   per modality a GEMM over its rows: workgroup tile 256
 //                     output features x 256 tokens, 8 waves of 128 x 64,
-//                     v_mfma_f32_32x32x16_bf16 with D = W' X^T (lane = token),
+//                     v_mfma_f32_16x16x32_bf16 with D = W' X^T (lane = token),
 //                     K staged 64 channels at a time in LDS by direct-to-LDS
 //                     copies, double-buffered; the epilogue scales by 1 / r_t
 //                     and writes q, k, v rows directly. A last round that
@@ -256,13 +256,22 @@ struct QkvGemmArgs {
   int32_t ncu;         // compute units for the halved last round (0: never halve)
 };
 
+// D (16 x 16, fp32) += A (16 x 32, bf16) B (32 x 16, bf16): lane l supplies A
+// row l % 16 and B column l % 16, k = 8 (l / 16) .. +7 of each; it receives D
+// column l % 16, rows 4 (l / 16) .. +3.
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+__device__ inline f32x4 mfma16(const bf16x8& a, const bf16x8& b, const f32x4& c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+}
+
 // One GEMM unit (256 output features x 256 tokens of one modality) or, with
-// NB = 2, one 128-feature half of it starting at feature fbase of the tile:
-// every wave owns NB * 32 features x 64 tokens. Both halves copy the whole
-// stages (the tiled layout keeps a stage contiguous) and read their features.
-// Per output element the products are summed in the same stage and k-step
-// order in both forms, so a half unit's outputs equal the whole unit's bit
-// for bit.
+// NB = 4, one 128-feature half of it starting at feature fbase of the tile:
+// every wave owns NB * 16 features x 64 tokens, on v_mfma_f32_16x16x32_bf16
+// (which sustains a higher rate on this chip than the 32 x 32 form). Both
+// halves copy the whole stages (the tiled layout keeps a stage contiguous) and
+// read their features. Per output element the products are summed in the
+// same stage and k-step order in both forms, so a half unit's outputs equal
+// the whole unit's bit for bit.
 template <int NB>
 __device__ inline void qkv_gemm_unit(const QkvGemmArgs& a, const QkvHeader* hdr, int unit, int fbase,
                                      u32x4 (*lds)[2 * QKV_CH]) {
@@ -280,9 +289,9 @@ __device__ inline void qkv_gemm_unit(const QkvGemmArgs& a, const QkvHeader* hdr,
   const int32_t* rows = reinterpret_cast<const int32_t*>(a.ws + (m ? a.l.off_img : a.l.off_txt));
   const int32_t row0 = tt * QKV_TT;
   const int tid = threadIdx.x;
-  const int wave = tid >> 6, lane = tid & 63, hf = lane >> 5, l32 = lane & 31;
+  const int wave = tid >> 6, lane = tid & 63, g = lane >> 4, l16 = lane & 15;
   const int wt = wave >> 1;                     // 64-token quarter
-  const int fw = fbase + (wave & 1) * NB * 32;  // this wave's first feature in the tile
+  const int fw = fbase + (wave & 1) * NB * 16;  // this wave's first feature in the tile
 
   // Both operands are tiled: a stage of one operand is 2048 contiguous chunks,
   // copied verbatim (chunk c of row r lands at c * 256 + r).
@@ -295,55 +304,56 @@ __device__ inline void qkv_gemm_unit(const QkvGemmArgs& a, const QkvHeader* hdr,
     copy_to_lds<QKV_CH, QKV_THREADS / 64>(xsrc + int64_t(s) * QKV_CH, dst + QKV_CH, wave, lane);
   };
 
-  f32x16 acc[NB][2];
+  f32x4 acc[NB][4];
 #pragma unroll
-  for (int nb = 0; nb < NB; ++nb) acc[nb][0] = acc[nb][1] = f32x16{};
+  for (int nb = 0; nb < NB; ++nb)
+#pragma unroll
+    for (int tb = 0; tb < 4; ++tb) acc[nb][tb] = f32x4{};
   const int stages = a.hidden / QKV_KS;
   load_stage(0, lds[0]);
   wait_vm_and_sync();
   for (int s = 0; s < stages; ++s) {
     const u32x4* cur = lds[s & 1];
     if (s + 1 < stages) load_stage(s + 1, lds[(s + 1) & 1]);
-    const u32x4* al = cur + hf * QKV_NT + fw + l32;
-    const u32x4* bl = cur + QKV_CH + hf * QKV_NT + wt * 64 + l32;
+    // Lane (g, l16) reads chunk 4 ks + g of row l16 of every 16-row block.
+    const u32x4* al = cur + g * QKV_NT + fw + l16;
+    const u32x4* bl = cur + QKV_CH + g * QKV_TT + wt * 64 + l16;
 #pragma unroll
-    for (int ks = 0; ks < QKV_KS / 16; ++ks) {
-      bf16x8 bo[2];
+    for (int ks = 0; ks < QKV_KS / 32; ++ks) {
+      bf16x8 bo[4];
 #pragma unroll
-      for (int tb = 0; tb < 2; ++tb) bo[tb] = as_bf16x8(bl[2 * QKV_NT * ks + 32 * tb]);
+      for (int tb = 0; tb < 4; ++tb) bo[tb] = as_bf16x8(bl[4 * QKV_TT * ks + 16 * tb]);
 #pragma unroll
       for (int nb = 0; nb < NB; ++nb) {
-        const bf16x8 ao = as_bf16x8(al[2 * QKV_NT * ks + 32 * nb]);
-        acc[nb][0] = mfma32(ao, bo[0], acc[nb][0]);
-        acc[nb][1] = mfma32(ao, bo[1], acc[nb][1]);
+        const bf16x8 ao = as_bf16x8(al[4 * QKV_NT * ks + 16 * nb]);
+#pragma unroll
+        for (int tb = 0; tb < 4; ++tb) acc[nb][tb] = mfma16(ao, bo[tb], acc[nb][tb]);
       }
     }
     wait_vm_and_sync();
   }
 
-  // Epilogue: lane = token, entry e of block nb = feature fw + 32nb + 8(e/4) + 4hf + e%4.
+  // Epilogue: lane (g, l16) holds features fw + 16 nb + 4 g .. +3 of token
+  // wt * 64 + 16 tb + l16 in acc[nb][tb].
   const float* ssq = reinterpret_cast<const float*>(a.ws + a.l.off_inv);
   const int32_t groups = rms_groups(a.hidden);
 #pragma unroll
-  for (int tb = 0; tb < 2; ++tb) {
-    const int32_t row = row0 + wt * 64 + tb * 32 + l32;
+  for (int tb = 0; tb < 4; ++tb) {
+    const int32_t row = row0 + wt * 64 + tb * 16 + l16;
     if (row >= count) continue;
     const int32_t tok = rows[row];
     float ss = 0.f;
-    for (int g = 0; g < groups; ++g) ss += ssq[int64_t(tok) * groups + g];
+    for (int gg = 0; gg < groups; ++gg) ss += ssq[int64_t(tok) * groups + gg];
     const float sc = 1.0f / sqrtf(ss / float(a.hidden) + a.eps);
 #pragma unroll
     for (int nb = 0; nb < NB; ++nb) {
-#pragma unroll
-      for (int g = 0; g < 4; ++g) {
-        const int n = nt * QKV_NT + fw + nb * 32 + 8 * g + 4 * hf;
-        const int which = n / a.hd, rem = n - which * a.hd;
-        uint16_t* dst = (which == 0 ? a.q : which == 1 ? a.k : a.v) + int64_t(tok) * a.hd + rem;
-        uint2 o;
-        o.x = pack_bf16x2(acc[nb][tb][4 * g] * sc, acc[nb][tb][4 * g + 1] * sc);
-        o.y = pack_bf16x2(acc[nb][tb][4 * g + 2] * sc, acc[nb][tb][4 * g + 3] * sc);
-        *reinterpret_cast<uint2*>(dst) = o;
-      }
+      const int n = nt * QKV_NT + fw + nb * 16 + 4 * g;
+      const int which = n / a.hd, rem = n - which * a.hd;
+      uint16_t* dst = (which == 0 ? a.q : which == 1 ? a.k : a.v) + int64_t(tok) * a.hd + rem;
+      uint2 o;
+      o.x = pack_bf16x2(acc[nb][tb][0] * sc, acc[nb][tb][1] * sc);
+      o.y = pack_bf16x2(acc[nb][tb][2] * sc, acc[nb][tb][3] * sc);
+      *reinterpret_cast<uint2*>(dst) = o;
     }
   }
 }
@@ -384,10 +394,10 @@ __global__ void __launch_bounds__(QKV_THREADS, 2) qkv_gemm_kernel(QkvGemmArgs a)
   const int b = int(blockIdx.x);
   const int token_tiles = units / a.n_tiles;
   if (b < n_full) {
-    qkv_gemm_unit<4>(a, hdr, unit_at(xcd_position(b, n_full), a.n_tiles, token_tiles), 0, lds);
+    qkv_gemm_unit<8>(a, hdr, unit_at(xcd_position(b, n_full), a.n_tiles, token_tiles), 0, lds);
   } else if (halve && b < n_full + 2 * tail) {
     const int piece = b - n_full;
-    qkv_gemm_unit<2>(a, hdr, unit_at(n_full + piece / 2, a.n_tiles, token_tiles), (piece % 2) * (QKV_NT / 2), lds);
+    qkv_gemm_unit<4>(a, hdr, unit_at(n_full + piece / 2, a.n_tiles, token_tiles), (piece % 2) * (QKV_NT / 2), lds);
   }
 }
 
