@@ -78,102 +78,135 @@ __device__ inline void wait_tile_and_sync() { wait_vm_and_sync(); }
 template <int D>
 struct Bf16Tile {
   static constexpr int CHUNKS = KTILE * D / 8;  // 16-byte chunks per K~ (or V~^T) tile
-  static constexpr int KSTEPS = D / 16;         // MFMA k-steps of the score product
-  static constexpr int DBLK = D / 32;           // 32-channel blocks of the output
+  static constexpr int KSTEPS = D / 32;         // MFMA k-steps of the score product
+  static constexpr int CBLK = D / 16;           // 16-channel blocks of the output
 };
 
-// One 64-key tile of one wave's 32 query rows: S^T = K~ Q~^T, online softmax,
-// O^T += V~^T P^T. kt / vt point at the chunk-major K~ and V~^T tiles in LDS.
-template <int D, bool MASKED>
-__device__ inline void attend_tile(const u32x4* kt, const u32x4* vt, const bf16x8 (&qreg)[D / 16],
-                                   f32x16 (&acc)[D / 32], float& m, float& lsum, float c,
-                                   int kbase_key, int L, int hf, int l32) {
-  constexpr int KSTEPS = Bf16Tile<D>::KSTEPS;
-  constexpr int DBLK = Bf16Tile<D>::DBLK;
-  constexpr float REF_SLACK = 8.0f;
-  // K~ chunk (c, n) sits at c * KTILE + n: lane (l32, hf) reads key n = l32 (+32)
-  // and channel chunk 2*ks + hf, i.e. base + 2*KTILE*ks (+32).
-  const u32x4* kl = kt + hf * KTILE + l32;
-  // V~^T chunk (g, r) sits at g * D + r: lane reads channel r = 32*b + l32, key chunk 2*ks2 + hf.
-  const u32x4* vl = vt + hf * D + l32;
+// Max / sum of a value over the four lanes l % 16 + 16 r (r = 0..3): rows r
+// and r ^ 2 through v_permlane32_swap, then rows r and r ^ 1 through
+// v_permlane16_swap (with both operands equal, the two results hold the value
+// of the lane's row pair, so the combine needs no lane test).
+__device__ inline float quad_max(float x) {
+  x = halves_max(x);
+  const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return __builtin_elementwise_maximum(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ inline float quad_sum(float x) {
+  x = halves_sum(x);
+  const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
 
-  f32x16 s0 = {}, s1 = {};
-  bf16x8 kb0[4], kb1[4];
+// One 64-key tile of one wave's 32 query rows (two blocks of 16): S^T = K~ Q~^T,
+// online softmax, O^T += V~^T P^T. kt / vt point at the chunk-major K~ and
+// V~^T tiles in LDS. Lane (g, l16) = (lane / 16, lane % 16) holds, for query
+// 16 qb + l16, the scores of keys 16 kb + 4 g + i (i = 0..3) in s[kb][qb] and
+// the output channels 16 cb + 4 g + i in acc[cb][qb].
+template <int D, bool MASKED>
+__device__ inline void attend_tile(const u32x4* kt, const u32x4* vt, const bf16x8 (&qreg)[2][D / 32],
+                                   f32x4 (&acc)[D / 16][2], float (&m)[2], float (&lsum)[2], float c,
+                                   int kbase_key, int L, int g, int l16) {
+  constexpr int KSTEPS = Bf16Tile<D>::KSTEPS;
+  constexpr int CBLK = Bf16Tile<D>::CBLK;
+  constexpr float REF_SLACK = 8.0f;
+  // K~ chunk (c, n) sits at c * KTILE + n: lane reads key 16 kb + l16, channel
+  // chunk 4 ks + g.
+  const u32x4* kl = kt + g * KTILE + l16;
+  // V~^T chunk (k8, r) sits at k8 * D + r and holds, for channel r, keys
+  // 32 (k8 / 4) + 4 (k8 % 4) + {0..3, 16..19}: lane reads channel 16 cb + l16,
+  // key chunk 4 j + g, the keys its own P^T operand carries.
+  const u32x4* vl = vt + g * D + l16;
+
+  f32x4 s[4][2];
 #pragma unroll
-  for (int ks = 0; ks < 4; ++ks) {
-    kb0[ks] = __builtin_bit_cast(bf16x8, kl[2 * KTILE * ks]);
-    kb1[ks] = __builtin_bit_cast(bf16x8, kl[2 * KTILE * ks + 32]);
-  }
+  for (int kb = 0; kb < 4; ++kb) s[kb][0] = s[kb][1] = f32x4{};
 #pragma unroll
   for (int ks = 0; ks < KSTEPS; ++ks) {
-    const bf16x8 a0 = kb0[ks & 3], a1 = kb1[ks & 3];
-    if (ks + 4 < KSTEPS) {
-      kb0[ks & 3] = __builtin_bit_cast(bf16x8, kl[2 * KTILE * (ks + 4)]);
-      kb1[ks & 3] = __builtin_bit_cast(bf16x8, kl[2 * KTILE * (ks + 4) + 32]);
+#pragma unroll
+    for (int kb = 0; kb < 4; ++kb) {
+      const bf16x8 kk = __builtin_bit_cast(bf16x8, kl[4 * KTILE * ks + 16 * kb]);
+      s[kb][0] = mfma16(kk, qreg[0][ks], s[kb][0]);
+      s[kb][1] = mfma16(kk, qreg[1][ks], s[kb][1]);
     }
-    s0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a0, qreg[ks], s0, 0, 0, 0);
-    s1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a1, qreg[ks], s1, 0, 0, 0);
   }
-  // V operands of the first two k-steps, read while the softmax runs.
-  bf16x8 vb[2][DBLK];
+  // V operands of the first 32 keys, read while the softmax runs.
+  bf16x8 vb[CBLK];
 #pragma unroll
-  for (int k2 = 0; k2 < 2; ++k2) {
-#pragma unroll
-    for (int b = 0; b < DBLK; ++b) vb[k2][b] = __builtin_bit_cast(bf16x8, vl[2 * D * k2 + 32 * b]);
-  }
-  // Accumulator entry e holds key 8*(e/4) + 4*hf + e%4 of the tile (s1: +32).
+  for (int cb = 0; cb < CBLK; ++cb) vb[cb] = __builtin_bit_cast(bf16x8, vl[16 * cb]);
   if constexpr (MASKED) {
-    const int kb = kbase_key + 4 * hf;
+    const int kb0 = kbase_key + 4 * g;
 #pragma unroll
-    for (int e = 0; e < 16; ++e) {
-      const int key = kb + 8 * (e >> 2) + (e & 3);
-      if (key >= L) s0[e] = -INFINITY;
-      if (key + 32 >= L) s1[e] = -INFINITY;
+    for (int kb = 0; kb < 4; ++kb)
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+        if (kb0 + 16 * kb + i >= L) s[kb][0][i] = s[kb][1][i] = -INFINITY;
+  }
+  // Row max: this lane's 16 keys of each query, then the other 48 from the
+  // lanes of the same query.
+  float mt[2];
+  bool grow[2];
+#pragma unroll
+  for (int qb = 0; qb < 2; ++qb) {
+    float mx = s[0][qb][0];
+#pragma unroll
+    for (int kb = 0; kb < 4; ++kb)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) mx = __builtin_elementwise_maximum(mx, s[kb][qb][i]);
+    mt[qb] = quad_max(mx) * c;
+    // The reference max only moves when a tile's max exceeds it by more than
+    // REF_SLACK, so p = exp2(s*c - m) <= 2^REF_SLACK and the accumulator is
+    // rescaled only on those tiles; numerator and denominator share m.
+    grow[qb] = mt[qb] > m[qb] + REF_SLACK;  // always true on the first tile (m = -inf)
+  }
+  if (__any(grow[0] || grow[1])) {
+#pragma unroll
+    for (int qb = 0; qb < 2; ++qb) {
+      const float mnew = grow[qb] ? mt[qb] : m[qb];
+      const float alpha = __builtin_amdgcn_exp2f(m[qb] - mnew);  // 0 on the first tile, 1 where unchanged
+      lsum[qb] *= alpha;
+#pragma unroll
+      for (int cb = 0; cb < CBLK; ++cb) acc[cb][qb] *= alpha;
+      m[qb] = mnew;
     }
   }
-  // Row max: this lane's 32 keys, then the other 32 from lane ^ 32.
-  float mx = __builtin_elementwise_maximum(s0[0], s1[0]);
+  // P^T operand of query block qb for keys 32 j .. 32 j + 31: k-slots 8 g .. +3
+  // are keys 32 j + 4 g + i, slots 8 g + 4 .. +7 keys 32 j + 16 + 4 g + i,
+  // i.e. s[2 j][qb] and s[2 j + 1][qb] of this lane.
+  u32x4 pk[2][2];
 #pragma unroll
-  for (int e = 1; e < 16; ++e) mx = __builtin_elementwise_maximum(__builtin_elementwise_maximum(mx, s0[e]), s1[e]);
-  const float mt = halves_max(mx) * c;
-  // The reference max only moves when a tile's max exceeds it by more than
-  // REF_SLACK, so p = exp2(s*c - m) <= 2^REF_SLACK and the accumulator is
-  // rescaled only on those tiles; numerator and denominator share m.
-  const bool grow = mt > m + REF_SLACK;  // always true on the first tile (m = -inf)
-  if (__any(grow)) {
-    const float mnew = grow ? mt : m;
-    const float alpha = __builtin_amdgcn_exp2f(m - mnew);  // 0 on the first tile, 1 where unchanged
-    lsum *= alpha;
+  for (int qb = 0; qb < 2; ++qb) {
+    const float nm = -m[qb];
 #pragma unroll
-    for (int b = 0; b < DBLK; ++b) acc[b] *= alpha;
-    m = mnew;
+    for (int j = 0; j < 2; ++j) {
+#pragma unroll
+      for (int h = 0; h < 2; ++h) {
+        const f32x4 x = s[2 * j + h][qb];
+        const float p0 = __builtin_amdgcn_exp2f(__builtin_fmaf(x[0], c, nm));
+        const float p1 = __builtin_amdgcn_exp2f(__builtin_fmaf(x[1], c, nm));
+        const float p2 = __builtin_amdgcn_exp2f(__builtin_fmaf(x[2], c, nm));
+        const float p3 = __builtin_amdgcn_exp2f(__builtin_fmaf(x[3], c, nm));
+        pk[j][qb][2 * h] = pack_bf16x2(p0, p1);
+        pk[j][qb][2 * h + 1] = pack_bf16x2(p2, p3);
+      }
+    }
   }
-  const float nm = -m;
-  uint32_t pk[4][4];  // P^T operand: k-step ks2 holds keys 16*ks2 + {4hf..4hf+3, 8+4hf..8+4hf+3}
+  // Row sums of the bf16 P actually multiplied into V (two keys per v_dot2).
 #pragma unroll
-  for (int e = 0; e < 16; e += 2) {
-    const float p0 = __builtin_amdgcn_exp2f(__builtin_fmaf(s0[e], c, nm));
-    const float p1 = __builtin_amdgcn_exp2f(__builtin_fmaf(s0[e + 1], c, nm));
-    const float p2 = __builtin_amdgcn_exp2f(__builtin_fmaf(s1[e], c, nm));
-    const float p3 = __builtin_amdgcn_exp2f(__builtin_fmaf(s1[e + 1], c, nm));
-    pk[e >> 3][(e & 7) >> 1] = pack_bf16x2(p0, p1);
-    pk[2 + (e >> 3)][(e & 7) >> 1] = pack_bf16x2(p2, p3);
-  }
-  // Row sum of the bf16 P actually multiplied into V (two keys per v_dot2).
+  for (int qb = 0; qb < 2; ++qb)
 #pragma unroll
-  for (int k2 = 0; k2 < 4; ++k2) {
+    for (int j = 0; j < 2; ++j)
 #pragma unroll
-    for (int i = 0; i < 4; ++i) lsum = dot2_bf16_sum(pk[k2][i], lsum);
-  }
+      for (int i = 0; i < 4; ++i) lsum[qb] = dot2_bf16_sum(pk[j][qb][i], lsum[qb]);
   // O^T += V~^T x P^T
 #pragma unroll
-  for (int ks2 = 0; ks2 < 4; ++ks2) {
-    const bf16x8 pb8 = __builtin_bit_cast(bf16x8, u32x4{pk[ks2][0], pk[ks2][1], pk[ks2][2], pk[ks2][3]});
+  for (int j = 0; j < 2; ++j) {
+    const bf16x8 p0 = __builtin_bit_cast(bf16x8, pk[j][0]), p1 = __builtin_bit_cast(bf16x8, pk[j][1]);
 #pragma unroll
-    for (int b = 0; b < DBLK; ++b) {
-      const bf16x8 vv = vb[ks2 & 1][b];
-      if (ks2 + 2 < 4) vb[ks2 & 1][b] = __builtin_bit_cast(bf16x8, vl[2 * D * (ks2 + 2) + 32 * b]);
-      acc[b] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vv, pb8, acc[b], 0, 0, 0);
+    for (int cb = 0; cb < CBLK; ++cb) {
+      const bf16x8 vv = vb[cb];
+      if (j == 0) vb[cb] = __builtin_bit_cast(bf16x8, vl[4 * D + 16 * cb]);
+      acc[cb][0] = mfma16(vv, p0, acc[cb][0]);
+      acc[cb][1] = mfma16(vv, p1, acc[cb][1]);
     }
   }
 }
@@ -182,7 +215,7 @@ template <int D, bool R3>
 __global__ void __launch_bounds__(ATTN_THREADS, 2) attn_fwd_bf16_kernel(AttnArgs a) {
   constexpr int CHUNKS = Bf16Tile<D>::CHUNKS;
   constexpr int KSTEPS = Bf16Tile<D>::KSTEPS;
-  constexpr int DBLK = Bf16Tile<D>::DBLK;
+  constexpr int CBLK = Bf16Tile<D>::CBLK;
 
   const WsHeader* hdr = reinterpret_cast<const WsHeader*>(a.ws);
   const int32_t heads = a.heads;
@@ -219,27 +252,30 @@ __global__ void __launch_bounds__(ATTN_THREADS, 2) attn_fwd_bf16_kernel(AttnArgs
   }
 
   const int tid = threadIdx.x;
-  const int wave = tid >> 6, lane = tid & 63, hf = lane >> 5, l32 = lane & 31;
+  const int wave = tid >> 6, lane = tid & 63, g = lane >> 4, l16 = lane & 15;
   const int64_t head_row0 = int64_t(h) * a.rows + pb;  // first padded row of this (sample, head)
 
-  // Rotated query row of this lane as the B operand of S^T = K~ Q~^T: lane
-  // holds query l32, channels 16*ks + 8*hf .. +7 for every k-step ks. The row
-  // is read from the caller's q and rotated here (once per workgroup); rows
-  // past the sample's end read its last token and are never stored.
-  bf16x8 qreg[KSTEPS];
-  {
-    const int32_t u = min(qs + 32 * wave + l32, L - 1);
+  // Rotated query rows of this lane as the B operand of S^T = K~ Q~^T: for
+  // query block qb the lane holds query 16 qb + l16 of the wave, channels
+  // 32 ks + 8 g .. +7 for every k-step ks. The rows are read from the caller's
+  // q and rotated here (once per workgroup); rows past the sample's end read
+  // its last token and are never stored.
+  bf16x8 qreg[2][KSTEPS];
+#pragma unroll
+  for (int qb = 0; qb < 2; ++qb) {
+    const int32_t u = min(qs + 32 * wave + 16 * qb + l16, L - 1);
     int32_t row, col, frame = 0;
     if constexpr (R3) token_position3(u, a.text_len[seg], a.grid_hw[2 * seg], a.grid_hw[2 * seg + 1], row, col, frame);
     else token_position(u, a.text_len[seg], a.grid_hw[2 * seg + 1], row, col);
-    const uint16_t* qrow = static_cast<const uint16_t*>(a.q) + int64_t(cb + u) * a.q_st + int64_t(h) * a.q_sh + 8 * hf;
+    const uint16_t* qrow = static_cast<const uint16_t*>(a.q) + int64_t(cb + u) * a.q_st + int64_t(h) * a.q_sh + 8 * g;
 #pragma unroll
     for (int ks = 0; ks < KSTEPS; ++ks) {
-      const Chunk<uint16_t> raw = *reinterpret_cast<const Chunk<uint16_t>*>(qrow + 16 * ks);
+      const Chunk<uint16_t> raw = *reinterpret_cast<const Chunk<uint16_t>*>(qrow + 32 * ks);
       if constexpr (R3)
-        qreg[ks] = __builtin_bit_cast(bf16x8, rotate_chunk3<uint16_t, D>(raw, 16 * ks + 8 * hf, row, col, frame, a.r3));
+        qreg[qb][ks] =
+            __builtin_bit_cast(bf16x8, rotate_chunk3<uint16_t, D>(raw, 32 * ks + 8 * g, row, col, frame, a.r3));
       else
-        qreg[ks] = __builtin_bit_cast(bf16x8, rotate_chunk<uint16_t, D>(raw, 16 * ks + 8 * hf, row, col, a.cs));
+        qreg[qb][ks] = __builtin_bit_cast(bf16x8, rotate_chunk<uint16_t, D>(raw, 32 * ks + 8 * g, row, col, a.cs));
     }
   }
   // The tile copies share the in-order vector-memory counter with these
@@ -258,11 +294,11 @@ __global__ void __launch_bounds__(ATTN_THREADS, 2) attn_fwd_bf16_kernel(AttnArgs
   const bool mask_last = kt1 == nkt_all;
 
   const float c = a.c_log2;
-  float m = -INFINITY;  // reference row max (log2 units)
-  float lsum = 0.f;     // this lane's partial row sum (its 32 keys of every tile)
-  f32x16 acc[DBLK];
+  float m[2] = {-INFINITY, -INFINITY};  // reference row max (log2 units) of both queries
+  float lsum[2] = {0.f, 0.f};           // this lane's partial row sums (its 16 keys of every tile)
+  f32x4 acc[CBLK][2];
 #pragma unroll
-  for (int b = 0; b < DBLK; ++b) acc[b] = f32x16{};
+  for (int b = 0; b < CBLK; ++b) acc[b][0] = acc[b][1] = f32x4{};
 
   tile_to_lds<CHUNKS>(kg, kA, wave, lane);
   tile_to_lds<CHUNKS>(vg, vA, wave, lane);
@@ -273,62 +309,62 @@ __global__ void __launch_bounds__(ATTN_THREADS, 2) attn_fwd_bf16_kernel(AttnArgs
   for (; j + 2 < nkt; j += 2) {
     tile_to_lds<CHUNKS>(kg + (j + 1) * CHUNKS, kB, wave, lane);
     tile_to_lds<CHUNKS>(vg + (j + 1) * CHUNKS, vB, wave, lane);
-    attend_tile<D, false>(kA, vA, qreg, acc, m, lsum, c, key0 + KTILE * j, L, hf, l32);
+    attend_tile<D, false>(kA, vA, qreg, acc, m, lsum, c, key0 + KTILE * j, L, g, l16);
     wait_tile_and_sync();
     tile_to_lds<CHUNKS>(kg + (j + 2) * CHUNKS, kA, wave, lane);
     tile_to_lds<CHUNKS>(vg + (j + 2) * CHUNKS, vA, wave, lane);
-    attend_tile<D, false>(kB, vB, qreg, acc, m, lsum, c, key0 + KTILE * (j + 1), L, hf, l32);
+    attend_tile<D, false>(kB, vB, qreg, acc, m, lsum, c, key0 + KTILE * (j + 1), L, g, l16);
     wait_tile_and_sync();
   }
   if (j + 1 < nkt) {
     tile_to_lds<CHUNKS>(kg + (j + 1) * CHUNKS, kB, wave, lane);
     tile_to_lds<CHUNKS>(vg + (j + 1) * CHUNKS, vB, wave, lane);
-    attend_tile<D, false>(kA, vA, qreg, acc, m, lsum, c, key0 + KTILE * j, L, hf, l32);
+    attend_tile<D, false>(kA, vA, qreg, acc, m, lsum, c, key0 + KTILE * j, L, g, l16);
     wait_tile_and_sync();
-    if (mask_last) attend_tile<D, true>(kB, vB, qreg, acc, m, lsum, c, key0 + KTILE * (j + 1), L, hf, l32);
-    else attend_tile<D, false>(kB, vB, qreg, acc, m, lsum, c, key0 + KTILE * (j + 1), L, hf, l32);
+    if (mask_last) attend_tile<D, true>(kB, vB, qreg, acc, m, lsum, c, key0 + KTILE * (j + 1), L, g, l16);
+    else attend_tile<D, false>(kB, vB, qreg, acc, m, lsum, c, key0 + KTILE * (j + 1), L, g, l16);
   } else {
-    if (mask_last) attend_tile<D, true>(kA, vA, qreg, acc, m, lsum, c, key0 + KTILE * j, L, hf, l32);
-    else attend_tile<D, false>(kA, vA, qreg, acc, m, lsum, c, key0 + KTILE * j, L, hf, l32);
+    if (mask_last) attend_tile<D, true>(kA, vA, qreg, acc, m, lsum, c, key0 + KTILE * j, L, g, l16);
+    else attend_tile<D, false>(kA, vA, qreg, acc, m, lsum, c, key0 + KTILE * j, L, g, l16);
   }
 
-  // Epilogue: O = acc / l. Accumulator entry e of block b holds channel
-  // 32*b + 8*(e/4) + 4*hf + e%4 of query l32.
-  lsum = halves_sum(lsum);
+  // Epilogue: O = acc / l. acc[b][qb] holds channels 16 b + 4 g .. +3 of query
+  // 16 qb + l16 of the wave.
+#pragma unroll
+  for (int qb = 0; qb < 2; ++qb) lsum[qb] = quad_sum(lsum[qb]);
   if (part >= 0) {
     // Piece of a split unit: unnormalized accumulator, reference max and row
     // sum into its slot, for the merge kernel.
-    const int r = 32 * wave + l32;
     float* slot = a.part + int64_t(blockIdx.x - plan.n_full) * QTILE * (D + 2);
 #pragma unroll
-    for (int b = 0; b < DBLK; ++b) {
+    for (int qb = 0; qb < 2; ++qb) {
+      const int r = 32 * wave + 16 * qb + l16;
 #pragma unroll
-      for (int g = 0; g < 4; ++g)
-        *reinterpret_cast<float4*>(slot + int64_t(r) * D + 32 * b + 8 * g + 4 * hf) =
-            make_float4(acc[b][4 * g], acc[b][4 * g + 1], acc[b][4 * g + 2], acc[b][4 * g + 3]);
-    }
-    if (hf == 0) {
-      slot[QTILE * D + r] = m;
-      slot[QTILE * D + QTILE + r] = lsum;
+      for (int b = 0; b < CBLK; ++b)
+        *reinterpret_cast<float4*>(slot + int64_t(r) * D + 16 * b + 4 * g) =
+            make_float4(acc[b][qb][0], acc[b][qb][1], acc[b][qb][2], acc[b][qb][3]);
+      if (g == 0) {
+        slot[QTILE * D + r] = m[qb];
+        slot[QTILE * D + QTILE + r] = lsum[qb];
+      }
     }
     return;
   }
-  const float inv = 1.f / lsum;
-  const int32_t qrel = qs + 32 * wave + l32;
-  // log-sum-exp in natural-log units: p = 2^(s c - m) / lsum, so
-  // ln sum_k e^(s_k * scale) = (m + log2 lsum) * ln 2.
-  if (a.lse && qrel < L && hf == 0) a.lse[int64_t(h) * a.tokens + cb + qrel] = (m + log2f(lsum)) * 0.6931471805599453f;
-  if (qrel < L) {
-    uint16_t* orow = static_cast<uint16_t*>(a.out) + int64_t(cb + qrel) * a.o_st + int64_t(h) * a.o_sh;
 #pragma unroll
-    for (int b = 0; b < DBLK; ++b) {
+  for (int qb = 0; qb < 2; ++qb) {
+    const float inv = 1.f / lsum[qb];
+    const int32_t qrel = qs + 32 * wave + 16 * qb + l16;
+    if (qrel >= L) continue;
+    // log-sum-exp in natural-log units: p = 2^(s c - m) / lsum, so
+    // ln sum_k e^(s_k * scale) = (m + log2 lsum) * ln 2.
+    if (a.lse && g == 0) a.lse[int64_t(h) * a.tokens + cb + qrel] = (m[qb] + log2f(lsum[qb])) * 0.6931471805599453f;
+    uint16_t* orow = static_cast<uint16_t*>(a.out) + int64_t(cb + qrel) * a.o_st + int64_t(h) * a.o_sh + 4 * g;
 #pragma unroll
-      for (int g = 0; g < 4; ++g) {
-        uint2 v2;
-        v2.x = pack_bf16x2(acc[b][4 * g] * inv, acc[b][4 * g + 1] * inv);
-        v2.y = pack_bf16x2(acc[b][4 * g + 2] * inv, acc[b][4 * g + 3] * inv);
-        *reinterpret_cast<uint2*>(orow + 32 * b + 8 * g + 4 * hf) = v2;
-      }
+    for (int b = 0; b < CBLK; ++b) {
+      uint2 v2;
+      v2.x = pack_bf16x2(acc[b][qb][0] * inv, acc[b][qb][1] * inv);
+      v2.y = pack_bf16x2(acc[b][qb][2] * inv, acc[b][qb][3] * inv);
+      *reinterpret_cast<uint2*>(orow + 16 * b) = v2;
     }
   }
 }

@@ -256,14 +256,6 @@ struct QkvGemmArgs {
   int32_t ncu;         // compute units for the halved last round (0: never halve)
 };
 
-// D (16 x 16, fp32) += A (16 x 32, bf16) B (32 x 16, bf16): lane l supplies A
-// row l % 16 and B column l % 16, k = 8 (l / 16) .. +7 of each; it receives D
-// column l % 16, rows 4 (l / 16) .. +3.
-typedef float f32x4 __attribute__((ext_vector_type(4)));
-__device__ inline f32x4 mfma16(const bf16x8& a, const bf16x8& b, const f32x4& c) {
-  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
-}
-
 // One GEMM unit (256 output features x 256 tokens of one modality) or, with
 // NB = 4, one 128-feature half of it starting at feature fbase of the tile:
 // every wave owns NB * 16 features x 64 tokens, on v_mfma_f32_16x16x32_bf16

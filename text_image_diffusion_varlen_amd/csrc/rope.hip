@@ -231,16 +231,16 @@ __global__ void __launch_bounds__(256) prologue_bf16_kernel(PrologueArgs a) {
     const int cc = f2 / KTILE, rr = f2 % KTILE;
     *reinterpret_cast<Chunk<uint16_t>*>(a.kw + tile_off + int64_t(f2) * 8) = ks[cc * KS + rr];
   }
-  // V~^T chunk f2 = g * D + c: channel c, keys b..b+3 and b+8..b+11 of the
-  // tile (b = 16 (g / 2) + 4 (g % 2): the score MFMA's accumulator order).
+  // V~^T chunk f2 = g * D + c: channel c, keys b..b+3 and b+16..b+19 of the
+  // tile (b = 32 (g / 4) + 4 (g % 4): the score MFMA's accumulator order).
   for (int f2 = t; f2 < D * (KTILE / 8); f2 += 256) {
     const int g = f2 / D, c = f2 % D;
-    const int b = 16 * (g >> 1) + 4 * (g & 1);
+    const int b = 32 * (g >> 2) + 4 * (g & 3);
     Chunk<uint16_t> o;
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
       o.v[e] = vs[(b + e) * VS + c];
-      o.v[4 + e] = vs[(b + 8 + e) * VS + c];
+      o.v[4 + e] = vs[(b + 16 + e) * VS + c];
     }
     *reinterpret_cast<Chunk<uint16_t>*>(a.vw + tile_off + int64_t(f2) * 8) = o;
   }
