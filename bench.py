@@ -120,8 +120,10 @@ def cpu_baseline(w, budget_s: float, gpu_out=None, gpu_meta=None, max_workers: i
     """The fp64 oracle (as it stands) on host cores: a process pool over
     (sample, head) work items, one BLAS thread per worker, workers = the cores
     this process may run on (at most `max_workers`, the host share of one GPU).
-    Heads are submitted whole (all samples of head 0, then head 1, ...) until
-    the time budget is spent; the heads finished by then are the sample.
+    Heads are submitted whole (all samples of head 0, then head 1, ..., then
+    head 0 again) until `budget_s` seconds of CPU work (wall time x workers)
+    are spent, at least one pass over all heads; the head computations
+    finished by then are the sample.
 
     After the timed region, the oracle's outputs of those heads are compared with
     the GPU output of the same workload (`gpu_out`, [T][H][d] on the host) and
@@ -164,24 +166,27 @@ def cpu_baseline(w, budget_s: float, gpu_out=None, gpu_meta=None, max_workers: i
             done_heads = 0
             next_head = 0
             left = {}
-            # keep the pool busy with a little more than one head's items in flight
-            while done_heads < w.heads:
-                while next_head < w.heads and len(pending) < 2 * cores and time.perf_counter() - t0 <= budget_s:
+            wall_budget = budget_s / cores
+            # keep the pool busy with a little more than one head's items in flight;
+            # head instance n is head n % heads (pass n // heads)
+            while True:
+                while len(pending) < 2 * cores and (next_head < w.heads or time.perf_counter() - t0 <= wall_budget):
                     for i in range(w.n_seg):
-                        pending[ex.submit(_oracle_item, item(i, next_head))] = (i, next_head)
+                        pending[ex.submit(_oracle_item, item(i, next_head % w.heads))] = (i, next_head)
                     left[next_head] = w.n_seg
                     next_head += 1
                 if not pending:
                     break
                 finished, _ = concurrent.futures.wait(pending, return_when=concurrent.futures.FIRST_COMPLETED)
                 for f in finished:
-                    i, h = pending.pop(f)
-                    outs[int(cu[i]):int(cu[i + 1]), h] = f.result()[:, 0]
-                    left[h] -= 1
+                    i, n = pending.pop(f)
+                    if n < w.heads:
+                        outs[int(cu[i]):int(cu[i + 1]), n] = f.result()[:, 0]
+                    left[n] -= 1
                 while done_heads < next_head and left[done_heads] == 0:
                     done_heads += 1
             dt = time.perf_counter() - t0
-            heads = done_heads
+            heads = min(done_heads, w.heads)
     finally:
         for var, val in saved.items():
             if val is None:
@@ -189,13 +194,13 @@ def cpu_baseline(w, budget_s: float, gpu_out=None, gpu_meta=None, max_workers: i
             else:
                 os.environ[var] = val
     res = {
-        "value": per_head * heads / dt / 1e12,
+        "value": per_head * done_heads / dt / 1e12,
         "unit": "TFLOP/s",
         "cores": cores,
         "kind": "oracle",
-        "sample": f"{heads} of {w.heads} heads of the same workload (all rows, fp64 numpy, "
-                  f"{w.n_seg * heads} (sample, head) items over {cores} worker processes with one BLAS thread each),"
-                  f" {dt:.1f} s",
+        "sample": f"{done_heads} head computations ({done_heads / w.heads:.2f} passes over all {w.heads} heads) of the "
+                  f"same workload (all rows, fp64 numpy, {w.n_seg * done_heads} (sample, head) items over {cores} "
+                  f"worker processes with one BLAS thread each), {dt:.1f} s wall, {dt * cores:.0f} s of CPU work",
     }
     if gpu_out is not None and heads > 0:
         err = np.abs(gpu_out[:, :heads].astype(np.float64) - outs[:, :heads])
@@ -647,6 +652,40 @@ def gemm_context(steps: int = 20):
     return {"torch_matmul_bf16_8192cube_tflops": round(tf, 1), "frac_of_peak": round(tf * 1e12 / PEAK["bf16"], 4)}
 
 
+def mfma_context(iters: int = 40000, reps: int = 5):
+    """For context: the rate a loop of independent bf16 MFMAs on random
+    register operands (no memory traffic) sustains on this device in this run,
+    for the two MFMA shapes (libmfprobe.so, two waves per SIMD). The dense
+    peak is a nominal-clock figure; under a sustained MFMA load the chip runs
+    below it, and the two shapes do not reach the same rate."""
+    import torch
+
+    lib = ctypes.CDLL(os.path.join(ROOT, "text_image_diffusion_varlen_amd", "libmfprobe.so"))
+    lib.mf_probe_mfma_loop.argtypes = [ctypes.c_void_p, ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_void_p]
+    props = torch.cuda.get_device_properties(0)
+    blocks = 2 * props.multi_processor_count  # 4 waves each: two waves per SIMD
+    out = torch.empty(blocks * 256, dtype=torch.float32, device="cuda")
+    stream = torch.cuda.current_stream().cuda_stream
+    flop = float(blocks) * 4 * iters * 262144
+    res = {}
+    for shape, name in ((0, "mfma_16x16x32_bf16"), (1, "mfma_32x32x16_bf16")):
+        for _ in range(2):
+            if lib.mf_probe_mfma_loop(ctypes.c_void_p(out.data_ptr()), shape, blocks, iters, ctypes.c_void_p(stream)):
+                raise RuntimeError("mf_probe_mfma_loop launch failed")
+        start, stop = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        start.record()
+        for _ in range(reps):
+            lib.mf_probe_mfma_loop(ctypes.c_void_p(out.data_ptr()), shape, blocks, iters, ctypes.c_void_p(stream))
+        stop.record()
+        torch.cuda.synchronize()
+        ms = start.elapsed_time(stop) / reps
+        tf = flop / (ms / 1e3) / 1e12
+        res[name + "_loop_tflops"] = round(tf, 1)
+        res[name + "_frac_of_peak"] = round(tf * 1e12 / PEAK["bf16"], 4)
+    return res
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -654,7 +693,8 @@ def main():
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--config", default="1024sq", choices=sorted(DESCRIPTIONS))
     ap.add_argument("--seed", type=int, default=None)
-    ap.add_argument("--cpu-budget", type=float, default=15.0, help="seconds of oracle work for cpu_baseline")
+    ap.add_argument("--cpu-budget", type=float, default=20.0,
+                    help="seconds of CPU work (wall time x worker processes) for cpu_baseline")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-sampler", action="store_true", help="skip the packed CFG Euler-step measurement")
     ap.add_argument("--no-backward", action="store_true", help="skip the packed backward measurement")
@@ -717,6 +757,7 @@ def main():
                                             frames if edit else None)
     if w.dtype == "bf16":
         result["gemm_context"] = gemm_context()
+        result["mfma_context"] = mfma_context()
     if not args.no_pack:
         result["joint_pack"] = pack_bench(w, cu, grid, text, args.steps, args.warmup, frames)
     if w.dtype == "bf16" and not args.no_qkv:

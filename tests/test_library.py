@@ -20,6 +20,22 @@ def test_library_loads_and_exports_header_symbols():
     assert binding.version() == 100
 
 
+def test_mfma_probe_library_loads_and_rejects_bad_arguments():
+    """The benchmark's MFMA-rate aid is a separate library; its entry point
+    checks its arguments on the host (hipErrorInvalidValue = 1)."""
+    import os
+
+    path = os.path.join(os.path.dirname(binding.LIB_PATH), "libmfprobe.so")
+    lib = ctypes.CDLL(path)
+    f = lib.mf_probe_mfma_loop
+    f.argtypes = [ctypes.c_void_p, ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_void_p]
+    assert f(None, 0, 1, 1, None) == 1
+    buf = ctypes.create_string_buffer(16)
+    assert f(ctypes.cast(buf, ctypes.c_void_p), 2, 1, 1, None) == 1
+    assert f(ctypes.cast(buf, ctypes.c_void_p), 0, 0, 1, None) == 1
+    assert f(ctypes.cast(buf, ctypes.c_void_p), 1, 1, 0, None) == 1
+
+
 def test_workspace_bytes():
     import torch
     wb = binding.workspace_bytes

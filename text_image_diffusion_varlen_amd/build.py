@@ -2,7 +2,9 @@
 
 Usage: python -m text_image_diffusion_varlen_amd.build
 Every .hip file under csrc/ is compiled to an object under _build/ and the
-objects are linked into text_image_diffusion_varlen_amd/libmfattn.so.
+objects are linked into text_image_diffusion_varlen_amd/libmfattn.so. The
+measurement aid under csrc/probe/ (an MFMA-rate loop the benchmark reports
+for context) is built into its own libmfprobe.so.
 """
 from __future__ import annotations
 
@@ -17,6 +19,7 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(PKG, "libmfattn.so")
+PROBE_LIB = os.path.join(PKG, "libmfprobe.so")
 ARCH = "gfx950"
 
 # Packed fp32 VALU forms are disabled for all device code.
@@ -41,7 +44,7 @@ def sources():
 
 
 def _compile(src: str) -> str:
-    obj = os.path.join(BUILD, os.path.basename(src)[:-4] + ".o")
+    obj = os.path.join(BUILD, os.path.relpath(src, CSRC).replace(os.sep, "_")[:-4] + ".o")
     cmd = [hipcc(), *COMMON, *DEVICE_FLAGS, *EXTRA.get(os.path.basename(src), []), "-c", src, "-o", obj]
     r = subprocess.run(cmd, capture_output=True, text=True)
     # hipcc's host pass does not know the device feature flag; that warning is expected.
@@ -54,22 +57,32 @@ def _compile(src: str) -> str:
     return obj
 
 
-def build(verbose: bool = False) -> str:
-    os.makedirs(BUILD, exist_ok=True)
-    srcs = sources()
-    with concurrent.futures.ThreadPoolExecutor(max_workers=min(8, len(srcs))) as ex:
-        objs = list(ex.map(_compile, srcs))
-    tmp = LIB + ".tmp"
-    rocm_lib = os.path.join(os.path.dirname(os.path.dirname(os.path.realpath(hipcc()))), "lib")
-    # roctx: the host-side ranges around each stage's launches (rocprofv3 --marker-trace)
-    cmd = [hipcc(), "-shared", "-fPIC", f"--offload-arch={ARCH}", "-o", tmp, *objs,
-           "-L", rocm_lib, f"-Wl,-rpath,{rocm_lib}", "-lrocprofiler-sdk-roctx"]
+def probe_sources():
+    d = os.path.join(CSRC, "probe")
+    return sorted(os.path.join(d, f) for f in os.listdir(d) if f.endswith(".hip"))
+
+
+def _link(objs, out, extra=()):
+    tmp = out + ".tmp"
+    cmd = [hipcc(), "-shared", "-fPIC", f"--offload-arch={ARCH}", "-o", tmp, *objs, *extra]
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError(f"link failed: {' '.join(cmd)}\n{r.stderr}")
-    os.replace(tmp, LIB)
+    os.replace(tmp, out)
+
+
+def build(verbose: bool = False) -> str:
+    os.makedirs(BUILD, exist_ok=True)
+    srcs, probes = sources(), probe_sources()
+    with concurrent.futures.ThreadPoolExecutor(max_workers=8) as ex:
+        objs = list(ex.map(_compile, srcs))
+        probe_objs = list(ex.map(_compile, probes))
+    rocm_lib = os.path.join(os.path.dirname(os.path.dirname(os.path.realpath(hipcc()))), "lib")
+    # roctx: the host-side ranges around each stage's launches (rocprofv3 --marker-trace)
+    _link(objs, LIB, ["-L", rocm_lib, f"-Wl,-rpath,{rocm_lib}", "-lrocprofiler-sdk-roctx"])
+    _link(probe_objs, PROBE_LIB)
     if verbose:
-        print(f"built {LIB}")
+        print(f"built {LIB} and {PROBE_LIB}")
     return LIB
 
 

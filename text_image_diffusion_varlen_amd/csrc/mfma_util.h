@@ -24,8 +24,8 @@ typedef float f32x4 __attribute__((ext_vector_type(4)));
 // D (16 x 16, fp32) += A (16 x 32, bf16) B (32 x 16, bf16). Lane l supplies A
 // row l % 16 and B column l % 16, k = 8 (l / 16) .. +7 of each; it receives D
 // column l % 16, rows 4 (l / 16) .. +3. On gfx950 this form sustains a higher
-// rate than the 32 x 32 x 16 one (about 2.0 against 1.75 PFLOP/s in a loop of
-// independent MFMAs on random data).
+// rate than the 32 x 32 x 16 one (about 14 % more in a loop of independent
+// MFMAs on random register operands).
 __device__ inline f32x4 mfma16(const bf16x8& a, const bf16x8& b, const f32x4& c) {
   return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
 }
