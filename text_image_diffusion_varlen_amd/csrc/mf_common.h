@@ -55,7 +55,10 @@ __host__ __device__ inline int64_t max_tiles(int64_t tokens, int32_t n_seg) {
 // of `parts` pieces each. Every kernel derives the same plan from
 // (U, ncu, nkt_short), so nothing is stored.
 constexpr int PART_SLOTS = 512;      // partial-result slots in the workspace (pieces per call)
-constexpr int SPLIT_MIN_SAVED = 96;  // key tiles a split must save on the tail's shortest unit
+#ifndef MF_SPLIT_MIN_SAVED
+#define MF_SPLIT_MIN_SAVED 96
+#endif
+constexpr int SPLIT_MIN_SAVED = MF_SPLIT_MIN_SAVED;  // key tiles a split must save on the tail's shortest unit
 // A split needs a shortest unit of at least 4/3 * SPLIT_MIN_SAVED key tiles
 // (4 parts in one round), i.e. a shortest sample of more than
 // (4/3 * SPLIT_MIN_SAVED - 1) * KTILE tokens; the shortest sample is never
