@@ -67,6 +67,26 @@ def stored_traffic(config: str):
     return rec.get("traffic_bytes")
 
 
+class ColdFlush:
+    """Empties the 256 MB MALL of the workload's data before a timed call.
+    flush(i): writes a 512 MB buffer, then reads another 512 MB buffer, so the
+    cache ends up holding clean lines (the dirty ones were written back during
+    the read, outside the timed region) and the timed call pays only for its
+    own HBM traffic. flush(i, dirty=True): the write only, so the cache is left
+    full of dirty lines and the call's misses also write those back."""
+
+    def __init__(self):
+        import torch
+
+        self.dirty = torch.empty(512 << 20, dtype=torch.uint8, device="cuda")
+        self.clean = torch.ones((512 << 20) // 4, dtype=torch.int32, device="cuda")
+
+    def __call__(self, i: int, dirty: bool = False):
+        self.dirty.fill_(i & 255)
+        if not dirty:
+            self.clean.amax()
+
+
 class HipEvents:
     """Raw hipEvent_t handles from the HIP runtime already loaded by torch."""
 
@@ -377,8 +397,9 @@ def pack_bench(w, cu, grid, text, steps: int, warmup: int, frames=None):
     """Joint-layout pack of q, k, v (one launch, from the text and image streams)
     and unpack of the attention output back to the two streams, on the same
     batch. GB/s count the algorithmic bytes (every row read once and written
-    once); each call is timed by HIP events, back to back (warm) and with the
-    256 MB MALL flushed before it by writing a 512 MB buffer (cold)."""
+    once); each call is timed by HIP events, back to back (warm), with the
+    256 MB MALL emptied of the batch before it (cold: ColdFlush, clean lines)
+    and with the MALL left full of dirty lines (cold_dirty)."""
     import torch
     from text_image_diffusion_varlen_amd import binding
 
@@ -400,18 +421,18 @@ def pack_bench(w, cu, grid, text, steps: int, warmup: int, frames=None):
                      2 * w.tokens * row),
     }
     ev = HipEvents(2 * steps)
-    flush = torch.empty(512 << 20, dtype=torch.uint8, device="cuda")
+    flush = ColdFlush()
     res = {}
     for name, (fn, nbytes) in calls.items():
         for _ in range(warmup):
             fn()
         times = {}
-        for mode in ("warm", "cold"):
+        for mode in ("warm", "cold", "cold_dirty"):
             torch.cuda.synchronize()
             stream = torch.cuda.current_stream().cuda_stream
             for st in range(steps):
-                if mode == "cold":
-                    flush.fill_(st & 255)
+                if mode != "warm":
+                    flush(st, mode == "cold_dirty")
                 ev.hip.hipEventRecord(ev.ev[2 * st], stream)
                 fn()
                 ev.hip.hipEventRecord(ev.ev[2 * st + 1], stream)
@@ -423,6 +444,7 @@ def pack_bench(w, cu, grid, text, steps: int, warmup: int, frames=None):
             "us_cold_mall": round(times["cold"] * 1e3, 2),
             "gbps_cold_mall": round(nbytes / (times["cold"] / 1e3) / 1e9, 1),
             "frac_hbm_cold_mall": round(nbytes / (times["cold"] / 1e3) / HBM_PEAK, 4),
+            "gbps_cold_mall_dirty": round(nbytes / (times["cold_dirty"] / 1e3) / 1e9, 1),
             "algorithmic_bytes": nbytes,
         }
     if binding.get_device_error() != binding.MF_OK:
@@ -492,7 +514,8 @@ def forward_bench(config: str, seed, steps: int, warmup: int, keep_host: bool):
     inputs; K steps between two synchronizations, torch events on the stream the
     library launches on. Then the same K calls with HIP events between the three
     kernels (2D path) give per-kernel times, and K more with the 256 MB MALL
-    flushed before each give the prologue's cold-cache rate."""
+    emptied of the workload before each give the prologue's cold-cache rate
+    (and K more the rate with the MALL left full of dirty lines)."""
     import torch
     from text_image_diffusion_varlen_amd import binding, workloads
 
@@ -558,16 +581,21 @@ def forward_bench(config: str, seed, steps: int, warmup: int, keep_host: bool):
             stage["rope_pack"] += ev.elapsed_ms(b + 1, b + 2) / steps
             attn_each.append(ev.elapsed_ms(b + 2, b + 3))
         stage["attn"] = sum(attn_each) / steps
-        # The same calls with the 256 MB MALL flushed before each (a 512 MB
-        # buffer written in between): the RoPE prologue then reads k and v from HBM.
-        flush = torch.empty(512 << 20, dtype=torch.uint8, device="cuda")
-        pack_cold = []
-        for s in range(steps):
-            flush.fill_(s & 255)
-            binding.attn_packed_profiled(q, k, v, cu, grid, text, ev.ev[4 * s : 4 * s + 4], out=out)
-        torch.cuda.synchronize()
-        for s in range(steps):
-            pack_cold.append(ev.elapsed_ms(4 * s + 1, 4 * s + 2))
+        # The same calls with the 256 MB MALL emptied of this workload before
+        # each, so the RoPE prologue reads k and v from HBM: ColdFlush
+        # leaves the MALL holding clean lines of another buffer (its dirty
+        # lines already written back), so the timed kernel pays only for its
+        # own traffic; and, for reference, with the MALL left full of dirty
+        # lines (the kernel's misses then also write those back).
+        flush = ColdFlush()
+        pack_cold, pack_cold_dirty = [], []
+        for dirty, times in ((False, pack_cold), (True, pack_cold_dirty)):
+            for s in range(steps):
+                flush(s, dirty)
+                binding.attn_packed_profiled(q, k, v, cu, grid, text, ev.ev[4 * s : 4 * s + 4], out=out)
+            torch.cuda.synchronize()
+            for s in range(steps):
+                times.append(ev.elapsed_ms(4 * s + 1, 4 * s + 2))
         del flush
         ev.close()
 
@@ -610,6 +638,8 @@ def forward_bench(config: str, seed, steps: int, warmup: int, keep_host: bool):
         "frac_back_to_back_est": round(flops / (b2b_ms / 1e3) / PEAK[w.dtype], 4) if not edit else None,
         "rope_pack_gbps": round(rope_bytes / (stage["rope_pack"] / 1e3) / 1e9, 1) if not edit else None,
         "rope_pack_gbps_cold_mall": round(rope_bytes / (float(np.median(pack_cold)) / 1e3) / 1e9, 1) if not edit else None,
+        "rope_pack_gbps_cold_mall_dirty": (round(rope_bytes / (float(np.median(pack_cold_dirty)) / 1e3) / 1e9, 1)
+                                           if not edit else None),
         "roofline": {
             "kernel": f"attn_fwd_{w.dtype}_kernel<{w.head_dim}, {'true' if edit else 'false'}>"
                       + (" (whole step: no per-kernel events on the frame-aware path)" if edit else ""),

@@ -23,11 +23,11 @@
 //       its query rows itself while loading them)
 //   K~  bf16: each KTILE x d tile stored chunk-major: 16-byte chunk c (channels
 //       8c..8c+7) of tile row n at chunk index c * KTILE + n. f32: row-major.
-//   V~  bf16: V transposed per tile, [d][KTILE] inside each tile, keys inside
-//       every group of 16 stored in the order 0-3, 8-11, 4-7, 12-15 (the order
-//       in which the MFMA accumulator of the score tile holds them), and the
-//       tile stored chunk-major: chunk g (8 keys) of channel r at g * d + r.
-//       f32: plain row-major copy.
+//   V~  bf16: V transposed per tile, [d][KTILE] inside each tile, stored
+//       chunk-major: chunk g (8 keys) of channel r at g * d + r, holding keys
+//       b..b+3 and b+16..b+19 (b = 32 (g / 4) + 4 (g % 4)), the keys one lane
+//       of the 16 x 16 score MFMA's accumulators holds for a 32-key k-step of
+//       the P.V product. f32: plain row-major copy.
 // Chunk-major tiles are copied verbatim into LDS by the attention kernel;
 // there, the 16 lanes that read one MFMA operand row block touch 16
 // consecutive chunks (no bank conflicts) and every read is a fixed offset
