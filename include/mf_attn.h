@@ -110,9 +110,14 @@ const char* mf_last_error(void);
  * cu_seqlens consistent, cu_seqlens[n_seg] == total_tokens). On a mismatch no
  * output is written and mf_get_device_error() reports MF_ERR_METADATA.
  * Uses a library-owned workspace per device (grown on demand, never shrunk,
- * freed at process exit); calls on one device are serialized by the caller's
- * stream order only, so concurrent calls on different streams of one device
- * must use mf_attn_packed_ws with separate workspaces.
+ * freed at process exit). Calls on that workspace are ordered on the device:
+ * a call enqueued on a stream other than the previous call's first makes its
+ * stream wait for that call (an event; the host is not blocked), so calls on
+ * several streams of one device run one after the other. Calls enqueued while
+ * their stream is being captured into a graph are not ordered this way, and
+ * replays of such a graph must not overlap other calls on the device. Calls
+ * that should run concurrently use mf_attn_packed_ws with separate
+ * workspaces.
  * Results are deterministic (no atomics). For bf16, when the last round of
  * (256-query tile, head) units would fill the device poorly and its units are
  * long, those units are split over key ranges and a second kernel merges the

@@ -132,8 +132,17 @@ int debug_stage(hipStream_t s, const char* stage, const int32_t* flag = nullptr,
 
 const int32_t* ws_flag(const char* ws) { return reinterpret_cast<const int32_t*>(ws); }  // WsHeader::flag
 
+// Stream order of the calls that share one library workspace: the stream of
+// the last call and an event recorded after its kernels.
+struct WsOrder {
+  hipEvent_t done = nullptr;
+  hipStream_t last = nullptr;
+  bool valid = false;
+};
+
 struct DeviceState {
   int32_t* status = nullptr;  // sticky FLAG_* of the standalone metadata / RoPE / sampler calls
+  WsOrder ord_ws, ord_bws, ord_qws;  // order of the calls on ws, bws, qws
   char* ws = nullptr;         // library workspace of mf_attn_packed
   size_t ws_bytes = 0;
   char* bws = nullptr;        // library workspace of mf_attn_packed_bwd
@@ -298,6 +307,41 @@ int ensure_buffer(char*& buf, size_t& have, size_t bytes) {
 
 int ensure_workspace(DeviceState& st, size_t bytes) { return ensure_buffer(st.ws, st.ws_bytes, bytes); }
 
+// Runs launch() (which enqueues a call's kernels on stream s, all using one
+// library workspace) after the previous call on that workspace: when that
+// call was enqueued on another stream, s first waits (on the device) for the
+// event recorded after it. Calls enqueued while s is being captured into a
+// graph are not ordered this way (a captured graph cannot wait on an event
+// recorded outside it), and the next call does not wait for them; a failed
+// capture-status query counts as capturing. Caller holds g_mu.
+template <typename F>
+int ordered(WsOrder& o, hipStream_t s, F&& launch) {
+  hipStreamCaptureStatus cs = hipStreamCaptureStatusNone;
+  bool capturing = true;
+  if (hipStreamIsCapturing(s, &cs) == hipSuccess) capturing = cs != hipStreamCaptureStatusNone;
+  else (void)hipGetLastError();
+  hipError_t e;
+  if (!capturing && o.valid && o.last != s && (e = hipStreamWaitEvent(s, o.done, 0)) != hipSuccess)
+    return hip_fail(e, "hipStreamWaitEvent (workspace order)");
+  const int rc = launch();
+  if (capturing) {
+    o.valid = false;
+    return rc;
+  }
+  if (!o.done && (e = hipEventCreateWithFlags(&o.done, hipEventDisableTiming)) != hipSuccess) {
+    o.done = nullptr;
+    o.valid = false;
+    return rc ? rc : hip_fail(e, "hipEventCreateWithFlags (workspace order)");
+  }
+  if ((e = hipEventRecord(o.done, s)) != hipSuccess) {
+    o.valid = false;
+    return rc ? rc : hip_fail(e, "hipEventRecord (workspace order)");
+  }
+  o.last = s;
+  o.valid = true;
+  return rc;
+}
+
 int elem_bytes(int32_t dtype) { return dtype == MF_BF16 ? 2 : dtype == MF_F32 ? 4 : 0; }
 
 bool overlaps(const void* a, size_t na, const void* b, size_t nb) {
@@ -430,8 +474,10 @@ int mf_attn_packed_profiled(const void* q, const void* k, const void* v, const i
   if ((rc = ensure_table(st, head_dim, MF_ROPE_THETA, &cs))) return rc;
   if ((rc = ensure_cus(st, dev, &ncu))) return rc;
   if ((rc = ensure_workspace(st, need))) return rc;
-  return run_attn(q, k, v, cu_seqlens, grid_hw, text_len, out, n_seg, total_tokens, heads, head_dim,
-                  dtype, st.ws, cs, ncu, stream, events);
+  return ordered(st.ord_ws, stream, [&] {
+    return run_attn(q, k, v, cu_seqlens, grid_hw, text_len, out, n_seg, total_tokens, heads, head_dim, dtype,
+                    st.ws, cs, ncu, stream, events);
+  });
 }
 
 int mf_attn_packed(const void* q, const void* k, const void* v, const int32_t* cu_seqlens,
@@ -513,9 +559,17 @@ int attn_impl(const void* q, const void* k, const void* v, const int32_t* cu_seq
   int32_t ncu = 0;
   if ((rc = ensure_cus(st, dev, &ncu))) return rc;
   if ((rc = ensure_workspace(st, need))) return rc;
-  return run_attn(q, k, v, cu_seqlens, grid_hw, text_len, out, n_seg, total_tokens, heads, head_dim, dtype,
-                  st.ws, cs, ncu, stream, nullptr, lse, frames, split ? &r3 : nullptr);
+  return ordered(st.ord_ws, stream, [&] {
+    return run_attn(q, k, v, cu_seqlens, grid_hw, text_len, out, n_seg, total_tokens, heads, head_dim, dtype,
+                    st.ws, cs, ncu, stream, nullptr, lse, frames, split ? &r3 : nullptr);
+  });
 }
+
+int bwd_launch(const void* q, const void* k, const void* v, const void* out, const void* d_out, const float* lse,
+               const int32_t* cu_seqlens, const int32_t* grid_hw, const int32_t* text_len, const int32_t* frames,
+               const mf::Rope3* r3, const float2* cs, void* dq, void* dk, void* dv, int32_t n_seg,
+               int64_t total_tokens, int32_t heads, int32_t head_dim, char* bws, const mf::BwdLayout& l, int32_t ncu,
+               int32_t ncu_q, hipEvent_t const* events, hipStream_t stream);
 
 int bwd_impl(const void* q, const void* k, const void* v, const void* out, const void* d_out, const float* lse,
              const int32_t* cu_seqlens, const int32_t* grid_hw, const int32_t* text_len, const int32_t* frames,
@@ -568,19 +622,32 @@ int bwd_impl(const void* q, const void* k, const void* v, const void* out, const
   // dQ units split with the forward's threshold, dK/dV units with the backward's.
   const int32_t ncu_q = mf::split_possible(total_tokens, n_seg) ? ncu : 0;
   if (!mf::split_possible(total_tokens, n_seg, mf::SPLIT_MIN_SAVED_BWD)) ncu = 0;
+  return ordered(st.ord_bws, stream, [&] {
+    return bwd_launch(q, k, v, out, d_out, lse, cu_seqlens, grid_hw, text_len, frames, split ? &r3 : nullptr, cs,
+                      dq, dk, dv, n_seg, total_tokens, heads, head_dim, st.bws, l, ncu, ncu_q, events, stream);
+  });
+}
+
+// The backward's kernels on the library workspace bws (layout l).
+int bwd_launch(const void* q, const void* k, const void* v, const void* out, const void* d_out, const float* lse,
+               const int32_t* cu_seqlens, const int32_t* grid_hw, const int32_t* text_len, const int32_t* frames,
+               const mf::Rope3* r3, const float2* cs, void* dq, void* dk, void* dv, int32_t n_seg,
+               int64_t total_tokens, int32_t heads, int32_t head_dim, char* bws, const mf::BwdLayout& l, int32_t ncu,
+               int32_t ncu_q, hipEvent_t const* events, hipStream_t stream) {
+  int rc;
   hipError_t e;
   if (events && (e = hipEventRecord(events[0], stream)) != hipSuccess) return hip_fail(e, "hipEventRecord");
   {
     Range r("mf meta_kernel");
-    e = mf::launch_meta(grid_hw, text_len, frames, cu_seqlens, n_seg, total_tokens, st.bws, l.m, stream);
+    e = mf::launch_meta(grid_hw, text_len, frames, cu_seqlens, n_seg, total_tokens, bws, l.m, stream);
   }
   if (e != hipSuccess) return hip_fail(e, "meta_kernel launch");
-  if ((rc = debug_stage(stream, "meta_kernel", ws_flag(st.bws)))) return rc;
+  if ((rc = debug_stage(stream, "meta_kernel", ws_flag(bws)))) return rc;
   {
     Range r("mf attn_bwd");
-    e = mf::launch_attn_bwd(q, k, v, out, d_out, lse, grid_hw, text_len, cs, split ? &r3 : nullptr, st.bws, l, dq,
-                            dk, dv, total_tokens, heads, head_dim, float(1.0 / std::sqrt(double(head_dim))), ncu,
-                            ncu_q, stream, events ? events + 1 : nullptr);
+    e = mf::launch_attn_bwd(q, k, v, out, d_out, lse, grid_hw, text_len, cs, r3, bws, l, dq, dk, dv, total_tokens,
+                            heads, head_dim, float(1.0 / std::sqrt(double(head_dim))), ncu, ncu_q, stream,
+                            events ? events + 1 : nullptr);
   }
   if (e != hipSuccess) return hip_fail(e, "backward kernels launch");
   if ((rc = debug_stage(stream, "backward kernels"))) return rc;
@@ -800,17 +867,20 @@ int mf_qkv_rmsnorm_profiled(const void* x, const void* w_folded, const int32_t* 
   if ((rc = ensure_buffer(st.qws, st.qws_bytes, mf::qkv_workspace_bytes(total_tokens, n_seg, hidden)))) return rc;
   int32_t ncu = 0;
   if ((rc = ensure_cus(st, dev, &ncu))) return rc;
-  hipError_t e;
-  if (events && (e = hipEventRecord(events[0], stream)) != hipSuccess) return hip_fail(e, "hipEventRecord");
-  {
-    Range r("mf qkv_rmsnorm");
-    e = mf::launch_qkv(x, w_folded, cu_seqlens, grid_hw, text_len, frames, n_seg, total_tokens, hidden, hd, eps,
-                       st.qws, q, k, v, ncu, stream, events ? events + 1 : nullptr);
-  }
-  if (e != hipSuccess) return hip_fail(e, "qkv kernels launch");
-  if ((rc = debug_stage(stream, "qkv kernels", ws_flag(st.qws)))) return rc;
-  if (events && (e = hipEventRecord(events[2], stream)) != hipSuccess) return hip_fail(e, "hipEventRecord");
-  return MF_OK;
+  return ordered(st.ord_qws, stream, [&] {
+    hipError_t e;
+    int rc2;
+    if (events && (e = hipEventRecord(events[0], stream)) != hipSuccess) return hip_fail(e, "hipEventRecord");
+    {
+      Range r("mf qkv_rmsnorm");
+      e = mf::launch_qkv(x, w_folded, cu_seqlens, grid_hw, text_len, frames, n_seg, total_tokens, hidden, hd, eps,
+                         st.qws, q, k, v, ncu, stream, events ? events + 1 : nullptr);
+    }
+    if (e != hipSuccess) return hip_fail(e, "qkv kernels launch");
+    if ((rc2 = debug_stage(stream, "qkv kernels", ws_flag(st.qws)))) return rc2;
+    if (events && (e = hipEventRecord(events[2], stream)) != hipSuccess) return hip_fail(e, "hipEventRecord");
+    return int(MF_OK);
+  });
 }
 
 int mf_qkv_rmsnorm(const void* x, const void* w_folded, const int32_t* cu_seqlens, const int32_t* grid_hw,
@@ -1092,8 +1162,10 @@ int mf_attn_packed_strided(const mf_tensor* q, const mf_tensor* k, const mf_tens
   if ((rc = ensure_table(ds, D, MF_ROPE_THETA, &cs))) return rc;
   if ((rc = ensure_cus(ds, dev, &ncu))) return rc;
   if ((rc = ensure_workspace(ds, need))) return rc;
-  return run_attn(q->data, k->data, v->data, cu_seqlens, grid_hw, text_len, out->data, n_seg, T, H, D, q->dtype,
-                  ds.ws, cs, ncu, stream, nullptr, nullptr, nullptr, nullptr, true, &st);
+  return ordered(ds.ord_ws, stream, [&] {
+    return run_attn(q->data, k->data, v->data, cu_seqlens, grid_hw, text_len, out->data, n_seg, T, H, D,
+                    q->dtype, ds.ws, cs, ncu, stream, nullptr, nullptr, nullptr, nullptr, true, &st);
+  });
 }
 
 }  // extern "C"
