@@ -446,7 +446,8 @@ __global__ void __launch_bounds__(64 * KV_WAVES, 2) bwd_kv_kernel(BwdArgs a) {
     copy_to_lds<CH, KV_WAVES>(qtg + int64_t(j) * CH, dst + 2 * CH, wave, lane);
     copy_to_lds<CH, KV_WAVES>(otg + int64_t(j) * CH, dst + 3 * CH, wave, lane);
     if (wave == 0 && lane < 2 * KTILE / 4)
-      __builtin_amdgcn_global_load_lds(stg + int64_t(j) * (2 * KTILE / 4) + lane, (lds_ptr_t)(dst + 4 * CH), 16, 0, 0);
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(raw_rsrc(stg + int64_t(j) * (2 * KTILE / 4), 2 * KTILE * 4),
+                                               (lds_ptr_t)(dst + 4 * CH), 16, lane * 16, 0, 0, 0);
   };
 
   f32x16 acc[DBLK];

@@ -60,17 +60,29 @@ __device__ inline float dot2_bf16_sum(uint32_t pair, float acc) {
   return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, pair), one, acc, false);
 }
 
+// Raw buffer resource over `bytes` bytes at p (no stride, no format
+// conversion; lanes past the range read zeros).
+__device__ inline __amdgpu_buffer_rsrc_t raw_rsrc(const void* p, int32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(p), 0, bytes, 0x00020000);
+}
+
 // Copies CHUNKS consecutive 16-byte chunks from global memory into LDS with
 // gfx950 direct-to-LDS loads: each of WAVES waves moves CHUNKS / WAVES chunks,
 // one contiguous 1 KB per instruction, without passing through registers.
+// The loads are buffer loads (MUBUF), not global (FLAT) ones: the compiler
+// treats a FLAT load into LDS as pending on both memory counters, and while
+// one is in flight every LDS-read wait it places becomes a full drain
+// (lgkmcnt(0)); with the buffer form it keeps exact counts, so operand reads
+// stay pipelined behind the copies. src must be the same in every lane.
 template <int CHUNKS, int WAVES>
 __device__ inline void copy_to_lds(const u32x4* __restrict__ src, u32x4* dst, int wave, int lane) {
   constexpr int PER_WAVE = CHUNKS / WAVES;
   static_assert(PER_WAVE % 64 == 0, "whole 1 KB copies per wave");
+  const __amdgpu_buffer_rsrc_t rs = raw_rsrc(src, CHUNKS * 16);
 #pragma unroll
   for (int i = 0; i < PER_WAVE / 64; ++i) {
     const int c = wave * PER_WAVE + i * 64;
-    __builtin_amdgcn_global_load_lds(src + c + lane, (lds_ptr_t)(dst + c), 16, 0, 0);
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_ptr_t)(dst + c), 16, (c + lane) * 16, 0, 0, 0);
   }
 }
 
