@@ -313,7 +313,10 @@ int ensure_workspace(DeviceState& st, size_t bytes) { return ensure_buffer(st.ws
 // event recorded after it. Calls enqueued while s is being captured into a
 // graph are not ordered this way (a captured graph cannot wait on an event
 // recorded outside it), and the next call does not wait for them; a failed
-// capture-status query counts as capturing. Caller holds g_mu.
+// capture-status query counts as capturing. The event only orders work on
+// this device, so it is recorded without the system-scope fence (which would
+// write the L2 caches back for host visibility after every call). Caller
+// holds g_mu.
 template <typename F>
 int ordered(WsOrder& o, hipStream_t s, F&& launch) {
   hipStreamCaptureStatus cs = hipStreamCaptureStatusNone;
@@ -328,7 +331,7 @@ int ordered(WsOrder& o, hipStream_t s, F&& launch) {
     o.valid = false;
     return rc;
   }
-  if (!o.done && (e = hipEventCreateWithFlags(&o.done, hipEventDisableTiming)) != hipSuccess) {
+  if (!o.done && (e = hipEventCreateWithFlags(&o.done, hipEventDisableTiming | hipEventDisableSystemFence)) != hipSuccess) {
     o.done = nullptr;
     o.valid = false;
     return rc ? rc : hip_fail(e, "hipEventCreateWithFlags (workspace order)");
