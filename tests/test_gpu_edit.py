@@ -170,6 +170,54 @@ def test_backward_3d(case):
         _check_grad(name, to_f64(g), r)
 
 
+def _heads(w, sel):
+    return workloads.Workload(f"{w.name}[heads {sel}]", w.grid_hw, w.text_len, len(sel), w.head_dim, w.dtype,
+                              w.q[:, sel], w.k[:, sel], w.v[:, sel], w.seed, w.frames, w.rope_split)
+
+
+# The editing batches at their real 24 heads: edit1024 (one 8448-token
+# sequence, 66 query tiles per head) fills the chip in a few rounds of units
+# and takes the split last round; both run the XCD-aware unit order that the
+# two- and three-head cases never reach. Heads are independent, so a few of
+# them are compared with the oracle run on those head slices alone.
+EDIT_ALL_HEADS = {"edit1024": [0, 7, 8, 23], "edit_mixed": [0, 9, 16, 23]}
+
+
+@pytest.mark.parametrize("config", sorted(EDIT_ALL_HEADS))
+def test_attention_3d_configs_all_heads(config):
+    w = workloads.make_edit(config)
+    sel = EDIT_ALL_HEADS[config]
+    print(f"edit {config} T={w.tokens} H={w.heads} compared heads {sel}", flush=True)
+    out, lse = _forward(w)
+    ws = _heads(w, sel)
+    exp = attention.joint_attention_3d(ws.q, ws.k, ws.v, ws.grid_hw, ws.text_len, ws.frames, ws.rope_split)
+    check_close(to_f64(out[:, sel]), exp, w.dtype)
+    ref_lse = attention.joint_attention_3d_lse(ws.q, ws.k, ws.grid_hw, ws.text_len, ws.frames, ws.rope_split)
+    check_lse(lse.cpu().numpy()[sel], ref_lse, ws)
+    assert torch.isfinite(out.float()).all() and torch.isfinite(lse).all()
+
+
+@pytest.mark.parametrize("config,sel", [("edit1024", [0, 8, 23]), ("edit_mixed", [9, 16])])
+def test_backward_3d_configs_all_heads(config, sel):
+    w = workloads.make_edit(config)
+    print(f"edit backward {config} T={w.tokens} H={w.heads} compared heads {sel}", flush=True)
+    rng = np.random.default_rng(66)
+    do = workloads.bf16_bits_to_f32(workloads.f32_to_bf16_bits(rng.standard_normal(w.q.shape, dtype=np.float32)))
+    q, k, v, grid, text, frames = _dev(w)
+    cu, _, _ = binding.build_metadata_3d(grid, text, frames, w.tokens)
+    out, lse = binding.attn_packed_3d(q, k, v, cu, grid, text, frames, w.rope_split, lse=True)
+    dot = torch.from_numpy(do).to(torch.bfloat16).cuda()
+    dq, dk, dv = binding.attn_packed_3d_bwd(q, k, v, out, dot, lse, cu, grid, text, frames, w.rope_split)
+    torch.cuda.synchronize()
+    assert binding.get_device_error() == binding.MF_OK, binding.last_error()
+    ws = _heads(w, sel)
+    rq, rk, rv = attention.joint_attention_3d_backward(ws.q, ws.k, ws.v, do[:, sel], ws.grid_hw, ws.text_len,
+                                                       ws.frames, ws.rope_split)
+    for name, g, r in (("dq", dq, rq), ("dk", dk, rk), ("dv", dv, rv)):
+        _check_grad(name, to_f64(g[:, sel]), r)
+        assert torch.isfinite(g.float()).all(), f"{name}: non-finite"
+
+
 def test_attention_3d_rejects_bad_split():
     w = workloads.make_edit(grids=[[2, 2]], texts=[1], frames=[2], heads=1, head_dim=64, dtype="bf16", seed=1)
     q, k, v, grid, text, frames = _dev(w)
