@@ -12,18 +12,20 @@
 //
 // bf16 kernel (d = 64 or 128), one workgroup = QTILE / 32 waves = QTILE queries
 // (the queries are read from the caller's q and rotated while loading)
-// of one (sample, head), each wave owning 32 query rows:
-//   S^T (64 keys x 32 queries) = K~ tile (LDS) x Q~^T (registers), on
-//       v_mfma_f32_32x32x16_bf16 with fp32 accumulation. In this orientation
-//       every lane holds one query row: 32 of the 64 keys in registers, the
-//       other 32 in lane ^ 32, so row max / sum need one cross-half exchange.
+// of one (sample, head), each wave owning 32 query rows as two blocks of 16:
+//   S^T (64 keys x 16 queries per block) = K~ tile (LDS) x Q~^T (registers),
+//       on v_mfma_f32_16x16x32_bf16 with fp32 accumulation; each K~ operand
+//       read feeds the MFMAs of both blocks. In this orientation a lane holds
+//       16 of the 64 scores of one query and the other 48 sit in lanes l ^ 16,
+//       l ^ 32 and l ^ 48, so row max / sum need two lane swaps.
 //   online softmax in the exp2 domain (scale * log2(e) folded into one FMA),
-//       running max m, per-lane partial row sums (combined once at the end),
-//       accumulator rescale skipped when no row max moved;
-//   O^T (d x 32 queries) += V~^T tile (LDS) x P^T (registers, bf16 RNE).
-// K~ and V~^T tiles (KTILE x d each) are double-buffered in LDS: the global
-// loads of tile j+1 are issued before the math of tile j and written to the
-// other LDS buffer after it, one barrier per tile.
+//       a reference max that moves only when a tile exceeds it by 2^8 (the
+//       accumulator rescale is skipped otherwise), per-lane partial row sums
+//       (combined once at the end);
+//   O^T (d x 16 queries per block) += V~^T tile (LDS) x P^T (registers, bf16 RNE).
+// K~ and V~^T tiles (KTILE x d each) are double-buffered in LDS: the
+// direct-to-LDS copies of tile j+1 into the other buffer are issued before the
+// math of tile j, one barrier per tile.
 //
 // f32 kernel: the same tiling of work with plain fp32 FMAs (no reduced
 // precision anywhere); each query row is split over two lanes (channel halves).
