@@ -23,9 +23,12 @@
 //       accumulator rescale is skipped otherwise), per-lane partial row sums
 //       (combined once at the end);
 //   O^T (d x 16 queries per block) += V~^T tile (LDS) x P^T (registers, bf16 RNE).
-// K~ and V~^T tiles (KTILE x d each) are double-buffered in LDS: the
-// direct-to-LDS copies of tile j+1 into the other buffer are issued before the
-// math of tile j, one barrier per tile.
+// Per key tile a wave has an MFMA phase (P.V of the previous tile, scores of
+// this tile, LDS operands read ahead) and a VALU phase (softmax). The two
+// waves sharing a SIMD are one phase apart (waves 0-3 and 4-7, a barrier
+// after every phase), so one issues MFMAs while the other runs its softmax.
+// K~ and V~^T tiles (KTILE x d each) are triple-buffered in LDS and copied
+// there by direct-to-LDS loads two tiles ahead.
 //
 // f32 kernel: the same tiling of work with plain fp32 FMAs (no reduced
 // precision anywhere); each query row is split over two lanes (channel halves).
@@ -99,42 +102,74 @@ __device__ inline float quad_sum(float x) {
   return __uint_as_float(r[0]) + __uint_as_float(r[1]);
 }
 
-// One 64-key tile of one wave's 32 query rows (two blocks of 16): S^T = K~ Q~^T,
-// online softmax, O^T += V~^T P^T. kt / vt point at the chunk-major K~ and
-// V~^T tiles in LDS. Lane (g, l16) = (lane / 16, lane % 16) holds, for query
-// 16 qb + l16, the scores of keys 16 kb + 4 g + i (i = 0..3) in s[kb][qb] and
-// the output channels 16 cb + 4 g + i in acc[cb][qb].
+// LDS operand reads issued ahead of their MFMAs in an MFMA phase.
+constexpr int PF_DEPTH = 6;
+
+// MFMA phase of tile j for one wave's 32 query rows (two blocks of 16): with
+// PV, O^T += V~^T P^T for tile j-1 (P^T in pk, V~^T tile vt), then, with SC,
+// S^T = K~ Q~^T for tile j (K~ tile kt) into s. Lane (g, l16) = (lane / 16,
+// lane % 16) holds, for query 16 qb + l16, the scores of keys 16 kb + 4 g + i
+// (i = 0..3) in s[kb][qb] and the output channels 16 cb + 4 g + i in
+// acc[cb][qb]. Each 16-byte operand read from LDS feeds the MFMAs of both
+// query blocks and is issued PF_DEPTH operands ahead of them (the order is
+// pinned by scheduling fences): in this phase the wave's SIMD partner runs
+// its softmax, so no other wave's MFMAs cover the LDS latency. The products
+// are summed in the same order as a plain loop (k-steps ks = 0.. for S, key
+// halves jj = 0, 1 for O).
+template <int D, bool PV, bool SC>
+__device__ __attribute__((always_inline)) inline void mfma_phase(const u32x4* kt, const u32x4* vt,
+                                                                 const bf16x8 (&qreg)[2][D / 32],
+                                                                 f32x4 (&acc)[D / 16][2], f32x4 (&s)[4][2],
+                                                                 const u32x4 (&pk)[2][2], int g, int l16) {
+  constexpr int CBLK = Bf16Tile<D>::CBLK;
+  constexpr int NV = PV ? 2 * CBLK : 0;              // V~^T operands: key half jj, channel block cb
+  constexpr int NK = SC ? 4 * Bf16Tile<D>::KSTEPS : 0;  // K~ operands: k-step ks, key block kb
+  constexpr int N = NV + NK;
+  // K~ chunk (c, n) sits at c * KTILE + n: lane reads key 16 kb + l16, channel
+  // chunk 4 ks + g. V~^T chunk (k8, r) sits at k8 * D + r and holds, for
+  // channel r, keys 32 (k8 / 4) + 4 (k8 % 4) + {0..3, 16..19}: lane reads
+  // channel 16 cb + l16, key chunk 4 jj + g, the keys its own P^T operand carries.
+  const u32x4* kl = kt + g * KTILE + l16;
+  const u32x4* vl = vt + g * D + l16;
+  auto operand = [&](int r) __attribute__((always_inline)) {
+    return __builtin_bit_cast(bf16x8, r < NV ? vl[4 * D * (r / CBLK) + 16 * (r % CBLK)]
+                                             : kl[4 * KTILE * ((r - NV) / 4) + 16 * ((r - NV) % 4)]);
+  };
+  bf16x8 op[N];
+#pragma unroll
+  for (int r = 0; r < PF_DEPTH && r < N; ++r) op[r] = operand(r);
+  if constexpr (SC) {
+#pragma unroll
+    for (int kb = 0; kb < 4; ++kb) s[kb][0] = s[kb][1] = f32x4{};
+  }
+#pragma unroll
+  for (int i = 0; i < N; ++i) {
+    if (i + PF_DEPTH < N) op[i + PF_DEPTH] = operand(i + PF_DEPTH);
+    __builtin_amdgcn_sched_barrier(0);
+    if (i < NV) {
+      const int jj = i / CBLK, cb = i % CBLK;
+      acc[cb][0] = mfma16(op[i], __builtin_bit_cast(bf16x8, pk[jj][0]), acc[cb][0]);
+      acc[cb][1] = mfma16(op[i], __builtin_bit_cast(bf16x8, pk[jj][1]), acc[cb][1]);
+    } else {
+      const int ks = (i - NV) / 4, kb = (i - NV) % 4;
+      s[kb][0] = mfma16(op[i], qreg[0][ks], s[kb][0]);
+      s[kb][1] = mfma16(op[i], qreg[1][ks], s[kb][1]);
+    }
+    __builtin_amdgcn_sched_barrier(0);
+  }
+}
+
+// VALU phase of tile j: key mask (MASKED: keys from kbase_key on at or past L),
+// online softmax in the exp2 domain and the bf16 P^T operand. P^T of query
+// block qb for keys 32 jj .. 32 jj + 31: k-slots 8 g .. +3 are keys
+// 32 jj + 4 g + i, slots 8 g + 4 .. +7 keys 32 jj + 16 + 4 g + i, i.e.
+// s[2 jj][qb] and s[2 jj + 1][qb] of this lane.
 template <int D, bool MASKED>
-__device__ inline void attend_tile(const u32x4* kt, const u32x4* vt, const bf16x8 (&qreg)[2][D / 32],
-                                   f32x4 (&acc)[D / 16][2], float (&m)[2], float (&lsum)[2], float c,
-                                   int kbase_key, int L, int g, int l16) {
-  constexpr int KSTEPS = Bf16Tile<D>::KSTEPS;
+__device__ __attribute__((always_inline)) inline void valu_phase(f32x4 (&s)[4][2], f32x4 (&acc)[D / 16][2],
+                                                                 float (&m)[2], float (&lsum)[2], u32x4 (&pk)[2][2],
+                                                                 float c, int kbase_key, int L, int g) {
   constexpr int CBLK = Bf16Tile<D>::CBLK;
   constexpr float REF_SLACK = 8.0f;
-  // K~ chunk (c, n) sits at c * KTILE + n: lane reads key 16 kb + l16, channel
-  // chunk 4 ks + g.
-  const u32x4* kl = kt + g * KTILE + l16;
-  // V~^T chunk (k8, r) sits at k8 * D + r and holds, for channel r, keys
-  // 32 (k8 / 4) + 4 (k8 % 4) + {0..3, 16..19}: lane reads channel 16 cb + l16,
-  // key chunk 4 j + g, the keys its own P^T operand carries.
-  const u32x4* vl = vt + g * D + l16;
-
-  f32x4 s[4][2];
-#pragma unroll
-  for (int kb = 0; kb < 4; ++kb) s[kb][0] = s[kb][1] = f32x4{};
-#pragma unroll
-  for (int ks = 0; ks < KSTEPS; ++ks) {
-#pragma unroll
-    for (int kb = 0; kb < 4; ++kb) {
-      const bf16x8 kk = __builtin_bit_cast(bf16x8, kl[4 * KTILE * ks + 16 * kb]);
-      s[kb][0] = mfma16(kk, qreg[0][ks], s[kb][0]);
-      s[kb][1] = mfma16(kk, qreg[1][ks], s[kb][1]);
-    }
-  }
-  // V operands of the first 32 keys, read while the softmax runs.
-  bf16x8 vb[CBLK];
-#pragma unroll
-  for (int cb = 0; cb < CBLK; ++cb) vb[cb] = __builtin_bit_cast(bf16x8, vl[16 * cb]);
   if constexpr (MASKED) {
     const int kb0 = kbase_key + 4 * g;
 #pragma unroll
@@ -171,24 +206,20 @@ __device__ inline void attend_tile(const u32x4* kt, const u32x4* vt, const bf16x
       m[qb] = mnew;
     }
   }
-  // P^T operand of query block qb for keys 32 j .. 32 j + 31: k-slots 8 g .. +3
-  // are keys 32 j + 4 g + i, slots 8 g + 4 .. +7 keys 32 j + 16 + 4 g + i,
-  // i.e. s[2 j][qb] and s[2 j + 1][qb] of this lane.
-  u32x4 pk[2][2];
 #pragma unroll
   for (int qb = 0; qb < 2; ++qb) {
     const float nm = -m[qb];
 #pragma unroll
-    for (int j = 0; j < 2; ++j) {
+    for (int jj = 0; jj < 2; ++jj) {
 #pragma unroll
       for (int h = 0; h < 2; ++h) {
-        const f32x4 x = s[2 * j + h][qb];
+        const f32x4 x = s[2 * jj + h][qb];
         const float p0 = __builtin_amdgcn_exp2f(__builtin_fmaf(x[0], c, nm));
         const float p1 = __builtin_amdgcn_exp2f(__builtin_fmaf(x[1], c, nm));
         const float p2 = __builtin_amdgcn_exp2f(__builtin_fmaf(x[2], c, nm));
         const float p3 = __builtin_amdgcn_exp2f(__builtin_fmaf(x[3], c, nm));
-        pk[j][qb][2 * h] = pack_bf16x2(p0, p1);
-        pk[j][qb][2 * h + 1] = pack_bf16x2(p2, p3);
+        pk[jj][qb][2 * h] = pack_bf16x2(p0, p1);
+        pk[jj][qb][2 * h + 1] = pack_bf16x2(p2, p3);
       }
     }
   }
@@ -196,21 +227,9 @@ __device__ inline void attend_tile(const u32x4* kt, const u32x4* vt, const bf16x
 #pragma unroll
   for (int qb = 0; qb < 2; ++qb)
 #pragma unroll
-    for (int j = 0; j < 2; ++j)
+    for (int jj = 0; jj < 2; ++jj)
 #pragma unroll
-      for (int i = 0; i < 4; ++i) lsum[qb] = dot2_bf16_sum(pk[j][qb][i], lsum[qb]);
-  // O^T += V~^T x P^T
-#pragma unroll
-  for (int j = 0; j < 2; ++j) {
-    const bf16x8 p0 = __builtin_bit_cast(bf16x8, pk[j][0]), p1 = __builtin_bit_cast(bf16x8, pk[j][1]);
-#pragma unroll
-    for (int cb = 0; cb < CBLK; ++cb) {
-      const bf16x8 vv = vb[cb];
-      if (j == 0) vb[cb] = __builtin_bit_cast(bf16x8, vl[4 * D + 16 * cb]);
-      acc[cb][0] = mfma16(vv, p0, acc[cb][0]);
-      acc[cb][1] = mfma16(vv, p1, acc[cb][1]);
-    }
-  }
+      for (int i = 0; i < 4; ++i) lsum[qb] = dot2_bf16_sum(pk[jj][qb][i], lsum[qb]);
 }
 
 template <int D, bool R3>
@@ -286,8 +305,8 @@ __global__ void __launch_bounds__(ATTN_THREADS, 2) attn_fwd_bf16_kernel(AttnArgs
   __builtin_amdgcn_s_waitcnt(0xF70);  // vmcnt(0)
   __builtin_amdgcn_sched_barrier(0);
 
-  // Two LDS buffers, each one K~ tile and one V~^T tile (chunk-major, verbatim copies).
-  __shared__ u32x4 kA[CHUNKS], vA[CHUNKS], kB[CHUNKS], vB[CHUNKS];
+  // Three K~ and three V~^T tile buffers (chunk-major, verbatim copies).
+  __shared__ u32x4 kA[CHUNKS], kB[CHUNKS], kC[CHUNKS], vA[CHUNKS], vB[CHUNKS], vC[CHUNKS];
   // Key tiles [kt0, kt1) of the sample; the sample's last tile carries the key mask.
   const u32x4* kg = reinterpret_cast<const u32x4*>(static_cast<const uint16_t*>(a.kw) + head_row0 * D) + kt0 * CHUNKS;
   const u32x4* vg = reinterpret_cast<const u32x4*>(static_cast<const uint16_t*>(a.vw) + head_row0 * D) + kt0 * CHUNKS;
@@ -302,33 +321,84 @@ __global__ void __launch_bounds__(ATTN_THREADS, 2) attn_fwd_bf16_kernel(AttnArgs
 #pragma unroll
   for (int b = 0; b < CBLK; ++b) acc[b][0] = acc[b][1] = f32x4{};
 
-  tile_to_lds<CHUNKS>(kg, kA, wave, lane);
-  tile_to_lds<CHUNKS>(vg, vA, wave, lane);
+  // Two groups of waves, 0-3 and 4-7 (waves w and w + 4 share a SIMD), run the
+  // same program, for every tile j an MFMA phase (P.V of tile j-1, scores of
+  // tile j) and then a VALU phase (softmax of tile j), with a barrier after
+  // each phase and group 1 one barrier behind group 0: between two barriers
+  // one wave of every SIMD issues MFMAs while the other runs its softmax.
+  // K~(j) sits in kbuf[j % 3], V~^T(j) in vbuf[j % 3]. At the start of its MFMA
+  // phase of tile j every wave issues its share of the copies of K~(j+2) and
+  // V~^T(j+1) (past the sample's last tile: the last tile again, into a free
+  // buffer, never read), and at the end of that phase it waits for the copies
+  // it issued one tile earlier. Counted in phases of the two groups together,
+  // a buffer is refilled only after both groups' last read of it, and every
+  // copy has landed at least one barrier before the first read of its tile.
+  const int grp = wave >> 2;
+  f32x4 s[4][2];
+  u32x4 pk[2][2];
+  constexpr int NCOPY = 2 * (CHUNKS / ATTN_WAVES) / 64;  // copy instructions per wave per tile
+  static_assert(NCOPY <= 15, "fits the low vmcnt field");
+  auto bar = [&]() __attribute__((always_inline)) {
+    __builtin_amdgcn_sched_barrier(0);
+    __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0): this wave's LDS reads are complete
+    __builtin_amdgcn_s_barrier();
+    __builtin_amdgcn_sched_barrier(0);
+  };
+  auto wait_older_copies = [&]() __attribute__((always_inline)) {
+    __builtin_amdgcn_sched_barrier(0);
+    __builtin_amdgcn_s_waitcnt(0xF70 | NCOPY);  // vmcnt(NCOPY): all but the newest tile's copies
+    __builtin_amdgcn_sched_barrier(0);
+  };
+  const int last = nkt - 1;
+  auto copy_k = [=](int t, u32x4* dst) __attribute__((always_inline)) {
+    tile_to_lds<CHUNKS>(kg + min(t, last) * CHUNKS, dst, wave, lane);
+  };
+  auto copy_v = [=](int t, u32x4* dst) __attribute__((always_inline)) {
+    tile_to_lds<CHUNKS>(vg + min(t, last) * CHUNKS, dst, wave, lane);
+  };
+  // Tile jt with K~(jt) in kc and V~^T(jt-1) in vp; copies of K~(jt+2) into kn
+  // and V~^T(jt+1) into vn. The buffers are named statically (loop unrolled by
+  // three) so that the compiler can tell the copies' targets from the tiles read.
+  auto key_tile = [&](int jt, auto pv, u32x4* kc, u32x4* vp, u32x4* kn, u32x4* vn) __attribute__((always_inline)) {
+    copy_k(jt + 2, kn);
+    copy_v(jt + 1, vn);
+    if constexpr (decltype(pv)::value) mfma_phase<D, true, true>(kc, vp, qreg, acc, s, pk, g, l16);
+    else mfma_phase<D, false, true>(kc, vp, qreg, acc, s, pk, g, l16);
+    wait_older_copies();
+    bar();
+    if (mask_last && jt == last) valu_phase<D, true>(s, acc, m, lsum, pk, c, key0 + KTILE * jt, L, g);
+    else valu_phase<D, false>(s, acc, m, lsum, pk, c, key0 + KTILE * jt, L, g);
+    bar();
+  };
+  using Yes = std::true_type;
+  using No = std::false_type;
+  copy_k(0, kA);
+  copy_k(1, kB);
+  copy_v(0, vA);
   wait_tile_and_sync();
-  // Tiles alternate between buffer A (even j) and B (odd j); the copy of tile
-  // j+1 runs while tile j is processed. The last tile carries the key mask.
-  int j = 0;
-  for (; j + 2 < nkt; j += 2) {
-    tile_to_lds<CHUNKS>(kg + (j + 1) * CHUNKS, kB, wave, lane);
-    tile_to_lds<CHUNKS>(vg + (j + 1) * CHUNKS, vB, wave, lane);
-    attend_tile<D, false>(kA, vA, qreg, acc, m, lsum, c, key0 + KTILE * j, L, g, l16);
-    wait_tile_and_sync();
-    tile_to_lds<CHUNKS>(kg + (j + 2) * CHUNKS, kA, wave, lane);
-    tile_to_lds<CHUNKS>(vg + (j + 2) * CHUNKS, vA, wave, lane);
-    attend_tile<D, false>(kB, vB, qreg, acc, m, lsum, c, key0 + KTILE * (j + 1), L, g, l16);
-    wait_tile_and_sync();
+  if (grp == 1) bar();
+  // j % 3 == 0: K~ kA, V~^T(j-1) vC, copies into kC, vB
+  // j % 3 == 1: K~ kB, V~^T(j-1) vA, copies into kA, vC
+  // j % 3 == 2: K~ kC, V~^T(j-1) vB, copies into kB, vA
+  key_tile(0, No{}, kA, vC, kC, vB);
+  int j = 1;
+  if (j < nkt) key_tile(j++, Yes{}, kB, vA, kA, vC);
+  if (j < nkt) key_tile(j++, Yes{}, kC, vB, kB, vA);
+  for (; j + 3 <= nkt; j += 3) {
+    key_tile(j, Yes{}, kA, vC, kC, vB);
+    key_tile(j + 1, Yes{}, kB, vA, kA, vC);
+    key_tile(j + 2, Yes{}, kC, vB, kB, vA);
   }
-  if (j + 1 < nkt) {
-    tile_to_lds<CHUNKS>(kg + (j + 1) * CHUNKS, kB, wave, lane);
-    tile_to_lds<CHUNKS>(vg + (j + 1) * CHUNKS, vB, wave, lane);
-    attend_tile<D, false>(kA, vA, qreg, acc, m, lsum, c, key0 + KTILE * j, L, g, l16);
-    wait_tile_and_sync();
-    if (mask_last) attend_tile<D, true>(kB, vB, qreg, acc, m, lsum, c, key0 + KTILE * (j + 1), L, g, l16);
-    else attend_tile<D, false>(kB, vB, qreg, acc, m, lsum, c, key0 + KTILE * (j + 1), L, g, l16);
-  } else {
-    if (mask_last) attend_tile<D, true>(kA, vA, qreg, acc, m, lsum, c, key0 + KTILE * j, L, g, l16);
-    else attend_tile<D, false>(kA, vA, qreg, acc, m, lsum, c, key0 + KTILE * j, L, g, l16);
+  if (j < nkt) key_tile(j++, Yes{}, kA, vC, kC, vB);
+  if (j < nkt) key_tile(j++, Yes{}, kB, vA, kA, vC);
+  // P.V of the last tile, V~^T(last) in vbuf[last % 3].
+  switch (last % 3) {
+    case 0: mfma_phase<D, true, false>(kA, vA, qreg, acc, s, pk, g, l16); break;
+    case 1: mfma_phase<D, true, false>(kA, vB, qreg, acc, s, pk, g, l16); break;
+    default: mfma_phase<D, true, false>(kA, vC, qreg, acc, s, pk, g, l16); break;
   }
+  __builtin_amdgcn_s_waitcnt(0xF70);  // vmcnt(0): no copy into LDS left in flight
+  if (grp == 0) bar();
 
   // Epilogue: O = acc / l. acc[b][qb] holds channels 16 b + 4 g .. +3 of query
   // 16 qb + l16 of the wave.
