@@ -195,14 +195,16 @@ __device__ __attribute__((always_inline)) inline void valu_phase(f32x4 (&s)[4][2
     // rescaled only on those tiles; numerator and denominator share m.
     grow[qb] = mt[qb] > m[qb] + REF_SLACK;  // always true on the first tile (m = -inf)
   }
-  if (__any(grow[0] || grow[1])) {
+  // Reference max, row sums and the factor alpha of the accumulator; the
+  // accumulator itself is rescaled at the end of the phase (see there).
+  const bool any_grow = __any(grow[0] || grow[1]);
+  float alpha[2] = {1.f, 1.f};
+  if (any_grow) {
 #pragma unroll
     for (int qb = 0; qb < 2; ++qb) {
       const float mnew = grow[qb] ? mt[qb] : m[qb];
-      const float alpha = __builtin_amdgcn_exp2f(m[qb] - mnew);  // 0 on the first tile, 1 where unchanged
-      lsum[qb] *= alpha;
-#pragma unroll
-      for (int cb = 0; cb < CBLK; ++cb) acc[cb][qb] *= alpha;
+      alpha[qb] = __builtin_amdgcn_exp2f(m[qb] - mnew);  // 0 on the first tile, 1 where unchanged
+      lsum[qb] *= alpha[qb];
       m[qb] = mnew;
     }
   }
@@ -230,6 +232,16 @@ __device__ __attribute__((always_inline)) inline void valu_phase(f32x4 (&s)[4][2
     for (int jj = 0; jj < 2; ++jj)
 #pragma unroll
       for (int i = 0; i < 4; ++i) lsum[qb] = dot2_bf16_sum(pk[jj][qb][i], lsum[qb]);
+  // The rare accumulator rescale comes last: the accumulator is not read in
+  // this phase, and with the conditional update ahead of the exponentials the
+  // register allocator moved all 64 accumulator registers on every tile
+  // (32 v_mov_b64 per tile and wave) to merge the two paths.
+  if (any_grow) {
+#pragma unroll
+    for (int qb = 0; qb < 2; ++qb)
+#pragma unroll
+      for (int cb = 0; cb < CBLK; ++cb) acc[cb][qb] *= alpha[qb];
+  }
 }
 
 template <int D, bool R3>
@@ -360,11 +372,15 @@ __global__ void __launch_bounds__(ATTN_THREADS, 2) attn_fwd_bf16_kernel(AttnArgs
   // and V~^T(jt+1) into vn. The buffers are named statically (loop unrolled by
   // three) so that the compiler can tell the copies' targets from the tiles read.
   auto key_tile = [&](int jt, auto pv, u32x4* kc, u32x4* vp, u32x4* kn, u32x4* vn) __attribute__((always_inline)) {
+    // The MFMA phase runs at raised wave priority, so that the SIMD issues its
+    // MFMAs and operand reads ahead of the partner wave's softmax.
+    __builtin_amdgcn_s_setprio(1);
     copy_k(jt + 2, kn);
     copy_v(jt + 1, vn);
     if constexpr (decltype(pv)::value) mfma_phase<D, true, true>(kc, vp, qreg, acc, s, pk, g, l16);
     else mfma_phase<D, false, true>(kc, vp, qreg, acc, s, pk, g, l16);
     wait_older_copies();
+    __builtin_amdgcn_s_setprio(0);
     bar();
     if (mask_last && jt == last) valu_phase<D, true>(s, acc, m, lsum, pk, c, key0 + KTILE * jt, L, g);
     else valu_phase<D, false>(s, acc, m, lsum, pk, c, key0 + KTILE * jt, L, g);
