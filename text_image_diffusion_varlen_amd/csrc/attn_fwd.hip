@@ -338,27 +338,29 @@ __global__ void __launch_bounds__(ATTN_THREADS, 2) attn_fwd_bf16_kernel(AttnArgs
   // tile j) and then a VALU phase (softmax of tile j), with a barrier after
   // each phase and group 1 one barrier behind group 0: between two barriers
   // one wave of every SIMD issues MFMAs while the other runs its softmax.
-  // K~(j) sits in kbuf[j % 3], V~^T(j) in vbuf[j % 3]. At the start of its MFMA
+  // K~(j) sits in kbuf[j % 3], V~^T(j) in vbuf[j % 3]. At the start of its VALU
   // phase of tile j every wave issues its share of the copies of K~(j+2) and
   // V~^T(j+1) (past the sample's last tile: the last tile again, into a free
-  // buffer, never read), and at the end of that phase it waits for the copies
-  // it issued one tile earlier. Counted in phases of the two groups together,
-  // a buffer is refilled only after both groups' last read of it, and every
-  // copy has landed at least one barrier before the first read of its tile.
+  // buffer, never read), and at the end of its next MFMA phase it waits for
+  // them (vmcnt(0)), so the MFMA phase carries no copy instructions. Counted
+  // in phases of the two groups together (group 0's MFMA phase of tile j is
+  // phase 2j, group 1's is 2j+1), a buffer is refilled only after both
+  // groups' last read of it (K~(j-1) is last read in phase 2j-1, refilled from
+  // phase 2j+1; V~^T(j-2) likewise), and every wave's share of K~(j+2) and
+  // V~^T(j+1) has landed by the end of phase 2j+3, before the first read of
+  // those tiles in phase 2j+4.
   const int grp = wave >> 2;
   f32x4 s[4][2];
   u32x4 pk[2][2];
-  constexpr int NCOPY = 2 * (CHUNKS / ATTN_WAVES) / 64;  // copy instructions per wave per tile
-  static_assert(NCOPY <= 15, "fits the low vmcnt field");
   auto bar = [&]() __attribute__((always_inline)) {
     __builtin_amdgcn_sched_barrier(0);
     __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0): this wave's LDS reads are complete
     __builtin_amdgcn_s_barrier();
     __builtin_amdgcn_sched_barrier(0);
   };
-  auto wait_older_copies = [&]() __attribute__((always_inline)) {
+  auto wait_copies = [&]() __attribute__((always_inline)) {
     __builtin_amdgcn_sched_barrier(0);
-    __builtin_amdgcn_s_waitcnt(0xF70 | NCOPY);  // vmcnt(NCOPY): all but the newest tile's copies
+    __builtin_amdgcn_s_waitcnt(0xF70);  // vmcnt(0): this wave's tile copies have landed
     __builtin_amdgcn_sched_barrier(0);
   };
   const int last = nkt - 1;
@@ -375,13 +377,13 @@ __global__ void __launch_bounds__(ATTN_THREADS, 2) attn_fwd_bf16_kernel(AttnArgs
     // The MFMA phase runs at raised wave priority, so that the SIMD issues its
     // MFMAs and operand reads ahead of the partner wave's softmax.
     __builtin_amdgcn_s_setprio(1);
-    copy_k(jt + 2, kn);
-    copy_v(jt + 1, vn);
     if constexpr (decltype(pv)::value) mfma_phase<D, true, true>(kc, vp, qreg, acc, s, pk, g, l16);
     else mfma_phase<D, false, true>(kc, vp, qreg, acc, s, pk, g, l16);
-    wait_older_copies();
+    wait_copies();
     __builtin_amdgcn_s_setprio(0);
     bar();
+    copy_k(jt + 2, kn);
+    copy_v(jt + 1, vn);
     if (mask_last && jt == last) valu_phase<D, true>(s, acc, m, lsum, pk, c, key0 + KTILE * jt, L, g);
     else valu_phase<D, false>(s, acc, m, lsum, pk, c, key0 + KTILE * jt, L, g);
     bar();
