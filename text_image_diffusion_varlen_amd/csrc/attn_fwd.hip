@@ -20,8 +20,8 @@
 //       l ^ 32 and l ^ 48, so row max / sum need two lane swaps.
 //   online softmax in the exp2 domain (scale * log2(e) folded into one FMA),
 //       a reference max that moves only when a tile exceeds it by 2^8 (the
-//       accumulator rescale is skipped otherwise), per-lane partial row sums
-//       (combined once at the end);
+//       accumulator rescale is skipped otherwise), row sums of the bf16 P
+//       formed by MFMAs against an all-ones operand;
 //   O^T (d x 16 queries per block) += V~^T tile (LDS) x P^T (registers, bf16 RNE).
 // Per key tile a wave has an MFMA phase (P.V of the previous tile, scores of
 // this tile, LDS operands read ahead) and a VALU phase (softmax). The two
@@ -120,7 +120,8 @@ template <int D, bool PV, bool SC>
 __device__ __attribute__((always_inline)) inline void mfma_phase(const u32x4* kt, const u32x4* vt,
                                                                  const bf16x8 (&qreg)[2][D / 32],
                                                                  f32x4 (&acc)[D / 16][2], f32x4 (&s)[4][2],
-                                                                 const u32x4 (&pk)[2][2], int g, int l16) {
+                                                                 const u32x4 (&pk)[2][2], f32x4 (&lsv)[2], int g,
+                                                                 int l16) {
   constexpr int CBLK = Bf16Tile<D>::CBLK;
   constexpr int NV = PV ? 2 * CBLK : 0;              // V~^T operands: key half jj, channel block cb
   constexpr int NK = SC ? 4 * Bf16Tile<D>::KSTEPS : 0;  // K~ operands: k-step ks, key block kb
@@ -157,6 +158,22 @@ __device__ __attribute__((always_inline)) inline void mfma_phase(const u32x4* kt
     }
     __builtin_amdgcn_sched_barrier(0);
   }
+  // Row sums of tile j-1's bf16 P (the values just multiplied into V~^T): the
+  // same MFMA with an all-ones A operand sums P^T over the 32 keys of a k-step
+  // into every entry of lsv[qb]. Four MFMAs per tile take the 16 v_dot2 of
+  // per-lane sums out of the softmax phase, whose VALU work (its exponentials
+  // above all, which run slower while the SIMD partner issues MFMAs) is the
+  // longer side of the two phases.
+  if constexpr (PV) {
+    typedef __bf16 bf16x8v __attribute__((ext_vector_type(8)));
+    const bf16x8v ones = {(__bf16)1.f, (__bf16)1.f, (__bf16)1.f, (__bf16)1.f,
+                          (__bf16)1.f, (__bf16)1.f, (__bf16)1.f, (__bf16)1.f};
+#pragma unroll
+    for (int jj = 0; jj < 2; ++jj) {
+      lsv[0] = mfma16(__builtin_bit_cast(bf16x8, ones), __builtin_bit_cast(bf16x8, pk[jj][0]), lsv[0]);
+      lsv[1] = mfma16(__builtin_bit_cast(bf16x8, ones), __builtin_bit_cast(bf16x8, pk[jj][1]), lsv[1]);
+    }
+  }
 }
 
 // VALU phase of tile j: key mask (MASKED: keys from kbase_key on at or past L),
@@ -166,7 +183,7 @@ __device__ __attribute__((always_inline)) inline void mfma_phase(const u32x4* kt
 // s[2 jj][qb] and s[2 jj + 1][qb] of this lane.
 template <int D, bool MASKED>
 __device__ __attribute__((always_inline)) inline void valu_phase(f32x4 (&s)[4][2], f32x4 (&acc)[D / 16][2],
-                                                                 float (&m)[2], float (&lsum)[2], u32x4 (&pk)[2][2],
+                                                                 float (&m)[2], f32x4 (&lsv)[2], u32x4 (&pk)[2][2],
                                                                  float c, int kbase_key, int L, int g) {
   constexpr int CBLK = Bf16Tile<D>::CBLK;
   constexpr float REF_SLACK = 8.0f;
@@ -195,8 +212,8 @@ __device__ __attribute__((always_inline)) inline void valu_phase(f32x4 (&s)[4][2
     // rescaled only on those tiles; numerator and denominator share m.
     grow[qb] = mt[qb] > m[qb] + REF_SLACK;  // always true on the first tile (m = -inf)
   }
-  // Reference max, row sums and the factor alpha of the accumulator; the
-  // accumulator itself is rescaled at the end of the phase (see there).
+  // Reference max and the factor alpha of the accumulator and the row sums,
+  // which are rescaled at the end of the phase (see there).
   const bool any_grow = __any(grow[0] || grow[1]);
   float alpha[2] = {1.f, 1.f};
   if (any_grow) {
@@ -204,7 +221,6 @@ __device__ __attribute__((always_inline)) inline void valu_phase(f32x4 (&s)[4][2
     for (int qb = 0; qb < 2; ++qb) {
       const float mnew = grow[qb] ? mt[qb] : m[qb];
       alpha[qb] = __builtin_amdgcn_exp2f(m[qb] - mnew);  // 0 on the first tile, 1 where unchanged
-      lsum[qb] *= alpha[qb];
       m[qb] = mnew;
     }
   }
@@ -225,13 +241,6 @@ __device__ __attribute__((always_inline)) inline void valu_phase(f32x4 (&s)[4][2
       }
     }
   }
-  // Row sums of the bf16 P actually multiplied into V (two keys per v_dot2).
-#pragma unroll
-  for (int qb = 0; qb < 2; ++qb)
-#pragma unroll
-    for (int jj = 0; jj < 2; ++jj)
-#pragma unroll
-      for (int i = 0; i < 4; ++i) lsum[qb] = dot2_bf16_sum(pk[jj][qb][i], lsum[qb]);
   // The rare accumulator rescale comes last: the accumulator is not read in
   // this phase, and with the conditional update ahead of the exponentials the
   // register allocator moved all 64 accumulator registers on every tile
@@ -241,6 +250,8 @@ __device__ __attribute__((always_inline)) inline void valu_phase(f32x4 (&s)[4][2
     for (int qb = 0; qb < 2; ++qb)
 #pragma unroll
       for (int cb = 0; cb < CBLK; ++cb) acc[cb][qb] *= alpha[qb];
+#pragma unroll
+    for (int qb = 0; qb < 2; ++qb) lsv[qb] *= alpha[qb];
   }
 }
 
@@ -328,7 +339,7 @@ __global__ void __launch_bounds__(ATTN_THREADS, 2) attn_fwd_bf16_kernel(AttnArgs
 
   const float c = a.c_log2;
   float m[2] = {-INFINITY, -INFINITY};  // reference row max (log2 units) of both queries
-  float lsum[2] = {0.f, 0.f};           // this lane's partial row sums (its 16 keys of every tile)
+  f32x4 lsv[2] = {f32x4{}, f32x4{}};    // row sums (every entry), accumulated by MFMAs against ones
   f32x4 acc[CBLK][2];
 #pragma unroll
   for (int b = 0; b < CBLK; ++b) acc[b][0] = acc[b][1] = f32x4{};
@@ -377,15 +388,15 @@ __global__ void __launch_bounds__(ATTN_THREADS, 2) attn_fwd_bf16_kernel(AttnArgs
     // The MFMA phase runs at raised wave priority, so that the SIMD issues its
     // MFMAs and operand reads ahead of the partner wave's softmax.
     __builtin_amdgcn_s_setprio(1);
-    if constexpr (decltype(pv)::value) mfma_phase<D, true, true>(kc, vp, qreg, acc, s, pk, g, l16);
-    else mfma_phase<D, false, true>(kc, vp, qreg, acc, s, pk, g, l16);
+    if constexpr (decltype(pv)::value) mfma_phase<D, true, true>(kc, vp, qreg, acc, s, pk, lsv, g, l16);
+    else mfma_phase<D, false, true>(kc, vp, qreg, acc, s, pk, lsv, g, l16);
     wait_copies();
     __builtin_amdgcn_s_setprio(0);
     bar();
     copy_k(jt + 2, kn);
     copy_v(jt + 1, vn);
-    if (mask_last && jt == last) valu_phase<D, true>(s, acc, m, lsum, pk, c, key0 + KTILE * jt, L, g);
-    else valu_phase<D, false>(s, acc, m, lsum, pk, c, key0 + KTILE * jt, L, g);
+    if (mask_last && jt == last) valu_phase<D, true>(s, acc, m, lsv, pk, c, key0 + KTILE * jt, L, g);
+    else valu_phase<D, false>(s, acc, m, lsv, pk, c, key0 + KTILE * jt, L, g);
     bar();
   };
   using Yes = std::true_type;
@@ -411,17 +422,18 @@ __global__ void __launch_bounds__(ATTN_THREADS, 2) attn_fwd_bf16_kernel(AttnArgs
   if (j < nkt) key_tile(j++, Yes{}, kB, vA, kA, vC);
   // P.V of the last tile, V~^T(last) in vbuf[last % 3].
   switch (last % 3) {
-    case 0: mfma_phase<D, true, false>(kA, vA, qreg, acc, s, pk, g, l16); break;
-    case 1: mfma_phase<D, true, false>(kA, vB, qreg, acc, s, pk, g, l16); break;
-    default: mfma_phase<D, true, false>(kA, vC, qreg, acc, s, pk, g, l16); break;
+    case 0: mfma_phase<D, true, false>(kA, vA, qreg, acc, s, pk, lsv, g, l16); break;
+    case 1: mfma_phase<D, true, false>(kA, vB, qreg, acc, s, pk, lsv, g, l16); break;
+    default: mfma_phase<D, true, false>(kA, vC, qreg, acc, s, pk, lsv, g, l16); break;
   }
   __builtin_amdgcn_s_waitcnt(0xF70);  // vmcnt(0): no copy into LDS left in flight
   if (grp == 0) bar();
 
   // Epilogue: O = acc / l. acc[b][qb] holds channels 16 b + 4 g .. +3 of query
   // 16 qb + l16 of the wave.
+  float lsum[2];
 #pragma unroll
-  for (int qb = 0; qb < 2; ++qb) lsum[qb] = quad_sum(lsum[qb]);
+  for (int qb = 0; qb < 2; ++qb) lsum[qb] = lsv[qb][0];
   if (part >= 0) {
     // Piece of a split unit: unnormalized accumulator, reference max and row
     // sum into its slot, for the merge kernel.
