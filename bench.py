@@ -716,6 +716,39 @@ def mfma_context(iters: int = 40000, reps: int = 5):
     return res
 
 
+def coexec_probe():
+    """For context (flag --probe-coexec): how the VALU work of one wave of a
+    SIMD slows down while the other wave issues MFMAs (libmfprobe.so,
+    mf_probe_coexec; one workgroup of 8 waves per CU). Cycles per MFMA and per
+    VALU instruction from s_memtime stamps, each wave kind alone and both."""
+    import torch
+
+    lib = ctypes.CDLL(os.path.join(ROOT, "text_image_diffusion_varlen_amd", "libmfprobe.so"))
+    lib.mf_probe_coexec.argtypes = [ctypes.c_void_p, ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_int,
+                                    ctypes.c_int, ctypes.c_void_p]
+    blocks = torch.cuda.get_device_properties(0).multi_processor_count
+    out = torch.zeros(16 * blocks, dtype=torch.int64, device="cuda")
+    stream = torch.cuda.current_stream().cuda_stream
+    mfma_iters = 20000
+    kinds = {0: ("fma", 40000, 16), 1: ("exp2+mul", 8000, 32), 2: ("max+mul", 40000, 16)}
+    res = {"mfma_16x16x32_bf16_cycles_alone": None}
+    for vkind, (name, valu_iters, per_iter) in kinds.items():
+        for mode, tag in ((1, "mfma"), (2, "alone"), (3, "with_mfma")):
+            for _ in range(2):  # the second launch is the one kept
+                if lib.mf_probe_coexec(ctypes.c_void_p(out.data_ptr()), blocks, mode, vkind, mfma_iters, valu_iters,
+                                       ctypes.c_void_p(stream)):
+                    raise RuntimeError("mf_probe_coexec launch failed")
+                torch.cuda.synchronize()
+            t = out.view(blocks, 8, 2).cpu().numpy().astype(np.float64)
+            d = t[:, :, 1] - t[:, :, 0]
+            if mode & 1:
+                key = "mfma_16x16x32_bf16_cycles_" + ("alone" if mode == 1 else f"beside_{name}")
+                res[key] = round(float(np.median(d[:, :4])) / (mfma_iters * 8), 2)
+            if mode & 2:
+                res[f"{name}_cycles_per_instr_{tag}"] = round(float(np.median(d[:, 4:])) / (valu_iters * per_iter), 2)
+    return res
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -732,6 +765,8 @@ def main():
     ap.add_argument("--no-pack", action="store_true", help="skip the joint-layout pack / unpack measurement")
     ap.add_argument("--no-mixed", action="store_true",
                     help="with the default 1024sq workload, skip the second (mixed-aspect) forward record")
+    ap.add_argument("--probe-coexec", action="store_true",
+                    help="only run the MFMA / VALU co-execution probe (libmfprobe.so) and print its rates")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="only run a plain device copy of 1 GiB (HBM-counter calibration for profiling)")
     args = ap.parse_args()
@@ -748,6 +783,9 @@ def main():
         print("bench.py needs a GPU", file=sys.stderr)
         sys.exit(1)
     torch.cuda.set_device(0)
+    if args.probe_coexec:
+        print(json.dumps({"coexec_probe": coexec_probe()}), flush=True)
+        return
     if args.calibrate_copy:
         n = 1 << 30
         src = torch.ones(n, dtype=torch.uint8, device="cuda")
