@@ -18,10 +18,13 @@
 //       read feeds the MFMAs of both blocks. In this orientation a lane holds
 //       16 of the 64 scores of one query and the other 48 sit in lanes l ^ 16,
 //       l ^ 32 and l ^ 48, so row max / sum need two lane swaps.
-//   online softmax in the exp2 domain (scale * log2(e) folded into one FMA),
-//       a reference max that moves only when a tile exceeds it by 2^8 (the
-//       accumulator rescale is skipped otherwise), row sums of the bf16 P
-//       formed by MFMAs against an all-ones operand;
+//   online softmax in the exp2 domain: the queries carry scale * log2(e)
+//       (multiplied in as they are rotated) and the score accumulators start
+//       from -m, the reference max, so the MFMAs produce s c - m and P is
+//       exp2 of the accumulator with no per-score VALU arithmetic; the
+//       reference moves only when a tile exceeds it by 2^8 (the accumulator
+//       rescale is skipped otherwise); row sums of the bf16 P formed by MFMAs
+//       against an all-ones operand;
 //   O^T (d x 16 queries per block) += V~^T tile (LDS) x P^T (registers, bf16 RNE).
 // Per key tile a wave has an MFMA phase (P.V of the previous tile, scores of
 // this tile, LDS operands read ahead) and a VALU phase (softmax). The two
@@ -107,7 +110,8 @@ constexpr int PF_DEPTH = 6;
 
 // MFMA phase of tile j for one wave's 32 query rows (two blocks of 16): with
 // PV, O^T += V~^T P^T for tile j-1 (P^T in pk, V~^T tile vt), then, with SC,
-// S^T = K~ Q~^T for tile j (K~ tile kt) into s. Lane (g, l16) = (lane / 16,
+// S^T = K~ Q~^T c - m for tile j (K~ tile kt; negm = -m as the accumulators'
+// initial value) into s. Lane (g, l16) = (lane / 16,
 // lane % 16) holds, for query 16 qb + l16, the scores of keys 16 kb + 4 g + i
 // (i = 0..3) in s[kb][qb] and the output channels 16 cb + 4 g + i in
 // acc[cb][qb]. Each 16-byte operand read from LDS feeds the MFMAs of both
@@ -120,8 +124,8 @@ template <int D, bool PV, bool SC>
 __device__ __attribute__((always_inline)) inline void mfma_phase(const u32x4* kt, const u32x4* vt,
                                                                  const bf16x8 (&qreg)[2][D / 32],
                                                                  f32x4 (&acc)[D / 16][2], f32x4 (&s)[4][2],
-                                                                 const u32x4 (&pk)[2][2], f32x4 (&lsv)[2], int g,
-                                                                 int l16) {
+                                                                 const u32x4 (&pk)[2][2], f32x4 (&lsv)[2],
+                                                                 const f32x4 (&negm)[2], int g, int l16) {
   constexpr int CBLK = Bf16Tile<D>::CBLK;
   constexpr int NV = PV ? 2 * CBLK : 0;              // V~^T operands: key half jj, channel block cb
   constexpr int NK = SC ? 4 * Bf16Tile<D>::KSTEPS : 0;  // K~ operands: k-step ks, key block kb
@@ -141,7 +145,10 @@ __device__ __attribute__((always_inline)) inline void mfma_phase(const u32x4* kt
   for (int r = 0; r < PF_DEPTH && r < N; ++r) op[r] = operand(r);
   if constexpr (SC) {
 #pragma unroll
-    for (int kb = 0; kb < 4; ++kb) s[kb][0] = s[kb][1] = f32x4{};
+    for (int kb = 0; kb < 4; ++kb) {
+      s[kb][0] = negm[0];
+      s[kb][1] = negm[1];
+    }
   }
 #pragma unroll
   for (int i = 0; i < N; ++i) {
@@ -184,7 +191,8 @@ __device__ __attribute__((always_inline)) inline void mfma_phase(const u32x4* kt
 template <int D, bool MASKED>
 __device__ __attribute__((always_inline)) inline void valu_phase(f32x4 (&s)[4][2], f32x4 (&acc)[D / 16][2],
                                                                  float (&m)[2], f32x4 (&lsv)[2], u32x4 (&pk)[2][2],
-                                                                 float c, int kbase_key, int L, int g) {
+                                                                 f32x4 (&negm)[2], bool first, int kbase_key, int L,
+                                                                 int g) {
   constexpr int CBLK = Bf16Tile<D>::CBLK;
   constexpr float REF_SLACK = 8.0f;
   if constexpr (MASKED) {
@@ -195,8 +203,31 @@ __device__ __attribute__((always_inline)) inline void valu_phase(f32x4 (&s)[4][2
       for (int i = 0; i < 4; ++i)
         if (kb0 + 16 * kb + i >= L) s[kb][0][i] = s[kb][1][i] = -INFINITY;
   }
-  // Row max: this lane's 16 keys of each query, then the other 48 from the
-  // lanes of the same query.
+  // P with the current reference: the score accumulators started from -m
+  // and the queries carry the scale, so they hold s c - m. Only on a tile
+  // where the reference moves is P formed again, shifted by the move.
+  auto make_p = [&](float d0, float d1, auto shift) __attribute__((always_inline)) {
+#pragma unroll
+    for (int qb = 0; qb < 2; ++qb) {
+      const float d = qb ? d1 : d0;
+#pragma unroll
+      for (int jj = 0; jj < 2; ++jj) {
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+          f32x4 x = s[2 * jj + h][qb];
+          if constexpr (decltype(shift)::value) x -= d;
+          pk[jj][qb][2 * h] = pack_bf16x2(__builtin_amdgcn_exp2f(x[0]), __builtin_amdgcn_exp2f(x[1]));
+          pk[jj][qb][2 * h + 1] = pack_bf16x2(__builtin_amdgcn_exp2f(x[2]), __builtin_amdgcn_exp2f(x[3]));
+        }
+      }
+    }
+  };
+  make_p(0.f, 0.f, std::false_type{});
+  // Row max of the tile relative to the reference: this lane's 16 keys of each
+  // query, then the other 48 from the lanes of the same query. The reference
+  // only moves when a tile exceeds it by more than REF_SLACK (and on the first
+  // tile), so p <= 2^REF_SLACK and the accumulator is rescaled only on those
+  // tiles; numerator and denominator share m.
   float mt[2];
   bool grow[2];
 #pragma unroll
@@ -206,40 +237,21 @@ __device__ __attribute__((always_inline)) inline void valu_phase(f32x4 (&s)[4][2
     for (int kb = 0; kb < 4; ++kb)
 #pragma unroll
       for (int i = 0; i < 4; ++i) mx = __builtin_elementwise_maximum(mx, s[kb][qb][i]);
-    mt[qb] = quad_max(mx) * c;
-    // The reference max only moves when a tile's max exceeds it by more than
-    // REF_SLACK, so p = exp2(s*c - m) <= 2^REF_SLACK and the accumulator is
-    // rescaled only on those tiles; numerator and denominator share m.
-    grow[qb] = mt[qb] > m[qb] + REF_SLACK;  // always true on the first tile (m = -inf)
+    mt[qb] = quad_max(mx);
+    grow[qb] = first || mt[qb] > REF_SLACK;
   }
-  // Reference max and the factor alpha of the accumulator and the row sums,
-  // which are rescaled at the end of the phase (see there).
   const bool any_grow = __any(grow[0] || grow[1]);
   float alpha[2] = {1.f, 1.f};
   if (any_grow) {
+    float d[2];
 #pragma unroll
     for (int qb = 0; qb < 2; ++qb) {
-      const float mnew = grow[qb] ? mt[qb] : m[qb];
-      alpha[qb] = __builtin_amdgcn_exp2f(m[qb] - mnew);  // 0 on the first tile, 1 where unchanged
-      m[qb] = mnew;
+      d[qb] = grow[qb] ? mt[qb] : 0.f;
+      alpha[qb] = first ? 0.f : __builtin_amdgcn_exp2f(-d[qb]);  // accumulator and sums are zero on the first tile
+      m[qb] += d[qb];
+      negm[qb] = f32x4{-m[qb], -m[qb], -m[qb], -m[qb]};
     }
-  }
-#pragma unroll
-  for (int qb = 0; qb < 2; ++qb) {
-    const float nm = -m[qb];
-#pragma unroll
-    for (int jj = 0; jj < 2; ++jj) {
-#pragma unroll
-      for (int h = 0; h < 2; ++h) {
-        const f32x4 x = s[2 * jj + h][qb];
-        const float p0 = __builtin_amdgcn_exp2f(__builtin_fmaf(x[0], c, nm));
-        const float p1 = __builtin_amdgcn_exp2f(__builtin_fmaf(x[1], c, nm));
-        const float p2 = __builtin_amdgcn_exp2f(__builtin_fmaf(x[2], c, nm));
-        const float p3 = __builtin_amdgcn_exp2f(__builtin_fmaf(x[3], c, nm));
-        pk[jj][qb][2 * h] = pack_bf16x2(p0, p1);
-        pk[jj][qb][2 * h + 1] = pack_bf16x2(p2, p3);
-      }
-    }
+    make_p(d[0], d[1], std::true_type{});
   }
   // The rare accumulator rescale comes last: the accumulator is not read in
   // this phase, and with the conditional update ahead of the exponentials the
@@ -302,8 +314,9 @@ __global__ void __launch_bounds__(ATTN_THREADS, 2) attn_fwd_bf16_kernel(AttnArgs
   // Rotated query rows of this lane as the B operand of S^T = K~ Q~^T: for
   // query block qb the lane holds query 16 qb + l16 of the wave, channels
   // 32 ks + 8 g .. +7 for every k-step ks. The rows are read from the caller's
-  // q and rotated here (once per workgroup); rows past the sample's end read
-  // its last token and are never stored.
+  // q, rotated and multiplied by scale * log2(e) here (once per workgroup,
+  // rounded to bf16 once); rows past the sample's end read its last token and
+  // are never stored.
   bf16x8 qreg[2][KSTEPS];
 #pragma unroll
   for (int qb = 0; qb < 2; ++qb) {
@@ -317,9 +330,11 @@ __global__ void __launch_bounds__(ATTN_THREADS, 2) attn_fwd_bf16_kernel(AttnArgs
       const Chunk<uint16_t> raw = *reinterpret_cast<const Chunk<uint16_t>*>(qrow + 32 * ks);
       if constexpr (R3)
         qreg[qb][ks] =
-            __builtin_bit_cast(bf16x8, rotate_chunk3<uint16_t, D>(raw, 32 * ks + 8 * g, row, col, frame, a.r3));
+            __builtin_bit_cast(bf16x8, rotate_chunk3<uint16_t, D, true>(raw, 32 * ks + 8 * g, row, col, frame, a.r3,
+                                                                        a.c_log2));
       else
-        qreg[qb][ks] = __builtin_bit_cast(bf16x8, rotate_chunk<uint16_t, D>(raw, 32 * ks + 8 * g, row, col, a.cs));
+        qreg[qb][ks] =
+            __builtin_bit_cast(bf16x8, rotate_chunk<uint16_t, D, true>(raw, 32 * ks + 8 * g, row, col, a.cs, a.c_log2));
     }
   }
   // The tile copies share the in-order vector-memory counter with these
@@ -337,8 +352,8 @@ __global__ void __launch_bounds__(ATTN_THREADS, 2) attn_fwd_bf16_kernel(AttnArgs
   const int key0 = KTILE * kt0;
   const bool mask_last = kt1 == nkt_all;
 
-  const float c = a.c_log2;
-  float m[2] = {-INFINITY, -INFINITY};  // reference row max (log2 units) of both queries
+  float m[2] = {0.f, 0.f};              // reference row max (log2 units) of both queries
+  f32x4 negm[2] = {f32x4{}, f32x4{}};   // -m, the score accumulators' initial value
   f32x4 lsv[2] = {f32x4{}, f32x4{}};    // row sums (every entry), accumulated by MFMAs against ones
   f32x4 acc[CBLK][2];
 #pragma unroll
@@ -388,15 +403,15 @@ __global__ void __launch_bounds__(ATTN_THREADS, 2) attn_fwd_bf16_kernel(AttnArgs
     // The MFMA phase runs at raised wave priority, so that the SIMD issues its
     // MFMAs and operand reads ahead of the partner wave's softmax.
     __builtin_amdgcn_s_setprio(1);
-    if constexpr (decltype(pv)::value) mfma_phase<D, true, true>(kc, vp, qreg, acc, s, pk, lsv, g, l16);
-    else mfma_phase<D, false, true>(kc, vp, qreg, acc, s, pk, lsv, g, l16);
+    if constexpr (decltype(pv)::value) mfma_phase<D, true, true>(kc, vp, qreg, acc, s, pk, lsv, negm, g, l16);
+    else mfma_phase<D, false, true>(kc, vp, qreg, acc, s, pk, lsv, negm, g, l16);
     wait_copies();
     __builtin_amdgcn_s_setprio(0);
     bar();
     copy_k(jt + 2, kn);
     copy_v(jt + 1, vn);
-    if (mask_last && jt == last) valu_phase<D, true>(s, acc, m, lsv, pk, c, key0 + KTILE * jt, L, g);
-    else valu_phase<D, false>(s, acc, m, lsv, pk, c, key0 + KTILE * jt, L, g);
+    if (mask_last && jt == last) valu_phase<D, true>(s, acc, m, lsv, pk, negm, jt == 0, key0 + KTILE * jt, L, g);
+    else valu_phase<D, false>(s, acc, m, lsv, pk, negm, jt == 0, key0 + KTILE * jt, L, g);
     bar();
   };
   using Yes = std::true_type;
@@ -422,9 +437,9 @@ __global__ void __launch_bounds__(ATTN_THREADS, 2) attn_fwd_bf16_kernel(AttnArgs
   if (j < nkt) key_tile(j++, Yes{}, kB, vA, kA, vC);
   // P.V of the last tile, V~^T(last) in vbuf[last % 3].
   switch (last % 3) {
-    case 0: mfma_phase<D, true, false>(kA, vA, qreg, acc, s, pk, lsv, g, l16); break;
-    case 1: mfma_phase<D, true, false>(kA, vB, qreg, acc, s, pk, lsv, g, l16); break;
-    default: mfma_phase<D, true, false>(kA, vC, qreg, acc, s, pk, lsv, g, l16); break;
+    case 0: mfma_phase<D, true, false>(kA, vA, qreg, acc, s, pk, lsv, negm, g, l16); break;
+    case 1: mfma_phase<D, true, false>(kA, vB, qreg, acc, s, pk, lsv, negm, g, l16); break;
+    default: mfma_phase<D, true, false>(kA, vC, qreg, acc, s, pk, lsv, negm, g, l16); break;
   }
   __builtin_amdgcn_s_waitcnt(0xF70);  // vmcnt(0): no copy into LDS left in flight
   if (grp == 0) bar();

@@ -31,10 +31,11 @@ __device__ inline float2 rotate_pair(float x0, float x1, float c, float s) {
   return make_float2(__builtin_fmaf(x0, c, -(x1 * s)), __builtin_fmaf(x0, s, x1 * c));
 }
 
-// Rotates one 16-byte chunk (channels d0 .. d0+E-1, E even) of a row at (row, col).
-template <typename T, int D>
+// Rotates one 16-byte chunk (channels d0 .. d0+E-1, E even) of a row at (row, col);
+// with SCALED, each rotated value is also multiplied by `scale` before it is stored.
+template <typename T, int D, bool SCALED = false>
 __device__ inline Chunk<T> rotate_chunk(const Chunk<T>& in, int d0, int32_t row, int32_t col,
-                                        const float2* __restrict__ cs) {
+                                        const float2* __restrict__ cs, float scale = 1.f) {
   constexpr int E = Elem<T>::PER_CHUNK;
   Chunk<T> out;
 #pragma unroll
@@ -47,8 +48,8 @@ __device__ inline Chunk<T> rotate_chunk(const Chunk<T>& in, int d0, int32_t row,
     const float x0 = Elem<T>::load(in.v[2 * pp]);
     const float x1 = Elem<T>::load(in.v[2 * pp + 1]);
     const float2 y = rotate_pair(x0, x1, r.x, r.y);
-    out.v[2 * pp] = Elem<T>::store(y.x);
-    out.v[2 * pp + 1] = Elem<T>::store(y.y);
+    out.v[2 * pp] = Elem<T>::store(SCALED ? y.x * scale : y.x);
+    out.v[2 * pp + 1] = Elem<T>::store(SCALED ? y.y * scale : y.y);
   }
   return out;
 }
@@ -69,9 +70,9 @@ __device__ inline float2 rope3_cs(const Rope3& r, int D, int k, int32_t row, int
   return r.cs[p * (D / 2) + k];
 }
 
-template <typename T, int D>
+template <typename T, int D, bool SCALED = false>
 __device__ inline Chunk<T> rotate_chunk3(const Chunk<T>& in, int d0, int32_t row, int32_t col, int32_t frame,
-                                         const Rope3& r) {
+                                         const Rope3& r, float scale = 1.f) {
   constexpr int E = Elem<T>::PER_CHUNK;
   Chunk<T> out;
 #pragma unroll
@@ -80,8 +81,8 @@ __device__ inline Chunk<T> rotate_chunk3(const Chunk<T>& in, int d0, int32_t row
     const float x0 = Elem<T>::load(in.v[2 * pp]);
     const float x1 = Elem<T>::load(in.v[2 * pp + 1]);
     const float2 y = rotate_pair(x0, x1, c.x, c.y);
-    out.v[2 * pp] = Elem<T>::store(y.x);
-    out.v[2 * pp + 1] = Elem<T>::store(y.y);
+    out.v[2 * pp] = Elem<T>::store(SCALED ? y.x * scale : y.x);
+    out.v[2 * pp + 1] = Elem<T>::store(SCALED ? y.y * scale : y.y);
   }
   return out;
 }
