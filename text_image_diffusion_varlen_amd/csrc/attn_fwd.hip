@@ -223,30 +223,32 @@ __device__ __attribute__((always_inline)) inline void valu_phase(f32x4 (&s)[4][2
     }
   };
   make_p(0.f, 0.f, std::false_type{});
-  // Row max of the tile relative to the reference: this lane's 16 keys of each
-  // query, then the other 48 from the lanes of the same query. The reference
-  // only moves when a tile exceeds it by more than REF_SLACK (and on the first
-  // tile), so p <= 2^REF_SLACK and the accumulator is rescaled only on those
-  // tiles; numerator and denominator share m.
-  float mt[2];
-  bool grow[2];
+  // Whether the reference moves: it only does when a tile exceeds it by more
+  // than REF_SLACK (and on the first tile), so p <= 2^REF_SLACK and the
+  // accumulator is rescaled only on those tiles; numerator and denominator
+  // share m. The common case needs only this lane's own 32 scores (any one
+  // above REF_SLACK); the row maxima over the four lanes of each query are
+  // formed only when some score of the wave is above it.
+  float mx = __builtin_elementwise_maximum(s[0][0][0], s[0][1][0]);
 #pragma unroll
-  for (int qb = 0; qb < 2; ++qb) {
-    float mx = s[0][qb][0];
+  for (int kb = 0; kb < 4; ++kb)
 #pragma unroll
-    for (int kb = 0; kb < 4; ++kb)
-#pragma unroll
-      for (int i = 0; i < 4; ++i) mx = __builtin_elementwise_maximum(mx, s[kb][qb][i]);
-    mt[qb] = quad_max(mx);
-    grow[qb] = first || mt[qb] > REF_SLACK;
-  }
-  const bool any_grow = __any(grow[0] || grow[1]);
+    for (int i = 0; i < 4; ++i)
+      mx = __builtin_elementwise_maximum(__builtin_elementwise_maximum(mx, s[kb][0][i]), s[kb][1][i]);
+  const bool any_grow = __any(first || mx > REF_SLACK);
   float alpha[2] = {1.f, 1.f};
   if (any_grow) {
     float d[2];
 #pragma unroll
     for (int qb = 0; qb < 2; ++qb) {
-      d[qb] = grow[qb] ? mt[qb] : 0.f;
+      float mq = s[0][qb][0];
+#pragma unroll
+      for (int kb = 0; kb < 4; ++kb)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) mq = __builtin_elementwise_maximum(mq, s[kb][qb][i]);
+      const float mt = quad_max(mq);
+      const bool grow = first || mt > REF_SLACK;
+      d[qb] = grow ? mt : 0.f;
       alpha[qb] = first ? 0.f : __builtin_amdgcn_exp2f(-d[qb]);  // accumulator and sums are zero on the first tile
       m[qb] += d[qb];
       negm[qb] = f32x4{-m[qb], -m[qb], -m[qb], -m[qb]};
