@@ -150,6 +150,22 @@ __device__ __attribute__((always_inline)) inline void mfma_phase(const u32x4* kt
       s[kb][1] = negm[1];
     }
   }
+  // Row sums of tile j-1's bf16 P (the values just multiplied into V~^T): the
+  // same MFMA with an all-ones A operand sums P^T over the 32 keys of a k-step
+  // into every entry of lsv[qb]. Four MFMAs per tile take the 16 v_dot2 of
+  // per-lane sums out of the softmax phase, whose exponentials run slower
+  // while the SIMD partner issues MFMAs. They read no LDS operand, so they go
+  // first, while the first operand reads are in flight.
+  if constexpr (PV) {
+    typedef __bf16 bf16x8v __attribute__((ext_vector_type(8)));
+    const bf16x8v ones = {(__bf16)1.f, (__bf16)1.f, (__bf16)1.f, (__bf16)1.f,
+                          (__bf16)1.f, (__bf16)1.f, (__bf16)1.f, (__bf16)1.f};
+#pragma unroll
+    for (int jj = 0; jj < 2; ++jj) {
+      lsv[0] = mfma16(__builtin_bit_cast(bf16x8, ones), __builtin_bit_cast(bf16x8, pk[jj][0]), lsv[0]);
+      lsv[1] = mfma16(__builtin_bit_cast(bf16x8, ones), __builtin_bit_cast(bf16x8, pk[jj][1]), lsv[1]);
+    }
+  }
 #pragma unroll
   for (int i = 0; i < N; ++i) {
     if (i + PF_DEPTH < N) op[i + PF_DEPTH] = operand(i + PF_DEPTH);
@@ -164,22 +180,6 @@ __device__ __attribute__((always_inline)) inline void mfma_phase(const u32x4* kt
       s[kb][1] = mfma16(op[i], qreg[1][ks], s[kb][1]);
     }
     __builtin_amdgcn_sched_barrier(0);
-  }
-  // Row sums of tile j-1's bf16 P (the values just multiplied into V~^T): the
-  // same MFMA with an all-ones A operand sums P^T over the 32 keys of a k-step
-  // into every entry of lsv[qb]. Four MFMAs per tile take the 16 v_dot2 of
-  // per-lane sums out of the softmax phase, whose VALU work (its exponentials
-  // above all, which run slower while the SIMD partner issues MFMAs) is the
-  // longer side of the two phases.
-  if constexpr (PV) {
-    typedef __bf16 bf16x8v __attribute__((ext_vector_type(8)));
-    const bf16x8v ones = {(__bf16)1.f, (__bf16)1.f, (__bf16)1.f, (__bf16)1.f,
-                          (__bf16)1.f, (__bf16)1.f, (__bf16)1.f, (__bf16)1.f};
-#pragma unroll
-    for (int jj = 0; jj < 2; ++jj) {
-      lsv[0] = mfma16(__builtin_bit_cast(bf16x8, ones), __builtin_bit_cast(bf16x8, pk[jj][0]), lsv[0]);
-      lsv[1] = mfma16(__builtin_bit_cast(bf16x8, ones), __builtin_bit_cast(bf16x8, pk[jj][1]), lsv[1]);
-    }
   }
 }
 
